@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""MoE-layer forward throughput on one MI355X.
+
+One step = the whole hot path on one batch: router + top-k + dispatch
+(moe_route, or moe_route_forced when the workload replays recorded choices)
+then the expert FFNs and the combine (moe_forward).  Inputs and weights are
+resident in HBM before timing starts; the expert weights rotate over several
+device copies so every step streams them from HBM rather than from the 256 MB
+last-level cache.
+
+Prints one JSON line.  `value` is tokens/s of the whole step; `roofline` is
+for the dominant kernel (the grouped gate/up projection), from its average
+duration measured with HIP events on the stream it runs on; `cpu_baseline` is
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix
+METRIC = "MoE-layer tokens/s (decode T=32, prefill T=2048); % HBM BW / % FP8 MFMA peak"
+
+DESCRIPTION = {
+    "decode_t32": "decode batch, T=32 tokens, d=2048, E=384 experts, top-6, SwiGLU F=640 + shared F=640, "
+                  "FP8 E4M3 128x128-block-scaled expert weights, bf16 activations, fp32 router, free routing",
+    "prefill_t2048": "prefill chunk, T=2048 tokens, same layer, routing forced from ids recorded by a free pass",
+    "skew_t8192": "skewed prefill, T=8192 tokens, same layer, Zipf(1.1) selection bias, free routing",
+    "ties_t256": "near-tie batch, T=256, integer activations, 1/64-grid router, free routing",
+    "ties_t256_bf16w": "near-tie batch, T=256, bf16 expert weights, free routing",
+}
+FORCED = {"prefill_t2048"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_t32", choices=sorted(DESCRIPTION))
+    ap.add_argument("--rotate", type=int, default=4, help="device copies of the expert weights")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0: skip)")
+    ap.add_argument("--also", default="prefill_t2048", help="extra workloads timed after the main one (comma list)")
+    return ap.parse_args()
+
+
+def algorithmic(s, counts):
+    """Algorithmic bytes and flops (what the method must move / compute)."""
+    bw = {"fp8": 1, "bf16": 2, "f32": 4}[s.w]
+    ba = {"bf16": 2, "f32": 4}[s.act]
+    U = int((counts > 0).sum())
+    P = s.T * s.k
+    fp8 = s.w == "fp8"
+    nb = lambda r, c: (r // 128) * (c // 128) * 4 if fp8 else 0  # block-scale bytes
+    gu_w = U * 2 * (s.F * s.d * bw + nb(s.F, s.d)) + 2 * (s.Fs * s.d * bw + nb(s.Fs, s.d))
+    dn_w = U * (s.d * s.F * bw + nb(s.d, s.F)) + (s.d * s.Fs * bw + nb(s.d, s.Fs))
+    act_in = s.T * s.d + s.T * (s.d // 128) * 4 if fp8 else s.T * s.d * ba
+    h_rows = P + s.T
+    h_bytes = h_rows * s.F * (1 if fp8 else 2) + (h_rows * (s.F // 128) * 4 if fp8 else 0)
+    return {
+        "U": U,
+        "gateup_bytes": gu_w + act_in + h_bytes,
+        "down_bytes": dn_w + h_bytes + h_rows * s.d * 4,
+        "B_alg": gu_w + dn_w + 4 * s.E * s.d + 2 * s.T * s.d * ba,
+        "F_mm": 2 * (P + s.T) * 3 * s.d * s.F,
+        "F_router": 2 * s.T * s.d * s.E,
+    }
+
+
+def run_workload(name, steps, warmup, rotate):
+    import torch
+    from mixture_experts_moe_amd import moe, synth
+
+    inp = synth.make_inputs(name)
+    s = inp["shape"]
+    dev = synth.to_device(inp, "cuda:0")
+    shape = moe.shape_of(s)
+    wkeys = ("w_gate", "w_up", "w_down")
+    copies = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, rotate - 1))]
+    r = moe.alloc_routing(shape, "cuda:0")
+    ws = moe.alloc_workspace(shape, "cuda:0")
+    y = torch.empty((s.T, s.d), dtype=torch.bfloat16 if s.act == "bf16" else torch.float32, device="cuda:0")
+    forced = None
+    if name in FORCED:  # record the choices of a free routing pass, then replay them
+        moe.route(shape, dev, dev["x"], r, ws)
+        torch.cuda.synchronize()
+        forced = r.topk_idx.clone()
+
+    st = torch.cuda.current_stream()
+    bound = [moe.Bound(shape, w, w["x"], r, y, ws, forced_idx=forced, stream=st) for w in copies]
+    stages = (moe.STAGE_PREPARE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
+    n_ev = 6
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
+
+    def step(i, ev=None):
+        b = bound[i % len(bound)]
+        if ev:
+            ev[0].record(st)
+        b.route()
+        if ev:
+            ev[1].record(st)
+        for j, stage in enumerate(stages):
+            b.forward(stage)
+            if ev:
+                ev[2 + j].record(st)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    names = ("route", "prepare", "gate_up", "down", "combine")
+    stage_us = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) * 1e3
+                for j, n in enumerate(names)}
+    counts = r.counts.cpu().numpy()
+    assert r.status.item() == 0
+    return s, wall, stage_us, algorithmic(s, counts), counts
+
+
+def cpu_baseline(name, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of the workload."""
+    from mixture_experts_moe_amd import synth
+    from oracle import moe_oracle as O
+
+    inp = synth.make_inputs(name)
+    s = inp["shape"]
+    L = O.Layer(inp)
+    n_tok = min(s.T, 32)
+    tok = np.linspace(0, s.T - 1, n_tok).astype(np.int32)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        _, _, idx, w = O.route(L, tok)
+        O.forward(L, idx, w, tok)
+        done += n_tok
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done // n_tok} passes of route + forward over {n_tok} of the workload's {s.T} tokens "
+                      f"({el:.1f} s, single-threaded C++ oracle, double-accumulated dot products)"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    s, wall, st_us, alg, counts = run_workload(a.workload, a.steps, a.warmup, a.rotate)
+    t_step = wall
+    gu_s = st_us["gate_up"] * 1e-6
+    achieved = alg["gateup_bytes"] / gu_s / 1e9
+    out = {
+        "metric": METRIC, "value": s.T / t_step, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3" if s.w == "fp8" else s.w, "data": "synthetic",
+        "config": {"workload": f"{a.workload}: {DESCRIPTION[a.workload]}", "T": s.T, "d_model": s.d,
+                   "n_experts": s.E, "top_k": s.k, "d_ffn": s.F, "d_ffn_shared": s.Fs,
+                   "weight_copies_rotated": a.rotate},
+        "roofline": {"bound": "hbm", "kernel": "gateup_mfma_kernel (grouped gate/up + SwiGLU + h quantisation)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": st_us["gate_up"]},
+        "stage_us": st_us,
+        "step_roofline": {"B_alg_bytes": alg["B_alg"], "distinct_experts": alg["U"],
+                          "hbm_frac": alg["B_alg"] / t_step / (HBM_PEAK_GBS * 1e9),
+                          "fp8_mfma_frac": alg["F_mm"] / t_step / (FP8_PEAK_TFLOPS * 1e12)},
+    }
+    extra = {}
+    for name in [w for w in a.also.split(",") if w and w != a.workload]:
+        s2, wall2, st2, alg2, counts2 = run_workload(name, max(10, a.steps // 4), max(3, a.warmup // 4), a.rotate)
+        extra[name] = {"tokens_per_s": s2.T / wall2, "ms_per_step": wall2 * 1e3, "stage_us": st2,
+                       "gateup_GBs": alg2["gateup_bytes"] / (st2["gate_up"] * 1e-6) / 1e9,
+                       "hbm_frac": alg2["B_alg"] / wall2 / (HBM_PEAK_GBS * 1e9),
+                       "fp8_mfma_frac": alg2["F_mm"] / wall2 / (FP8_PEAK_TFLOPS * 1e12),
+                       "max_over_mean_expert_load": float(counts2.max() / max(1e-9, counts2.mean()))}
+    if extra:
+        out["also"] = extra
+    if a.cpu_seconds > 0:
+        out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,180 @@
+/*
+ * moe.h - C ABI of the MI355X (gfx950) mixture-of-experts layer forward pass.
+ *
+ * One layer: a float32 router scores every expert for every token; each token
+ * goes to its top-k experts (free routing, selection by logit plus an optional
+ * per-expert selection bias, lowest expert index on ties) or to experts the
+ * caller recorded earlier (forced routing); the routed experts and one shared
+ * expert run a SwiGLU FFN; a fixed-order weighted sum combines their outputs.
+ *
+ * Sources, cited by page title and section:
+ *   [port]  "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No."
+ *           (localfirstai.eu, 5 October 2026)
+ *   [bench] "We Stopped the Kolibri Benchmark Before Scoring One Answer"
+ *           (localfirstai.eu, 9 October 2026)
+ *   [cache] "Kolibri-1 CPU dequant cache" (vllm.cpp pull request 3488)
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
+ *     row-major, densely packed.  The caller allocates and owns every buffer,
+ *     including the workspace; the library never allocates or frees memory and
+ *     keeps no state between calls (calls are reentrant).
+ *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the default
+ *     stream) and return without synchronising.  No device-to-host copy is made.
+ *   - Errors the host can detect return a negative moe_status and enqueue
+ *     nothing.  A failed kernel launch returns MOE_ERR_HIP.  Errors only the
+ *     device can see (invalid forced expert ids) are written to the device
+ *     status word `moe_routing.status`, which the caller reads after its own
+ *     synchronisation.
+ *   - T == 0 returns MOE_OK and enqueues nothing.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size */
+  MOE_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape or dtype combination */
+  MOE_ERR_WORKSPACE = -3,    /* ws_bytes below moe_workspace_bytes() */
+  MOE_ERR_HIP = -4,          /* a HIP launch failed */
+  MOE_ERR_FORCED_INDEX = -5  /* (device status) a forced expert id was outside [0, E) */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,           /* float32 */
+  MOE_BF16 = 1,          /* bfloat16 */
+  MOE_FP8E4M3_B128 = 2   /* OCP FP8 E4M3 codes, value = decode(code) * scale of its
+                            128 x 128 block (fp32 scales); weights only */
+} moe_dtype;
+
+/* Supported (act_dtype, w_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8E4M3_B128).
+ * Limits: 1 <= top_k <= 8, top_k <= n_experts <= 512, d_model and d_ffn multiples
+ * of 128 with d_model <= 8192 and d_ffn <= 4096, d_ffn_shared 0 (no shared expert)
+ * or a multiple of 128 <= 4096, T * top_k < 2^31. */
+typedef struct {
+  int32_t T;             /* tokens in this call */
+  int32_t d_model;       /* d */
+  int32_t n_experts;     /* E (routed experts) */
+  int32_t top_k;         /* k */
+  int32_t d_ffn;         /* F, routed expert FFN width */
+  int32_t d_ffn_shared;  /* Fs, shared expert FFN width; 0 = no shared expert */
+  int32_t act_dtype;     /* moe_dtype of x and y: MOE_F32 or MOE_BF16 */
+  int32_t w_dtype;       /* moe_dtype of the expert weights */
+} moe_shape;
+
+/* Layer weights.  Expert matrices are (out, in) row-major and stacked by expert.
+ * Scales are required for MOE_FP8E4M3_B128 and ignored otherwise.
+ *   [port] "The gate": a router scores the experts for every token and a shared
+ *   expert serves every token; part 1 of "Taking it apart": selection uses the
+ *   router score plus a per-expert selection bias; part 3: the router runs in
+ *   float32.  [cache], first paragraph: the expert weights are FP8 and must be
+ *   decoded for compute. */
+typedef struct {
+  const float *w_router;  /* [E, d] fp32 */
+  const float *sel_bias;  /* [E] fp32, or NULL; enters expert selection only */
+  const void *w_gate;     /* [E, F, d] */
+  const void *w_up;       /* [E, F, d] */
+  const void *w_down;     /* [E, d, F] */
+  const float *s_gate;    /* [E, F/128, d/128] block scales */
+  const float *s_up;      /* [E, F/128, d/128] */
+  const float *s_down;    /* [E, d/128, F/128] */
+  const void *sh_gate;    /* shared expert [Fs, d] (ignored when Fs == 0) */
+  const void *sh_up;      /* [Fs, d] */
+  const void *sh_down;    /* [d, Fs] */
+  const float *ss_gate;   /* [Fs/128, d/128] */
+  const float *ss_up;     /* [Fs/128, d/128] */
+  const float *ss_down;   /* [d/128, Fs/128] */
+} moe_weights;
+
+/* Routing results (written by moe_route / moe_route_forced, read by moe_forward).
+ * Pairs are numbered p = t * k + j (token t, slot j). */
+typedef struct {
+  float *logits;       /* [T, E] fp32 router logits, or NULL (then not written) */
+  int32_t *topk_idx;   /* [T, k] expert ids; free: descending selection score;
+                          forced: the caller's order; -1 marks an invalid forced id */
+  float *topk_w;       /* [T, k] routing weights: softmax over the chosen experts'
+                          (unbiased) logits; 0 for an invalid slot */
+  int32_t *counts;     /* [E] pairs per expert */
+  int32_t *offsets;    /* [E + 1] exclusive prefix sum of counts */
+  int32_t *perm;       /* [T * k] perm[q] = p: pairs sorted by expert, ascending p
+                          within an expert; entries past offsets[E] are -1 */
+  int32_t *inv_perm;   /* [T * k] inv_perm[p] = q, or -1 for an invalid pair */
+  int32_t *status;     /* [1] device status word: MOE_OK or MOE_ERR_FORCED_INDEX */
+} moe_routing;
+
+/* Workspace bytes needed by moe_route, moe_route_forced and moe_forward for this
+ * shape (one size serves all three).  Returns 0 for an invalid shape. */
+size_t moe_workspace_bytes(const moe_shape *shape);
+
+/* Free routing.  Router logits l = x W_r^T (fp32 accumulation); selection score
+ * s = l + sel_bias (selection only); top-k of s, lowest expert index on ties;
+ * weights softmax over the k chosen logits; then the dispatch: counts, offsets,
+ * and the stable permutation of pairs by expert ([port] part 3 and its update:
+ * the expert matmul runs over (token, expert) rows sorted by expert).
+ * x is [T, d] in act_dtype.  Sets *status = MOE_OK. */
+int moe_route(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *out,
+              void *ws, size_t ws_bytes, void *stream);
+
+/* Forced routing ([bench] "The gate, forced": recorded expert choices are
+ * replayed).  forced_idx [T, k] int32 device array; ids are used as given and in
+ * the given slot order (duplicates are computed literally); weights are the
+ * softmax over the logits at those ids.  An id outside [0, E) sets
+ * *status = MOE_ERR_FORCED_INDEX, is stored as -1 with weight 0, is not
+ * dispatched, and the token's other slots are renormalised among themselves. */
+int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x, const int32_t *forced_idx,
+                     const moe_routing *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Expert FFNs and combine.  For every routed pair and for the shared expert:
+ * SwiGLU h = silu(W_gate x) * (W_up x), y_e = W_down h.  With FP8 weights the
+ * activations entering each projection are quantised per token and per
+ * 128-element group to E4M3 with scale amax/448 (round to nearest even,
+ * saturating), and the block scales are applied in fp32.  Combine per token, in
+ * fp32 and this order: acc = shared; acc += w_j * y_j for j = 0..k-1;
+ * y = acc rounded to act_dtype (bf16: round to nearest even).
+ * `r` must hold the results of moe_route / moe_route_forced for the same shape
+ * and x (logits and inv_perm are not read).  y is [T, d] in act_dtype. */
+int moe_forward(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
+                void *ws, size_t ws_bytes, void *stream);
+
+/* Stages of moe_forward, in launch order. */
+enum {
+  MOE_STAGE_PREPARE = 1,   /* activation quantisation (FP8 weights) and the expert tile plan */
+  MOE_STAGE_GATE_UP = 2,   /* grouped gate/up projections + SwiGLU (+ h quantisation) */
+  MOE_STAGE_DOWN = 4,      /* grouped down projection, times the routing weight */
+  MOE_STAGE_COMBINE = 8,   /* fixed-order combine into y */
+  MOE_STAGE_ALL = 15
+};
+
+/* moe_forward restricted to a subset of its stages (bitmask of MOE_STAGE_*).
+ * Calling the stages one at a time, in order, on one stream with the same
+ * arguments and workspace gives bitwise the result of moe_forward; the
+ * intermediate results live in the workspace between the calls.  Used to time
+ * each stage on the stream.  Unknown bits: MOE_ERR_INVALID_ARG. */
+int moe_forward_stages(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
+                       void *ws, size_t ws_bytes, uint32_t stages, void *stream);
+
+/* The activation quantisation used by moe_forward on its own: each of the n_rows
+ * rows of `in` ([n_rows, n_cols], act_dtype MOE_F32 or MOE_BF16, n_cols a multiple
+ * of 128) is cut into groups of 128; per group scale = amax/448 (1 for an all-zero
+ * group) and codes = E4M3(v / scale), round to nearest even, saturating at 448.
+ * codes [n_rows, n_cols] uint8, scales [n_rows, n_cols/128] fp32.  The pages do
+ * not say how FP8 activations are formed; this is the per-token, per-128-group
+ * dynamic reading. */
+int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const void *in, uint8_t *codes,
+                      float *scales, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

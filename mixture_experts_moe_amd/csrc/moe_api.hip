@@ -1,0 +1,248 @@
+// Host side of the C ABI declared in include/moe.h: argument validation,
+// workspace layout, kernel launches on the caller's stream.  Holds no state.
+#include <limits.h>
+
+#include "moe.h"
+#include "moe_kernels.h"
+
+namespace {
+
+using moe::ExpertArgs;
+
+constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t logits, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
+};
+
+int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
+
+int64_t max_tiles_for(const moe_shape& s, int BM) {
+  const int64_t P = (int64_t)s.T * s.top_k;
+  int64_t n = (P + BM - 1) / BM + (P < s.n_experts ? P : s.n_experts);
+  if (s.d_ffn_shared > 0) n += (s.T + BM - 1) / BM;
+  return n;
+}
+
+Layout layout(const moe_shape& s) {
+  const size_t T = s.T, d = s.d_model, E = s.n_experts, P = T * s.top_k;
+  const size_t Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
+  const bool fp8 = s.w_dtype == MOE_FP8E4M3_B128;
+  Layout L;
+  size_t o = 0;
+  auto seg = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  L.logits = seg(T * E * 4);
+  L.chunk_hist = seg(moe::dispatch_chunk_hist_ints((int)P, (int)E) * 4);
+  L.local_rank = seg(P * 4);
+  L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int2));
+  L.tile_count = seg(4);
+  L.xq = seg(fp8 ? T * d : 0);
+  L.sx = seg(fp8 ? T * (d / 128) * 4 : 0);
+  L.h = seg((P + T) * Fmax * h_elem_bytes(s.w_dtype));
+  L.sh = seg(fp8 ? (P + T) * (Fmax / 128) * 4 : 0);
+  L.part = seg((P + T) * d * 4);
+  L.total = o;
+  return L;
+}
+
+int validate_shape(const moe_shape* s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->T < 0 || s->d_model <= 0 || s->n_experts <= 0 || s->top_k <= 0 || s->d_ffn <= 0 || s->d_ffn_shared < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+  if (s->top_k > moe::kMaxTopK || s->n_experts > moe::kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if ((int64_t)s->T * s->top_k > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128);
+  if (!combo) return MOE_ERR_UNSUPPORTED;
+  if (s->d_model % 128 || s->d_ffn % 128 || s->d_ffn_shared % 128) return MOE_ERR_UNSUPPORTED;
+  if (s->d_model > 8192 || s->d_ffn > 4096 || s->d_ffn_shared > 4096) return MOE_ERR_UNSUPPORTED;
+  const int Fmax = s->d_ffn > s->d_ffn_shared ? s->d_ffn : s->d_ffn_shared;
+  if (moe::gateup_lds_bytes(16, s->w_dtype, s->d_model) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+  if (moe::down_lds_bytes(16, s->w_dtype, Fmax) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+  if (max_tiles_for(*s, 16) > 65535) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Rows per tile of the grouped expert GEMMs: more rows per expert -> taller
+// tiles (weights re-streamed less often), within the LDS budget.
+int pick_bm(const moe_shape& s) {
+  if (s.w_dtype != MOE_FP8E4M3_B128) return 16;
+  const int64_t per_expert = (int64_t)s.T * s.top_k / s.n_experts;
+  int bm = per_expert <= 16 ? 16 : (per_expert <= 48 ? 32 : 64);
+  const int Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
+  while (bm > 16 && (moe::gateup_lds_bytes(bm, s.w_dtype, s.d_model) > kMaxLds ||
+                     moe::down_lds_bytes(bm, s.w_dtype, Fmax) > kMaxLds))
+    bm /= 2;
+  return bm;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+int check_routing_out(const moe_routing* r) {
+  if (!r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm || !r->status)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+int route_common(const moe_shape* shape, const moe_weights* w, const void* x, const int32_t* forced,
+                 const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!w || !w->w_router || !x || check_routing_out(out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  if (shape->T == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(*shape);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const int T = shape->T, d = shape->d_model, E = shape->n_experts, k = shape->top_k, P = T * k;
+  float* logits = out->logits ? out->logits : (float*)(base + L.logits);
+  hipError_t e = moe::launch_router_logits(x, shape->act_dtype == MOE_BF16, w->w_router, logits, T, d, E,
+                                           out->status, st);
+  if (e != hipSuccess) return hip_status(e);
+  if (forced)
+    e = moe::launch_topk_forced(logits, forced, T, E, k, out->topk_idx, out->topk_w, out->status, st);
+  else
+    e = moe::launch_topk_free(logits, w->sel_bias, T, E, k, out->topk_idx, out->topk_w, st);
+  if (e != hipSuccess) return hip_status(e);
+  e = moe::launch_dispatch(out->topk_idx, P, E, (int32_t*)(base + L.chunk_hist), (int32_t*)(base + L.local_rank),
+                           out->counts, out->offsets, out->perm, out->inv_perm, st);
+  return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_bytes(const moe_shape* shape) {
+  if (validate_shape(shape) != MOE_OK) return 0;
+  return layout(*shape).total;
+}
+
+int moe_route(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* out, void* ws,
+              size_t ws_bytes, void* stream) {
+  return route_common(shape, w, x, nullptr, out, ws, ws_bytes, stream);
+}
+
+int moe_route_forced(const moe_shape* shape, const moe_weights* w, const void* x, const int32_t* forced_idx,
+                     const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!forced_idx) return MOE_ERR_INVALID_ARG;
+  return route_common(shape, w, x, forced_idx, out, ws, ws_bytes, stream);
+}
+
+int moe_forward(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y, void* ws,
+                size_t ws_bytes, void* stream) {
+  return moe_forward_stages(shape, w, x, r, y, ws, ws_bytes, MOE_STAGE_ALL, stream);
+}
+
+int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
+                       void* ws, size_t ws_bytes, uint32_t stages, void* stream) {
+  if (stages & ~(uint32_t)MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
+  int rc = validate_shape(shape);
+  if (rc != MOE_OK) return rc;
+  if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm)
+    return MOE_ERR_INVALID_ARG;
+  const bool fp8 = shape->w_dtype == MOE_FP8E4M3_B128;
+  const bool has_shared = shape->d_ffn_shared > 0;
+  if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+  if (fp8 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+  if (has_shared && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_INVALID_ARG;
+  if (has_shared && fp8 && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_INVALID_ARG;
+  if (shape->T == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout(*shape);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  hipStream_t st = (hipStream_t)stream;
+  char* base = (char*)ws;
+  const int T = shape->T, d = shape->d_model, E = shape->n_experts, k = shape->top_k, P = T * k;
+  const int BM = pick_bm(*shape);
+
+  ExpertArgs a;
+  a.tiles = (const int2*)(base + L.tiles);
+  a.tile_count = (const int32_t*)(base + L.tile_count);
+  a.offsets = r->offsets;
+  a.perm = r->perm;
+  a.topk_w = r->topk_w;
+  a.T = T;
+  a.d = d;
+  a.E = E;
+  a.k = k;
+  a.F = shape->d_ffn;
+  a.Fs = shape->d_ffn_shared;
+  a.P = P;
+  a.hstride = a.F > a.Fs ? a.F : a.Fs;
+  a.xa = fp8 ? (const void*)(base + L.xq) : x;
+  a.sxa = (const float*)(base + L.sx);
+  a.wg = w->w_gate;
+  a.wu = w->w_up;
+  a.wd = w->w_down;
+  a.sg = w->s_gate;
+  a.su = w->s_up;
+  a.sd = w->s_down;
+  a.shg = w->sh_gate;
+  a.shu = w->sh_up;
+  a.shd = w->sh_down;
+  a.ssg = w->ss_gate;
+  a.ssu = w->ss_up;
+  a.ssd = w->ss_down;
+  a.h = base + L.h;
+  a.sh = (float*)(base + L.sh);
+  a.part = (float*)(base + L.part);
+
+  hipError_t e = hipSuccess;
+  if (stages & MOE_STAGE_PREPARE) {
+    if (fp8) {
+      e = moe::launch_quantize_rows(x, true, T, d, (uint8_t*)(base + L.xq), (float*)(base + L.sx), st);
+      if (e != hipSuccess) return hip_status(e);
+    }
+    e = moe::launch_plan_tiles(r->counts, E, T, has_shared, BM, (int2*)(base + L.tiles),
+                               (int32_t*)(base + L.tile_count), st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  const int max_tiles = (int)max_tiles_for(*shape, BM);
+  if (stages & MOE_STAGE_GATE_UP) {
+    e = moe::launch_gateup(a, shape->w_dtype, BM, max_tiles, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (stages & MOE_STAGE_DOWN) {
+    e = moe::launch_down(a, shape->w_dtype, BM, max_tiles, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (stages & MOE_STAGE_COMBINE)
+    e = moe::launch_combine(a.part, r->topk_idx, T, k, d, E, P, has_shared, y, shape->act_dtype == MOE_BF16, st);
+  return hip_status(e);
+}
+
+int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const void* in, uint8_t* codes,
+                      float* scales, void* stream) {
+  if (n_rows < 0 || n_cols <= 0 || n_cols % 128 || (act_dtype != MOE_F32 && act_dtype != MOE_BF16))
+    return n_cols > 0 && n_cols % 128 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
+  if (n_rows == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_ERR_INVALID_ARG;
+  if (n_rows * (n_cols / 128) / 4 >= (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_quantize_rows(in, act_dtype == MOE_BF16, n_rows, n_cols, codes, scales,
+                                              (hipStream_t)stream));
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: null pointer or invalid size";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or dtype combination not supported";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
+    case MOE_ERR_FORCED_INDEX: return "MOE_ERR_FORCED_INDEX: a forced expert id was outside [0, n_experts)";
+    default: return "unknown moe status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI (moe_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 512;
+constexpr int kMaxTopK = 8;
+
+// Everything the expert kernels read or write (device pointers).
+struct ExpertArgs {
+  const int2* tiles;          // [max_tiles] (group, first row)
+  const int32_t* tile_count;  // [1]
+  const int32_t* offsets;     // [E+1]
+  const int32_t* perm;        // [P]
+  const float* topk_w;        // [P]
+  int T, d, E, k, F, Fs, P;
+  int hstride;                // elements per h row = max(F, Fs)
+  const void* xa;             // gate/up input rows: E4M3 codes, bf16 or fp32 [T][d]
+  const float* sxa;           // E4M3 activation scales [T][d/128]
+  const void *wg, *wu, *wd;
+  const float *sg, *su, *sd;
+  const void *shg, *shu, *shd;
+  const float *ssg, *ssu, *ssd;
+  void* h;                    // [P+T][hstride]: E4M3 codes, bf16 or fp32
+  float* sh;                  // [P+T][hstride/128] E4M3 scales of h
+  float* part;                // [P+T][d] weighted expert outputs
+};
+
+hipError_t launch_router_logits(const void* x, bool x_bf16, const float* W, float* logits, int T, int d, int E,
+                                int32_t* status, hipStream_t st);
+hipError_t launch_topk_free(const float* logits, const float* bias, int T, int E, int k, int32_t* idx, float* w,
+                            hipStream_t st);
+hipError_t launch_topk_forced(const float* logits, const int32_t* forced, int T, int E, int k, int32_t* idx, float* w,
+                              int32_t* status, hipStream_t st);
+hipError_t launch_dispatch(const int32_t* idx, int P, int E, int32_t* chunk_hist, int32_t* local_rank,
+                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, hipStream_t st);
+size_t dispatch_chunk_hist_ints(int P, int E);
+
+hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n_cols, uint8_t* codes, float* scales,
+                                hipStream_t st);
+hipError_t launch_plan_tiles(const int32_t* counts, int E, int T, bool has_shared, int BM, int2* tiles,
+                             int32_t* tile_count, hipStream_t st);
+hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
+hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
+hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,
+                          void* y, bool bf16_out, hipStream_t st);
+size_t gateup_lds_bytes(int BM, int wmode, int d);
+size_t down_lds_bytes(int BM, int wmode, int Fg);
+
+}  // namespace moe

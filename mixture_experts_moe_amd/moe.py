@@ -1,0 +1,218 @@
+"""Python binding of the C ABI in include/moe.h (argument marshalling only).
+
+Every step of the layer runs in the HIP library ``libmoe.so``; this module only
+turns torch tensors into device pointers and the current torch stream into the
+``stream`` argument.  There is no fallback: if the library is missing or fails
+to load, every entry point raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import dataclasses
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_FORCED_INDEX = 0, -1, -2, -3, -4, -5
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+
+# Every function the header declares (checked against include/moe.h by the tests).
+ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
+                 "moe_quantize_rows", "moe_status_string")
+STAGE_PREPARE, STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 8, 15
+
+
+class MoeError(RuntimeError):
+    def __init__(self, rc: int, what: str):
+        super().__init__(f"{what}: {status_string(rc)} ({rc})")
+        self.rc = rc
+
+
+class Shape(C.Structure):
+    _fields_ = [(n, C.c_int32) for n in ("T", "d_model", "n_experts", "top_k", "d_ffn", "d_ffn_shared",
+                                         "act_dtype", "w_dtype")]
+
+
+_WEIGHT_FIELDS = ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                  "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")
+
+
+class Weights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in _WEIGHT_FIELDS]
+
+
+_ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "status")
+
+
+class RoutingStruct(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in _ROUTING_FIELDS]
+
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libmoe.so (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950)")
+        L = C.CDLL(LIB_PATH)
+        p, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
+        L.moe_workspace_bytes.restype = C.c_size_t
+        L.moe_workspace_bytes.argtypes = [p]
+        L.moe_route.argtypes = [p, p, p, p, p, C.c_size_t, p]
+        L.moe_route_forced.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
+        L.moe_forward.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
+        L.moe_forward_stages.argtypes = [p, p, p, p, p, p, C.c_size_t, C.c_uint32, p]
+        L.moe_quantize_rows.argtypes = [i64, i32, i32, p, p, p, p]
+        L.moe_status_string.restype = C.c_char_p
+        L.moe_status_string.argtypes = [C.c_int]
+        _lib = L
+    return _lib
+
+
+def status_string(rc: int) -> str:
+    return lib().moe_status_string(rc).decode()
+
+
+def make_shape(T, d, E, k, F, Fs, act="bf16", w="fp8") -> Shape:
+    return Shape(int(T), int(d), int(E), int(k), int(F), int(Fs), DTYPES[act], DTYPES[w])
+
+
+def shape_of(layer_shape, T=None) -> Shape:
+    """Shape from any object with attributes T, d, E, k, F, Fs, act, w."""
+    s = layer_shape
+    return make_shape(s.T if T is None else T, s.d, s.E, s.k, s.F, s.Fs, s.act, s.w)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("moe: tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("moe: tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def weights_struct(w: dict) -> Weights:
+    return Weights(*[_ptr(w.get(n)) for n in _WEIGHT_FIELDS])
+
+
+@dataclasses.dataclass
+class Routing:
+    """Device buffers of one routing result (see moe_routing in include/moe.h)."""
+    logits: torch.Tensor | None
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    counts: torch.Tensor
+    offsets: torch.Tensor
+    perm: torch.Tensor
+    inv_perm: torch.Tensor
+    status: torch.Tensor
+
+    def struct(self) -> RoutingStruct:
+        return RoutingStruct(*[_ptr(getattr(self, n)) for n in _ROUTING_FIELDS])
+
+
+def alloc_routing(shape: Shape, device="cuda", with_logits=True) -> Routing:
+    T, E, k = shape.T, shape.n_experts, shape.top_k
+    i32 = dict(dtype=torch.int32, device=device)
+    return Routing(
+        logits=torch.empty((T, E), dtype=torch.float32, device=device) if with_logits else None,
+        topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
+        counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+        perm=torch.empty(T * k, **i32), inv_perm=torch.empty(T * k, **i32), status=torch.empty(1, **i32))
+
+
+def workspace_bytes(shape: Shape) -> int:
+    return int(lib().moe_workspace_bytes(C.byref(shape)))
+
+
+def alloc_workspace(shape: Shape, device="cuda") -> torch.Tensor:
+    n = workspace_bytes(shape)
+    if n == 0 and shape.T > 0:
+        raise MoeError(MOE_ERR_UNSUPPORTED, "moe_workspace_bytes")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def _check(rc, what):
+    if rc != MOE_OK:
+        raise MoeError(rc, what)
+
+
+def route(shape: Shape, w: dict, x: torch.Tensor, out: Routing, ws: torch.Tensor, stream=None):
+    rc = lib().moe_route(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), C.byref(out.struct()),
+                         _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "moe_route")
+
+
+def route_forced(shape: Shape, w: dict, x: torch.Tensor, forced_idx: torch.Tensor, out: Routing, ws: torch.Tensor,
+                 stream=None):
+    rc = lib().moe_route_forced(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), _ptr(forced_idx),
+                                C.byref(out.struct()), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "moe_route_forced")
+
+
+def forward(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor, ws: torch.Tensor, stream=None):
+    rc = lib().moe_forward(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), C.byref(r.struct()), _ptr(y),
+                           _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "moe_forward")
+
+
+def forward_stages(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor, ws: torch.Tensor,
+                   stages: int, stream=None):
+    rc = lib().moe_forward_stages(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), C.byref(r.struct()), _ptr(y),
+                                  _ptr(ws), ws.numel(), stages, _stream(stream))
+    _check(rc, "moe_forward_stages")
+
+
+def quantize_rows(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):
+    act = {torch.float32: DTYPES["f32"], torch.bfloat16: DTYPES["bf16"]}[x.dtype]
+    rc = lib().moe_quantize_rows(x.shape[0], x.shape[1], act, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream))
+    _check(rc, "moe_quantize_rows")
+
+
+def raw_call(name: str, *args):
+    """Call an ABI function with raw ctypes arguments (host-side validation tests)."""
+    return getattr(lib(), name)(*args)
+
+
+class Bound:
+    """One layer's arguments marshalled once (structs and pointers prebuilt), for
+    launch loops where per-call Python overhead would show: each method is a
+    single ctypes call."""
+
+    def __init__(self, shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor, ws: torch.Tensor,
+                 forced_idx: torch.Tensor | None = None, stream=None):
+        self._keep = (w, x, r, y, ws, forced_idx)
+        self.shape = shape
+        self.w = weights_struct(w)
+        self.r = r.struct()
+        self.args = (C.byref(self.shape), C.byref(self.w), C.c_void_p(_ptr(x)))
+        self.y = C.c_void_p(_ptr(y))
+        self.ws = (C.c_void_p(_ptr(ws)), ws.numel())
+        self.forced = C.c_void_p(_ptr(forced_idx)) if forced_idx is not None else None
+        self.stream = _stream(stream)
+        self.L = lib()
+
+    def route(self):
+        if self.forced is None:
+            _check(self.L.moe_route(*self.args, C.byref(self.r), *self.ws, self.stream), "moe_route")
+        else:
+            _check(self.L.moe_route_forced(*self.args, self.forced, C.byref(self.r), *self.ws, self.stream),
+                   "moe_route_forced")
+
+    def forward(self, stages: int = STAGE_ALL):
+        _check(self.L.moe_forward_stages(*self.args, C.byref(self.r), self.y, *self.ws, stages, self.stream),
+               "moe_forward_stages")

@@ -214,3 +214,19 @@ def make_inputs(case: str, T: int | None = None, seed: int = 0) -> dict:
     out = dict(shape=shape, x=x, w_router=np.ascontiguousarray(w_router), sel_bias=sel_bias)
     out.update(_expert_weights(layer, seed, w_dtype))
     return out
+
+
+def to_device(inp: dict, device="cuda") -> dict:
+    """The workload's arrays as torch tensors on `device`, keyed like the C ABI's
+    moe_weights fields plus ``x``: bf16 bit patterns become torch.bfloat16,
+    E4M3 codes stay uint8."""
+    out = {}
+    for k, v in inp.items():
+        if not isinstance(v, np.ndarray):
+            continue
+        if v.dtype == np.uint16:
+            t = torch.from_numpy(v.view(np.int16)).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(v)
+        out[k] = t.to(device)
+    return out

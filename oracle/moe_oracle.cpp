@@ -172,6 +172,17 @@ struct Mat {
   int rows, cols, w_dtype;
 };
 
+// The 256 E4M3 values, filled once from e4m3_decode (a lookup, same values).
+const float* e4m3_table() {
+  static float table[256];
+  static bool ready = false;
+  if (!ready) {
+    for (int c = 0; c < 256; ++c) table[c] = e4m3_decode((uint8_t)c);
+    ready = true;
+  }
+  return table;
+}
+
 // Element (r, c) of a weight matrix, decoded to fp32.
 float mat_at(const Mat& m, int r, int c) {
   size_t i = (size_t)r * m.cols + c;
@@ -180,7 +191,7 @@ float mat_at(const Mat& m, int r, int c) {
   int nrb = m.rows / 128, ncb = m.cols / 128;
   int si = (r / 128) * ncb + (c / 128);
   if (g_mutant == MUT_SCALE_TRANSPOSED) si = (c / 128) * nrb + (r / 128);
-  return e4m3_decode(((const uint8_t*)m.data)[i]) * m.scale[si];
+  return e4m3_table()[((const uint8_t*)m.data)[i]] * m.scale[si];
 }
 
 float act_at(const Shape& s, const void* x, int t, int i) {

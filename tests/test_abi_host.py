@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and
+rejects invalid arguments on the host before any HIP call (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from mixture_experts_moe_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(moe.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return moe.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "moe.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?[A-Za-z_]\w*\s*\**\s*(moe_\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_function():
+    L = _lib()
+    names = header_functions()
+    assert set(names) == set(moe.ABI_FUNCTIONS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    _lib()
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert moe.status_string(rc).startswith("MOE_")
+    assert "unknown" in moe.status_string(7)
+
+
+def test_workspace_bytes():
+    _lib()
+    s = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    n32 = moe.workspace_bytes(s)
+    n2048 = moe.workspace_bytes(moe.make_shape(2048, 2048, 384, 6, 640, 640))
+    assert 0 < n32 < n2048
+    # the per-pair fp32 partials dominate: (P + T) * d * 4 bytes
+    assert n2048 >= (2048 * 7) * 2048 * 4
+    assert moe.workspace_bytes(moe.make_shape(0, 2048, 384, 6, 640, 640)) >= 0
+    for bad in (moe.make_shape(32, 2048, 384, 9, 640, 640),      # k > 8
+                moe.make_shape(32, 2048, 4, 6, 640, 640),        # k > E
+                moe.make_shape(32, 2000, 384, 6, 640, 640),      # d not a multiple of 128
+                moe.make_shape(32, 2048, 384, 6, 640, 640, act="f32", w="fp8"),
+                moe.make_shape(32, 2048, 600, 6, 640, 640),      # E > 512
+                moe.make_shape(-1, 2048, 384, 6, 640, 640)):
+        assert moe.workspace_bytes(bad) == 0
+
+
+FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below returns before launching
+
+
+def _routing_struct(**null):
+    vals = {n: 0x2000 for n in ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "status")}
+    vals.update({k: None for k in null})
+    return moe.RoutingStruct(*[vals[n] for n in ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm",
+                                                 "inv_perm", "status")])
+
+
+def _weights_struct(**null):
+    vals = {n: 0x3000 for n in moe._WEIGHT_FIELDS}
+    vals.update({k: None for k in null})
+    return moe.Weights(*[vals[n] for n in moe._WEIGHT_FIELDS])
+
+
+def _route(shape, ws_bytes=1 << 40, w=None, r=None, x=FAKE, ws=FAKE):
+    L = _lib()
+    w = w or _weights_struct()
+    r = r or _routing_struct()
+    return L.moe_route(C.byref(shape) if shape is not None else None, C.byref(w), x, C.byref(r), ws, ws_bytes, None)
+
+
+def test_route_host_validation():
+    good = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    assert _route(None) == moe.MOE_ERR_INVALID_ARG
+    assert _route(moe.make_shape(32, 2048, 4, 6, 640, 640)) == moe.MOE_ERR_INVALID_ARG
+    assert _route(moe.make_shape(32, 2048, 384, 9, 640, 640)) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(moe.make_shape(32, 2048, 384, 6, 640, 640, act="f32", w="bf16")) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(moe.make_shape(32, 2040, 384, 6, 640, 640)) == moe.MOE_ERR_UNSUPPORTED
+    assert _route(good, w=_weights_struct(w_router=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _route(good, r=_routing_struct(perm=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _route(good, r=_routing_struct(status=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _route(good, x=None) == moe.MOE_ERR_INVALID_ARG
+    assert _route(good, ws_bytes=moe.workspace_bytes(good) - 1) == moe.MOE_ERR_WORKSPACE
+    assert _route(good, ws=None) == moe.MOE_ERR_INVALID_ARG
+    # T = 0: nothing to do, nothing enqueued, and the logits pointer may be NULL
+    assert _route(moe.make_shape(0, 2048, 384, 6, 640, 640), ws_bytes=0, ws=None,
+                  r=_routing_struct(logits=1)) == moe.MOE_OK
+
+
+def test_route_forced_requires_ids():
+    L = _lib()
+    s = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    w, r = _weights_struct(), _routing_struct()
+    assert L.moe_route_forced(C.byref(s), C.byref(w), FAKE, None, C.byref(r), FAKE, 1 << 40, None) == \
+        moe.MOE_ERR_INVALID_ARG
+    s0 = moe.make_shape(0, 2048, 384, 6, 640, 640)
+    assert L.moe_route_forced(C.byref(s0), C.byref(w), FAKE, FAKE, C.byref(r), None, 0, None) == moe.MOE_OK
+
+
+def _forward(shape, w=None, r=None, y=FAKE, ws_bytes=1 << 40):
+    L = _lib()
+    w = w or _weights_struct()
+    r = r or _routing_struct()
+    return L.moe_forward(C.byref(shape), C.byref(w), FAKE, C.byref(r), y, FAKE, ws_bytes, None)
+
+
+def test_forward_host_validation():
+    fp8 = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    assert _forward(fp8, w=_weights_struct(s_gate=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _forward(fp8, w=_weights_struct(ss_down=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _forward(fp8, w=_weights_struct(sh_up=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _forward(fp8, r=_routing_struct(topk_w=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _forward(fp8, y=None) == moe.MOE_ERR_INVALID_ARG
+    assert _forward(fp8, ws_bytes=16) == moe.MOE_ERR_WORKSPACE
+    # no shared expert: the shared pointers are not needed
+    noshared = moe.make_shape(0, 2048, 384, 6, 640, 0)
+    assert _forward(noshared, w=_weights_struct(sh_gate=1, sh_up=1, sh_down=1, ss_gate=1, ss_up=1, ss_down=1)) \
+        == moe.MOE_OK
+    # bf16 weights need no scales
+    bf = moe.make_shape(0, 2048, 384, 6, 640, 640, act="bf16", w="bf16")
+    assert _forward(bf, w=_weights_struct(s_gate=1, s_up=1, s_down=1, ss_gate=1, ss_up=1, ss_down=1)) == moe.MOE_OK
+
+
+def test_quantize_rows_host_validation():
+    L = _lib()
+    assert L.moe_quantize_rows(4, 100, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_quantize_rows(4, 128, 2, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(-1, 128, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(0, 128, 1, None, None, None, None) == moe.MOE_OK
+    assert L.moe_quantize_rows(4, 128, 1, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG

@@ -1,0 +1,414 @@
+"""GPU parity: the HIP path, called through the C ABI, against the CPU oracle on
+the same seeded inputs.
+
+Bars (written here, derived in the design notes):
+  * router logits: |dl| <= 1e-4 * max(|l|, rms of the token's logits);
+  * free-routing ids: the ordered row must match wherever every adjacent gap
+    among the top k+1 selection scores exceeds 1e-3; the set must match where
+    the k / k+1 gap exceeds 1e-3; other tokens are exempt and counted (on the
+    integer-grid workload, where logits are exact, every token must match);
+  * forced ids and the dispatch (counts, offsets, perm, inv_perm): bit-exact;
+  * routing weights: |dw| <= 1e-5;
+  * layer output: max |dy| <= 2e-2 * RMS(y_oracle) over the compared tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_moe_amd import moe, synth
+from oracle import moe_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+LOGIT_REL = 1e-4
+GAP = 1e-3
+W_ABS = 1e-5
+Y_REL = 2e-2
+
+_weights_dev: dict = {}
+_WKEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
+          "ss_gate", "ss_up", "ss_down")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_inputs(inp):
+    """Device tensors of one workload; the (large) expert weights are uploaded
+    once per process and shared by every workload of the same layer."""
+    key = id(inp["w_gate"])
+    if key not in _weights_dev:
+        _weights_dev[key] = synth.to_device({k: inp[k] for k in _WKEYS if inp.get(k) is not None}, DEV)
+    d = dict(_weights_dev[key])
+    d.update(synth.to_device({k: inp[k] for k in ("x", "w_router", "sel_bias") if inp.get(k) is not None}, DEV))
+    return d
+
+
+def run_gpu(inp, forced=None, dev=None, routing=None):
+    s = inp["shape"]
+    shape = moe.shape_of(s)
+    dev = dev or gpu_inputs(inp)
+    r = routing or moe.alloc_routing(shape, DEV)
+    ws = moe.alloc_workspace(shape, DEV)
+    y = torch.empty((s.T, s.d), dtype=torch.float32 if s.act == "f32" else torch.bfloat16, device=DEV)
+    if forced is None:
+        moe.route(shape, dev, dev["x"], r, ws)
+    else:
+        moe.route_forced(shape, dev, dev["x"], torch.from_numpy(np.ascontiguousarray(forced, np.int32)).to(DEV),
+                         r, ws)
+    moe.forward(shape, dev, dev["x"], r, y, ws)
+    torch.cuda.synchronize()
+    out = {n: getattr(r, n).cpu().numpy() for n in ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm",
+                                                      "status")}
+    out["logits"] = r.logits.cpu().numpy() if r.logits is not None else None
+    out["y"] = y.float().cpu().numpy()
+    return out
+
+
+def selection_scores(inp, logits):
+    b = inp.get("sel_bias")
+    return logits if b is None else (logits + b[None, :]).astype(np.float32)
+
+
+def check_logits(gpu, ref):
+    rms = np.sqrt(np.mean(ref.astype(np.float64) ** 2, axis=1, keepdims=True))
+    bound = LOGIT_REL * np.maximum(np.abs(ref), rms)
+    bad = np.abs(gpu.astype(np.float64) - ref) > bound
+    assert not bad.any(), f"{bad.sum()} logits outside 1e-4 relative"
+
+
+def route_agreement(gpu_idx, ref_idx, ref_scores, k):
+    """Returns (mismatches on non-exempt tokens, exempt tokens)."""
+    srt = -np.sort(-ref_scores.astype(np.float64), axis=1)[:, :k + 1]
+    gaps = srt[:, :-1] - srt[:, 1:]
+    bad = exempt = 0
+    for t in range(gpu_idx.shape[0]):
+        if (gaps[t] > GAP).all():
+            bad += int(not np.array_equal(gpu_idx[t], ref_idx[t]))
+        elif gaps[t, k - 1] > GAP:
+            bad += int(set(gpu_idx[t].tolist()) != set(ref_idx[t].tolist()))
+        else:
+            exempt += 1
+    return bad, exempt
+
+
+def check_y(y_gpu, acc_ref):
+    """Layer output against the oracle's fp32 result before its final rounding.
+    (Two independently bf16-rounded outputs may differ by a whole bf16 ulp on a
+    rounding straddle; the GPU's own rounding adds at most half an ulp here.)"""
+    ref = acc_ref.astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(y_gpu.astype(np.float64) - ref)))
+    say(f"  max|dy| = {err:.3e}  rms(y) = {rms:.3e}  ratio = {err / rms:.3e}")
+    assert err <= Y_REL * rms, f"layer output error {err / rms:.3e} x rms exceeds {Y_REL}"
+    return err / rms
+
+
+def check_dispatch(gpu, ref_idx, E):
+    c, o, p, inv = O.dispatch(ref_idx, E)
+    assert np.array_equal(gpu["counts"], c)
+    assert np.array_equal(gpu["offsets"], o)
+    assert np.array_equal(gpu["perm"], p)
+    assert np.array_equal(gpu["inv_perm"], inv)
+
+
+def check_dispatch_properties(gpu, E):
+    """Holds at any size: the dispatch is the stable sort of the GPU's own ids."""
+    idx = gpu["topk_idx"].ravel()
+    valid = (idx >= 0) & (idx < E)
+    counts = np.bincount(idx[valid], minlength=E)
+    assert np.array_equal(gpu["counts"], counts)
+    assert np.array_equal(gpu["offsets"], np.concatenate([[0], np.cumsum(counts)]))
+    n = int(valid.sum())
+    perm = gpu["perm"]
+    assert np.array_equal(perm[:n], np.nonzero(valid)[0][np.argsort(idx[valid], kind="stable")])
+    assert (perm[n:] == -1).all()
+    inv = gpu["inv_perm"]
+    assert np.array_equal(inv[perm[:n]], np.arange(n))
+    assert (inv[~valid] == -1).all()
+
+
+# ------------------------------------------------------------------ activation quantisation
+
+def test_quantize_rows_bitexact():
+    rng = np.random.default_rng(1)
+    xf = (rng.standard_normal((512, 2048)) * np.exp(rng.standard_normal((512, 1)))).astype(np.float32)
+    xf[3, :128] = 0.0
+    xf[4, 128:256] = 1e-30
+    for act in ("bf16", "f32"):
+        say(f"quantize_rows {act} [512, 2048]")
+        x_np = synth.bf16_bits(xf) if act == "bf16" else xf
+        xv = synth.bf16_bits_to_f32(x_np) if act == "bf16" else xf
+        xt = synth.to_device({"x": x_np}, DEV)["x"]
+        codes = torch.empty((512, 2048), dtype=torch.uint8, device=DEV)
+        scales = torch.empty((512, 16), dtype=torch.float32, device=DEV)
+        moe.quantize_rows(xt, codes, scales)
+        torch.cuda.synchronize()
+        c_ref, s_ref = O.quant_groups(xv)
+        assert np.array_equal(scales.cpu().numpy().ravel(), s_ref)
+        assert np.array_equal(codes.cpu().numpy().ravel(), c_ref)
+
+
+# ------------------------------------------------------------------ tiny fp32 layer
+
+def test_tiny_free_and_forced():
+    inp = synth.make_inputs("tiny_f32")
+    s = inp["shape"]
+    say(f"tiny_f32 T={s.T} d={s.d} E={s.E} k={s.k} free")
+    L = O.Layer(inp)
+    _, lg, idx, w = O.route(L)
+    g = run_gpu(inp)
+    assert g["status"][0] == 0
+    check_logits(g["logits"], lg)
+    bad, ex = route_agreement(g["topk_idx"], idx, selection_scores(inp, lg), s.k)
+    assert bad == 0 and ex <= 2
+    same = (g["topk_idx"] == idx).all(axis=1)
+    if same.all():
+        check_dispatch(g, idx, s.E)
+    else:
+        check_dispatch_properties(g, s.E)
+    assert np.max(np.abs(g["topk_w"][same] - w[same])) <= W_ABS
+    _, acc_ref = O.forward(L, idx, w)
+    check_y(g["y"][same], acc_ref[same])
+    say("tiny_f32 forced from the oracle's recorded ids")
+    gf = run_gpu(inp, forced=idx)
+    assert np.array_equal(gf["topk_idx"], idx)
+    check_dispatch(gf, idx, s.E)
+    assert np.max(np.abs(gf["topk_w"] - w)) <= W_ABS
+    _, acc_ref = O.forward(L, idx, w)
+    r = check_y(gf["y"], acc_ref)
+    assert r < 1e-4  # all-fp32 path: only summation order differs
+
+
+# ------------------------------------------------------------------ decode shape, FP8 experts
+
+def test_decode_free():
+    inp = synth.make_inputs("decode_t32")
+    s = inp["shape"]
+    say(f"decode_t32 T={s.T} d={s.d} E={s.E} k={s.k} F={s.F} free")
+    L = O.Layer(inp)
+    _, lg, idx, w = O.route(L)
+    g = run_gpu(inp)
+    check_logits(g["logits"], lg)
+    bad, ex = route_agreement(g["topk_idx"], idx, selection_scores(inp, lg), s.k)
+    say(f"  ids: {bad} mismatches, {ex} exempt")
+    assert bad == 0
+    check_dispatch_properties(g, s.E)
+    same = (g["topk_idx"] == idx).all(axis=1)
+    assert np.max(np.abs(g["topk_w"][same] - w[same])) <= W_ABS
+    if same.all():
+        check_dispatch(g, idx, s.E)
+    # output against the oracle's own routing, on the tokens whose ids agree
+    _, acc_ref = O.forward(L, idx, w)
+    check_y(g["y"][same], acc_ref[same])
+
+
+def test_decode_forced_and_free_equivalence():
+    inp = synth.make_inputs("decode_t32")
+    s = inp["shape"]
+    L = O.Layer(inp)
+    _, _, idx, w = O.route(L)
+    say("decode_t32 forced from the oracle's recorded ids")
+    g = run_gpu(inp, forced=idx)
+    assert g["status"][0] == 0
+    assert np.array_equal(g["topk_idx"], idx)
+    check_dispatch(g, idx, s.E)
+    assert np.max(np.abs(g["topk_w"] - w)) <= W_ABS
+    _, acc_ref = O.forward(L, idx, w)
+    check_y(g["y"], acc_ref)
+    say("decode_t32: forced(free ids) is bitwise the free result")
+    gfree = run_gpu(inp)
+    gforce = run_gpu(inp, forced=gfree["topk_idx"])
+    for n in ("topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "logits", "y"):
+        assert np.array_equal(gfree[n], gforce[n]), n
+
+
+def test_decode_deterministic():
+    inp = synth.make_inputs("decode_t32")
+    say("decode_t32 run twice: bitwise identical")
+    a, b = run_gpu(inp), run_gpu(inp)
+    for n in ("logits", "topk_idx", "topk_w", "perm", "inv_perm", "y"):
+        assert np.array_equal(a[n], b[n]), n
+
+
+# ------------------------------------------------------------------ near-ties workload
+
+@pytest.mark.parametrize("case", ["ties_t256", "ties_t256_bf16w"])
+def test_ties_exact_routing(case):
+    inp = synth.make_inputs(case)
+    s = inp["shape"]
+    say(f"{case} T={s.T} w={s.w}: exact logits, every token's ids must match")
+    L = O.Layer(inp)
+    _, lg, idx, w = O.route(L)
+    srt = -np.sort(-lg, axis=1)
+    say(f"  exact 6th/7th ties in the oracle: {int(np.sum(srt[:, 5] == srt[:, 6]))} tokens")
+    g = run_gpu(inp)
+    assert np.array_equal(g["logits"], lg)
+    assert np.array_equal(g["topk_idx"], idx)
+    check_dispatch(g, idx, s.E)
+    assert np.max(np.abs(g["topk_w"] - w)) <= W_ABS
+    tok = np.arange(0, s.T, 8)
+    _, acc_ref = O.forward(L, idx[tok], w[tok], tok)
+    check_y(g["y"][tok], acc_ref)
+
+
+# ------------------------------------------------------------------ prefill, forced routing
+
+def test_prefill_forced_full_size():
+    inp = synth.make_inputs("prefill_t2048")
+    s = inp["shape"]
+    L = O.Layer(inp)
+    say(f"prefill_t2048: oracle free pass over T={s.T} records the ids")
+    _, lg, idx, w = O.route(L)
+    g = run_gpu(inp, forced=idx)
+    say("  GPU forced pass")
+    assert g["status"][0] == 0
+    check_logits(g["logits"], lg)
+    assert np.array_equal(g["topk_idx"], idx)
+    check_dispatch(g, idx, s.E)
+    assert np.max(np.abs(g["topk_w"] - w)) <= W_ABS
+    tok = np.unique(np.concatenate([np.arange(0, s.T, 64), [1, s.T - 1]]))
+    _, acc_ref = O.forward(L, idx[tok], w[tok], tok)
+    check_y(g["y"][tok], acc_ref)
+
+
+# ------------------------------------------------------------------ skewed load, free routing
+
+def test_skew_free_full_size():
+    inp = synth.make_inputs("skew_t8192")
+    s = inp["shape"]
+    say(f"skew_t8192 T={s.T} free routing with the Zipf selection bias")
+    g = run_gpu(inp)
+    counts = g["counts"]
+    say(f"  expert load: max {counts.max()} mean {counts.mean():.1f} zeros {(counts == 0).sum()}")
+    assert counts.max() > 10 * counts.mean()
+    check_dispatch_properties(g, s.E)
+    L = O.Layer(inp)
+    tok = np.unique(np.concatenate([np.arange(0, s.T, 97), [s.T - 1]]))
+    _, lg, idx, w = O.route(L, tok)
+    check_logits(g["logits"][tok], lg)
+    bad, ex = route_agreement(g["topk_idx"][tok], idx, selection_scores(inp, lg), s.k)
+    say(f"  ids on {len(tok)} sampled tokens: {bad} mismatches, {ex} exempt")
+    assert bad == 0
+    same = (g["topk_idx"][tok] == idx).all(axis=1)
+    assert np.max(np.abs(g["topk_w"][tok][same] - w[same])) <= W_ABS
+    ts = tok[same][::2]
+    _, acc_ref = O.forward(L, idx[same][::2], w[same][::2], ts)
+    check_y(g["y"][ts], acc_ref)
+
+
+# ------------------------------------------------------------------ edge shapes
+
+def _forced_random(T, k, E, seed, n_experts_used=None):
+    rng = np.random.default_rng(seed)
+    pool = np.arange(E) if n_experts_used is None else rng.choice(E, n_experts_used, replace=False)
+    return pool[rng.integers(0, len(pool), size=(T, k))].astype(np.int32)
+
+
+@pytest.mark.parametrize("T,kind", [(1, "free"), (37, "free"), (64, "one_expert"), (300, "few_experts"),
+                                    (5462, "forced"), (8792, "forced")])
+def test_edge_shapes(T, kind):
+    """T=1; a ragged tail; every pair on one expert (duplicate ids per token);
+    most experts empty; pair counts 32,772 and 52,752 (just above 32,768 and not
+    a multiple of 64; and 8 x 1,099 x 6, the expert-GEMM row counts of section 3
+    of "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No.")."""
+    inp = synth.make_inputs("prefill_t2048", T=T)
+    s = inp["shape"]
+    say(f"edge T={T} ({T * s.k} pairs) {kind}")
+    L = O.Layer(inp)
+    if kind == "free":
+        g = run_gpu(inp)
+        _, lg, idx, w = O.route(L)
+        bad, ex = route_agreement(g["topk_idx"], idx, selection_scores(inp, lg), s.k)
+        assert bad == 0
+        assert np.array_equal(g["topk_idx"], idx), "tokens exempt by the gap rule: compare on a subset"
+        forced = idx
+    else:
+        forced = {"one_expert": lambda: np.full((T, s.k), 7, np.int32),
+                  "few_experts": lambda: _forced_random(T, s.k, s.E, 5, n_experts_used=3),
+                  "forced": lambda: _forced_random(T, s.k, s.E, T)}[kind]()
+        g = run_gpu(inp, forced=forced)
+        assert np.array_equal(g["topk_idx"], forced)
+    check_dispatch(g, forced, s.E)
+    tok = np.unique(np.linspace(0, T - 1, min(T, 24)).astype(int))
+    _, _, idf, wf = O.route_forced(L, forced, tok)
+    assert np.max(np.abs(g["topk_w"][tok] - wf)) <= W_ABS
+    _, acc_ref = O.forward(L, idf, wf, tok)
+    check_y(g["y"][tok], acc_ref)
+
+
+def test_invalid_forced_ids_flag_status_and_stay_in_bounds():
+    inp = synth.make_inputs("decode_t32")
+    s = inp["shape"]
+    L = O.Layer(inp)
+    _, _, idx, _ = O.route(L)
+    bad = idx.copy()
+    bad[2, 0], bad[5, 3], bad[31, 5], bad[7, 1] = -3, s.E, 100000, -1
+    say("decode_t32 forced with 4 invalid ids")
+    shape = moe.shape_of(s)
+    P, E, T, k = s.T * s.k, s.E, s.T, s.k
+    guard = 64
+    SENT = -123456
+
+    def padded(n, dtype):
+        t = torch.full((n + guard,), SENT, dtype=dtype, device=DEV)
+        return t, t[:n]
+
+    bufs = {n: padded(sz, dt) for n, sz, dt in (("topk_idx", T * k, torch.int32), ("topk_w", T * k, torch.float32),
+                                                  ("counts", E, torch.int32), ("offsets", E + 1, torch.int32),
+                                                  ("perm", P, torch.int32), ("inv_perm", P, torch.int32),
+                                                  ("status", 1, torch.int32), ("logits", T * E, torch.float32))}
+    r = moe.Routing(logits=bufs["logits"][1].view(T, E), topk_idx=bufs["topk_idx"][1].view(T, k),
+                    topk_w=bufs["topk_w"][1].view(T, k), counts=bufs["counts"][1], offsets=bufs["offsets"][1],
+                    perm=bufs["perm"][1], inv_perm=bufs["inv_perm"][1], status=bufs["status"][1])
+    g = run_gpu(inp, forced=bad, routing=r)
+    for n, (full, _) in bufs.items():
+        tail = full[-guard:].cpu().numpy()
+        assert (tail.view(np.int32) == SENT).all() if full.dtype == torch.int32 else \
+            (tail == np.float32(SENT)).all(), f"{n}: write past the end"
+    assert g["status"][0] == moe.MOE_ERR_FORCED_INDEX
+    rc, _, idf, wf = O.route_forced(L, bad)
+    assert rc == O.ERR_FORCED_INDEX
+    assert np.array_equal(g["topk_idx"], idf)
+    assert np.max(np.abs(g["topk_w"] - wf)) <= W_ABS
+    check_dispatch(g, idf, s.E)
+    _, acc_ref = O.forward(L, idf, wf)
+    check_y(g["y"], acc_ref)
+
+
+def test_zero_tokens_is_a_no_op():
+    inp = synth.make_inputs("decode_t32", T=1)
+    s = inp["shape"]
+    shape = moe.make_shape(0, s.d, s.E, s.k, s.F, s.Fs)
+    dev = gpu_inputs(inp)
+    r = moe.alloc_routing(moe.make_shape(1, s.d, s.E, s.k, s.F, s.Fs), DEV)
+    r.status.fill_(77)
+    y = torch.full((1, s.d), 3.0, dtype=torch.bfloat16, device=DEV)
+    ws = torch.empty(256, dtype=torch.uint8, device=DEV)
+    moe.route(shape, dev, dev["x"], r, ws)
+    moe.forward(shape, dev, dev["x"], r, y, ws)
+    torch.cuda.synchronize()
+    assert r.status.item() == 77 and (y.float() == 3.0).all()
+
+
+def test_forward_stages_match_forward():
+    inp = synth.make_inputs("decode_t32")
+    s = inp["shape"]
+    say("decode_t32: stages called one at a time == moe_forward, bitwise")
+    shape = moe.shape_of(s)
+    dev = gpu_inputs(inp)
+    r = moe.alloc_routing(shape, DEV)
+    ws = moe.alloc_workspace(shape, DEV)
+    y1 = torch.empty((s.T, s.d), dtype=torch.bfloat16, device=DEV)
+    y2 = torch.empty_like(y1)
+    moe.route(shape, dev, dev["x"], r, ws)
+    moe.forward(shape, dev, dev["x"], r, y1, ws)
+    b = moe.Bound(shape, dev, dev["x"], r, y2, ws)
+    for st in (moe.STAGE_PREPARE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE):
+        b.forward(st)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    with pytest.raises(moe.MoeError):
+        b.forward(16)
