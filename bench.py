@@ -96,33 +96,36 @@ def run_workload(name, steps, warmup, rotate):
 
     st = torch.cuda.current_stream()
     bound = [moe.Bound(shape, w, w["x"], r, y, ws, forced_idx=forced, stream=st) for w in copies]
-    stages = (moe.STAGE_PREPARE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE)
-    n_ev = 6
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
 
-    def step(i, ev=None):
+    def step(i):
         b = bound[i % len(bound)]
-        if ev:
-            ev[0].record(st)
         b.route()
-        if ev:
-            ev[1].record(st)
-        for j, stage in enumerate(stages):
-            b.forward(stage)
-            if ev:
-                ev[2 + j].record(st)
+        b.forward()
 
+    # timed pass: one routing call and one forward call per step
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(i, evs[i])
+        step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+
+    # attribution pass (same kernels): events around the routing call, and events
+    # the library records on the stream between the forward stages
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    for i in range(steps):
+        b = bound[i % len(bound)]
+        ev[i][0].record(st)
+        b.route()
+        ev[i][1].record(st)
+        b.forward(moe.STAGE_ALL, events=ev[i][2:])
+    torch.cuda.synchronize()
     names = ("route", "prepare", "gate_up", "down", "combine")
-    stage_us = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)])) * 1e3
-                for j, n in enumerate(names)}
+    pairs = ((0, 1), (2, 3), (3, 4), (4, 5), (5, 6))
+    stage_us = {n: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)])) * 1e3
+                for n, (a, b) in zip(names, pairs)}
     counts = r.counts.cpu().numpy()
     assert r.status.item() == 0
     return s, wall, stage_us, algorithmic(s, counts), counts

@@ -152,13 +152,17 @@ enum {
   MOE_STAGE_ALL = 15
 };
 
-/* moe_forward restricted to a subset of its stages (bitmask of MOE_STAGE_*).
- * Calling the stages one at a time, in order, on one stream with the same
- * arguments and workspace gives bitwise the result of moe_forward; the
- * intermediate results live in the workspace between the calls.  Used to time
- * each stage on the stream.  Unknown bits: MOE_ERR_INVALID_ARG. */
+/* moe_forward restricted to a subset of its stages (bitmask of MOE_STAGE_*),
+ * optionally timed.  Calling the stages one at a time, in order, on one stream
+ * with the same arguments and workspace gives bitwise the result of
+ * moe_forward; the intermediate results live in the workspace between the
+ * calls.  `events` is NULL or an array of 5 hipEvent_t created by the caller:
+ * events[0] is recorded on `stream` before the first stage and events[i] right
+ * after stage i (1 = prepare .. 4 = combine) when that stage is selected, so the
+ * interval between two records spans only that stage's kernels.  Unknown stage
+ * bits: MOE_ERR_INVALID_ARG. */
 int moe_forward_stages(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
-                       void *ws, size_t ws_bytes, uint32_t stages, void *stream);
+                       void *ws, size_t ws_bytes, uint32_t stages, void *const *events, void *stream);
 
 /* The activation quantisation used by moe_forward on its own: each of the n_rows
  * rows of `in` ([n_rows, n_cols], act_dtype MOE_F32 or MOE_BF16, n_cols a multiple

@@ -18,8 +18,9 @@ HIPCC_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
+def build(verbose: bool = False, extra_flags=(), out=None) -> str:
+    lib = out or LIB
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = ["hipcc", *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp]
     cmd += [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
@@ -30,8 +31,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -26,6 +26,22 @@
 
 namespace moe {
 
+#ifndef MOE_NT_LOADS
+#define MOE_NT_LOADS 0
+#endif
+#ifndef MOE_GU_KG
+#define MOE_GU_KG 4  // K blocks per weight stage in the gate/up stream
+#endif
+
+// Streaming load of 16 weight bytes (non-temporal: read once per call).
+__device__ __forceinline__ v4i stream_load(const uint8_t* p) {
+#if MOE_NT_LOADS
+  return __builtin_nontemporal_load((const v4i*)p);
+#else
+  return *(const v4i*)p;
+#endif
+}
+
 // ---------------------------------------------------------------------------
 // Activation quantisation: per row and 128-element group, s = amax/448 (1 for
 // an all-zero group), code = E4M3(v/s) round-to-nearest-even, saturating.  One
@@ -56,29 +72,45 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Tile plan: tiles per group = ceil(rows / BM); groups in order; one block.
+// Forward preparation: blocks 0..n-2 quantise the activations (four 128-element
+// groups per block, as above); the last block plans the expert tiles: tiles
+// per group = ceil(rows / BM), groups in order (routed experts 0..E-1, then the
+// shared expert with all T rows), tile i = (group, first row).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void plan_tiles_kernel(const int32_t* __restrict__ counts, int E, int T,
-                                                           int has_shared, int BM, int2* __restrict__ tiles,
-                                                           int32_t* __restrict__ tile_count) {
+__global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict__ x, int64_t n_groups, int gpr,
+                                                       uint8_t* __restrict__ xq, float* __restrict__ sx,
+                                                       const int32_t* __restrict__ counts, int E, int T,
+                                                       int has_shared, int BM, int2* __restrict__ tiles,
+                                                       int32_t* __restrict__ tile_count) {
+  if (blockIdx.x + 1 < gridDim.x) {
+    const int lane = threadIdx.x & 63;
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (g >= n_groups) return;
+    const int64_t o = (g / gpr) * (int64_t)gpr * 128 + (g % gpr) * 128 + 2 * lane;
+    const uint32_t pr = *(const uint32_t*)(x + o);
+    const float v0 = __uint_as_float(pr << 16), v1 = __uint_as_float(pr & 0xffff0000u);
+    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+    *(uint16_t*)(xq + o) = (uint16_t)pack2_e4m3(v0 / s, v1 / s);
+    if (lane == 0) sx[g] = s;
+    return;
+  }
   __shared__ int32_t tmp[17];
+  constexpr int PER = (kMaxExperts + 1 + 255) / 256;  // groups per thread
   const int G = E + (has_shared ? 1 : 0);
-  // each thread owns groups 2*tid and 2*tid + 1 (G <= 2048)
-  int nt[2];
+  int nt[PER], sum = 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int g = 2 * threadIdx.x + i;
-    int rows = 0;
-    if (g < E) rows = counts[g];
-    else if (g < G) rows = T;
+  for (int i = 0; i < PER; ++i) {
+    const int g = PER * threadIdx.x + i;
+    const int rows = g < E ? counts[g] : (g < G ? T : 0);
     nt[i] = (rows + BM - 1) / BM;
+    sum += nt[i];
   }
   int total;
-  const int start = block1024_excl_scan(nt[0] + nt[1], tmp, &total);
-  int s = start;
+  int s = block_excl_scan<256>(sum, tmp, &total);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int g = 2 * threadIdx.x + i;
+  for (int i = 0; i < PER; ++i) {
+    const int g = PER * threadIdx.x + i;
     for (int j = 0; j < nt[i]; ++j) tiles[s + j] = make_int2(g, j * BM);
     s += nt[i];
   }
@@ -113,15 +145,19 @@ __device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile, int
 //           epilogue.
 //   WT = 1: bf16 weights and activations, 16x16x32 MFMA accumulating in fp32;
 //           h stored as bf16.
-// Block = 256 threads = 4 waves; blockIdx.x = 128-feature slice nb of h,
-// blockIdx.y = tile.  Wave w owns h features nb*128 + w*32 + [0, 32): two
-// 16-row tiles of W_gate and the same two of W_up, so g and u of a feature meet
-// in one lane.
+// Block = 8 waves covering one 128-feature group nb of h (blockIdx.x) for one
+// tile (blockIdx.y).  Wave w owns h features nb*128 + w*16 + [0, 16): one 16-row
+// tile of W_gate and the same rows of W_up, so g and u of a feature meet in one
+// lane.  32 weight rows per wave keeps many short streams in flight, which the
+// HBM prefers to a few long ones.
 // ---------------------------------------------------------------------------
+constexpr int kGateUpWaves = 8;
+
 template <int BM, int WT>
-__global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertArgs a) {
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;  // bytes per element
+  constexpr int NT = kGateUpWaves * 64;
   const int tile = blockIdx.y;
   if (tile >= *a.tile_count) return;
   const TileRows tr = tile_rows(a, tile, BM);
@@ -134,43 +170,17 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertArgs a) {
   const int xstride = RB + 16;    // padded LDS row
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* xs = smem;
-  float* sxs = (float*)(smem + BM * xstride);       // [BM][d/128] (FP8 only)
-  float* red = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [4][BM]
-  int* tok = (int*)(red + 4 * BM);                  // [BM] token of each row
+  float* sxs = (float*)(smem + BM * xstride);           // [BM][d/128] (FP8 only)
+  float* red = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [waves][BM]
+  int* tok = (int*)(red + kGateUpWaves * BM);           // [BM] token of each row
 
   const int tid = threadIdx.x;
-  if (tid < BM) {
-    int t = -1;
-    if (tid < tr.rows) t = tr.shared ? tr.m0 + tid : a.perm[a.offsets[tr.g] + tr.m0 + tid] / a.k;
-    tok[tid] = t;
-  }
-  __syncthreads();
-  {
-    const int cpr = RB / 16;
-    const uint8_t* xa = (const uint8_t*)a.xa;
-    for (int i = tid; i < BM * cpr; i += 256) {
-      const int r = i / cpr, c = i - r * cpr, t = tok[r];
-      v4i v = {0, 0, 0, 0};
-      if (t >= 0) v = *(const v4i*)(xa + (size_t)t * RB + c * 16);
-      *(v4i*)(xs + r * xstride + c * 16) = v;
-    }
-    if (WT == 2) {
-      const int nkb = a.d / 128;
-      for (int i = tid; i < BM * nkb; i += 256) {
-        const int r = i / nkb, c = i - r * nkb, t = tok[r];
-        sxs[i] = t >= 0 ? a.sxa[(size_t)t * nkb + c] : 0.f;
-      }
-    }
-  }
-  __syncthreads();
-
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
   const size_t wsz = (size_t)a.F * RB;  // bytes of one routed expert matrix
   const uint8_t* wg = tr.shared ? (const uint8_t*)a.shg : (const uint8_t*)a.wg + (size_t)tr.g * wsz;
   const uint8_t* wu = tr.shared ? (const uint8_t*)a.shu : (const uint8_t*)a.wu + (size_t)tr.g * wsz;
-  const int frow = nb * 128 + wave * 32;
-  const uint8_t* pa[4] = {wg + (size_t)(frow + lr) * RB + lk, wg + (size_t)(frow + 16 + lr) * RB + lk,
-                          wu + (size_t)(frow + lr) * RB + lk, wu + (size_t)(frow + 16 + lr) * RB + lk};
+  const int f0 = nb * 128 + wave * 16;
+  const uint8_t* pa[2] = {wg + (size_t)(f0 + lr) * RB + lk, wu + (size_t)(f0 + lr) * RB + lk};
   const float* sgp = nullptr;
   const float* sup = nullptr;
   if (WT == 2) {
@@ -180,78 +190,108 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertArgs a) {
     sup = (tr.shared ? a.ssu : a.su + (size_t)tr.g * ssz) + (size_t)nb * nkb;
   }
 
-  v4f acc[4][NC];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < NC; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  v4i wlo[2][4], whi[2][4];
-  auto load = [&](int s, int bb) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      wlo[s][r] = __builtin_nontemporal_load((const v4i*)(pa[r] + bb * 128));
-      whi[s][r] = __builtin_nontemporal_load((const v4i*)(pa[r] + bb * 128 + 64));
-    }
-  };
-  auto compute = [&](int s, int bb) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
-      const v4i blo = *(const v4i*)bp;
-      const v4i bhi = *(const v4i*)(bp + 64);
-      if constexpr (WT == 2) {
-        const float sx = sxs[(c * 16 + lr) * nbb + bb];
-        const float cg = sx * sgp[bb], cu = sx * sup[bb];
-        v4i b[4];
-        e4m3x16_to_bf16(blo, b[0], b[1]);
-        e4m3x16_to_bf16(bhi, b[2], b[3]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const v4f p = kblock_e4m3_exact(wlo[s][r], whi[s][r], b);
-          const float cs = r < 2 ? cg : cu;
-          acc[r][c] += p * cs;
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[r][c] = mfma_bf16(wlo[s][r], blo, acc[r][c]);
-          acc[r][c] = mfma_bf16(whi[s][r], bhi, acc[r][c]);
-        }
-      }
-    }
-  };
-  load(0, 0);
-  if (nbb > 1) load(1, 1);
-  for (int bb = 0; bb < nbb; bb += 2) {
-    compute(0, bb);
-    if (bb + 2 < nbb) load(0, bb + 2);
-    if (bb + 1 < nbb) {
-      compute(1, bb + 1);
-      if (bb + 3 < nbb) load(1, bb + 3);
-    }
-  }
-
-  // Epilogue: h = silu(g) * u for features frow + r*16 + 4*(lane/16) + i, row c*16 + lane%16.
-  float h[2][NC][4];
+  v4f acc[2][NC];
 #pragma unroll
   for (int r = 0; r < 2; ++r)
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
+    for (int c = 0; c < NC; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Weight stream: stage = one 16-row tile (r = 0 gate, 1 up) across KG
+  // consecutive K blocks (q-th group); slot r holds tile r, two stages in
+  // flight.  The loop body issues its loads unconditionally (a short last group
+  // re-reads the final K block, in bounds and in cache) and the last group is
+  // peeled, so the memory-counter waits stay exact and nothing is fetched twice
+  // in the steady state.
+  constexpr int KG = MOE_GU_KG;
+  const int nq = (nbb + KG - 1) / KG;
+  v4i wlo[2][KG], whi[2][KG];
+  auto load = [&](int r, int q) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gv = acc[r][c][i], uv = acc[2 + r][c][i];
-        h[r][c][i] = gv / (1.0f + expf(-gv)) * uv;
+    for (int j = 0; j < KG; ++j) {
+      const int kb = min(q * KG + j, nbb - 1);
+      wlo[r][j] = stream_load(pa[r] + kb * 128);
+      whi[r][j] = stream_load(pa[r] + kb * 128 + 64);
+    }
+  };
+  // The weight stream depends only on the tile's expert and feature slice:
+  // start it before the activation rows are staged.
+  load(0, 0);
+  load(1, 0);
+
+  if (tid < BM) {
+    int t = -1;
+    if (tid < tr.rows) t = tr.shared ? tr.m0 + tid : a.perm[a.offsets[tr.g] + tr.m0 + tid] / a.k;
+    tok[tid] = t;
+  }
+  __syncthreads();
+  {
+    const int cpr = RB / 16;
+    const uint8_t* xa = (const uint8_t*)a.xa;
+    for (int i = tid; i < BM * cpr; i += NT) {
+      const int r = i / cpr, c = i - r * cpr, t = tok[r];
+      v4i v = {0, 0, 0, 0};
+      if (t >= 0) v = *(const v4i*)(xa + (size_t)t * RB + c * 16);
+      *(v4i*)(xs + r * xstride + c * 16) = v;
+    }
+    if (WT == 2) {
+      const int nkb = a.d / 128;
+      for (int i = tid; i < BM * nkb; i += NT) {
+        const int r = i / nkb, c = i - r * nkb, t = tok[r];
+        sxs[i] = t >= 0 ? a.sxa[(size_t)t * nkb + c] : 0.f;
       }
+    }
+  }
+  __syncthreads();
+
+  auto compute = [&](int r, int q) {
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const int bb = q * KG + j;
+      if (bb >= nbb) break;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
+        const v4i blo = *(const v4i*)bp;
+        const v4i bhi = *(const v4i*)(bp + 64);
+        if constexpr (WT == 2) {
+          const float cs = sxs[(c * 16 + lr) * nbb + bb] * (r == 0 ? sgp[bb] : sup[bb]);
+          v4i b[4];
+          e4m3x16_to_bf16(blo, b[0], b[1]);
+          e4m3x16_to_bf16(bhi, b[2], b[3]);
+          acc[r][c] += kblock_e4m3_exact(wlo[r][j], whi[r][j], b) * cs;
+        } else {
+          acc[r][c] = mfma_bf16(wlo[r][j], blo, acc[r][c]);
+          acc[r][c] = mfma_bf16(whi[r][j], bhi, acc[r][c]);
+        }
+      }
+    }
+  };
+  for (int q = 0; q + 1 < nq; ++q) {
+    compute(0, q);
+    load(0, q + 1);
+    compute(1, q);
+    load(1, q + 1);
+  }
+  compute(0, nq - 1);
+  compute(1, nq - 1);
+
+  // Epilogue: h = silu(g) * u for features f0 + 4*(lane/16) + i, row c*16 + lane%16.
+  float h[NC][4];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gv = acc[0][c][i], uv = acc[1][c][i];
+      h[c][i] = gv / (1.0f + expf(-gv)) * uv;
+    }
   const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
+  const int fcol = f0 + 4 * (lane >> 4);
   if constexpr (WT == 2) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       float m = 0.f;
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(h[r][c][i]));
+      for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(h[c][i]));
       m = fmaxf(m, __shfl_xor(m, 16, kWave));
       m = fmaxf(m, __shfl_xor(m, 32, kWave));
       if (lane < 16) red[wave * BM + c * 16 + lane] = m;
@@ -262,16 +302,15 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int rr = c * 16 + lr;
-      const float amax = fmaxf(fmaxf(red[rr], red[BM + rr]), fmaxf(red[2 * BM + rr], red[3 * BM + rr]));
-      const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+      float amax = 0.f;
+#pragma unroll
+      for (int w = 0; w < kGateUpWaves; ++w) amax = fmaxf(amax, red[w * BM + rr]);
+      const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
       if (rr < tr.rows) {
         const size_t row = (size_t)(hrow0 + rr);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const uint32_t pk = pack4_e4m3(h[r][c][0] / s, h[r][c][1] / s, h[r][c][2] / s, h[r][c][3] / s);
-          *(uint32_t*)(hq + row * a.hstride + frow + r * 16 + 4 * (lane >> 4)) = pk;
-        }
-        if (wave == 0 && lane < 16) a.sh[row * gpr + nb] = s;
+        *(uint32_t*)(hq + row * a.hstride + fcol) =
+            pack4_e4m3(h[c][0] / sc, h[c][1] / sc, h[c][2] / sc, h[c][3] / sc);
+        if (wave == 0 && lane < 16) a.sh[row * gpr + nb] = sc;
       }
     }
   } else {
@@ -281,13 +320,10 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertArgs a) {
       const int rr = c * 16 + lr;
       if (rr < tr.rows) {
         const size_t row = (size_t)(hrow0 + rr);
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16(h[r][c][0]) | ((uint32_t)f32_to_bf16(h[r][c][1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16(h[r][c][2]) | ((uint32_t)f32_to_bf16(h[r][c][3]) << 16);
-          *(uint2*)(hb + row * a.hstride + frow + r * 16 + 4 * (lane >> 4)) = pk;
-        }
+        uint2 pk;
+        pk.x = (uint32_t)f32_to_bf16(h[c][0]) | ((uint32_t)f32_to_bf16(h[c][1]) << 16);
+        pk.y = (uint32_t)f32_to_bf16(h[c][2]) | ((uint32_t)f32_to_bf16(h[c][3]) << 16);
+        *(uint2*)(hb + row * a.hstride + fcol) = pk;
       }
     }
   }
@@ -296,8 +332,8 @@ __global__ __launch_bounds__(256) void gateup_mfma_kernel(ExpertArgs a) {
 // ---------------------------------------------------------------------------
 // Down projection on the matrix cores; epilogue multiplies by the pair's
 // routing weight (1 for the shared expert) and writes the fp32 partial row of
-// pair p (or P + t).  blockIdx.x = 256-feature slice of d, blockIdx.y = tile;
-// wave w owns output features nb*256 + w*64 + [0, 64) as four 16-row tiles.
+// pair p (or P + t).  blockIdx.x = 64-feature slice of d, blockIdx.y = tile;
+// wave w owns output features nb*64 + w*16 + [0, 16) (one 16-row tile).
 // ---------------------------------------------------------------------------
 template <int BM, int WT>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
@@ -319,6 +355,32 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   int* orow = (int*)(wrow + BM);                             // [BM] partial-output row
 
   const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
+  const int n0 = nb * 64 + wave * 16;
+  const bool wave_live = n0 < a.d;  // d is a multiple of 16: whole waves are live or not
+  const uint8_t* wd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * a.d * RB;
+  const uint8_t* pa = wd + (size_t)((wave_live ? n0 : 0) + lr) * RB + lk;
+  const float* sdp = nullptr;
+  if (WT == 2) {
+    const int nkb = Fg / 128;
+    sdp = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)((wave_live ? n0 : 0) / 128) * nkb;
+  }
+
+  // The weight stream depends only on the tile's expert and feature slice:
+  // request the first group before the h rows are staged.
+  constexpr int KG = 10;
+  v4i wlo[KG], whi[KG];
+  auto load_group = [&](int q0) {
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      if (q0 + j < nbb) {
+        wlo[j] = stream_load(pa + (q0 + j) * 128);
+        whi[j] = stream_load(pa + (q0 + j) * 128 + 64);
+      }
+    }
+  };
+  load_group(0);
+
   const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
   if (tid < BM) {
     int o = -1;
@@ -354,67 +416,35 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   }
   __syncthreads();
 
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
-  if (nb * 256 + wave * 64 >= a.d) return;  // d is a multiple of 64: whole waves drop out
-  const uint8_t* wd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * a.d * RB;
-  const int n0 = nb * 256 + wave * 64;
-  const uint8_t* pa[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) pa[r] = wd + (size_t)(n0 + r * 16 + lr) * RB + lk;
-  const float* sdp[4] = {nullptr, nullptr, nullptr, nullptr};
-  if (WT == 2) {
-    const int nkb = Fg / 128;
-    const float* base = tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) sdp[r] = base + (size_t)((n0 + r * 16) / 128) * nkb;
-  }
+  if (!wave_live) return;
 
-  v4f acc[4][NC];
+  v4f acc[NC];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int c = 0; c < NC; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+  // Weight stream: the wave's 16 rows are short (Fg bytes each), so a group of
+  // up to KG K blocks is requested at once and then consumed; one group covers
+  // F <= 1280 (FP8) or 640 (bf16).
+  for (int q0 = 0; q0 < nbb; q0 += KG) {
+    if (q0 > 0) load_group(q0);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
-  v4i wlo[2][4], whi[2][4];
-  auto load = [&](int s, int bb) {
+    for (int j = 0; j < KG; ++j) {
+      const int bb = q0 + j;
+      if (bb >= nbb) break;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      wlo[s][r] = __builtin_nontemporal_load((const v4i*)(pa[r] + bb * 128));
-      whi[s][r] = __builtin_nontemporal_load((const v4i*)(pa[r] + bb * 128 + 64));
-    }
-  };
-  auto compute = [&](int s, int bb) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 128 + lk;
-      const v4i blo = *(const v4i*)bp;
-      const v4i bhi = *(const v4i*)(bp + 64);
-      if constexpr (WT == 2) {
-        const float sx = shs[(c * 16 + lr) * nbb + bb];
-        v4i b[4];
-        e4m3x16_to_bf16(blo, b[0], b[1]);
-        e4m3x16_to_bf16(bhi, b[2], b[3]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const v4f p = kblock_e4m3_exact(wlo[s][r], whi[s][r], b);
-          acc[r][c] += p * (sx * sdp[r][bb]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          acc[r][c] = mfma_bf16(wlo[s][r], blo, acc[r][c]);
-          acc[r][c] = mfma_bf16(whi[s][r], bhi, acc[r][c]);
+      for (int c = 0; c < NC; ++c) {
+        const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 128 + lk;
+        const v4i blo = *(const v4i*)bp;
+        const v4i bhi = *(const v4i*)(bp + 64);
+        if constexpr (WT == 2) {
+          v4i b[4];
+          e4m3x16_to_bf16(blo, b[0], b[1]);
+          e4m3x16_to_bf16(bhi, b[2], b[3]);
+          acc[c] += kblock_e4m3_exact(wlo[j], whi[j], b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
+        } else {
+          acc[c] = mfma_bf16(wlo[j], blo, acc[c]);
+          acc[c] = mfma_bf16(whi[j], bhi, acc[c]);
         }
       }
-    }
-  };
-  load(0, 0);
-  if (nbb > 1) load(1, 1);
-  for (int bb = 0; bb < nbb; bb += 2) {
-    compute(0, bb);
-    if (bb + 2 < nbb) load(0, bb + 2);
-    if (bb + 1 < nbb) {
-      compute(1, bb + 1);
-      if (bb + 3 < nbb) load(1, bb + 3);
     }
   }
 
@@ -422,13 +452,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   for (int c = 0; c < NC; ++c) {
     const int rr = c * 16 + lr;
     if (rr < tr.rows) {
-      const float w = wrow[rr];
-      float* dst = a.part + (size_t)orow[rr] * a.d + n0 + 4 * (lane >> 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const v4f v = acc[r][c] * w;
-        *(float4*)(dst + r * 16) = make_float4(v[0], v[1], v[2], v[3]);
-      }
+      const v4f v = acc[c] * wrow[rr];
+      *(float4*)(a.part + (size_t)orow[rr] * a.d + n0 + 4 * (lane >> 4)) = make_float4(v[0], v[1], v[2], v[3]);
     }
   }
 }
@@ -555,19 +580,24 @@ hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n
   return hipGetLastError();
 }
 
-hipError_t launch_plan_tiles(const int32_t* counts, int E, int T, bool has_shared, int BM, int2* tiles,
-                             int32_t* tile_count, hipStream_t st) {
-  plan_tiles_kernel<<<1, 1024, 0, st>>>(counts, E, T, has_shared ? 1 : 0, BM, tiles, tile_count);
+hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts, int E,
+                          bool has_shared, int BM, int2* tiles, int32_t* tile_count, hipStream_t st) {
+  const int gpr = d / 128;
+  const int64_t ng = xq ? (int64_t)T * gpr : 0;
+  const int64_t blocks = (ng + 3) / 4 + 1;
+  prepare_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)x, ng, gpr, xq, sx, counts, E, T,
+                                                   has_shared ? 1 : 0, BM, tiles, tile_count);
   return hipGetLastError();
 }
 
 template <typename K>
-static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, const ExpertArgs& a) {
+static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, const ExpertArgs& a,
+                             int threads = 256) {
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  kernel<<<grid, 256, lds, st>>>(a);
+  kernel<<<grid, threads, lds, st>>>(a);
   return hipGetLastError();
 }
 
@@ -576,7 +606,7 @@ size_t gateup_lds_bytes(int BM, int wmode, int d) {
   const int EB = wmode == 2 ? 1 : 2;
   size_t b = (size_t)BM * (d * EB + 16);
   if (wmode == 2) b += (size_t)BM * (d / 128) * 4;
-  return b + 4 * BM * 4 + BM * 4;
+  return b + kGateUpWaves * BM * 4 + BM * 4;
 }
 
 size_t down_lds_bytes(int BM, int wmode, int Fg) {
@@ -593,10 +623,11 @@ hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, 
     return launch_dyn(gateup_f32_kernel<16>, dim3((Fmax + 63) / 64, max_tiles), gateup_lds_bytes(16, 0, a.d), st, a);
   const dim3 grid(Fmax / 128, max_tiles);
   const size_t lds = gateup_lds_bytes(BM, wmode, a.d);
-  if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2>, grid, lds, st, a);
-  if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2>, grid, lds, st, a);
-  if (wmode == 2 && BM == 64) return launch_dyn(gateup_mfma_kernel<64, 2>, grid, lds, st, a);
-  if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1>, grid, lds, st, a);
+  const int nt = kGateUpWaves * 64;
+  if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2>, grid, lds, st, a, nt);
+  if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2>, grid, lds, st, a, nt);
+  if (wmode == 2 && BM == 64) return launch_dyn(gateup_mfma_kernel<64, 2>, grid, lds, st, a, nt);
+  if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1>, grid, lds, st, a, nt);
   return hipErrorInvalidValue;
 }
 
@@ -604,7 +635,7 @@ hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hi
   const int Fmax = a.F > a.Fs ? a.F : a.Fs;
   if (wmode == 0)
     return launch_dyn(down_f32_kernel<16>, dim3((a.d + 63) / 64, max_tiles), down_lds_bytes(16, 0, Fmax), st, a);
-  const dim3 grid((a.d + 255) / 256, max_tiles);
+  const dim3 grid((a.d + 63) / 64, max_tiles);
   const size_t lds = down_lds_bytes(BM, wmode, Fmax);
   if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2>, grid, lds, st, a);
   if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2>, grid, lds, st, a);

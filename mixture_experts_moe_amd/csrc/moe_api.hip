@@ -14,7 +14,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
+  size_t logits, partials, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -26,10 +26,14 @@ int64_t max_tiles_for(const moe_shape& s, int BM) {
   return n;
 }
 
+// Workspace segments (256-byte aligned).  Routing uses logits (when the caller
+// passes none), partials, chunk_hist and local_rank; the forward pass
+// uses the rest.  Nothing is carried from one call to the next.
 Layout layout(const moe_shape& s) {
   const size_t T = s.T, d = s.d_model, E = s.n_experts, P = T * s.top_k;
   const size_t Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
   const bool fp8 = s.w_dtype == MOE_FP8E4M3_B128;
+  const bool xbf = s.act_dtype == MOE_BF16;
   Layout L;
   size_t o = 0;
   auto seg = [&](size_t bytes) {
@@ -38,7 +42,8 @@ Layout layout(const moe_shape& s) {
     return at;
   };
   L.logits = seg(T * E * 4);
-  L.chunk_hist = seg(moe::dispatch_chunk_hist_ints((int)P, (int)E) * 4);
+  L.partials = seg(moe::router_partial_floats(s.T, s.d_model, s.n_experts, xbf) * 4);
+  L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
   L.local_rank = seg(P * 4);
   L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int2));
   L.tile_count = seg(4);
@@ -101,21 +106,30 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
-  hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
-  const int T = shape->T, d = shape->d_model, E = shape->n_experts, k = shape->top_k, P = T * k;
-  float* logits = out->logits ? out->logits : (float*)(base + L.logits);
-  hipError_t e = moe::launch_router_logits(x, shape->act_dtype == MOE_BF16, w->w_router, logits, T, d, E,
-                                           out->status, st);
-  if (e != hipSuccess) return hip_status(e);
-  if (forced)
-    e = moe::launch_topk_forced(logits, forced, T, E, k, out->topk_idx, out->topk_w, out->status, st);
-  else
-    e = moe::launch_topk_free(logits, w->sel_bias, T, E, k, out->topk_idx, out->topk_w, st);
-  if (e != hipSuccess) return hip_status(e);
-  e = moe::launch_dispatch(out->topk_idx, P, E, (int32_t*)(base + L.chunk_hist), (int32_t*)(base + L.local_rank),
-                           out->counts, out->offsets, out->perm, out->inv_perm, st);
-  return hip_status(e);
+  moe::RouteLaunch R;
+  R.x = x;
+  R.x_bf16 = shape->act_dtype == MOE_BF16;
+  R.w_router = w->w_router;
+  R.bias = w->sel_bias;
+  R.forced = forced;
+  R.T = shape->T;
+  R.d = shape->d_model;
+  R.E = shape->n_experts;
+  R.k = shape->top_k;
+  R.logits_user = out->logits;
+  R.logits = out->logits ? out->logits : (float*)(base + L.logits);
+  R.partials = (float*)(base + L.partials);
+  R.idx = out->topk_idx;
+  R.w = out->topk_w;
+  R.chunk_hist = (int32_t*)(base + L.chunk_hist);
+  R.local_rank = (int32_t*)(base + L.local_rank);
+  R.counts = out->counts;
+  R.offsets = out->offsets;
+  R.perm = out->perm;
+  R.inv_perm = out->inv_perm;
+  R.status = out->status;
+  return hip_status(moe::launch_route(R, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -140,11 +154,11 @@ int moe_route_forced(const moe_shape* shape, const moe_weights* w, const void* x
 
 int moe_forward(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y, void* ws,
                 size_t ws_bytes, void* stream) {
-  return moe_forward_stages(shape, w, x, r, y, ws, ws_bytes, MOE_STAGE_ALL, stream);
+  return moe_forward_stages(shape, w, x, r, y, ws, ws_bytes, MOE_STAGE_ALL, nullptr, stream);
 }
 
 int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
-                       void* ws, size_t ws_bytes, uint32_t stages, void* stream) {
+                       void* ws, size_t ws_bytes, uint32_t stages, void* const* events, void* stream) {
   if (stages & ~(uint32_t)MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
   int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
@@ -199,26 +213,28 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.part = (float*)(base + L.part);
 
   hipError_t e = hipSuccess;
+  auto mark = [&](int i) {
+    if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], st);
+  };
+  mark(0);
   if (stages & MOE_STAGE_PREPARE) {
-    if (fp8) {
-      e = moe::launch_quantize_rows(x, true, T, d, (uint8_t*)(base + L.xq), (float*)(base + L.sx), st);
-      if (e != hipSuccess) return hip_status(e);
-    }
-    e = moe::launch_plan_tiles(r->counts, E, T, has_shared, BM, (int2*)(base + L.tiles),
-                               (int32_t*)(base + L.tile_count), st);
-    if (e != hipSuccess) return hip_status(e);
+    e = moe::launch_prepare(x, T, d, fp8 ? (uint8_t*)(base + L.xq) : nullptr, (float*)(base + L.sx), r->counts, E,
+                            has_shared, BM, (int2*)(base + L.tiles), (int32_t*)(base + L.tile_count), st);
+    mark(1);
   }
   const int max_tiles = (int)max_tiles_for(*shape, BM);
-  if (stages & MOE_STAGE_GATE_UP) {
+  if (e == hipSuccess && (stages & MOE_STAGE_GATE_UP)) {
     e = moe::launch_gateup(a, shape->w_dtype, BM, max_tiles, st);
-    if (e != hipSuccess) return hip_status(e);
+    mark(2);
   }
-  if (stages & MOE_STAGE_DOWN) {
+  if (e == hipSuccess && (stages & MOE_STAGE_DOWN)) {
     e = moe::launch_down(a, shape->w_dtype, BM, max_tiles, st);
-    if (e != hipSuccess) return hip_status(e);
+    mark(3);
   }
-  if (stages & MOE_STAGE_COMBINE)
+  if (e == hipSuccess && (stages & MOE_STAGE_COMBINE)) {
     e = moe::launch_combine(a.part, r->topk_idx, T, k, d, E, P, has_shared, y, shape->act_dtype == MOE_BF16, st);
+    mark(4);
+  }
   return hip_status(e);
 }
 

@@ -65,7 +65,30 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
   return v;
 }
 
-// Exclusive prefix sum over a block of 1024 threads; `tmp` holds 16 ints of LDS.
+// Exclusive prefix sum over a block of NT threads (NT a multiple of 64, <= 1024);
+// `tmp` holds 17 ints of LDS.  Returns the thread's exclusive prefix; *total
+// receives the block sum.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int* total) {
+  constexpr int NW = NT / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+  int inc = wave_incl_scan(v);
+  if (lane == kWave - 1) tmp[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < NW ? tmp[lane] : 0;
+    int wi = wave_incl_scan(w);
+    if (lane < NW) tmp[lane] = wi - w;
+    if (lane == NW - 1) tmp[16] = wi;
+  }
+  __syncthreads();
+  int r = inc - v + tmp[wave];
+  *total = tmp[16];
+  __syncthreads();
+  return r;
+}
+
+// Exclusive prefix sum over a block of 1024 threads; `tmp` holds 17 ints of LDS.
 // Returns the thread's exclusive prefix; *total receives the block sum.
 __device__ __forceinline__ int block1024_excl_scan(int v, int* tmp, int* total) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;

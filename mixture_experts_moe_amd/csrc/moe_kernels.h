@@ -30,20 +30,37 @@ struct ExpertArgs {
   float* part;                // [P+T][d] weighted expert outputs
 };
 
-hipError_t launch_router_logits(const void* x, bool x_bf16, const float* W, float* logits, int T, int d, int E,
-                                int32_t* status, hipStream_t st);
-hipError_t launch_topk_free(const float* logits, const float* bias, int T, int E, int k, int32_t* idx, float* w,
-                            hipStream_t st);
-hipError_t launch_topk_forced(const float* logits, const int32_t* forced, int T, int E, int k, int32_t* idx, float* w,
-                              int32_t* status, hipStream_t st);
-hipError_t launch_dispatch(const int32_t* idx, int P, int E, int32_t* chunk_hist, int32_t* local_rank,
-                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, hipStream_t st);
-size_t dispatch_chunk_hist_ints(int P, int E);
+// Router launch shape: token tile TT and number of K slices S (S > 1: the
+// router writes partial sums that the top-k kernel adds in slice order).
+struct RouterPlan {
+  int TT, S;
+};
+RouterPlan plan_router(int T, int d, int E, bool x_bf16);
+size_t router_partial_floats(int T, int d, int E, bool x_bf16);
+size_t dispatch_chunk_hist_ints(int T, int k, int E);
+
+struct RouteLaunch {
+  const void* x;
+  bool x_bf16;
+  const float* w_router;
+  const float* bias;       // selection bias or null
+  const int32_t* forced;   // forced ids or null
+  int T, d, E, k;
+  float* logits;           // where the final logits go (the caller's buffer or workspace)
+  float* logits_user;      // the caller's logits buffer or null
+  float* partials;         // [S][T][E] workspace when S > 1
+  int32_t* idx;
+  float* w;
+  int32_t *chunk_hist, *local_rank, *counts, *offsets, *perm, *inv_perm, *status;
+};
+hipError_t launch_route(const RouteLaunch& L, hipStream_t st);
 
 hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n_cols, uint8_t* codes, float* scales,
                                 hipStream_t st);
-hipError_t launch_plan_tiles(const int32_t* counts, int E, int T, bool has_shared, int BM, int2* tiles,
-                             int32_t* tile_count, hipStream_t st);
+// Forward preparation in one launch: E4M3 activation quantisation (when
+// xq != null) and the expert tile plan (last block).
+hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts, int E,
+                          bool has_shared, int BM, int2* tiles, int32_t* tile_count, hipStream_t st);
 hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
 hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,

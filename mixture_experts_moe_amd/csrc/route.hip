@@ -4,43 +4,143 @@
 // Pages cited by title and section:
 //   [port]  "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No."
 //   [bench] "We Stopped the Kolibri Benchmark Before Scoring One Answer"
+//
+// Launch sequence of one routing call:
+//   1. router logits, split over (token tile, expert tile, K slice);
+//   2. top-k per token-chunk block: sum of the K-slice partials (fixed order),
+//      top-k (or the forced ids), softmax weights, and the chunk's share of the
+//      dispatch.  When one block holds every pair (up to 1024 pairs, e.g. a
+//      decode batch) it completes the dispatch and the call is two launches;
+//   3. (several chunks) scan of the chunk histograms into counts and offsets;
+//   4. (several chunks) placement of every pair.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Router logits l[t][e] = sum_i x[t][i] * W_r[e][i], fp32 multiply-add
-// ([port] "The gate": every expert is scored for every token; part 3: the
-// router stays in float32).  Tiles of TT tokens x TE experts; the K dimension
-// is staged through LDS in chunks of 32; each of the 256 threads owns a
-// (TT/16) x (TE/16) register tile.
+// Router logits for bf16 activations, on the matrix cores at fp32 accuracy
+// ([port] "The gate": every expert is scored for every token; part 3 of "Taking
+// it apart": the router stays in float32, a bf16 router being one of the
+// planted bugs).  Each fp32 router weight is split exactly into three bf16
+// terms, w = hi + mid + lo (each term is the bf16 rounding of what the previous
+// ones leave, and the last remainder has at most 8 significant bits); x is
+// already bf16, so every product x*hi, x*mid, x*lo is exact in fp32 and the
+// matrix core accumulates them in fp32.  The result is an fp32 dot product of
+// x and W_r; only the summation order differs from a scalar loop.
+//
+// Block = 4 waves; block tile = TT tokens x 64 experts (16 per wave) over one K
+// slice [k0, k0 + kper).  With more than one K slice the block writes partial
+// sums part[slice][t][e], which the top-k kernel adds in slice order.
 // ---------------------------------------------------------------------------
-template <int TT, int TE, bool XBF16>
-__global__ __launch_bounds__(256) void router_logits_kernel(const void* __restrict__ x, const float* __restrict__ W,
-                                                             float* __restrict__ logits, int T, int d, int E,
-                                                             int32_t* __restrict__ status) {
+__device__ __forceinline__ void split3_bf16(const float (&w)[8], v8bf& hi, v8bf& mid, v8bf& lo) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 h = (__bf16)w[j];
+    const float r1 = w[j] - (float)h;
+    const __bf16 m = (__bf16)r1;
+    const float r2 = r1 - (float)m;
+    hi[j] = h;
+    mid[j] = m;
+    lo[j] = (__bf16)r2;
+  }
+}
+
+template <int TT>
+__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ W,
+                                                           float* __restrict__ out, int T, int d, int E, int kper,
+                                                           int32_t* __restrict__ status) {
+  constexpr int NC = TT / 16;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = (lane >> 4) * 8;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * 64 + wave * 16, k0 = blockIdx.z * kper;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0;
+  const int e = e0 + lr;
+  const bool ev = e < E;
+  const float* wp = W + (size_t)(ev ? e : E - 1) * d + k0 + lk;
+  const uint16_t* xp[NC];
+  bool tv[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = t0 + c * 16 + lr;
+    tv[c] = t < T;
+    xp[c] = x + (size_t)(tv[c] ? t : T - 1) * d + k0 + lk;
+  }
+  v4f acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  // one K step = 32: lane l holds K = step + (l/16)*8 + [0, 8) of its expert row
+  // and of its token row (the same K map on both operands)
+  float4 wa0 = *(const float4*)wp, wa1 = *(const float4*)(wp + 4);
+  v4i xb[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) xb[c] = *(const v4i*)xp[c];
+  for (int kk = 0; kk < kper; kk += 32) {
+    float wv[8] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w};
+    v4i xc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) xc[c] = xb[c];
+    if (kk + 32 < kper) {  // prefetch the next step
+      wa0 = *(const float4*)(wp + kk + 32);
+      wa1 = *(const float4*)(wp + kk + 36);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) xb[c] = *(const v4i*)(xp[c] + kk + 32);
+    }
+    if (!ev) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[j] = 0.f;
+    }
+    v8bf hi, mid, lo;
+    split3_bf16(wv, hi, mid, lo);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const v8bf b = tv[c] ? __builtin_bit_cast(v8bf, xc[c]) : v8bf{};
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[c], 0, 0, 0);
+    }
+  }
+  // lane l holds experts e0 + 4*(l/16) + i for token t0 + c*16 + l%16
+  const int eo = e0 + 4 * (lane >> 4);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = t0 + c * 16 + lr;
+    if (!tv[c]) continue;
+    float* o = out + ((size_t)blockIdx.z * T + t) * E + eo;
+    if (eo + 3 < E) {
+      *(float4*)o = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (eo + i < E) o[i] = acc[c][i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Router logits for fp32 activations: plain fp32 multiply-add, LDS-tiled; tiles
+// of TT tokens x TE experts, each of the 256 threads owning a (TT/16) x (TE/16)
+// register tile.
+// ---------------------------------------------------------------------------
+template <int TT, int TE>
+__global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x, const float* __restrict__ W,
+                                                          float* __restrict__ logits, int T, int d, int E,
+                                                          int32_t* __restrict__ status) {
   constexpr int KC = 32, MT = TT / 16, ME = TE / 16;
   __shared__ float xs[KC][TT + 1];
   __shared__ float ws[KC][TE + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
-  if (status && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *status = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *status = 0;
   float acc[MT][ME];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < ME; ++j) acc[i][j] = 0.f;
-
   for (int k0 = 0; k0 < d; k0 += KC) {
     for (int i = tid; i < TT * KC; i += 256) {
       const int r = i / KC, c = i % KC, t = t0 + r;
-      float v = 0.f;
-      if (t < T) {
-        const size_t o = (size_t)t * d + k0 + c;
-        v = XBF16 ? bf16_to_f32(((const uint16_t*)x)[o]) : ((const float*)x)[o];
-      }
-      xs[c][r] = v;
+      xs[c][r] = t < T ? x[(size_t)t * d + k0 + c] : 0.f;
     }
     for (int i = tid; i < TE * KC; i += 256) {
       const int r = i / KC, c = i % KC, e = e0 + r;
@@ -82,191 +182,251 @@ __device__ __forceinline__ uint64_t select_key(float s, int e) {
 }
 
 // ---------------------------------------------------------------------------
-// Free top-k: one wave per token.  Lane l holds candidates e = l + 64 j.  The
-// selection score is logit + bias ([port] part 1 of "Taking it apart": router
-// score plus a per-expert selection bias); k rounds of a wave-wide maximum of
-// the 64-bit key pick the experts in descending score, lowest index on ties.
-// The weights are the softmax over the chosen experts' unbiased logits
-// (normalisation sum in slot order).
+// Top-k + weights + dispatch.  Block = 16 waves over one chunk of `tpc` tokens
+// (wave w takes tokens w, w+16, ...); lane l owns the candidate experts
+// e = l + 64 j of its token.
+//
+// Free: selection score = logit + bias ([port] part 1 of "Taking it apart":
+// router score plus a per-expert selection bias); k rounds of a wave-wide
+// maximum of the 64-bit key give the experts in descending score, lowest index
+// on ties.  Forced ([bench] "The gate, forced"): the recorded ids, in the given
+// slot order; an id outside [0, E) flags the status word, becomes -1 with
+// weight 0, and the token's other slots are renormalised among themselves.
+// Weights: softmax over the chosen experts' unbiased logits, normalisation sum
+// in slot order.
+//
+// Dispatch ([port] part 3 and its update: the expert matmul consumes (token,
+// expert) rows sorted by expert): a stable counting sort of the pairs
+// p = t*k + j by expert.  The block's pairs get an LDS-atomic histogram
+// (integer, order-free) and each pair's rank among the equal ids before it in
+// the chunk.  A single block (all pairs in one chunk) finishes the sort in
+// place: scan, counts, offsets, perm, inv_perm.  With several chunks the block
+// writes its histogram and ranks; dispatch_scan_kernel and
+// dispatch_place_kernel follow as separate launches (the launch boundary makes
+// every chunk's writes visible, so no block waits on another).
 // ---------------------------------------------------------------------------
-template <int J>
-__global__ __launch_bounds__(256) void topk_free_kernel(const float* __restrict__ logits, const float* __restrict__ bias,
-                                                         int T, int E, int k, int32_t* __restrict__ idx,
-                                                         float* __restrict__ wout) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  float lv[J];
-  uint64_t key[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) {
-    const int e = lane + 64 * j;
-    lv[j] = 0.f;
-    key[j] = 0;
-    if (e < E) {
-      const float l = logits[(size_t)t * E + e];
-      lv[j] = l;
-      key[j] = select_key(bias ? l + bias[e] : l, e);
+constexpr int kMaxChunkPairs = 1024;
+
+struct TopkArgs {
+  const float* part;     // [S][T][E] logit partials (S = 1: the logits)
+  int S;
+  float* logits_out;     // [T][E] written when S > 1, or null
+  const float* bias;     // [E] or null
+  const int32_t* forced; // [T][k] or null (free routing)
+  int T, E, k, tpc;      // tpc: tokens per chunk (block)
+  int32_t* idx;          // [T][k]
+  float* w;              // [T][k]
+  int32_t* chunk_hist;   // [n_chunks][E]
+  int32_t* local_rank;   // [P]
+  int32_t* counts;       // [E]
+  int32_t* offsets;      // [E+1]
+  int32_t* perm;         // [P]
+  int32_t* inv_perm;     // [P]
+  int32_t* status;
+};
+
+template <int J, bool FORCED>
+__global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
+  __shared__ int32_t hist[kMaxExperts];
+  __shared__ int32_t ids[kMaxChunkPairs];
+  __shared__ int32_t tmp[17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E, k = a.k, T = a.T;
+  const int tok0 = blockIdx.x * a.tpc;
+  for (int i = tid; i < E; i += 1024) hist[i] = 0;
+
+  for (int tl = wave; tl < a.tpc; tl += 16) {
+    const int t = tok0 + tl;
+    if (t >= T) {
+      if (lane < k) ids[tl * k + lane] = -1;
+      continue;
     }
-  }
-  int sel[8];
-  float sl[8];
+    // logits: the K-slice partials added in slice order; all loads of a group
+    // of four slices are issued before the first add
+    float lv[J];
+    const float* __restrict__ part = a.part;
+    const size_t slice = (size_t)T * E;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    sel[r] = 0;
-    sl[r] = 0.f;
-    if (r < k) {
-      uint64_t best = 0;
+    for (int j = 0; j < J; ++j) lv[j] = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += 4) {
+      float v[4][J];
 #pragma unroll
-      for (int j = 0; j < J; ++j) best = key[j] > best ? key[j] : best;
-      best = wave_max_u64(best);
-      const int e = (int)(~(uint32_t)best);
-      float mine = 0.f;
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+          const int e = lane + 64 * j;
+          v[u][j] = (s0 + u < a.S && e < E) ? part[(s0 + u) * slice + (size_t)t * E + e] : 0.f;
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (s0 + u < a.S) lv[j] = (s0 + u == 0) ? v[u][j] : lv[j] + v[u][j];
+    }
+    if (a.logits_out) {
 #pragma unroll
       for (int j = 0; j < J; ++j)
-        if (lane + 64 * j == e) {
-          key[j] = 0;
-          mine = lv[j];
+        if (lane + 64 * j < E) a.logits_out[(size_t)t * E + lane + 64 * j] = lv[j];
+    }
+    int sel[kMaxTopK];
+    float sl[kMaxTopK];
+    if (FORCED) {
+      bool bad = false;
+#pragma unroll
+      for (int r = 0; r < kMaxTopK; ++r) {
+        sel[r] = -1;
+        sl[r] = 0.f;
+        if (r < k) {
+          const int e = a.forced[(size_t)t * k + r];
+          float mine = 0.f;
+#pragma unroll
+          for (int j = 0; j < J; ++j)
+            if (lane + 64 * j == e) mine = lv[j];
+          const float le = __shfl(mine, e & 63, kWave);
+          if (e >= 0 && e < E) {
+            sel[r] = e;
+            sl[r] = le;
+          } else {
+            bad = true;
+          }
         }
-      sel[r] = e;
-      sl[r] = __shfl(mine, e & 63, kWave);
-    }
-  }
-  float m = -INFINITY;
+      }
+      if (bad && lane == 0) *a.status = -5;  // MOE_ERR_FORCED_INDEX; every writer stores the same value
+    } else {
+      uint64_t key[J];
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-    if (r < k) m = fmaxf(m, sl[r]);
-  float ex[8], Z = 0.f;
+      for (int j = 0; j < J; ++j) {
+        const int e = lane + 64 * j;
+        key[j] = e < E ? select_key(a.bias ? lv[j] + a.bias[e] : lv[j], e) : 0;
+      }
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    ex[r] = 0.f;
-    if (r < k) {
-      ex[r] = expf(sl[r] - m);
-      Z = Z + ex[r];
-    }
-  }
+      for (int r = 0; r < kMaxTopK; ++r) {
+        sel[r] = -1;
+        sl[r] = 0.f;
+        if (r < k) {
+          uint64_t best = 0;
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-    if (r < k && lane == r) {
-      idx[(size_t)t * k + r] = sel[r];
-      wout[(size_t)t * k + r] = ex[r] / Z;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Forced top-k ([bench] "The gate, forced": recorded choices replayed at every
-// position): one thread per token; the given ids keep their slot order; an id
-// outside [0, E) flags the status word, becomes -1 with weight 0, and the
-// remaining slots are renormalised among themselves.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void topk_forced_kernel(const float* __restrict__ logits,
-                                                           const int32_t* __restrict__ forced, int T, int E, int k,
-                                                           int32_t* __restrict__ idx, float* __restrict__ wout,
-                                                           int32_t* __restrict__ status) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= T) return;
-  int sel[8];
-  float sl[8];
-  bool bad = false;
-  float m = -INFINITY;
+          for (int j = 0; j < J; ++j) best = key[j] > best ? key[j] : best;
+          best = wave_max_u64(best);
+          const int e = (int)(~(uint32_t)best);
+          float mine = 0.f;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    sel[r] = -1;
-    sl[r] = 0.f;
-    if (r < k) {
-      const int e = forced[(size_t)t * k + r];
-      if (e >= 0 && e < E) {
-        sel[r] = e;
-        sl[r] = logits[(size_t)t * E + e];
-        m = fmaxf(m, sl[r]);
-      } else {
-        bad = true;
+          for (int j = 0; j < J; ++j)
+            if (lane + 64 * j == e) {
+              key[j] = 0;
+              mine = lv[j];
+            }
+          sel[r] = e;
+          sl[r] = __shfl(mine, e & 63, kWave);
+        }
       }
     }
-  }
-  float ex[8], Z = 0.f;
+    float m = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    ex[r] = 0.f;
-    if (r < k && sel[r] >= 0) {
-      ex[r] = expf(sl[r] - m);
-      Z = Z + ex[r];
-    }
-  }
+    for (int r = 0; r < kMaxTopK; ++r)
+      if (r < k && sel[r] >= 0) m = fmaxf(m, sl[r]);
+    float ex[kMaxTopK], Z = 0.f;
 #pragma unroll
-  for (int r = 0; r < 8; ++r)
-    if (r < k) {
-      idx[(size_t)t * k + r] = sel[r];
-      wout[(size_t)t * k + r] = sel[r] >= 0 ? ex[r] / Z : 0.f;
+    for (int r = 0; r < kMaxTopK; ++r) {
+      ex[r] = 0.f;
+      if (r < k && sel[r] >= 0) {
+        ex[r] = expf(sl[r] - m);
+        Z = Z + ex[r];
+      }
     }
-  if (bad) *status = -5;  // MOE_ERR_FORCED_INDEX; every writer stores the same value
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r)
+      if (r < k && lane == r) {
+        a.idx[(size_t)t * k + r] = sel[r];
+        a.w[(size_t)t * k + r] = sel[r] >= 0 ? ex[r] / Z : 0.f;
+        ids[tl * k + r] = sel[r];
+      }
+  }
+  __syncthreads();
+
+  // this chunk's pairs: q = 0..np-1 <-> p = blockIdx.x * np + q (one per thread)
+  const int np = a.tpc * k, P = T * k, p = blockIdx.x * np + tid;
+  int e = -1, rank = 0;
+  if (tid < np) {
+    e = ids[tid];
+    if (e >= 0) atomicAdd(&hist[e], 1);
+    for (int q = 0; q < tid; ++q) rank += (ids[q] == e);
+  }
+  __syncthreads();
+  if (gridDim.x > 1) {
+    if (tid < np && p < P) a.local_rank[p] = rank;
+    for (int i = tid; i < E; i += 1024) a.chunk_hist[(size_t)blockIdx.x * E + i] = hist[i];
+    return;
+  }
+  // one chunk holds every pair: finish the counting sort here
+  const int cnt = tid < E ? hist[tid] : 0;
+  int total;
+  const int off = block1024_excl_scan(cnt, tmp, &total);
+  if (tid < E) {
+    a.counts[tid] = cnt;
+    a.offsets[tid] = off;
+    hist[tid] = off;
+  }
+  if (tid == 0) a.offsets[E] = total;
+  __syncthreads();
+  if (tid < P) {
+    if (e >= 0) {
+      const int q = hist[e] + rank;
+      a.perm[q] = p;
+      a.inv_perm[p] = q;
+    } else {
+      a.inv_perm[p] = -1;
+    }
+    if (p >= total) a.perm[p] = -1;
+  }
 }
 
-// ---------------------------------------------------------------------------
-// Dispatch: a stable counting sort of the pairs p = t*k + j by expert
-// ([port] part 3 and its update: the expert matmul consumes (token, expert)
-// rows sorted by expert).  Deterministic in three launches:
-//   1. per chunk of 256 pairs: LDS-atomic histogram (order-free integer counts)
-//      and each pair's rank among the equal ids before it in the chunk;
-//   2. one block: per expert, an exclusive scan of the chunk histograms in
-//      chunk order, the expert totals, and their exclusive scan (offsets);
-//   3. per pair: q = offsets[e] + (pairs of e in earlier chunks) + rank.
-// ---------------------------------------------------------------------------
-constexpr int kChunk = 256;
-
-__global__ __launch_bounds__(256) void dispatch_local_kernel(const int32_t* __restrict__ idx, int P, int E,
-                                                              int32_t* __restrict__ chunk_hist,
-                                                              int32_t* __restrict__ local_rank) {
-  __shared__ int32_t hist[kMaxExperts];
-  __shared__ int32_t ids[kChunk];
-  const int tid = threadIdx.x, c = blockIdx.x, p = c * kChunk + tid;
-  for (int i = tid; i < E; i += kChunk) hist[i] = 0;
-  int e = -1;
-  if (p < P) {
-    e = idx[p];
-    if (e < 0 || e >= E) e = -1;
-  }
-  ids[tid] = e;
-  __syncthreads();
-  if (e >= 0) atomicAdd(&hist[e], 1);
-  int r = 0;
-  for (int j = 0; j < tid; ++j) r += (ids[j] == e);
-  if (p < P) local_rank[p] = r;
-  __syncthreads();
-  for (int i = tid; i < E; i += kChunk) chunk_hist[(size_t)c * E + i] = hist[i];
-}
-
+// Several chunks: per expert, an exclusive scan of the chunk histograms in chunk
+// order (in place: entry [c][e] becomes the pairs of e in chunks before c), the
+// expert totals and their exclusive scan.  One block, one thread per expert.
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks, int E,
                                                               int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets) {
   __shared__ int32_t tmp[17];
-  const int e = threadIdx.x;  // E <= kMaxExperts <= 1024
+  const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int c = 0; c < n_chunks; ++c) {
-      const int h = chunk_hist[(size_t)c * E + e];
-      chunk_hist[(size_t)c * E + e] = run;
-      run += h;
+    int c = 0;
+    for (; c + 4 <= n_chunks; c += 4) {
+      int32_t* h = chunk_hist + (size_t)c * E + e;
+      const int v0 = h[0], v1 = h[E], v2 = h[2 * E], v3 = h[3 * E];
+      h[0] = run;
+      h[E] = run + v0;
+      h[2 * E] = run + v0 + v1;
+      h[3 * E] = run + v0 + v1 + v2;
+      run += v0 + v1 + v2 + v3;
+    }
+    for (; c < n_chunks; ++c) {
+      int32_t* h = chunk_hist + (size_t)c * E + e;
+      const int v = *h;
+      *h = run;
+      run += v;
     }
     counts[e] = run;
   }
   int total;
-  const int ex = block1024_excl_scan(e < E ? run : 0, tmp, &total);
-  if (e < E) offsets[e] = ex;
+  const int off = block1024_excl_scan(e < E ? run : 0, tmp, &total);
+  if (e < E) offsets[e] = off;
   if (e == 0) offsets[E] = total;
 }
 
-__global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int P, int E,
+// Placement: q = offsets[e] + (pairs of e in earlier chunks) + rank in the chunk.
+__global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int P, int E, int np,
                                                               const int32_t* __restrict__ chunk_prefix,
                                                               const int32_t* __restrict__ local_rank,
                                                               const int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ perm,
                                                               int32_t* __restrict__ inv_perm) {
-  const int c = blockIdx.x, p = c * kChunk + threadIdx.x;
+  const int p = blockIdx.x * 256 + threadIdx.x;
   if (p >= P) return;
   const int e = idx[p];
   if (e >= 0 && e < E) {
-    const int q = offsets[e] + chunk_prefix[(size_t)c * E + e] + local_rank[p];
+    const int q = offsets[e] + chunk_prefix[(size_t)(p / np) * E + e] + local_rank[p];
     perm[q] = p;
     inv_perm[p] = q;
   } else {
@@ -276,56 +436,104 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Launchers
+// Launch planning and launchers
 // ---------------------------------------------------------------------------
-hipError_t launch_router_logits(const void* x, bool x_bf16, const float* W, float* logits, int T, int d, int E,
-                                int32_t* status, hipStream_t st) {
-  if (T >= 256) {
-    dim3 grid((T + 63) / 64, (E + 63) / 64);
-    if (x_bf16) router_logits_kernel<64, 64, true><<<grid, 256, 0, st>>>(x, W, logits, T, d, E, status);
-    else router_logits_kernel<64, 64, false><<<grid, 256, 0, st>>>(x, W, logits, T, d, E, status);
-  } else {
-    dim3 grid((T + 31) / 32, (E + 15) / 16);
-    if (x_bf16) router_logits_kernel<32, 16, true><<<grid, 256, 0, st>>>(x, W, logits, T, d, E, status);
-    else router_logits_kernel<32, 16, false><<<grid, 256, 0, st>>>(x, W, logits, T, d, E, status);
+RouterPlan plan_router(int T, int d, int E, bool x_bf16) {
+  RouterPlan p;
+  if (!x_bf16) {
+    p.TT = T >= 256 ? 64 : 32;
+    p.S = 1;
+    return p;
   }
-  return hipGetLastError();
+  p.TT = T <= 16 ? 16 : (T <= 32 ? 32 : 64);
+  const int tiles = ((T + p.TT - 1) / p.TT) * ((E + 63) / 64);
+  int S = 1;
+  while (tiles * S < 256 && S * 2 <= 16 && d % (S * 2 * 128) == 0) S *= 2;
+  p.S = S;
+  return p;
 }
 
-hipError_t launch_topk_free(const float* logits, const float* bias, int T, int E, int k, int32_t* idx, float* w,
-                            hipStream_t st) {
-  const int J = (E + 63) / 64;
-  dim3 grid((T + 3) / 4);
-#define MOE_TOPK_CASE(n) \
-  case n: topk_free_kernel<n><<<grid, 256, 0, st>>>(logits, bias, T, E, k, idx, w); break;
+size_t router_partial_floats(int T, int d, int E, bool x_bf16) {
+  const RouterPlan p = plan_router(T, d, E, x_bf16);
+  return p.S > 1 ? (size_t)p.S * T * E : 0;
+}
+
+// Tokens per top-k block: all of them when their pairs fit one block, else 16
+// (64 for long inputs, to keep the chunk count and the scan short).
+int tokens_per_chunk(int T, int k) {
+  if (T * k <= kMaxChunkPairs) return T > 0 ? T : 1;
+  return T <= 4096 ? 16 : 64;
+}
+
+size_t dispatch_chunk_hist_ints(int T, int k, int E) {
+  const int tpc = tokens_per_chunk(T, k);
+  const int n_chunks = (T + tpc - 1) / tpc;
+  return n_chunks > 1 ? (size_t)n_chunks * E : 0;
+}
+
+hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
+  const RouterPlan rp = plan_router(L.T, L.d, L.E, L.x_bf16);
+  // where the router writes: final logits when there is one K slice, else partials
+  float* rout = rp.S == 1 ? L.logits : L.partials;
+  if (L.x_bf16) {
+    const dim3 grid((L.T + rp.TT - 1) / rp.TT, (L.E + 63) / 64, rp.S);
+    const int kper = L.d / rp.S;
+    const uint16_t* x = (const uint16_t*)L.x;
+    if (rp.TT == 16) router_mfma_kernel<16><<<grid, 256, 0, st>>>(x, L.w_router, rout, L.T, L.d, L.E, kper, L.status);
+    else if (rp.TT == 32) router_mfma_kernel<32><<<grid, 256, 0, st>>>(x, L.w_router, rout, L.T, L.d, L.E, kper, L.status);
+    else router_mfma_kernel<64><<<grid, 256, 0, st>>>(x, L.w_router, rout, L.T, L.d, L.E, kper, L.status);
+  } else if (rp.TT == 64) {
+    const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64);
+    router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, rout, L.T, L.d, L.E, L.status);
+  } else {
+    const dim3 grid((L.T + 31) / 32, (L.E + 15) / 16);
+    router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, rout, L.T, L.d, L.E, L.status);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int P = L.T * L.k;
+  const int tpc = tokens_per_chunk(L.T, L.k);
+  const int n_chunks = (L.T + tpc - 1) / tpc;
+  TopkArgs a;
+  a.part = rout;
+  a.S = rp.S;
+  a.logits_out = rp.S > 1 ? L.logits_user : nullptr;
+  a.bias = L.forced ? nullptr : L.bias;
+  a.forced = L.forced;
+  a.T = L.T;
+  a.E = L.E;
+  a.k = L.k;
+  a.tpc = tpc;
+  a.idx = L.idx;
+  a.w = L.w;
+  a.chunk_hist = L.chunk_hist;
+  a.local_rank = L.local_rank;
+  a.counts = L.counts;
+  a.offsets = L.offsets;
+  a.perm = L.perm;
+  a.inv_perm = L.inv_perm;
+  a.status = L.status;
+  const int J = (L.E + 63) / 64;
+#define MOE_TOPK_CASE(n)                                                                \
+  case n:                                                                               \
+    if (L.forced) topk_dispatch_kernel<n, true><<<n_chunks, 1024, 0, st>>>(a);          \
+    else topk_dispatch_kernel<n, false><<<n_chunks, 1024, 0, st>>>(a);                  \
+    break;
   switch (J) {
-    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4) MOE_TOPK_CASE(5) MOE_TOPK_CASE(6)
-    MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
+    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
+    MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
     default: return hipErrorInvalidValue;
   }
 #undef MOE_TOPK_CASE
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_forced(const float* logits, const int32_t* forced, int T, int E, int k, int32_t* idx, float* w,
-                              int32_t* status, hipStream_t st) {
-  topk_forced_kernel<<<(T + 255) / 256, 256, 0, st>>>(logits, forced, T, E, k, idx, w, status);
-  return hipGetLastError();
-}
-
-hipError_t launch_dispatch(const int32_t* idx, int P, int E, int32_t* chunk_hist, int32_t* local_rank,
-                           int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv_perm, hipStream_t st) {
-  const int n_chunks = (P + kChunk - 1) / kChunk;
-  dispatch_local_kernel<<<n_chunks, kChunk, 0, st>>>(idx, P, E, chunk_hist, local_rank);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dispatch_scan_kernel<<<1, 1024, 0, st>>>(chunk_hist, n_chunks, E, counts, offsets);
+  e = hipGetLastError();
+  if (e != hipSuccess || n_chunks == 1) return e;
+  dispatch_scan_kernel<<<1, 1024, 0, st>>>(L.chunk_hist, n_chunks, L.E, L.counts, L.offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dispatch_place_kernel<<<n_chunks, kChunk, 0, st>>>(idx, P, E, chunk_hist, local_rank, offsets, perm, inv_perm);
+  dispatch_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(L.idx, P, L.E, tpc * L.k, L.chunk_hist, L.local_rank,
+                                                         L.offsets, L.perm, L.inv_perm);
   return hipGetLastError();
 }
-
-size_t dispatch_chunk_hist_ints(int P, int E) { return (size_t)((P + kChunk - 1) / kChunk) * E; }
 
 }  // namespace moe

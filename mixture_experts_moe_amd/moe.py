@@ -68,7 +68,7 @@ def lib() -> C.CDLL:
         L.moe_route.argtypes = [p, p, p, p, p, C.c_size_t, p]
         L.moe_route_forced.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
         L.moe_forward.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
-        L.moe_forward_stages.argtypes = [p, p, p, p, p, p, C.c_size_t, C.c_uint32, p]
+        L.moe_forward_stages.argtypes = [p, p, p, p, p, p, C.c_size_t, C.c_uint32, p, p]
         L.moe_quantize_rows.argtypes = [i64, i32, i32, p, p, p, p]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
@@ -170,10 +170,21 @@ def forward(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor,
     _check(rc, "moe_forward")
 
 
+def _events(events):
+    """torch.cuda.Event list -> hipEvent_t[5] (or None)."""
+    if events is None:
+        return None
+    assert len(events) == 5
+    for ev in events:
+        if ev.cuda_event == 0:  # torch creates the HIP event lazily
+            ev.record()
+    return (C.c_void_p * 5)(*[ev.cuda_event for ev in events])
+
+
 def forward_stages(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor, ws: torch.Tensor,
-                   stages: int, stream=None):
+                   stages: int, events=None, stream=None):
     rc = lib().moe_forward_stages(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), C.byref(r.struct()), _ptr(y),
-                                  _ptr(ws), ws.numel(), stages, _stream(stream))
+                                  _ptr(ws), ws.numel(), stages, _events(events), _stream(stream))
     _check(rc, "moe_forward_stages")
 
 
@@ -213,6 +224,6 @@ class Bound:
             _check(self.L.moe_route_forced(*self.args, self.forced, C.byref(self.r), *self.ws, self.stream),
                    "moe_route_forced")
 
-    def forward(self, stages: int = STAGE_ALL):
-        _check(self.L.moe_forward_stages(*self.args, C.byref(self.r), self.y, *self.ws, stages, self.stream),
-               "moe_forward_stages")
+    def forward(self, stages: int = STAGE_ALL, events=None):
+        _check(self.L.moe_forward_stages(*self.args, C.byref(self.r), self.y, *self.ws, stages, _events(events),
+                                         self.stream), "moe_forward_stages")
