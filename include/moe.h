@@ -58,6 +58,13 @@ typedef enum {
  * Limits: 1 <= top_k <= 8, top_k <= n_experts <= 512, d_model and d_ffn multiples
  * of 128 with d_model <= 8192 and d_ffn <= 4096, d_ffn_shared 0 (no shared expert)
  * or a multiple of 128 <= 4096, T * top_k < 2^31. */
+/* Layouts of the expert weight matrices (moe_shape.w_layout). */
+typedef enum {
+  MOE_LAYOUT_ROWMAJOR = 0,   /* [rows][cols] row-major, as documented per tensor */
+  MOE_LAYOUT_TILED = 1       /* the same bytes regrouped by moe_pack_weights into 2 KB
+                                tiles of 16 rows x 128 bytes (bf16: 64 columns) */
+} moe_layout;
+
 typedef struct {
   int32_t T;             /* tokens in this call */
   int32_t d_model;       /* d */
@@ -67,6 +74,8 @@ typedef struct {
   int32_t d_ffn_shared;  /* Fs, shared expert FFN width; 0 = no shared expert */
   int32_t act_dtype;     /* moe_dtype of x and y: MOE_F32 or MOE_BF16 */
   int32_t w_dtype;       /* moe_dtype of the expert weights */
+  int32_t w_layout;      /* moe_layout of w_gate, w_up, w_down, sh_gate, sh_up, sh_down;
+                            MOE_LAYOUT_TILED needs w_dtype BF16 or FP8E4M3_B128 */
 } moe_shape;
 
 /* Layer weights.  Expert matrices are (out, in) row-major and stacked by expert.
@@ -173,6 +182,19 @@ int moe_forward_stages(const moe_shape *shape, const moe_weights *w, const void 
  * dynamic reading. */
 int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const void *in, uint8_t *codes,
                       float *scales, void *stream);
+
+/* Regroups n_mats row-major matrices of [rows][row_bytes] bytes (rows a multiple
+ * of 16, row_bytes a multiple of 128) into MOE_LAYOUT_TILED, one matrix after the
+ * other in `out` (same total size; `in` and `out` must not overlap).  Tile
+ * (rt, kb) of a matrix -- rows 16*rt .. 16*rt+15, bytes 128*kb .. 128*kb+127 of
+ * each -- is stored at byte 2048*(rt*(row_bytes/128) + kb); inside a tile, byte j
+ * (0..15) of slot (h, l) at 1024*h + 16*l holds row 16*rt + l%16, byte
+ * 128*kb + 16*(l/16) + 64*h + j.  Each 16-row tile of a matrix is then one
+ * contiguous run that the expert kernels stream in full cache lines.  Pack
+ * w_gate and w_up as (E, F, d*bytes), w_down as (E, d, F*bytes), the shared
+ * matrices with n_mats = 1; scales, router and bias keep their layout.  This
+ * is a data-layout choice of this library, not something the method needs. */
+int moe_pack_weights(int64_t n_mats, int32_t rows, int32_t row_bytes, const void *in, void *out, void *stream);
 
 /* Static description of a status code. */
 const char *moe_status_string(int status);

@@ -21,6 +21,8 @@
 // weights stream from HBM straight into matrix-core operand registers (each
 // weight byte is read once per tile), while the tile's activation rows sit in
 // LDS for the whole K loop.
+#include <limits.h>
+
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -117,6 +119,30 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict
   if (threadIdx.x == 0) *tile_count = total;
 }
 
+// Address of the weight bytes a lane streams for one 16-row tile: in the
+// row-major layout lane l reads row (16*rt + l%16) at byte 16*(l/16) of each
+// 128-byte K block (and 64 further for the upper half); in the tiled layout the
+// same bytes sit at 16*l of the tile's 2 KB (upper half: +1024).
+struct WeightStream {
+  const uint8_t* p;  // this lane's first byte in K block 0 of the tile
+  int kb_stride;     // bytes from one K block to the next
+  int hi_off;        // bytes from the lower to the upper 64-byte half
+};
+__device__ __forceinline__ WeightStream weight_stream(const uint8_t* mat, int row_bytes, int row0, bool tiled,
+                                                      int lane) {
+  WeightStream w;
+  if (tiled) {
+    w.p = mat + (size_t)(row0 / 16) * (row_bytes / 128) * 2048 + lane * 16;
+    w.kb_stride = 2048;
+    w.hi_off = 1024;
+  } else {
+    w.p = mat + (size_t)(row0 + (lane & 15)) * row_bytes + (lane >> 4) * 16;
+    w.kb_stride = 128;
+    w.hi_off = 64;
+  }
+  return w;
+}
+
 // Rows of one tile: for each of its BM rows, the activation (token) row, the
 // output row of h (sorted pair index, or P + t for the shared expert), the
 // partial-output row (pair index p, or P + t) and the routing weight.
@@ -124,6 +150,22 @@ struct TileRows {
   int g, m0, rows;
   bool shared;
 };
+
+// Work item of a block in a 1-D grid of n_slices x max_tiles blocks (max_tiles
+// is an upper bound: the actual tile count is only known on the device).  Items
+// run slice-fastest, so the feature slices of one tile (all reading the tile's
+// activation rows, and together one contiguous run of its expert's weights) are
+// dispatched together.  Blocks past the live tiles are idle.
+struct WorkItem {
+  int tile, slice;
+};
+inline unsigned work_grid(int n_items) { return (unsigned)n_items; }
+__device__ __forceinline__ WorkItem work_item(int n_slices) {
+  WorkItem it;
+  it.tile = blockIdx.x / n_slices;
+  it.slice = blockIdx.x % n_slices;
+  return it;
+}
 
 __device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile, int BM) {
   const int2 td = a.tiles[tile];
@@ -145,8 +187,8 @@ __device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile, int
 //           epilogue.
 //   WT = 1: bf16 weights and activations, 16x16x32 MFMA accumulating in fp32;
 //           h stored as bf16.
-// Block = 8 waves covering one 128-feature group nb of h (blockIdx.x) for one
-// tile (blockIdx.y).  Wave w owns h features nb*128 + w*16 + [0, 16): one 16-row
+// Block = 8 waves covering one 128-feature group nb of h for one tile (see
+// work_item).  Wave w owns h features nb*128 + w*16 + [0, 16): one 16-row
 // tile of W_gate and the same rows of W_up, so g and u of a feature meet in one
 // lane.  32 weight rows per wave keeps many short streams in flight, which the
 // HBM prefers to a few long ones.
@@ -158,11 +200,12 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;  // bytes per element
   constexpr int NT = kGateUpWaves * 64;
-  const int tile = blockIdx.y;
+  const WorkItem it = work_item(a.n_slices);
+  const int tile = it.tile;
   if (tile >= *a.tile_count) return;
   const TileRows tr = tile_rows(a, tile, BM);
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int nb = blockIdx.x;
+  const int nb = it.slice;
   if (nb * 128 >= Fg) return;
 
   const int RB = a.d * EB;        // bytes per activation / weight row
@@ -180,7 +223,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
   const uint8_t* wg = tr.shared ? (const uint8_t*)a.shg : (const uint8_t*)a.wg + (size_t)tr.g * wsz;
   const uint8_t* wu = tr.shared ? (const uint8_t*)a.shu : (const uint8_t*)a.wu + (size_t)tr.g * wsz;
   const int f0 = nb * 128 + wave * 16;
-  const uint8_t* pa[2] = {wg + (size_t)(f0 + lr) * RB + lk, wu + (size_t)(f0 + lr) * RB + lk};
+  const WeightStream ws[2] = {weight_stream(wg, RB, f0, a.w_tiled, lane), weight_stream(wu, RB, f0, a.w_tiled, lane)};
   const float* sgp = nullptr;
   const float* sup = nullptr;
   if (WT == 2) {
@@ -209,8 +252,9 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       const int kb = min(q * KG + j, nbb - 1);
-      wlo[r][j] = stream_load(pa[r] + kb * 128);
-      whi[r][j] = stream_load(pa[r] + kb * 128 + 64);
+      const uint8_t* p = ws[r].p + (size_t)kb * ws[r].kb_stride;
+      wlo[r][j] = stream_load(p);
+      whi[r][j] = stream_load(p + ws[r].hi_off);
     }
   };
   // The weight stream depends only on the tile's expert and feature slice:
@@ -332,17 +376,21 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 // ---------------------------------------------------------------------------
 // Down projection on the matrix cores; epilogue multiplies by the pair's
 // routing weight (1 for the shared expert) and writes the fp32 partial row of
-// pair p (or P + t).  blockIdx.x = 64-feature slice of d, blockIdx.y = tile;
-// wave w owns output features nb*64 + w*16 + [0, 16) (one 16-row tile).
+// pair p (or P + t).  A block takes one tile and one slice of 64*RT output
+// features (see work_item); wave w owns RT 16-row tiles (features nb*64*RT + w*16*RT + 16 r).
+// RT = 1 for short tiles (many small blocks keep the HBM busy); RT = 4 for tall
+// tiles, so a tile's h rows are staged once per 256 features.
 // ---------------------------------------------------------------------------
-template <int BM, int WT>
+template <int BM, int WT, int RT>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;
-  const int tile = blockIdx.y;
+  constexpr int KG = RT == 1 ? 10 : 5;  // K blocks requested per stage
+  const WorkItem it = work_item(a.n_slices);
+  const int tile = it.tile;
   if (tile >= *a.tile_count) return;
   const TileRows tr = tile_rows(a, tile, BM);
-  const int nb = blockIdx.x;
+  const int nb = it.slice;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int RB = Fg * EB;          // bytes per h row / W_down row
   const int nbb = RB / 128;
@@ -356,30 +404,34 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
-  const int n0 = nb * 64 + wave * 16;
-  const bool wave_live = n0 < a.d;  // d is a multiple of 16: whole waves are live or not
+  const int n0 = (nb * 4 + wave) * 16 * RT;
+  const bool wave_live = n0 < a.d;  // d is a multiple of 16*RT here: whole waves are live or not
   const uint8_t* wd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * a.d * RB;
-  const uint8_t* pa = wd + (size_t)((wave_live ? n0 : 0) + lr) * RB + lk;
+  const int nl = wave_live ? n0 : 0;
+  const WeightStream ws = weight_stream(wd, RB, nl, a.w_tiled, lane);
+  // 16-row tile r of the wave starts 16*r rows (tiled: r tiles) further on
+  const size_t tile_step = a.w_tiled ? (size_t)nbb * 2048 : (size_t)16 * RB;
   const float* sdp = nullptr;
   if (WT == 2) {
     const int nkb = Fg / 128;
-    sdp = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)((wave_live ? n0 : 0) / 128) * nkb;
+    sdp = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)(nl / 128) * nkb;
   }
-
   // The weight stream depends only on the tile's expert and feature slice:
-  // request the first group before the h rows are staged.
-  constexpr int KG = 10;
-  v4i wlo[KG], whi[KG];
-  auto load_group = [&](int q0) {
+  // request it before the h rows are staged.  A stage = KG K blocks of one
+  // 16-row tile; two stages in flight.
+  v4i wlo[2][KG], whi[2][KG];
+  auto load = [&](int slot, int r, int q0) {
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       if (q0 + j < nbb) {
-        wlo[j] = stream_load(pa + (q0 + j) * 128);
-        whi[j] = stream_load(pa + (q0 + j) * 128 + 64);
+        const uint8_t* p = ws.p + r * tile_step + (size_t)(q0 + j) * ws.kb_stride;
+        wlo[slot][j] = stream_load(p);
+        whi[slot][j] = stream_load(p + ws.hi_off);
       }
     }
   };
-  load_group(0);
+  load(0, 0, 0);
+  if (RT > 1) load(1, 1, 0);
 
   const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
   if (tid < BM) {
@@ -415,17 +467,14 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
     }
   }
   __syncthreads();
-
   if (!wave_live) return;
 
-  v4f acc[NC];
+  v4f acc[RT][NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-  // Weight stream: the wave's 16 rows are short (Fg bytes each), so a group of
-  // up to KG K blocks is requested at once and then consumed; one group covers
-  // F <= 1280 (FP8) or 640 (bf16).
-  for (int q0 = 0; q0 < nbb; q0 += KG) {
-    if (q0 > 0) load_group(q0);
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int slot, int r, int q0) {
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       const int bb = q0 + j;
@@ -439,23 +488,42 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
           v4i b[4];
           e4m3x16_to_bf16(blo, b[0], b[1]);
           e4m3x16_to_bf16(bhi, b[2], b[3]);
-          acc[c] += kblock_e4m3_exact(wlo[j], whi[j], b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
+          // the wave's 16*RT <= 64 rows start at a multiple of 64: one 128-row scale block
+          acc[r][c] += kblock_e4m3_exact(wlo[slot][j], whi[slot][j], b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
         } else {
-          acc[c] = mfma_bf16(wlo[j], blo, acc[c]);
-          acc[c] = mfma_bf16(whi[j], bhi, acc[c]);
+          acc[r][c] = mfma_bf16(wlo[slot][j], blo, acc[r][c]);
+          acc[r][c] = mfma_bf16(whi[slot][j], bhi, acc[r][c]);
         }
       }
+    }
+  };
+  if constexpr (RT == 1) {
+    // short rows: one tile, groups of KG K blocks
+    compute(0, 0, 0);
+    for (int q0 = KG; q0 < nbb; q0 += KG) {
+      load(0, 0, q0);
+      compute(0, 0, q0);
+    }
+  } else {
+    // RT tiles of up to KG K blocks each (nbb <= KG), two in flight
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+      compute(r & 1, r, 0);
+      if (r + 2 < RT) load(r & 1, r + 2, 0);
     }
   }
 
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int rr = c * 16 + lr;
-    if (rr < tr.rows) {
-      const v4f v = acc[c] * wrow[rr];
-      *(float4*)(a.part + (size_t)orow[rr] * a.d + n0 + 4 * (lane >> 4)) = make_float4(v[0], v[1], v[2], v[3]);
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int rr = c * 16 + lr;
+      if (rr < tr.rows) {
+        const v4f v = acc[r][c] * wrow[rr];
+        *(float4*)(a.part + (size_t)orow[rr] * a.d + n0 + r * 16 + 4 * (lane >> 4)) =
+            make_float4(v[0], v[1], v[2], v[3]);
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -617,11 +685,14 @@ size_t down_lds_bytes(int BM, int wmode, int Fg) {
   return b + BM * 4 + BM * 4;
 }
 
-hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st) {
+hipError_t launch_gateup(const ExpertArgs& a0, int wmode, int BM, int max_tiles, hipStream_t st) {
+  ExpertArgs a = a0;
   const int Fmax = a.F > a.Fs ? a.F : a.Fs;
   if (wmode == 0)
     return launch_dyn(gateup_f32_kernel<16>, dim3((Fmax + 63) / 64, max_tiles), gateup_lds_bytes(16, 0, a.d), st, a);
-  const dim3 grid(Fmax / 128, max_tiles);
+  a.max_tiles = max_tiles;
+  a.n_slices = Fmax / 128;
+  const dim3 grid(work_grid(a.n_slices * max_tiles));
   const size_t lds = gateup_lds_bytes(BM, wmode, a.d);
   const int nt = kGateUpWaves * 64;
   if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2>, grid, lds, st, a, nt);
@@ -631,17 +702,53 @@ hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, 
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st) {
+hipError_t launch_down(const ExpertArgs& a0, int wmode, int BM, int max_tiles, hipStream_t st) {
+  ExpertArgs a = a0;
   const int Fmax = a.F > a.Fs ? a.F : a.Fs;
   if (wmode == 0)
     return launch_dyn(down_f32_kernel<16>, dim3((a.d + 63) / 64, max_tiles), down_lds_bytes(16, 0, Fmax), st, a);
-  const dim3 grid((a.d + 63) / 64, max_tiles);
   const size_t lds = down_lds_bytes(BM, wmode, Fmax);
-  if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2>, grid, lds, st, a);
-  if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2>, grid, lds, st, a);
-  if (wmode == 2 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2>, grid, lds, st, a);
-  if (wmode == 1 && BM == 16) return launch_dyn(down_mfma_kernel<16, 1>, grid, lds, st, a);
+  // tall tiles: 4 row tiles per wave (needs the whole K of a row in one stage)
+  const bool wide = BM >= 32 && Fmax * (wmode == 2 ? 1 : 2) <= 5 * 128 && a.d % 256 == 0;
+  a.max_tiles = max_tiles;
+  a.n_slices = wide ? a.d / 256 : (a.d + 63) / 64;
+  const dim3 grid(work_grid(a.n_slices * max_tiles));
+  if (wide) {
+    if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
+    if (wmode == 2 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 4>, grid, lds, st, a);
+  }
+  if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 1>, grid, lds, st, a);
+  if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 1>, grid, lds, st, a);
+  if (wmode == 2 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 1>, grid, lds, st, a);
+  if (wmode == 1 && BM == 16) return launch_dyn(down_mfma_kernel<16, 1, 1>, grid, lds, st, a);
   return hipErrorInvalidValue;
+}
+
+// ---------------------------------------------------------------------------
+// Weight packing into MOE_LAYOUT_TILED: one thread per 16-byte slot; writes are
+// consecutive, reads gather 16 rows.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_weights_kernel(const uint8_t* __restrict__ in, uint8_t* __restrict__ out,
+                                                           int64_t n_slots, int rows, int row_bytes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_slots) return;
+  const int nkb = row_bytes / 128;
+  const int64_t mat_slots = (int64_t)rows * row_bytes / 16;
+  const int64_t m = i / mat_slots;
+  const int64_t r = i - m * mat_slots;  // slot within the matrix
+  const int64_t tile = r / 128;         // 2 KB = 128 slots per tile
+  const int s = (int)(r % 128), h = s / 64, l = s % 64;
+  const int rt = (int)(tile / nkb), kb = (int)(tile % nkb);
+  const int row = rt * 16 + (l & 15), byte = kb * 128 + (l >> 4) * 16 + h * 64;
+  const uint8_t* src = in + m * rows * (int64_t)row_bytes + (int64_t)row * row_bytes + byte;
+  *(v4i*)(out + i * 16) = *(const v4i*)src;
+}
+
+hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out, hipStream_t st) {
+  const int64_t n_slots = n_mats * rows * (int64_t)row_bytes / 16;
+  const int64_t blocks = (n_slots + 255) / 256;
+  pack_weights_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint8_t*)in, (uint8_t*)out, n_slots, rows, row_bytes);
+  return hipGetLastError();
 }
 
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,

@@ -14,7 +14,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, partials, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
+  size_t logits, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -27,13 +27,12 @@ int64_t max_tiles_for(const moe_shape& s, int BM) {
 }
 
 // Workspace segments (256-byte aligned).  Routing uses logits (when the caller
-// passes none), partials, chunk_hist and local_rank; the forward pass
+// passes none), chunk_hist and local_rank; the forward pass
 // uses the rest.  Nothing is carried from one call to the next.
 Layout layout(const moe_shape& s) {
   const size_t T = s.T, d = s.d_model, E = s.n_experts, P = T * s.top_k;
   const size_t Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
   const bool fp8 = s.w_dtype == MOE_FP8E4M3_B128;
-  const bool xbf = s.act_dtype == MOE_BF16;
   Layout L;
   size_t o = 0;
   auto seg = [&](size_t bytes) {
@@ -42,7 +41,6 @@ Layout layout(const moe_shape& s) {
     return at;
   };
   L.logits = seg(T * E * 4);
-  L.partials = seg(moe::router_partial_floats(s.T, s.d_model, s.n_experts, xbf) * 4);
   L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
   L.local_rank = seg(P * 4);
   L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int2));
@@ -67,12 +65,14 @@ int validate_shape(const moe_shape* s) {
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128);
   if (!combo) return MOE_ERR_UNSUPPORTED;
+  if (s->w_layout != MOE_LAYOUT_ROWMAJOR && s->w_layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
+  if (s->w_layout == MOE_LAYOUT_TILED && s->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 128 || s->d_ffn % 128 || s->d_ffn_shared % 128) return MOE_ERR_UNSUPPORTED;
   if (s->d_model > 8192 || s->d_ffn > 4096 || s->d_ffn_shared > 4096) return MOE_ERR_UNSUPPORTED;
   const int Fmax = s->d_ffn > s->d_ffn_shared ? s->d_ffn : s->d_ffn_shared;
   if (moe::gateup_lds_bytes(16, s->w_dtype, s->d_model) > kMaxLds) return MOE_ERR_UNSUPPORTED;
   if (moe::down_lds_bytes(16, s->w_dtype, Fmax) > kMaxLds) return MOE_ERR_UNSUPPORTED;
-  if (max_tiles_for(*s, 16) > 65535) return MOE_ERR_UNSUPPORTED;
+  if (max_tiles_for(*s, 16) * (s->d_model / 64) > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -81,7 +81,7 @@ int validate_shape(const moe_shape* s) {
 int pick_bm(const moe_shape& s) {
   if (s.w_dtype != MOE_FP8E4M3_B128) return 16;
   const int64_t per_expert = (int64_t)s.T * s.top_k / s.n_experts;
-  int bm = per_expert <= 16 ? 16 : (per_expert <= 48 ? 32 : 64);
+  int bm = per_expert <= 12 ? 16 : 32;
   const int Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
   while (bm > 16 && (moe::gateup_lds_bytes(bm, s.w_dtype, s.d_model) > kMaxLds ||
                      moe::down_lds_bytes(bm, s.w_dtype, Fmax) > kMaxLds))
@@ -117,9 +117,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   R.d = shape->d_model;
   R.E = shape->n_experts;
   R.k = shape->top_k;
-  R.logits_user = out->logits;
   R.logits = out->logits ? out->logits : (float*)(base + L.logits);
-  R.partials = (float*)(base + L.partials);
   R.idx = out->topk_idx;
   R.w = out->topk_w;
   R.chunk_hist = (int32_t*)(base + L.chunk_hist);
@@ -194,6 +192,9 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.Fs = shape->d_ffn_shared;
   a.P = P;
   a.hstride = a.F > a.Fs ? a.F : a.Fs;
+  a.max_tiles = 0;
+  a.n_slices = 0;
+  a.w_tiled = shape->w_layout == MOE_LAYOUT_TILED;
   a.xa = fp8 ? (const void*)(base + L.xq) : x;
   a.sxa = (const float*)(base + L.sx);
   a.wg = w->w_gate;
@@ -247,6 +248,18 @@ int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const v
   if (n_rows * (n_cols / 128) / 4 >= (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_quantize_rows(in, act_dtype == MOE_BF16, n_rows, n_cols, codes, scales,
                                               (hipStream_t)stream));
+}
+
+int moe_pack_weights(int64_t n_mats, int32_t rows, int32_t row_bytes, const void* in, void* out, void* stream) {
+  if (n_mats < 0 || rows <= 0 || row_bytes <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 16 || row_bytes % 128) return MOE_ERR_UNSUPPORTED;
+  if (n_mats == 0) return MOE_OK;
+  if (!in || !out) return MOE_ERR_INVALID_ARG;
+  const int64_t bytes = n_mats * rows * (int64_t)row_bytes;
+  const char *i0 = (const char*)in, *o0 = (const char*)out;
+  if (i0 < o0 + bytes && o0 < i0 + bytes) return MOE_ERR_INVALID_ARG;  // overlap
+  if (bytes / 16 / 256 >= (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_pack_weights(n_mats, rows, row_bytes, in, out, (hipStream_t)stream));
 }
 
 const char* moe_status_string(int status) {

@@ -54,6 +54,24 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+// Maximum of an unsigned value over the 64 lanes of a wave, returned to every
+// lane.  DPP row shifts build each 16-lane row's maximum in its lane 15, two
+// row broadcasts carry it to lane 63, and readlane returns it; lanes whose DPP
+// source is out of range read 0, the identity of an unsigned maximum.
+__device__ __forceinline__ uint32_t wave_umax(uint32_t v) {
+#define MOE_DPP_MAX(ctrl, rmask, bmask) \
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, (ctrl), (rmask), (bmask), false))
+  MOE_DPP_MAX(0x111, 0xf, 0xf);  // row_shr:1
+  MOE_DPP_MAX(0x112, 0xf, 0xf);  // row_shr:2
+  MOE_DPP_MAX(0x113, 0xf, 0xf);  // row_shr:3
+  MOE_DPP_MAX(0x114, 0xf, 0xe);  // row_shr:4, banks 1-3
+  MOE_DPP_MAX(0x118, 0xf, 0xc);  // row_shr:8, banks 2-3
+  MOE_DPP_MAX(0x142, 0xa, 0xf);  // row_bcast:15 into rows 1 and 3
+  MOE_DPP_MAX(0x143, 0xc, 0xf);  // row_bcast:31 into rows 2 and 3
+#undef MOE_DPP_MAX
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int lane = threadIdx.x & (kWave - 1);

@@ -19,6 +19,8 @@ struct ExpertArgs {
   const float* topk_w;        // [P]
   int T, d, E, k, F, Fs, P;
   int hstride;                // elements per h row = max(F, Fs)
+  int max_tiles, n_slices;    // 1-D launch: n_slices feature slices x max_tiles tiles
+  int w_tiled;                // weights in MOE_LAYOUT_TILED
   const void* xa;             // gate/up input rows: E4M3 codes, bf16 or fp32 [T][d]
   const float* sxa;           // E4M3 activation scales [T][d/128]
   const void *wg, *wu, *wd;
@@ -30,13 +32,6 @@ struct ExpertArgs {
   float* part;                // [P+T][d] weighted expert outputs
 };
 
-// Router launch shape: token tile TT and number of K slices S (S > 1: the
-// router writes partial sums that the top-k kernel adds in slice order).
-struct RouterPlan {
-  int TT, S;
-};
-RouterPlan plan_router(int T, int d, int E, bool x_bf16);
-size_t router_partial_floats(int T, int d, int E, bool x_bf16);
 size_t dispatch_chunk_hist_ints(int T, int k, int E);
 
 struct RouteLaunch {
@@ -46,9 +41,7 @@ struct RouteLaunch {
   const float* bias;       // selection bias or null
   const int32_t* forced;   // forced ids or null
   int T, d, E, k;
-  float* logits;           // where the final logits go (the caller's buffer or workspace)
-  float* logits_user;      // the caller's logits buffer or null
-  float* partials;         // [S][T][E] workspace when S > 1
+  float* logits;           // where the logits go (the caller's buffer or workspace)
   int32_t* idx;
   float* w;
   int32_t *chunk_hist, *local_rank, *counts, *offsets, *perm, *inv_perm, *status;
@@ -63,6 +56,8 @@ hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, c
                           bool has_shared, int BM, int2* tiles, int32_t* tile_count, hipStream_t st);
 hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
 hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
+hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
+                               hipStream_t st);
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,
                           void* y, bool bf16_out, hipStream_t st);
 size_t gateup_lds_bytes(int BM, int wmode, int d);

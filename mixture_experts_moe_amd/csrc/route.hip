@@ -6,10 +6,9 @@
 //   [bench] "We Stopped the Kolibri Benchmark Before Scoring One Answer"
 //
 // Launch sequence of one routing call:
-//   1. router logits, split over (token tile, expert tile, K slice);
-//   2. top-k per token-chunk block: sum of the K-slice partials (fixed order),
-//      top-k (or the forced ids), softmax weights, and the chunk's share of the
-//      dispatch.  When one block holds every pair (up to 1024 pairs, e.g. a
+//   1. router logits, one block per (token tile, 16 experts);
+//   2. top-k per token-chunk block: top-k (or the forced ids), softmax weights,
+//      and the chunk's share of the dispatch.  When one block holds every pair (up to 1024 pairs, e.g. a
 //      decode batch) it completes the dispatch and the call is two launches;
 //   3. (several chunks) scan of the chunk histograms into counts and offsets;
 //   4. (several chunks) placement of every pair.
@@ -29,10 +28,13 @@ namespace moe {
 // matrix core accumulates them in fp32.  The result is an fp32 dot product of
 // x and W_r; only the summation order differs from a scalar loop.
 //
-// Block = 4 waves; block tile = TT tokens x 64 experts (16 per wave) over one K
-// slice [k0, k0 + kper).  With more than one K slice the block writes partial
-// sums part[slice][t][e], which the top-k kernel adds in slice order.
+// Block = 16 waves over one tile of 16 experts x TT tokens; wave w takes one
+// sixteenth of the K range (whole 128-wide blocks), so each wave's loads go out
+// in one round, and the sixteen partial sums are added through LDS in wave
+// order (fixed, so the result does not depend on timing).
 // ---------------------------------------------------------------------------
+constexpr int kRouterWaves = 16;
+
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], v8bf& hi, v8bf& mid, v8bf& lo) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -47,13 +49,18 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], v8bf& hi, v8bf&
 }
 
 template <int TT>
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ W,
-                                                           float* __restrict__ out, int T, int d, int E, int kper,
-                                                           int32_t* __restrict__ status) {
+__global__ __launch_bounds__(1024) void router_mfma_kernel(const uint16_t* __restrict__ x,
+                                                                         const float* __restrict__ W,
+                                                                         float* __restrict__ logits, int T, int d,
+                                                                         int E, int32_t* __restrict__ status) {
   constexpr int NC = TT / 16;
+  __shared__ float red[kRouterWaves][NC][4][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = (lane >> 4) * 8;
-  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * 64 + wave * 16, k0 = blockIdx.z * kper;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * 16;
+  // wave w takes K blocks [w*pw, min((w+1)*pw, nkb)) of 128 (d is a multiple of 128)
+  const int nkb = d / 128, pw = (nkb + kRouterWaves - 1) / kRouterWaves;
+  const int k0 = min(wave * pw, nkb) * 128, kper = min((wave + 1) * pw, nkb) * 128 - k0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
   const int e = e0 + lr;
   const bool ev = e < E;
   const float* wp = W + (size_t)(ev ? e : E - 1) * d + k0 + lk;
@@ -70,50 +77,50 @@ __global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t* __rest
   for (int c = 0; c < NC; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
 
   // one K step = 32: lane l holds K = step + (l/16)*8 + [0, 8) of its expert row
-  // and of its token row (the same K map on both operands)
-  float4 wa0 = *(const float4*)wp, wa1 = *(const float4*)(wp + 4);
-  v4i xb[NC];
+  // and of its token row (the same K map on both operands); all steps of the
+  // slice are requested before the first product
+  for (int kk = 0; kk < kper; kk += 128) {
+    float4 wa[4][2];
+    v4i xb[4][NC];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) xb[c] = *(const v4i*)xp[c];
-  for (int kk = 0; kk < kper; kk += 32) {
-    float wv[8] = {wa0.x, wa0.y, wa0.z, wa0.w, wa1.x, wa1.y, wa1.z, wa1.w};
-    v4i xc[NC];
+    for (int u = 0; u < 4; ++u) {
+      wa[u][0] = *(const float4*)(wp + kk + 32 * u);
+      wa[u][1] = *(const float4*)(wp + kk + 32 * u + 4);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) xc[c] = xb[c];
-    if (kk + 32 < kper) {  // prefetch the next step
-      wa0 = *(const float4*)(wp + kk + 32);
-      wa1 = *(const float4*)(wp + kk + 36);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) xb[c] = *(const v4i*)(xp[c] + kk + 32);
+      for (int c = 0; c < NC; ++c) xb[u][c] = *(const v4i*)(xp[c] + kk + 32 * u);
     }
-    if (!ev) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wv[j] = 0.f;
-    }
-    v8bf hi, mid, lo;
-    split3_bf16(wv, hi, mid, lo);
+    for (int u = 0; u < 4; ++u) {
+      float wv[8] = {wa[u][0].x, wa[u][0].y, wa[u][0].z, wa[u][0].w, wa[u][1].x, wa[u][1].y, wa[u][1].z, wa[u][1].w};
+      if (!ev) {
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const v8bf b = tv[c] ? __builtin_bit_cast(v8bf, xc[c]) : v8bf{};
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[c], 0, 0, 0);
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[c], 0, 0, 0);
-      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[c], 0, 0, 0);
+        for (int j = 0; j < 8; ++j) wv[j] = 0.f;
+      }
+      v8bf hi, mid, lo;
+      split3_bf16(wv, hi, mid, lo);
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const v8bf b = tv[c] ? __builtin_bit_cast(v8bf, xb[u][c]) : v8bf{};
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[c], 0, 0, 0);
+        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[c], 0, 0, 0);
+      }
     }
   }
-  // lane l holds experts e0 + 4*(l/16) + i for token t0 + c*16 + l%16
-  const int eo = e0 + 4 * (lane >> 4);
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = t0 + c * 16 + lr;
-    if (!tv[c]) continue;
-    float* o = out + ((size_t)blockIdx.z * T + t) * E + eo;
-    if (eo + 3 < E) {
-      *(float4*)o = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-    } else {
+  for (int c = 0; c < NC; ++c)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (eo + i < E) o[i] = acc[c][i];
-    }
+    for (int i = 0; i < 4; ++i) red[wave][c][i][lane] = acc[c][i];
+  __syncthreads();
+  // the block's 16 x TT outputs, one per thread: lane l of "wave slot" holds
+  // experts e0 + 4*(l/16) + i, token c*16 + l%16
+  for (int o = threadIdx.x; o < NC * 4 * 64; o += kRouterWaves * 64) {
+    const int c = o / 256, i = (o / 64) & 3, l = o & 63;
+    float v = red[0][c][i][l];
+#pragma unroll
+    for (int w = 1; w < kRouterWaves; ++w) v += red[w][c][i][l];
+    const int t = t0 + c * 16 + (l & 15), ee = e0 + 4 * (l >> 4) + i;
+    if (t < T && ee < E) logits[(size_t)t * E + ee] = v;
   }
 }
 
@@ -208,9 +215,7 @@ __device__ __forceinline__ uint64_t select_key(float s, int e) {
 constexpr int kMaxChunkPairs = 1024;
 
 struct TopkArgs {
-  const float* part;     // [S][T][E] logit partials (S = 1: the logits)
-  int S;
-  float* logits_out;     // [T][E] written when S > 1, or null
+  const float* logits;   // [T][E]
   const float* bias;     // [E] or null
   const int32_t* forced; // [T][k] or null (free routing)
   int T, E, k, tpc;      // tpc: tokens per chunk (block)
@@ -228,12 +233,12 @@ struct TopkArgs {
 template <int J, bool FORCED>
 __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
   __shared__ int32_t hist[kMaxExperts];
+  __shared__ int32_t wave_cnt[16 * kMaxExperts];
   __shared__ int32_t ids[kMaxChunkPairs];
   __shared__ int32_t tmp[17];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T;
   const int tok0 = blockIdx.x * a.tpc;
-  for (int i = tid; i < E; i += 1024) hist[i] = 0;
 
   for (int tl = wave; tl < a.tpc; tl += 16) {
     const int t = tok0 + tl;
@@ -241,32 +246,11 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
       if (lane < k) ids[tl * k + lane] = -1;
       continue;
     }
-    // logits: the K-slice partials added in slice order; all loads of a group
-    // of four slices are issued before the first add
     float lv[J];
-    const float* __restrict__ part = a.part;
-    const size_t slice = (size_t)T * E;
 #pragma unroll
-    for (int j = 0; j < J; ++j) lv[j] = 0.f;
-    for (int s0 = 0; s0 < a.S; s0 += 4) {
-      float v[4][J];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < J; ++j) {
-          const int e = lane + 64 * j;
-          v[u][j] = (s0 + u < a.S && e < E) ? part[(s0 + u) * slice + (size_t)t * E + e] : 0.f;
-        }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < J; ++j)
-          if (s0 + u < a.S) lv[j] = (s0 + u == 0) ? v[u][j] : lv[j] + v[u][j];
-    }
-    if (a.logits_out) {
-#pragma unroll
-      for (int j = 0; j < J; ++j)
-        if (lane + 64 * j < E) a.logits_out[(size_t)t * E + lane + 64 * j] = lv[j];
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      lv[j] = e < E ? a.logits[(size_t)t * E + e] : 0.f;
     }
     int sel[kMaxTopK];
     float sl[kMaxTopK];
@@ -282,7 +266,7 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
 #pragma unroll
           for (int j = 0; j < J; ++j)
             if (lane + 64 * j == e) mine = lv[j];
-          const float le = __shfl(mine, e & 63, kWave);
+          const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
           if (e >= 0 && e < E) {
             sel[r] = e;
             sl[r] = le;
@@ -304,11 +288,14 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
         sel[r] = -1;
         sl[r] = 0.f;
         if (r < k) {
+          // wave-wide maximum of the 64-bit key: the score word first, then the
+          // index word among the lanes that hold that score
           uint64_t best = 0;
 #pragma unroll
           for (int j = 0; j < J; ++j) best = key[j] > best ? key[j] : best;
-          best = wave_max_u64(best);
-          const int e = (int)(~(uint32_t)best);
+          const uint32_t hi = wave_umax((uint32_t)(best >> 32));
+          const uint32_t lo = wave_umax((uint32_t)(best >> 32) == hi ? (uint32_t)best : 0u);
+          const int e = (int)(~lo);
           float mine = 0.f;
 #pragma unroll
           for (int j = 0; j < J; ++j)
@@ -317,7 +304,7 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
               mine = lv[j];
             }
           sel[r] = e;
-          sl[r] = __shfl(mine, e & 63, kWave);
+          sl[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
         }
       }
     }
@@ -344,15 +331,36 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
   }
   __syncthreads();
 
-  // this chunk's pairs: q = 0..np-1 <-> p = blockIdx.x * np + q (one per thread)
+  // this chunk's pairs: q = 0..np-1 <-> p = blockIdx.x * np + q (one per thread).
+  // Rank of a pair among the equal ids before it: within its wave from ballots
+  // (lanes whose id agrees on every bit), plus the same id's count in earlier
+  // waves (per-wave counts scanned in wave order).
   const int np = a.tpc * k, P = T * k, p = blockIdx.x * np + tid;
-  int e = -1, rank = 0;
-  if (tid < np) {
-    e = ids[tid];
-    if (e >= 0) atomicAdd(&hist[e], 1);
-    for (int q = 0; q < tid; ++q) rank += (ids[q] == e);
+  const int e = tid < np ? ids[tid] : -1;
+  uint64_t peers = __ballot(1);
+#pragma unroll
+  for (int bit = 0; bit < 10; ++bit) {  // ids are -1 .. kMaxExperts-1 < 2^10 (as 10-bit two's complement)
+    const uint64_t b = __ballot((e >> bit) & 1);
+    peers &= ((e >> bit) & 1) ? b : ~b;
+  }
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int in_wave = __popcll(peers & below);
+  const bool leader = (peers & below) == 0;  // lowest lane of its id group
+  for (int i = tid; i < 16 * E; i += 1024) wave_cnt[i] = 0;
+  __syncthreads();
+  if (leader && e >= 0) wave_cnt[wave * E + e] = __popcll(peers);
+  __syncthreads();
+  for (int i = tid; i < E; i += 1024) {  // exclusive scan over waves, in wave order; totals -> hist
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = wave_cnt[w * E + i];
+      wave_cnt[w * E + i] = run;
+      run += c;
+    }
+    hist[i] = run;
   }
   __syncthreads();
+  const int rank = e >= 0 ? wave_cnt[wave * E + e] + in_wave : 0;
   if (gridDim.x > 1) {
     if (tid < np && p < P) a.local_rank[p] = rank;
     for (int i = tid; i < E; i += 1024) a.chunk_hist[(size_t)blockIdx.x * E + i] = hist[i];
@@ -436,28 +444,8 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 }
 
 // ---------------------------------------------------------------------------
-// Launch planning and launchers
+// Launchers
 // ---------------------------------------------------------------------------
-RouterPlan plan_router(int T, int d, int E, bool x_bf16) {
-  RouterPlan p;
-  if (!x_bf16) {
-    p.TT = T >= 256 ? 64 : 32;
-    p.S = 1;
-    return p;
-  }
-  p.TT = T <= 16 ? 16 : (T <= 32 ? 32 : 64);
-  const int tiles = ((T + p.TT - 1) / p.TT) * ((E + 63) / 64);
-  int S = 1;
-  while (tiles * S < 256 && S * 2 <= 16 && d % (S * 2 * 128) == 0) S *= 2;
-  p.S = S;
-  return p;
-}
-
-size_t router_partial_floats(int T, int d, int E, bool x_bf16) {
-  const RouterPlan p = plan_router(T, d, E, x_bf16);
-  return p.S > 1 ? (size_t)p.S * T * E : 0;
-}
-
 // Tokens per top-k block: all of them when their pairs fit one block, else 16
 // (64 for long inputs, to keep the chunk count and the scan short).
 int tokens_per_chunk(int T, int k) {
@@ -472,22 +460,20 @@ size_t dispatch_chunk_hist_ints(int T, int k, int E) {
 }
 
 hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
-  const RouterPlan rp = plan_router(L.T, L.d, L.E, L.x_bf16);
-  // where the router writes: final logits when there is one K slice, else partials
-  float* rout = rp.S == 1 ? L.logits : L.partials;
   if (L.x_bf16) {
-    const dim3 grid((L.T + rp.TT - 1) / rp.TT, (L.E + 63) / 64, rp.S);
-    const int kper = L.d / rp.S;
+    const int TT = L.T <= 16 ? 16 : (L.T <= 32 ? 32 : 64);
+    const dim3 grid((L.T + TT - 1) / TT, (L.E + 15) / 16);
     const uint16_t* x = (const uint16_t*)L.x;
-    if (rp.TT == 16) router_mfma_kernel<16><<<grid, 256, 0, st>>>(x, L.w_router, rout, L.T, L.d, L.E, kper, L.status);
-    else if (rp.TT == 32) router_mfma_kernel<32><<<grid, 256, 0, st>>>(x, L.w_router, rout, L.T, L.d, L.E, kper, L.status);
-    else router_mfma_kernel<64><<<grid, 256, 0, st>>>(x, L.w_router, rout, L.T, L.d, L.E, kper, L.status);
-  } else if (rp.TT == 64) {
+    const int nt = kRouterWaves * 64;
+    if (TT == 16) router_mfma_kernel<16><<<grid, nt, 0, st>>>(x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+    else if (TT == 32) router_mfma_kernel<32><<<grid, nt, 0, st>>>(x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+    else router_mfma_kernel<64><<<grid, nt, 0, st>>>(x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+  } else if (L.T >= 256) {
     const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64);
-    router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, rout, L.T, L.d, L.E, L.status);
+    router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
   } else {
     const dim3 grid((L.T + 31) / 32, (L.E + 15) / 16);
-    router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, rout, L.T, L.d, L.E, L.status);
+    router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -496,9 +482,7 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
   const int tpc = tokens_per_chunk(L.T, L.k);
   const int n_chunks = (L.T + tpc - 1) / tpc;
   TopkArgs a;
-  a.part = rout;
-  a.S = rp.S;
-  a.logits_out = rp.S > 1 ? L.logits_user : nullptr;
+  a.logits = L.logits;
   a.bias = L.forced ? nullptr : L.bias;
   a.forced = L.forced;
   a.T = L.T;

@@ -21,7 +21,8 @@ DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 
 # Every function the header declares (checked against include/moe.h by the tests).
 ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
-                 "moe_quantize_rows", "moe_status_string")
+                 "moe_quantize_rows", "moe_pack_weights", "moe_status_string")
+LAYOUTS = {"rowmajor": 0, "tiled": 1}
 STAGE_PREPARE, STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 8, 15
 
 
@@ -33,7 +34,7 @@ class MoeError(RuntimeError):
 
 class Shape(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "d_model", "n_experts", "top_k", "d_ffn", "d_ffn_shared",
-                                         "act_dtype", "w_dtype")]
+                                         "act_dtype", "w_dtype", "w_layout")]
 
 
 _WEIGHT_FIELDS = ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
@@ -70,6 +71,7 @@ def lib() -> C.CDLL:
         L.moe_forward.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
         L.moe_forward_stages.argtypes = [p, p, p, p, p, p, C.c_size_t, C.c_uint32, p, p]
         L.moe_quantize_rows.argtypes = [i64, i32, i32, p, p, p, p]
+        L.moe_pack_weights.argtypes = [i64, i32, i32, p, p, p]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         _lib = L
@@ -80,14 +82,14 @@ def status_string(rc: int) -> str:
     return lib().moe_status_string(rc).decode()
 
 
-def make_shape(T, d, E, k, F, Fs, act="bf16", w="fp8") -> Shape:
-    return Shape(int(T), int(d), int(E), int(k), int(F), int(Fs), DTYPES[act], DTYPES[w])
+def make_shape(T, d, E, k, F, Fs, act="bf16", w="fp8", layout="rowmajor") -> Shape:
+    return Shape(int(T), int(d), int(E), int(k), int(F), int(Fs), DTYPES[act], DTYPES[w], LAYOUTS[layout])
 
 
-def shape_of(layer_shape, T=None) -> Shape:
+def shape_of(layer_shape, T=None, layout="rowmajor") -> Shape:
     """Shape from any object with attributes T, d, E, k, F, Fs, act, w."""
     s = layer_shape
-    return make_shape(s.T if T is None else T, s.d, s.E, s.k, s.F, s.Fs, s.act, s.w)
+    return make_shape(s.T if T is None else T, s.d, s.E, s.k, s.F, s.Fs, s.act, s.w, layout)
 
 
 def _ptr(t):
@@ -192,6 +194,25 @@ def quantize_rows(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, st
     act = {torch.float32: DTYPES["f32"], torch.bfloat16: DTYPES["bf16"]}[x.dtype]
     rc = lib().moe_quantize_rows(x.shape[0], x.shape[1], act, _ptr(x), _ptr(codes), _ptr(scales), _stream(stream))
     _check(rc, "moe_quantize_rows")
+
+
+def pack_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
+    """MOE_LAYOUT_TILED copy of a [n, rows, cols] (or [rows, cols]) weight tensor."""
+    t = w if w.dim() == 3 else w.unsqueeze(0)
+    n, rows, cols = t.shape
+    out = torch.empty_like(w)
+    rc = lib().moe_pack_weights(n, rows, cols * t.element_size(), _ptr(w), _ptr(out), _stream(stream))
+    _check(rc, "moe_pack_weights")
+    return out
+
+
+def pack_layer_weights(w: dict, stream=None) -> dict:
+    """The weight dict with every expert matrix packed (scales, router, x untouched)."""
+    out = dict(w)
+    for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        if w.get(k) is not None:
+            out[k] = pack_weights(w[k], stream)
+    return out
 
 
 def raw_call(name: str, *args):

@@ -139,3 +139,28 @@ def test_quantize_rows_host_validation():
     assert L.moe_quantize_rows(-1, 128, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_rows(0, 128, 1, None, None, None, None) == moe.MOE_OK
     assert L.moe_quantize_rows(4, 128, 1, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_pack_weights_host_validation():
+    L = _lib()
+    buf = (C.c_uint8 * 8192)()
+    a = C.cast(buf, C.c_void_p)
+    assert L.moe_pack_weights(1, 16, 100, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED    # row_bytes % 128
+    assert L.moe_pack_weights(1, 24, 128, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED    # rows % 16
+    assert L.moe_pack_weights(-1, 16, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(1, 0, 128, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(1, 16, 128, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_weights(0, 16, 128, None, None, None) == moe.MOE_OK
+    # 2 x 16 x 128 bytes = 4 KB: a and a+2 KB overlap (rejected before any launch)
+    assert L.moe_pack_weights(2, 16, 128, a, C.c_void_p(C.addressof(buf) + 2048), None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_layout_field_validation():
+    _lib()
+    assert moe.workspace_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640, layout="tiled")) > 0
+    bad = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    bad.w_layout = 5
+    assert moe.workspace_bytes(bad) == 0
+    assert _forward(bad) == moe.MOE_ERR_INVALID_ARG
+    f32 = moe.make_shape(32, 2048, 384, 6, 640, 640, act="f32", w="f32", layout="tiled")
+    assert _forward(f32) == moe.MOE_ERR_UNSUPPORTED

@@ -412,3 +412,47 @@ def test_forward_stages_match_forward():
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     with pytest.raises(moe.MoeError):
         b.forward(16)
+
+
+# ------------------------------------------------------------------ tiled weight layout
+
+def test_pack_weights_layout():
+    """moe_pack_weights against the documented tile layout, rebuilt on the host."""
+    n, rows, rb = 3, 48, 384
+    src = torch.randint(0, 256, (n, rows, rb), dtype=torch.uint8)
+    say(f"pack {n} x {rows} x {rb} bytes")
+    got = moe.pack_weights(src.to(DEV)).cpu().numpy().reshape(n, -1)
+    a = src.numpy()
+    want = np.empty_like(got)
+    nkb = rb // 128
+    for m in range(n):
+        for rt in range(rows // 16):
+            for kb in range(nkb):
+                base = 2048 * (rt * nkb + kb)
+                for h in range(2):
+                    for l in range(64):
+                        o = base + 1024 * h + 16 * l
+                        c = 128 * kb + 16 * (l // 16) + 64 * h
+                        want[m, o:o + 16] = a[m, 16 * rt + l % 16, c:c + 16]
+    assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("case,T", [("decode_t32", None), ("prefill_t2048", 700), ("ties_t256_bf16w", None)])
+def test_tiled_layout_matches_rowmajor(case, T):
+    """The same layer with packed weights gives the same bits as with row-major ones."""
+    inp = synth.make_inputs(case, T=T)
+    s = inp["shape"]
+    say(f"{case} T={s.T}: tiled weights == row-major weights, bitwise")
+    dev = gpu_inputs(inp)
+    packed = moe.pack_layer_weights(dev)
+    ys = []
+    for layout, w in (("rowmajor", dev), ("tiled", packed)):
+        shape = moe.shape_of(s, layout=layout)
+        r = moe.alloc_routing(shape, DEV)
+        ws = moe.alloc_workspace(shape, DEV)
+        y = torch.empty((s.T, s.d), dtype=torch.bfloat16, device=DEV)
+        moe.route(shape, w, w["x"], r, ws)
+        moe.forward(shape, w, w["x"], r, y, ws)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
