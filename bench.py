@@ -4,9 +4,10 @@
 One step = the whole hot path on one batch: router + top-k + dispatch
 (moe_route, or moe_route_forced when the workload replays recorded choices)
 then the expert FFNs and the combine (moe_forward).  Inputs and weights are
-resident in HBM before timing starts; the expert weights rotate over several
-device copies so every step streams them from HBM rather than from the 256 MB
-last-level cache.
+resident in HBM before timing starts; the expert weights are packed once into
+the library's tiled layout (moe_pack_weights, a load-time step outside the
+timed region) and rotate over several device copies so every step streams
+them from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line.  `value` is tokens/s of the whole step; `roofline` is
 for the dominant kernel (the grouped gate/up projection), from its average
@@ -14,6 +15,7 @@ duration measured with HIP events on the stream it runs on; `cpu_baseline` is
 the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,6 +41,33 @@ DESCRIPTION = {
 }
 FORCED = {"prefill_t2048"}
 
+# HBM bytes per launch of the gate/up kernel on the default workload, from two
+# rocprofv3 --pmc passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by what the counter reads for the 480 MiB weight copies
+# the same run makes (fetch x2.0, write x1.0).  Valid only for the kernel sources
+# they were taken on: any change to them makes `traffic` null until re-measured.
+KERNEL_SOURCES = ("mixture_experts_moe_amd/csrc/experts.hip", "mixture_experts_moe_amd/csrc/moe_device.h",
+                  "mixture_experts_moe_amd/csrc/moe_kernels.h", "mixture_experts_moe_amd/csrc/moe_api.hip")
+TRAFFIC = {  # workload -> counters of the gate/up kernel, tiled layout
+    "decode_t32": {"sources_sha256": "74d7a6a3d022e665e63c5459e95d23e60819f948281a21b48a78d4111c2d1255",
+                   "fetch_bytes": 405370266, "write_bytes": 176128},
+}
+
+
+def sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    t = TRAFFIC.get(workload)
+    if t is None or t["sources_sha256"] != sources_sha256():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -47,8 +76,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t32", choices=sorted(DESCRIPTION))
     ap.add_argument("--rotate", type=int, default=4, help="device copies of the expert weights")
+    ap.add_argument("--layout", default="tiled", choices=("tiled", "rowmajor"), help="expert-weight layout")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0: skip)")
-    ap.add_argument("--also", default="prefill_t2048", help="extra workloads timed after the main one (comma list)")
+    ap.add_argument("--also", default="prefill_t2048,skew_t8192", help="extra workloads timed after the main one (comma list)")
     return ap.parse_args()
 
 
@@ -75,14 +105,16 @@ def algorithmic(s, counts):
     }
 
 
-def run_workload(name, steps, warmup, rotate):
+def run_workload(name, steps, warmup, rotate, layout):
     import torch
     from mixture_experts_moe_amd import moe, synth
 
     inp = synth.make_inputs(name)
     s = inp["shape"]
     dev = synth.to_device(inp, "cuda:0")
-    shape = moe.shape_of(s)
+    if layout == "tiled":
+        dev = moe.pack_layer_weights(dev)
+    shape = moe.shape_of(s, layout=layout)
     wkeys = ("w_gate", "w_up", "w_down")
     copies = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, rotate - 1))]
     r = moe.alloc_routing(shape, "cuda:0")
@@ -126,9 +158,11 @@ def run_workload(name, steps, warmup, rotate):
     pairs = ((0, 1), (2, 3), (3, 4), (4, 5), (5, 6))
     stage_us = {n: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)])) * 1e3
                 for n, (a, b) in zip(names, pairs)}
+    per_step = np.array([ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)]) * 1e3
+    pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
     counts = r.counts.cpu().numpy()
     assert r.status.item() == 0
-    return s, wall, stage_us, algorithmic(s, counts), counts
+    return s, wall, stage_us, algorithmic(s, counts), counts, pct
 
 
 def cpu_baseline(name, budget_s):
@@ -164,7 +198,7 @@ def main():
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
-    s, wall, st_us, alg, counts = run_workload(a.workload, a.steps, a.warmup, a.rotate)
+    s, wall, st_us, alg, counts, pct = run_workload(a.workload, a.steps, a.warmup, a.rotate, a.layout)
     t_step = wall
     gu_s = st_us["gate_up"] * 1e-6
     achieved = alg["gateup_bytes"] / gu_s / 1e9
@@ -174,22 +208,30 @@ def main():
         "vs_baseline": None, "dtype": "fp8e4m3" if s.w == "fp8" else s.w, "data": "synthetic",
         "config": {"workload": f"{a.workload}: {DESCRIPTION[a.workload]}", "T": s.T, "d_model": s.d,
                    "n_experts": s.E, "top_k": s.k, "d_ffn": s.F, "d_ffn_shared": s.Fs,
-                   "weight_copies_rotated": a.rotate},
+                   "weight_copies_rotated": a.rotate, "weight_layout": a.layout},
         "roofline": {"bound": "hbm", "kernel": "gateup_mfma_kernel (grouped gate/up + SwiGLU + h quantisation)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None, "bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": st_us["gate_up"]},
+                     "traffic": measured_traffic(a.workload) if a.layout == "tiled" else None,
+                     "bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": st_us["gate_up"]},
         "stage_us": st_us,
+        "step_us_event_percentiles": pct,
         "step_roofline": {"B_alg_bytes": alg["B_alg"], "distinct_experts": alg["U"],
                           "hbm_frac": alg["B_alg"] / t_step / (HBM_PEAK_GBS * 1e9),
-                          "fp8_mfma_frac": alg["F_mm"] / t_step / (FP8_PEAK_TFLOPS * 1e12)},
+                          "fp8_mfma_frac": alg["F_mm"] / t_step / (FP8_PEAK_TFLOPS * 1e12),
+                          "roofline_frac": max(alg["B_alg"] / (HBM_PEAK_GBS * 1e9),
+                                               alg["F_mm"] / (FP8_PEAK_TFLOPS * 1e12)) / t_step},
     }
     extra = {}
     for name in [w for w in a.also.split(",") if w and w != a.workload]:
-        s2, wall2, st2, alg2, counts2 = run_workload(name, max(10, a.steps // 4), max(3, a.warmup // 4), a.rotate)
+        s2, wall2, st2, alg2, counts2, pct2 = run_workload(name, max(10, a.steps // 4), max(3, a.warmup // 4),
+                                                           a.rotate, a.layout)
         extra[name] = {"tokens_per_s": s2.T / wall2, "ms_per_step": wall2 * 1e3, "stage_us": st2,
+                       "step_us_event_percentiles": pct2,
                        "gateup_GBs": alg2["gateup_bytes"] / (st2["gate_up"] * 1e-6) / 1e9,
                        "hbm_frac": alg2["B_alg"] / wall2 / (HBM_PEAK_GBS * 1e9),
                        "fp8_mfma_frac": alg2["F_mm"] / wall2 / (FP8_PEAK_TFLOPS * 1e12),
+                       "roofline_frac": max(alg2["B_alg"] / (HBM_PEAK_GBS * 1e9),
+                                            alg2["F_mm"] / (FP8_PEAK_TFLOPS * 1e12)) / wall2,
                        "max_over_mean_expert_load": float(counts2.max() / max(1e-9, counts2.mean()))}
     if extra:
         out["also"] = extra
