@@ -378,8 +378,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 // routing weight (1 for the shared expert) and writes the fp32 partial row of
 // pair p (or P + t).  A block takes one tile and one slice of 64*RT output
 // features (see work_item); wave w owns RT 16-row tiles (features nb*64*RT + w*16*RT + 16 r).
-// RT = 1 for short tiles (many small blocks keep the HBM busy); RT = 4 for tall
-// tiles, so a tile's h rows are staged once per 256 features.
+// RT = 2 for short tiles, RT = 4 for tall ones (a tile's h rows are staged once
+// per 256 features); RT = 1 when a row's K does not fit one stage.
 // ---------------------------------------------------------------------------
 template <int BM, int WT, int RT>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
@@ -708,15 +708,18 @@ hipError_t launch_down(const ExpertArgs& a0, int wmode, int BM, int max_tiles, h
   if (wmode == 0)
     return launch_dyn(down_f32_kernel<16>, dim3((a.d + 63) / 64, max_tiles), down_lds_bytes(16, 0, Fmax), st, a);
   const size_t lds = down_lds_bytes(BM, wmode, Fmax);
-  // tall tiles: 4 row tiles per wave (needs the whole K of a row in one stage)
-  const bool wide = BM >= 32 && Fmax * (wmode == 2 ? 1 : 2) <= 5 * 128 && a.d % 256 == 0;
+  // RT 16-row weight tiles per wave (RT > 1 needs a row's whole K in one stage):
+  // 2 for short tiles, 4 for tall ones, whose h rows are then staged once per
+  // 256 output features
+  const bool one_stage = Fmax * (wmode == 2 ? 1 : 2) <= 5 * 128;
+  const int RT = !one_stage ? 1 : (BM == 16 ? (a.d % 128 == 0 ? 2 : 1) : (a.d % 256 == 0 ? 4 : 1));
   a.max_tiles = max_tiles;
-  a.n_slices = wide ? a.d / 256 : (a.d + 63) / 64;
+  a.n_slices = (a.d + 64 * RT - 1) / (64 * RT);
   const dim3 grid(work_grid(a.n_slices * max_tiles));
-  if (wide) {
-    if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
-    if (wmode == 2 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 4>, grid, lds, st, a);
-  }
+  if (wmode == 2 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2>, grid, lds, st, a);
+  if (wmode == 2 && RT == 4 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
+  if (wmode == 2 && RT == 4 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 4>, grid, lds, st, a);
+  if (RT != 1) return hipErrorInvalidValue;
   if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 1>, grid, lds, st, a);
   if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 1>, grid, lds, st, a);
   if (wmode == 2 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 1>, grid, lds, st, a);

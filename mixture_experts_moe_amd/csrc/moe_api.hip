@@ -14,7 +14,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
+  size_t logits, rpart, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -27,7 +27,7 @@ int64_t max_tiles_for(const moe_shape& s, int BM) {
 }
 
 // Workspace segments (256-byte aligned).  Routing uses logits (when the caller
-// passes none), chunk_hist and local_rank; the forward pass
+// passes none), the router partial sums, chunk_hist and local_rank; the forward pass
 // uses the rest.  Nothing is carried from one call to the next.
 Layout layout(const moe_shape& s) {
   const size_t T = s.T, d = s.d_model, E = s.n_experts, P = T * s.top_k;
@@ -41,6 +41,7 @@ Layout layout(const moe_shape& s) {
     return at;
   };
   L.logits = seg(T * E * 4);
+  L.rpart = seg(moe::router_part_floats(s.T, s.top_k, s.d_model, s.n_experts, s.act_dtype == MOE_BF16) * 4);
   L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
   L.local_rank = seg(P * 4);
   L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int2));
@@ -118,6 +119,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   R.E = shape->n_experts;
   R.k = shape->top_k;
   R.logits = out->logits ? out->logits : (float*)(base + L.logits);
+  R.rpart = (float*)(base + L.rpart);
   R.idx = out->topk_idx;
   R.w = out->topk_w;
   R.chunk_hist = (int32_t*)(base + L.chunk_hist);

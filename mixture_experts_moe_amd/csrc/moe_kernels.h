@@ -33,6 +33,8 @@ struct ExpertArgs {
 };
 
 size_t dispatch_chunk_hist_ints(int T, int k, int E);
+// Router partial sums kept between the router and top-k launches (short inputs).
+size_t router_part_floats(int T, int k, int d, int E, bool x_bf16);
 
 struct RouteLaunch {
   const void* x;
@@ -42,6 +44,7 @@ struct RouteLaunch {
   const int32_t* forced;   // forced ids or null
   int T, d, E, k;
   float* logits;           // where the logits go (the caller's buffer or workspace)
+  float* rpart;            // [d/kslice][T][E] router partial sums (short inputs)
   int32_t* idx;
   float* w;
   int32_t *chunk_hist, *local_rank, *counts, *offsets, *perm, *inv_perm, *status;

@@ -5,13 +5,17 @@
 //   [port]  "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No."
 //   [bench] "We Stopped the Kolibri Benchmark Before Scoring One Answer"
 //
-// Launch sequence of one routing call:
+// Launch sequence of one routing call.
+// Short inputs (T * k <= 1024 pairs, e.g. a decode batch), three launches:
+//   1. router partial logits over K slices, one block per (16 experts, K slice,
+//      token tile), so the router weights stream through many CUs at once;
+//   2. top-k, one wave per token: adds the slices, selects, softmax weights;
+//   3. the whole counting sort in one block.
+// Long inputs:
 //   1. router logits, one block per (token tile, 16 experts);
-//   2. top-k per token-chunk block: top-k (or the forced ids), softmax weights,
-//      and the chunk's share of the dispatch.  When one block holds every pair (up to 1024 pairs, e.g. a
-//      decode batch) it completes the dispatch and the call is two launches;
-//   3. (several chunks) scan of the chunk histograms into counts and offsets;
-//   4. (several chunks) placement of every pair.
+//   2. top-k per chunk of tokens, and the chunk's share of the dispatch;
+//   3. scan of the chunk histograms into counts and offsets;
+//   4. placement of every pair.
 #include "moe_device.h"
 #include "moe_kernels.h"
 
@@ -124,6 +128,73 @@ __global__ __launch_bounds__(1024) void router_mfma_kernel(const uint16_t* __res
   }
 }
 
+// Router partial logits for short inputs, split along K: block (16 experts,
+// K slice ks of 4*32*NS, tile of 16*NC tokens) writes its slice's dot products
+// to part[ks][t][e]; the top-k kernel adds the slices in slice order.  Same
+// exact three-way split of the fp32 weights as above; each of the 4 waves takes
+// a quarter of the slice and the quarters are added through LDS in wave order.
+template <int NC, int NS>
+__global__ __launch_bounds__(256) void router_split_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ W, float* __restrict__ part,
+                                                           int T, int d, int E, int32_t* __restrict__ status) {
+  constexpr int KW = 32 * NS;  // K per wave
+  __shared__ float red[4][NC][4][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = (lane >> 4) * 8;
+  const int e0 = blockIdx.x * 16, ks = blockIdx.y, t0 = blockIdx.z * 16 * NC;
+  const int k0 = (ks * 4 + wave) * KW;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) *status = 0;
+  const int e = e0 + lr;
+  const bool ev = e < E;
+  const float* wp = W + (size_t)(ev ? e : E - 1) * d + k0 + lk;
+  float4 wa[NS][2];
+  v4i xb[NS][NC];
+  bool tv[NC];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    wa[u][0] = *(const float4*)(wp + 32 * u);
+    wa[u][1] = *(const float4*)(wp + 32 * u + 4);
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int t = t0 + c * 16 + lr;
+    tv[c] = t < T;
+    const uint16_t* xp = x + (size_t)(tv[c] ? t : T - 1) * d + k0 + lk;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) xb[u][c] = *(const v4i*)(xp + 32 * u);
+  }
+  v4f acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    float wv[8] = {wa[u][0].x, wa[u][0].y, wa[u][0].z, wa[u][0].w, wa[u][1].x, wa[u][1].y, wa[u][1].z, wa[u][1].w};
+    if (!ev) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) wv[j] = 0.f;
+    }
+    v8bf hi, mid, lo;
+    split3_bf16(wv, hi, mid, lo);
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const v8bf b = tv[c] ? __builtin_bit_cast(v8bf, xb[u][c]) : v8bf{};
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[c], 0, 0, 0);
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[c], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][c][i][lane] = acc[c][i];
+  __syncthreads();
+  for (int o = threadIdx.x; o < NC * 256; o += 256) {
+    const int c = o / 256, i = (o / 64) & 3, l = o & 63;
+    const float v = ((red[0][c][i][l] + red[1][c][i][l]) + red[2][c][i][l]) + red[3][c][i][l];
+    const int t = t0 + c * 16 + (l & 15), ee = e0 + 4 * (l >> 4) + i;
+    if (t < T && ee < E) part[((size_t)ks * T + t) * E + ee] = v;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Router logits for fp32 activations: plain fp32 multiply-add, LDS-tiled; tiles
 // of TT tokens x TE experts, each of the 256 threads owning a (TT/16) x (TE/16)
@@ -230,12 +301,174 @@ struct TopkArgs {
   int32_t* status;
 };
 
+// One token's selection by one wave (lane l holds the candidates e = l + 64 j
+// with logits lv[j]): writes idx and w of token t and returns, in lane r < k,
+// the id of slot r (other lanes: -1).
+template <int J, bool FORCED>
+__device__ __forceinline__ int route_token(const TopkArgs& a, int t, const float (&lv)[J], int lane) {
+  const int E = a.E, k = a.k;
+  int sel[kMaxTopK];
+  float sl[kMaxTopK];
+  if (FORCED) {
+    bool bad = false;
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {
+      sel[r] = -1;
+      sl[r] = 0.f;
+      if (r < k) {
+        const int e = a.forced[(size_t)t * k + r];
+        float mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (lane + 64 * j == e) mine = lv[j];
+        const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
+        if (e >= 0 && e < E) {
+          sel[r] = e;
+          sl[r] = le;
+        } else {
+          bad = true;
+        }
+      }
+    }
+    if (bad && lane == 0) *a.status = -5;  // MOE_ERR_FORCED_INDEX; every writer stores the same value
+  } else {
+    uint64_t key[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      key[j] = e < E ? select_key(a.bias ? lv[j] + a.bias[e] : lv[j], e) : 0;
+    }
+#pragma unroll
+    for (int r = 0; r < kMaxTopK; ++r) {
+      sel[r] = -1;
+      sl[r] = 0.f;
+      if (r < k) {
+        // wave-wide maximum of the 64-bit key: the score word first; when one
+        // lane holds it (the usual case) its index word is read directly,
+        // otherwise the index words of the tied lanes are maximised too
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) best = key[j] > best ? key[j] : best;
+        const uint32_t bhi = (uint32_t)(best >> 32);
+        const uint32_t hi = wave_umax(bhi);
+        const uint64_t tied = __ballot(bhi == hi);
+        uint32_t lo;
+        if (__popcll(tied) == 1)
+          lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)best, __builtin_ctzll(tied));
+        else
+          lo = wave_umax(bhi == hi ? (uint32_t)best : 0u);
+        const int e = (int)(~lo);
+        float mine = 0.f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+          if (lane + 64 * j == e) {
+            key[j] = 0;
+            mine = lv[j];
+          }
+        sel[r] = e;
+        sl[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
+      }
+    }
+  }
+  float m = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r)
+    if (r < k && sel[r] >= 0) m = fmaxf(m, sl[r]);
+  float ex[kMaxTopK], Z = 0.f;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r) {
+    ex[r] = 0.f;
+    if (r < k && sel[r] >= 0) {
+      ex[r] = expf(sl[r] - m);
+      Z = Z + ex[r];
+    }
+  }
+  int mine_id = -1;
+#pragma unroll
+  for (int r = 0; r < kMaxTopK; ++r)
+    if (r < k && lane == r) {
+      a.idx[(size_t)t * k + r] = sel[r];
+      a.w[(size_t)t * k + r] = sel[r] >= 0 ? ex[r] / Z : 0.f;
+      mine_id = sel[r];
+    }
+  return mine_id;
+}
+
+// LDS of the block-wide dispatch step.
+struct DispatchLds {
+  int32_t hist[kMaxExperts];
+  int32_t wave_cnt[16 * kMaxExperts];
+  int32_t tmp[17];
+};
+
+// Dispatch step over the up-to-1024 pairs of one block (1024 threads; thread
+// tid holds pair p with id e, or e = -1 for none/invalid).  Rank of a pair
+// among the equal ids before it: within its wave from ballots (lanes whose id
+// agrees on every bit), plus the same id's count in earlier waves (per-wave
+// counts scanned in wave order).  `whole`: the block holds every pair, so the
+// counting sort is finished here (counts, offsets, perm, inv_perm); otherwise
+// the block's histogram and ranks go to chunk_hist / local_rank.
+__device__ __forceinline__ void dispatch_block(const TopkArgs& a, DispatchLds& s, int e, int p, bool live,
+                                               bool whole) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int E = a.E;
+  uint64_t peers = __ballot(1);
+#pragma unroll
+  for (int bit = 0; bit < 10; ++bit) {  // ids are -1 .. kMaxExperts-1 < 2^10 (as 10-bit two's complement)
+    const uint64_t b = __ballot((e >> bit) & 1);
+    peers &= ((e >> bit) & 1) ? b : ~b;
+  }
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int in_wave = __popcll(peers & below);
+  const bool leader = (peers & below) == 0;  // lowest lane of its id group
+  for (int i = tid; i < 16 * E; i += 1024) s.wave_cnt[i] = 0;
+  __syncthreads();
+  if (leader && e >= 0) s.wave_cnt[wave * E + e] = __popcll(peers);
+  __syncthreads();
+  for (int i = tid; i < E; i += 1024) {  // exclusive scan over waves, in wave order; totals -> hist
+    int run = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int c = s.wave_cnt[w * E + i];
+      s.wave_cnt[w * E + i] = run;
+      run += c;
+    }
+    s.hist[i] = run;
+  }
+  __syncthreads();
+  const int rank = e >= 0 ? s.wave_cnt[wave * E + e] + in_wave : 0;
+  if (!whole) {
+    if (live) a.local_rank[p] = rank;
+    for (int i = tid; i < E; i += 1024) a.chunk_hist[(size_t)blockIdx.x * E + i] = s.hist[i];
+    return;
+  }
+  const int cnt = tid < E ? s.hist[tid] : 0;
+  int total;
+  const int off = block1024_excl_scan(cnt, s.tmp, &total);
+  if (tid < E) {
+    a.counts[tid] = cnt;
+    a.offsets[tid] = off;
+    s.hist[tid] = off;
+  }
+  if (tid == 0) a.offsets[E] = total;
+  __syncthreads();
+  if (live) {
+    if (e >= 0) {
+      const int q = s.hist[e] + rank;
+      a.perm[q] = p;
+      a.inv_perm[p] = q;
+    } else {
+      a.inv_perm[p] = -1;
+    }
+    if (p >= total) a.perm[p] = -1;
+  }
+}
+
+// Top-k + dispatch over chunks of `tpc` tokens (long inputs): block = 16 waves,
+// wave w takes tokens w, w+16, ... of its chunk.
 template <int J, bool FORCED>
 __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
-  __shared__ int32_t hist[kMaxExperts];
-  __shared__ int32_t wave_cnt[16 * kMaxExperts];
+  __shared__ DispatchLds s;
   __shared__ int32_t ids[kMaxChunkPairs];
-  __shared__ int32_t tmp[17];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E, k = a.k, T = a.T;
   const int tok0 = blockIdx.x * a.tpc;
@@ -252,141 +485,60 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
       const int e = lane + 64 * j;
       lv[j] = e < E ? a.logits[(size_t)t * E + e] : 0.f;
     }
-    int sel[kMaxTopK];
-    float sl[kMaxTopK];
-    if (FORCED) {
-      bool bad = false;
+    const int id = route_token<J, FORCED>(a, t, lv, lane);
+    if (lane < k) ids[tl * k + lane] = id;
+  }
+  __syncthreads();
+  const int np = a.tpc * k, p = blockIdx.x * np + tid;
+  const bool live = tid < np && p < T * k;
+  dispatch_block(a, s, tid < np ? ids[tid] : -1, p, live, gridDim.x == 1);
+}
+
+// Short inputs, step 2: one wave per token.  The router left n_parts partial
+// dot products per logit (K slices); they are added in slice order, the sum is
+// the logit (written to logits_out when given), then the selection.
+template <int J, bool FORCED>
+__global__ __launch_bounds__(64) void topk_small_kernel(TopkArgs a, const float* __restrict__ part, int n_parts,
+                                                        float* __restrict__ logits_out) {
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const int E = a.E, T = a.T;
+  // the slices are requested 8 at a time (all J candidates at once), then added in order
+  constexpr int QB = 8;
+  float lv[J];
 #pragma unroll
-      for (int r = 0; r < kMaxTopK; ++r) {
-        sel[r] = -1;
-        sl[r] = 0.f;
-        if (r < k) {
-          const int e = a.forced[(size_t)t * k + r];
-          float mine = 0.f;
+  for (int j = 0; j < J; ++j) lv[j] = 0.f;
+  for (int q0 = 0; q0 < n_parts; q0 += QB) {
+    float v[QB][J];
 #pragma unroll
-          for (int j = 0; j < J; ++j)
-            if (lane + 64 * j == e) mine = lv[j];
-          const float le = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
-          if (e >= 0 && e < E) {
-            sel[r] = e;
-            sl[r] = le;
-          } else {
-            bad = true;
-          }
-        }
-      }
-      if (bad && lane == 0) *a.status = -5;  // MOE_ERR_FORCED_INDEX; every writer stores the same value
-    } else {
-      uint64_t key[J];
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
       for (int j = 0; j < J; ++j) {
         const int e = lane + 64 * j;
-        key[j] = e < E ? select_key(a.bias ? lv[j] + a.bias[e] : lv[j], e) : 0;
+        v[q][j] = (q0 + q < n_parts && e < E) ? part[((size_t)(q0 + q) * T + t) * E + e] : 0.f;
       }
 #pragma unroll
-      for (int r = 0; r < kMaxTopK; ++r) {
-        sel[r] = -1;
-        sl[r] = 0.f;
-        if (r < k) {
-          // wave-wide maximum of the 64-bit key: the score word first, then the
-          // index word among the lanes that hold that score
-          uint64_t best = 0;
+    for (int q = 0; q < QB; ++q)
 #pragma unroll
-          for (int j = 0; j < J; ++j) best = key[j] > best ? key[j] : best;
-          const uint32_t hi = wave_umax((uint32_t)(best >> 32));
-          const uint32_t lo = wave_umax((uint32_t)(best >> 32) == hi ? (uint32_t)best : 0u);
-          const int e = (int)(~lo);
-          float mine = 0.f;
-#pragma unroll
-          for (int j = 0; j < J; ++j)
-            if (lane + 64 * j == e) {
-              key[j] = 0;
-              mine = lv[j];
-            }
-          sel[r] = e;
-          sl[r] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), e & 63));
-        }
-      }
-    }
-    float m = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r)
-      if (r < k && sel[r] >= 0) m = fmaxf(m, sl[r]);
-    float ex[kMaxTopK], Z = 0.f;
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r) {
-      ex[r] = 0.f;
-      if (r < k && sel[r] >= 0) {
-        ex[r] = expf(sl[r] - m);
-        Z = Z + ex[r];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kMaxTopK; ++r)
-      if (r < k && lane == r) {
-        a.idx[(size_t)t * k + r] = sel[r];
-        a.w[(size_t)t * k + r] = sel[r] >= 0 ? ex[r] / Z : 0.f;
-        ids[tl * k + r] = sel[r];
-      }
+      for (int j = 0; j < J; ++j)
+        if (q0 + q < n_parts) lv[j] = (q0 + q == 0) ? v[q][j] : lv[j] + v[q][j];
   }
-  __syncthreads();
+  if (logits_out) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) logits_out[(size_t)t * E + e] = lv[j];
+    }
+  }
+  route_token<J, FORCED>(a, t, lv, lane);
+}
 
-  // this chunk's pairs: q = 0..np-1 <-> p = blockIdx.x * np + q (one per thread).
-  // Rank of a pair among the equal ids before it: within its wave from ballots
-  // (lanes whose id agrees on every bit), plus the same id's count in earlier
-  // waves (per-wave counts scanned in wave order).
-  const int np = a.tpc * k, P = T * k, p = blockIdx.x * np + tid;
-  const int e = tid < np ? ids[tid] : -1;
-  uint64_t peers = __ballot(1);
-#pragma unroll
-  for (int bit = 0; bit < 10; ++bit) {  // ids are -1 .. kMaxExperts-1 < 2^10 (as 10-bit two's complement)
-    const uint64_t b = __ballot((e >> bit) & 1);
-    peers &= ((e >> bit) & 1) ? b : ~b;
-  }
-  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
-  const int in_wave = __popcll(peers & below);
-  const bool leader = (peers & below) == 0;  // lowest lane of its id group
-  for (int i = tid; i < 16 * E; i += 1024) wave_cnt[i] = 0;
-  __syncthreads();
-  if (leader && e >= 0) wave_cnt[wave * E + e] = __popcll(peers);
-  __syncthreads();
-  for (int i = tid; i < E; i += 1024) {  // exclusive scan over waves, in wave order; totals -> hist
-    int run = 0;
-    for (int w = 0; w < 16; ++w) {
-      const int c = wave_cnt[w * E + i];
-      wave_cnt[w * E + i] = run;
-      run += c;
-    }
-    hist[i] = run;
-  }
-  __syncthreads();
-  const int rank = e >= 0 ? wave_cnt[wave * E + e] + in_wave : 0;
-  if (gridDim.x > 1) {
-    if (tid < np && p < P) a.local_rank[p] = rank;
-    for (int i = tid; i < E; i += 1024) a.chunk_hist[(size_t)blockIdx.x * E + i] = hist[i];
-    return;
-  }
-  // one chunk holds every pair: finish the counting sort here
-  const int cnt = tid < E ? hist[tid] : 0;
-  int total;
-  const int off = block1024_excl_scan(cnt, tmp, &total);
-  if (tid < E) {
-    a.counts[tid] = cnt;
-    a.offsets[tid] = off;
-    hist[tid] = off;
-  }
-  if (tid == 0) a.offsets[E] = total;
-  __syncthreads();
-  if (tid < P) {
-    if (e >= 0) {
-      const int q = hist[e] + rank;
-      a.perm[q] = p;
-      a.inv_perm[p] = q;
-    } else {
-      a.inv_perm[p] = -1;
-    }
-    if (p >= total) a.perm[p] = -1;
-  }
+// Short inputs, step 3: the whole counting sort in one block (T * k <= 1024).
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(TopkArgs a) {
+  __shared__ DispatchLds s;
+  const int P = a.T * a.k, p = threadIdx.x;
+  const bool live = p < P;
+  const int e = live ? a.idx[p] : -1;
+  dispatch_block(a, s, e, p, live, true);
 }
 
 // Several chunks: per expert, an exclusive scan of the chunk histograms in chunk
@@ -459,28 +611,14 @@ size_t dispatch_chunk_hist_ints(int T, int k, int E) {
   return n_chunks > 1 ? (size_t)n_chunks * E : 0;
 }
 
-hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
-  if (L.x_bf16) {
-    const int TT = L.T <= 16 ? 16 : (L.T <= 32 ? 32 : 64);
-    const dim3 grid((L.T + TT - 1) / TT, (L.E + 15) / 16);
-    const uint16_t* x = (const uint16_t*)L.x;
-    const int nt = kRouterWaves * 64;
-    if (TT == 16) router_mfma_kernel<16><<<grid, nt, 0, st>>>(x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
-    else if (TT == 32) router_mfma_kernel<32><<<grid, nt, 0, st>>>(x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
-    else router_mfma_kernel<64><<<grid, nt, 0, st>>>(x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
-  } else if (L.T >= 256) {
-    const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64);
-    router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
-  } else {
-    const dim3 grid((L.T + 31) / 32, (L.E + 15) / 16);
-    router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+int router_kslice(int d) { return d % 256 == 0 ? 256 : 128; }
 
-  const int P = L.T * L.k;
-  const int tpc = tokens_per_chunk(L.T, L.k);
-  const int n_chunks = (L.T + tpc - 1) / tpc;
+size_t router_part_floats(int T, int k, int d, int E, bool x_bf16) {
+  if (!x_bf16 || (int64_t)T * k > kMaxChunkPairs) return 0;
+  return (size_t)(d / router_kslice(d)) * T * E;
+}
+
+static TopkArgs topk_args(const RouteLaunch& L, int tpc) {
   TopkArgs a;
   a.logits = L.logits;
   a.bias = L.forced ? nullptr : L.bias;
@@ -498,17 +636,82 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
   a.perm = L.perm;
   a.inv_perm = L.inv_perm;
   a.status = L.status;
-  const int J = (L.E + 63) / 64;
+  return a;
+}
+
+#define MOE_J_SWITCH(J, CASE)                                                            \
+  switch (J) {                                                                           \
+    CASE(1) CASE(2) CASE(3) CASE(4) CASE(5) CASE(6) CASE(7) CASE(8)                      \
+    default: return hipErrorInvalidValue;                                                \
+  }
+
+// Short inputs: split router, one wave per token, one-block dispatch.
+static hipError_t launch_route_short(const RouteLaunch& L, hipStream_t st) {
+  const float* part;
+  int n_parts;
+  float* logits_out;
+  if (L.x_bf16) {
+    const int ksl = router_kslice(L.d), NS = ksl / 128, NC = L.T <= 16 ? 1 : (L.T <= 32 ? 2 : (L.T <= 48 ? 3 : 4));
+    const dim3 grid((L.E + 15) / 16, L.d / ksl, (L.T + 16 * NC - 1) / (16 * NC));
+    const uint16_t* x = (const uint16_t*)L.x;
+#define MOE_SPLIT(nc, ns) \
+  router_split_kernel<nc, ns><<<grid, 256, 0, st>>>(x, L.w_router, L.rpart, L.T, L.d, L.E, L.status)
+    if (NS == 2) {
+      if (NC == 1) MOE_SPLIT(1, 2); else if (NC == 2) MOE_SPLIT(2, 2); else if (NC == 3) MOE_SPLIT(3, 2); else MOE_SPLIT(4, 2);
+    } else {
+      if (NC == 1) MOE_SPLIT(1, 1); else if (NC == 2) MOE_SPLIT(2, 1); else if (NC == 3) MOE_SPLIT(3, 1); else MOE_SPLIT(4, 1);
+    }
+#undef MOE_SPLIT
+    part = L.rpart;
+    n_parts = L.d / ksl;
+    logits_out = L.logits;
+  } else {
+    const dim3 grid((L.T + 31) / 32, (L.E + 15) / 16);
+    router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+    part = L.logits;
+    n_parts = 1;
+    logits_out = nullptr;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const TopkArgs a = topk_args(L, L.T);
+#define MOE_TOPK_SMALL(n)                                                                        \
+  case n:                                                                                        \
+    if (L.forced) topk_small_kernel<n, true><<<L.T, 64, 0, st>>>(a, part, n_parts, logits_out);  \
+    else topk_small_kernel<n, false><<<L.T, 64, 0, st>>>(a, part, n_parts, logits_out);          \
+    break;
+  MOE_J_SWITCH((L.E + 63) / 64, MOE_TOPK_SMALL)
+#undef MOE_TOPK_SMALL
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dispatch_small_kernel<<<1, 1024, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
+  if ((int64_t)L.T * L.k <= kMaxChunkPairs) return launch_route_short(L, st);
+  if (L.x_bf16) {
+    const int TT = 64;
+    const dim3 grid((L.T + TT - 1) / TT, (L.E + 15) / 16);
+    router_mfma_kernel<64><<<grid, kRouterWaves * 64, 0, st>>>((const uint16_t*)L.x, L.w_router, L.logits, L.T, L.d,
+                                                               L.E, L.status);
+  } else {
+    const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64);
+    router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  const int P = L.T * L.k;
+  const int tpc = tokens_per_chunk(L.T, L.k);
+  const int n_chunks = (L.T + tpc - 1) / tpc;
+  const TopkArgs a = topk_args(L, tpc);
 #define MOE_TOPK_CASE(n)                                                                \
   case n:                                                                               \
     if (L.forced) topk_dispatch_kernel<n, true><<<n_chunks, 1024, 0, st>>>(a);          \
     else topk_dispatch_kernel<n, false><<<n_chunks, 1024, 0, st>>>(a);                  \
     break;
-  switch (J) {
-    MOE_TOPK_CASE(1) MOE_TOPK_CASE(2) MOE_TOPK_CASE(3) MOE_TOPK_CASE(4)
-    MOE_TOPK_CASE(5) MOE_TOPK_CASE(6) MOE_TOPK_CASE(7) MOE_TOPK_CASE(8)
-    default: return hipErrorInvalidValue;
-  }
+  MOE_J_SWITCH((L.E + 63) / 64, MOE_TOPK_CASE)
 #undef MOE_TOPK_CASE
   e = hipGetLastError();
   if (e != hipSuccess || n_chunks == 1) return e;
@@ -519,5 +722,6 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
                                                          L.offsets, L.perm, L.inv_perm);
   return hipGetLastError();
 }
+#undef MOE_J_SWITCH
 
 }  // namespace moe
