@@ -74,16 +74,37 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Forward preparation: blocks 0..n-2 quantise the activations (four 128-element
-// groups per block, as above); the last block plans the expert tiles: tiles
+// Forward preparation, one launch: the first blocks quantise the activations
+// (four 128-element groups per block, as above); the next ones write, for every
+// h row q (sorted pairs, then the shared expert's rows P + t), its token, its
+// partial-output row and its routing weight, so the expert kernels read them
+// with one load per row; the last block plans the expert tiles: tiles
 // per group = ceil(rows / BM), groups in order (routed experts 0..E-1, then the
-// shared expert with all T rows), tile i = (group, first row).
+// shared expert with all T rows); tile i = (group, first row, its first h row,
+// rows), so an expert block finds all it needs in one load; the slots past the
+// last tile get group -1.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict__ x, int64_t n_groups, int gpr,
                                                        uint8_t* __restrict__ xq, float* __restrict__ sx,
-                                                       const int32_t* __restrict__ counts, int E, int T,
-                                                       int has_shared, int BM, int2* __restrict__ tiles,
-                                                       int32_t* __restrict__ tile_count) {
+                                                       const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ offsets, int E, int T, int P,
+                                                       int has_shared, int BM, int4* __restrict__ tiles, int max_tiles,
+                                                       int n_qblocks, RowInfo ri, const int32_t* __restrict__ perm,
+                                                       const float* __restrict__ topk_w, int k) {
+  if (blockIdx.x >= n_qblocks && blockIdx.x + 1 < gridDim.x) {
+    const int q = (blockIdx.x - n_qblocks) * 256 + threadIdx.x;
+    if (q < P) {
+      const int p = perm[q];
+      ri.tok[q] = p >= 0 ? p / k : 0;
+      ri.prow[q] = p;
+      ri.w[q] = p >= 0 ? topk_w[p] : 0.f;
+    } else if (q < P + (has_shared ? T : 0)) {
+      ri.tok[q] = q - P;
+      ri.prow[q] = q;
+      ri.w[q] = 1.f;
+    }
+    return;
+  }
   if (blockIdx.x + 1 < gridDim.x) {
     const int lane = threadIdx.x & 63;
     const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -100,12 +121,13 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict
   __shared__ int32_t tmp[17];
   constexpr int PER = (kMaxExperts + 1 + 255) / 256;  // groups per thread
   const int G = E + (has_shared ? 1 : 0);
-  int nt[PER], sum = 0;
+  int nt[PER], rows[PER], h0[PER], sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int g = PER * threadIdx.x + i;
-    const int rows = g < E ? counts[g] : (g < G ? T : 0);
-    nt[i] = (rows + BM - 1) / BM;
+    rows[i] = g < E ? counts[g] : (g < G ? T : 0);
+    h0[i] = g < E ? offsets[g] : P;
+    nt[i] = (rows[i] + BM - 1) / BM;
     sum += nt[i];
   }
   int total;
@@ -113,10 +135,11 @@ __global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int g = PER * threadIdx.x + i;
-    for (int j = 0; j < nt[i]; ++j) tiles[s + j] = make_int2(g, j * BM);
+    for (int j = 0; j < nt[i]; ++j)
+      tiles[s + j] = make_int4(g, j * BM, h0[i] + j * BM, min(BM, rows[i] - j * BM));
     s += nt[i];
   }
-  if (threadIdx.x == 0) *tile_count = total;
+  for (int i = total + threadIdx.x; i < max_tiles; i += 256) tiles[i] = make_int4(-1, 0, 0, 0);
 }
 
 // Address of the weight bytes a lane streams for one 16-row tile: in the
@@ -147,7 +170,7 @@ __device__ __forceinline__ WeightStream weight_stream(const uint8_t* mat, int ro
 // output row of h (sorted pair index, or P + t for the shared expert), the
 // partial-output row (pair index p, or P + t) and the routing weight.
 struct TileRows {
-  int g, m0, rows;
+  int g, m0, hrow0, rows;  // g < 0: no tile
   bool shared;
 };
 
@@ -167,14 +190,14 @@ __device__ __forceinline__ WorkItem work_item(int n_slices) {
   return it;
 }
 
-__device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile, int BM) {
-  const int2 td = a.tiles[tile];
+__device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile) {
+  const int4 td = a.tiles[tile];
   TileRows r;
   r.g = td.x;
   r.m0 = td.y;
+  r.hrow0 = td.z;
+  r.rows = td.w;
   r.shared = td.x == a.E;
-  const int n = r.shared ? a.T : a.offsets[td.x + 1] - a.offsets[td.x];
-  r.rows = min(BM, n - td.y);
   return r;
 }
 
@@ -202,23 +225,22 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
   constexpr int NT = kGateUpWaves * 64;
   const WorkItem it = work_item(a.n_slices);
   const int tile = it.tile;
-  if (tile >= *a.tile_count) return;
-  const TileRows tr = tile_rows(a, tile, BM);
+  const TileRows tr = tile_rows(a, tile);
+  if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int nb = it.slice;
   if (nb * 128 >= Fg) return;
 
-  const int RB = a.d * EB;        // bytes per activation / weight row
-  const int nbb = RB / 128;       // 128-byte K blocks
-  const int xstride = RB + 16;    // padded LDS row
+  const int RB = a.d * EB;        // bytes per activation / weight row in HBM
+  const int nbb = RB / 128;       // 128-byte K blocks of a weight row
+  const int xstride = a.d * 2 + 16;  // padded LDS row: the activations as bf16
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* xs = smem;
-  float* sxs = (float*)(smem + BM * xstride);           // [BM][d/128] (FP8 only)
+  float* sxs = (float*)(smem + (BM + 1) * xstride);     // [BM][d/128] (FP8 only)
   float* red = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [waves][BM]
-  int* tok = (int*)(red + kGateUpWaves * BM);           // [BM] token of each row
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
   const size_t wsz = (size_t)a.F * RB;  // bytes of one routed expert matrix
   const uint8_t* wg = tr.shared ? (const uint8_t*)a.shg : (const uint8_t*)a.wg + (size_t)tr.g * wsz;
   const uint8_t* wu = tr.shared ? (const uint8_t*)a.shu : (const uint8_t*)a.wu + (size_t)tr.g * wsz;
@@ -257,33 +279,59 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       whi[r][j] = stream_load(p + ws[r].hi_off);
     }
   };
-  // The weight stream depends only on the tile's expert and feature slice:
-  // start it before the activation rows are staged.
-  load(0, 0);
-  load(1, 0);
-
-  if (tid < BM) {
-    int t = -1;
-    if (tid < tr.rows) t = tr.shared ? tr.m0 + tid : a.perm[a.offsets[tr.g] + tr.m0 + tid] / a.k;
-    tok[tid] = t;
-  }
-  __syncthreads();
-  {
-    const int cpr = RB / 16;
-    const uint8_t* xa = (const uint8_t*)a.xa;
-    for (int i = tid; i < BM * cpr; i += NT) {
-      const int r = i / cpr, c = i - r * cpr, t = tok[r];
-      v4i v = {0, 0, 0, 0};
-      if (t >= 0) v = *(const v4i*)(xa + (size_t)t * RB + c * 16);
-      *(v4i*)(xs + r * xstride + c * 16) = v;
+  // Staging.  Loads complete in issue order as far as the wait counter goes,
+  // so the order is pinned: the token of each row this thread stages (perm),
+  // then the weight stream, then the activation rows (which need the tokens).
+  // All loads are unconditional (clamped addresses, zero by select) and the
+  // chunks past the tile land in a spare LDS row, so the code is straight-line
+  // and every wait is exact.  The first batch of SB chunks per thread covers a
+  // 16-row tile at d = 2048.
+  constexpr int SB = 4;
+  const int cpr = RB / 16, nch = BM * cpr, nkb = a.d / 128;
+  const uint8_t* xa = (const uint8_t*)a.xa;
+  const int rlast = tr.rows - 1;
+  auto row_token = [&](int r) { return a.ri.tok[tr.hrow0 + min(r, rlast)]; };  // token of tile row r (clamped)
+  auto stage = [&](int i0, bool first) {
+    int tk[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / cpr);
+    float sv = 0.f;
+    if (WT == 2 && first) sv = a.sxa[(size_t)row_token(tid / nkb) * nkb + tid % nkb];
+    if (first) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(0, 0);
+      load(1, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (WT == 2) {
-      const int nkb = a.d / 128;
-      for (int i = tid; i < BM * nkb; i += NT) {
-        const int r = i / nkb, c = i - r * nkb, t = tok[r];
-        sxs[i] = t >= 0 ? a.sxa[(size_t)t * nkb + c] : 0.f;
+    v4i v[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * NT, c = i % cpr;
+      v[u] = *(const v4i*)(xa + (size_t)tk[u] * RB + c * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
+      const bool live = i < nch && r <= rlast;
+      const v4i z = {0, 0, 0, 0};
+      const v4i x = live ? v[u] : z;
+      uint8_t* dst = xs + (i < nch ? r : BM) * xstride;
+      if constexpr (WT == 2) {  // E4M3 codes -> bf16 once per block (exact)
+        v4i lo, hi;
+        e4m3x16_to_bf16(x, lo, hi);
+        *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
+        *(v4i*)(dst + (i < nch ? c : 0) * 32 + 16) = hi;
+      } else {
+        *(v4i*)(dst + (i < nch ? c : 0) * 16) = x;
       }
     }
+    if (WT == 2 && first && tid < BM * nkb) sxs[tid] = tid / nkb <= rlast ? sv : 0.f;
+  };
+  stage(tid, true);
+  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
+  if (WT == 2) {
+    for (int i = tid + NT; i < BM * nkb; i += NT)  // tall tiles or wide rows only
+      sxs[i] = i / nkb <= rlast ? a.sxa[(size_t)row_token(i / nkb) * nkb + i % nkb] : 0.f;
   }
   __syncthreads();
 
@@ -294,16 +342,18 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       if (bb >= nbb) break;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
-        const v4i blo = *(const v4i*)bp;
-        const v4i bhi = *(const v4i*)(bp + 64);
         if constexpr (WT == 2) {
+          // bf16 activations of K block bb in the weight codes' K order: codes
+          // 16*(lane/16) + [0,16) of each 64-element half
+          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 256 + 2 * lk;
+          const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 16), *(const v4i*)(bp + 128),
+                            *(const v4i*)(bp + 144)};
           const float cs = sxs[(c * 16 + lr) * nbb + bb] * (r == 0 ? sgp[bb] : sup[bb]);
-          v4i b[4];
-          e4m3x16_to_bf16(blo, b[0], b[1]);
-          e4m3x16_to_bf16(bhi, b[2], b[3]);
           acc[r][c] += kblock_e4m3_exact(wlo[r][j], whi[r][j], b) * cs;
         } else {
+          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
+          const v4i blo = *(const v4i*)bp;
+          const v4i bhi = *(const v4i*)(bp + 64);
           acc[r][c] = mfma_bf16(wlo[r][j], blo, acc[r][c]);
           acc[r][c] = mfma_bf16(whi[r][j], bhi, acc[r][c]);
         }
@@ -328,7 +378,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       const float gv = acc[0][c][i], uv = acc[1][c][i];
       h[c][i] = gv / (1.0f + expf(-gv)) * uv;
     }
-  const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
+  const int hrow0 = tr.hrow0;
   const int fcol = f0 + 4 * (lane >> 4);
   if constexpr (WT == 2) {
 #pragma unroll
@@ -388,22 +438,23 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   constexpr int KG = RT == 1 ? 10 : 5;  // K blocks requested per stage
   const WorkItem it = work_item(a.n_slices);
   const int tile = it.tile;
-  if (tile >= *a.tile_count) return;
-  const TileRows tr = tile_rows(a, tile, BM);
+  const TileRows tr = tile_rows(a, tile);
+  if (tr.g < 0) return;
   const int nb = it.slice;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int RB = Fg * EB;          // bytes per h row / W_down row
   const int nbb = RB / 128;
   const int hstride_b = a.hstride * EB;
-  const int lstride = RB + 16;
+  const int lstride = Fg * 2 + 16;  // padded LDS row: h as bf16
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* hs = smem;
-  float* shs = (float*)(smem + BM * lstride);                // [BM][Fg/128] (FP8)
+  float* shs = (float*)(smem + (BM + 1) * lstride);          // [BM][Fg/128] (FP8)
   float* wrow = shs + (WT == 2 ? BM * (Fg / 128) : 0);       // [BM] routing weight
   int* orow = (int*)(wrow + BM);                             // [BM] partial-output row
+  float* wsd = (float*)(orow + BM);                          // [1 or 2][Fg/128] W_down block scales
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
   const int n0 = (nb * 4 + wave) * 16 * RT;
   const bool wave_live = n0 < a.d;  // d is a multiple of 16*RT here: whole waves are live or not
   const uint8_t* wd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * a.d * RB;
@@ -411,60 +462,85 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   const WeightStream ws = weight_stream(wd, RB, nl, a.w_tiled, lane);
   // 16-row tile r of the wave starts 16*r rows (tiled: r tiles) further on
   const size_t tile_step = a.w_tiled ? (size_t)nbb * 2048 : (size_t)16 * RB;
-  const float* sdp = nullptr;
-  if (WT == 2) {
-    const int nkb = Fg / 128;
-    sdp = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)(nl / 128) * nkb;
-  }
+  // W_down block scales of the block's 64*RT rows (one or two 128-row scale
+  // blocks), staged in LDS with h; the wave's row of them
+  const int nsr = RT == 4 ? 2 : 1, srow0 = nb * 64 * RT / 128;
+  const float* sdp = wsd + (nl / 128 - srow0) * (Fg / 128);
   // The weight stream depends only on the tile's expert and feature slice:
   // request it before the h rows are staged.  A stage = KG K blocks of one
   // 16-row tile; two stages in flight.
   v4i wlo[2][KG], whi[2][KG];
   auto load = [&](int slot, int r, int q0) {
 #pragma unroll
-    for (int j = 0; j < KG; ++j) {
-      if (q0 + j < nbb) {
-        const uint8_t* p = ws.p + r * tile_step + (size_t)(q0 + j) * ws.kb_stride;
-        wlo[slot][j] = stream_load(p);
-        whi[slot][j] = stream_load(p + ws.hi_off);
+    for (int j = 0; j < KG; ++j) {  // unconditional: past the row's end the last K block is read again
+      const uint8_t* p = ws.p + r * tile_step + (size_t)min(q0 + j, nbb - 1) * ws.kb_stride;
+      wlo[slot][j] = stream_load(p);
+      whi[slot][j] = stream_load(p + ws.hi_off);
+    }
+  };
+  // Staging, in pinned issue order (loads complete in issue order as far as
+  // the wait counter goes): the pair rows, the h scales, the W_down scales and
+  // the first batch of h rows, then the weight stream, then the routing
+  // weights (which need the pair rows).  Unconditional loads from clamped
+  // addresses, zero by select, a spare LDS row for chunks past the tile: the
+  // code is straight-line and every wait is exact.
+  constexpr int SB = 4;
+  const int hrow0 = tr.hrow0, rlast = tr.rows - 1;
+  const int cpr = RB / 16, nch = BM * cpr, nkb = Fg / 128, gpr = a.hstride / 128;
+  const uint8_t* hsrc = (const uint8_t*)a.h;
+  const int o = a.ri.prow[hrow0 + min(tid, rlast)];
+  float sv = 0.f, dv = 0.f;
+  if (WT == 2) {
+    sv = a.sh[(size_t)(hrow0 + min(tid / nkb, rlast)) * gpr + tid % nkb];
+    const float* sd = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)srow0 * nkb;
+    dv = sd[min(tid, nsr * nkb - 1)];
+  }
+  auto stage_load = [&](int i0, v4i (&v)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * 256, r = min(i / cpr, rlast), c = i % cpr;
+      v[u] = *(const v4i*)(hsrc + (size_t)(hrow0 + r) * hstride_b + c * 16);
+    }
+  };
+  auto stage_store = [&](int i0, const v4i (&v)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * 256, r = i / cpr, c = i % cpr;
+      const bool live = i < nch && r <= rlast;
+      const v4i z = {0, 0, 0, 0};
+      const v4i x = live ? v[u] : z;
+      uint8_t* dst = hs + (i < nch ? r : BM) * lstride;
+      if constexpr (WT == 2) {  // E4M3 codes -> bf16 once per block (exact)
+        v4i lo, hi;
+        e4m3x16_to_bf16(x, lo, hi);
+        *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
+        *(v4i*)(dst + (i < nch ? c : 0) * 32 + 16) = hi;
+      } else {
+        *(v4i*)(dst + (i < nch ? c : 0) * 16) = x;
       }
     }
   };
+  v4i hv[SB];
+  stage_load(tid, hv);
+  __builtin_amdgcn_sched_barrier(0);
   load(0, 0, 0);
   if (RT > 1) load(1, 1, 0);
-
-  const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
-  if (tid < BM) {
-    int o = -1;
-    float w = 0.f;
-    if (tid < tr.rows) {
-      if (tr.shared) {
-        o = a.P + tr.m0 + tid;
-        w = 1.f;
-      } else {
-        o = a.perm[hrow0 + tid];
-        w = a.topk_w[o];
-      }
-    }
-    orow[tid] = o;
-    wrow[tid] = w;
+  __builtin_amdgcn_sched_barrier(0);
+  const float wt = a.ri.w[hrow0 + min(tid, rlast)];
+  stage_store(tid, hv);
+  for (int i0 = tid + 256 * SB; i0 < nch; i0 += 256 * SB) {  // tall tiles or wide rows only
+    stage_load(i0, hv);
+    stage_store(i0, hv);
   }
-  {
-    const int cpr = RB / 16;
-    const uint8_t* hsrc = (const uint8_t*)a.h;
-    for (int i = tid; i < BM * cpr; i += 256) {
-      const int r = i / cpr, c = i - r * cpr;
-      v4i v = {0, 0, 0, 0};
-      if (r < tr.rows) v = *(const v4i*)(hsrc + (size_t)(hrow0 + r) * hstride_b + c * 16);
-      *(v4i*)(hs + r * lstride + c * 16) = v;
-    }
-    if (WT == 2) {
-      const int nkb = Fg / 128, gpr = a.hstride / 128;
-      for (int i = tid; i < BM * nkb; i += 256) {
-        const int r = i / nkb, c = i - r * nkb;
-        shs[i] = r < tr.rows ? a.sh[(size_t)(hrow0 + r) * gpr + c] : 0.f;
-      }
-    }
+  if (WT == 2) {
+    if (tid < BM * nkb) shs[tid] = tid / nkb <= rlast ? sv : 0.f;
+    for (int i = tid + 256; i < BM * nkb; i += 256)  // tall tiles or wide rows only
+      shs[i] = i / nkb <= rlast ? a.sh[(size_t)(hrow0 + i / nkb) * gpr + i % nkb] : 0.f;
+    if (tid < nsr * nkb) wsd[tid] = dv;
+  }
+  if (tid < BM) {
+    orow[tid] = tid <= rlast ? o : -1;
+    wrow[tid] = tid <= rlast ? wt : 0.f;
   }
   __syncthreads();
   if (!wave_live) return;
@@ -481,16 +557,16 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
       if (bb >= nbb) break;
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 128 + lk;
-        const v4i blo = *(const v4i*)bp;
-        const v4i bhi = *(const v4i*)(bp + 64);
         if constexpr (WT == 2) {
-          v4i b[4];
-          e4m3x16_to_bf16(blo, b[0], b[1]);
-          e4m3x16_to_bf16(bhi, b[2], b[3]);
+          const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 256 + 2 * lk;
+          const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 16), *(const v4i*)(bp + 128),
+                            *(const v4i*)(bp + 144)};
           // the wave's 16*RT <= 64 rows start at a multiple of 64: one 128-row scale block
           acc[r][c] += kblock_e4m3_exact(wlo[slot][j], whi[slot][j], b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
         } else {
+          const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 128 + lk;
+          const v4i blo = *(const v4i*)bp;
+          const v4i bhi = *(const v4i*)(bp + 64);
           acc[r][c] = mfma_bf16(wlo[slot][j], blo, acc[r][c]);
           acc[r][c] = mfma_bf16(whi[slot][j], bhi, acc[r][c]);
         }
@@ -533,8 +609,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 template <int BM>
 __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
   const int tile = blockIdx.y;
-  if (tile >= *a.tile_count) return;
-  const TileRows tr = tile_rows(a, tile, BM);
+  const TileRows tr = tile_rows(a, tile);
+  if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int f = blockIdx.x * 64 + (threadIdx.x & 63);
   if (blockIdx.x * 64 >= Fg) return;
@@ -546,7 +622,7 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
     const int r = i / a.d, c = i - r * a.d;
     float v = 0.f;
     if (r < tr.rows) {
-      const int t = tr.shared ? tr.m0 + r : a.perm[a.offsets[tr.g] + tr.m0 + r] / a.k;
+      const int t = tr.shared ? tr.m0 + r : a.perm[tr.hrow0 + r] / a.k;
       v = x[(size_t)t * a.d + c];
     }
     xs[i] = v;
@@ -556,7 +632,7 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
   const size_t wsz = (size_t)a.F * a.d;
   const float* wg = (tr.shared ? (const float*)a.shg : (const float*)a.wg + tr.g * wsz) + (size_t)f * a.d;
   const float* wu = (tr.shared ? (const float*)a.shu : (const float*)a.wu + tr.g * wsz) + (size_t)f * a.d;
-  const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
+  const int hrow0 = tr.hrow0;
   for (int r = tid >> 6; r < tr.rows; r += 4) {
     float g = 0.f, u = 0.f;
     for (int c = 0; c < a.d; ++c) {
@@ -570,14 +646,14 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
 template <int BM>
 __global__ __launch_bounds__(256) void down_f32_kernel(ExpertArgs a) {
   const int tile = blockIdx.y;
-  if (tile >= *a.tile_count) return;
-  const TileRows tr = tile_rows(a, tile, BM);
+  const TileRows tr = tile_rows(a, tile);
+  if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int n = blockIdx.x * 64 + (threadIdx.x & 63);
   extern __shared__ __align__(16) uint8_t smem[];
   float* hs = (float*)smem;  // [BM][Fg]
   const int tid = threadIdx.x;
-  const int hrow0 = tr.shared ? a.P + tr.m0 : a.offsets[tr.g] + tr.m0;
+  const int hrow0 = tr.hrow0;
   for (int i = tid; i < BM * Fg; i += 256) {
     const int r = i / Fg, c = i - r * Fg;
     hs[i] = r < tr.rows ? ((const float*)a.h)[(size_t)(hrow0 + r) * a.hstride + c] : 0.f;
@@ -648,13 +724,16 @@ hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n
   return hipGetLastError();
 }
 
-hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts, int E,
-                          bool has_shared, int BM, int2* tiles, int32_t* tile_count, hipStream_t st) {
+hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts,
+                          const int32_t* offsets, int E, int P, bool has_shared, int BM, int4* tiles, int max_tiles,
+                          const RowInfo& ri, const int32_t* perm, const float* topk_w, int k, hipStream_t st) {
   const int gpr = d / 128;
   const int64_t ng = xq ? (int64_t)T * gpr : 0;
-  const int64_t blocks = (ng + 3) / 4 + 1;
-  prepare_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint16_t*)x, ng, gpr, xq, sx, counts, E, T,
-                                                   has_shared ? 1 : 0, BM, tiles, tile_count);
+  const int64_t nqb = (ng + 3) / 4;
+  const int64_t nrb = ((int64_t)P + (has_shared ? T : 0) + 255) / 256;
+  prepare_kernel<<<(unsigned)(nqb + nrb + 1), 256, 0, st>>>((const uint16_t*)x, ng, gpr, xq, sx, counts, offsets, E,
+                                                            T, P, has_shared ? 1 : 0, BM, tiles, max_tiles, (int)nqb,
+                                                            ri, perm, topk_w, k);
   return hipGetLastError();
 }
 
@@ -671,17 +750,15 @@ static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, co
 
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
-  const int EB = wmode == 2 ? 1 : 2;
-  size_t b = (size_t)BM * (d * EB + 16);
+  size_t b = (size_t)(BM + 1) * (d * 2 + 16);  // activations as bf16, plus a spare row
   if (wmode == 2) b += (size_t)BM * (d / 128) * 4;
-  return b + kGateUpWaves * BM * 4 + BM * 4;
+  return b + kGateUpWaves * BM * 4;
 }
 
 size_t down_lds_bytes(int BM, int wmode, int Fg) {
   if (wmode == 0) return (size_t)BM * Fg * 4;
-  const int EB = wmode == 2 ? 1 : 2;
-  size_t b = (size_t)BM * (Fg * EB + 16);
-  if (wmode == 2) b += (size_t)BM * (Fg / 128) * 4;
+  size_t b = (size_t)(BM + 1) * (Fg * 2 + 16);  // h as bf16, plus a spare row
+  if (wmode == 2) b += (size_t)BM * (Fg / 128) * 4 + 2 * (Fg / 128) * 4;
   return b + BM * 4 + BM * 4;
 }
 

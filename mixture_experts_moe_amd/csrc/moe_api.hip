@@ -14,7 +14,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, rpart, chunk_hist, local_rank, tiles, tile_count, xq, sx, h, sh, part, total;
+  size_t logits, rpart, chunk_hist, local_rank, tiles, rinfo, xq, sx, h, sh, part, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -44,8 +44,8 @@ Layout layout(const moe_shape& s) {
   L.rpart = seg(moe::router_part_floats(s.T, s.top_k, s.d_model, s.n_experts, s.act_dtype == MOE_BF16) * 4);
   L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
   L.local_rank = seg(P * 4);
-  L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int2));
-  L.tile_count = seg(4);
+  L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int4));
+  L.rinfo = seg((P + T) * 12);
   L.xq = seg(fp8 ? T * d : 0);
   L.sx = seg(fp8 ? T * (d / 128) * 4 : 0);
   L.h = seg((P + T) * Fmax * h_elem_bytes(s.w_dtype));
@@ -181,8 +181,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   const int BM = pick_bm(*shape);
 
   ExpertArgs a;
-  a.tiles = (const int2*)(base + L.tiles);
-  a.tile_count = (const int32_t*)(base + L.tile_count);
+  a.tiles = (const int4*)(base + L.tiles);
   a.offsets = r->offsets;
   a.perm = r->perm;
   a.topk_w = r->topk_w;
@@ -214,18 +213,22 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.h = base + L.h;
   a.sh = (float*)(base + L.sh);
   a.part = (float*)(base + L.part);
+  a.ri.tok = (int32_t*)(base + L.rinfo);
+  a.ri.prow = a.ri.tok + (P + T);
+  a.ri.w = (float*)(a.ri.prow + (P + T));
 
   hipError_t e = hipSuccess;
   auto mark = [&](int i) {
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], st);
   };
+  const int max_tiles = (int)max_tiles_for(*shape, BM);
   mark(0);
   if (stages & MOE_STAGE_PREPARE) {
-    e = moe::launch_prepare(x, T, d, fp8 ? (uint8_t*)(base + L.xq) : nullptr, (float*)(base + L.sx), r->counts, E,
-                            has_shared, BM, (int2*)(base + L.tiles), (int32_t*)(base + L.tile_count), st);
+    e = moe::launch_prepare(x, T, d, fp8 ? (uint8_t*)(base + L.xq) : nullptr, (float*)(base + L.sx), r->counts,
+                            r->offsets, E, P, has_shared, BM, (int4*)(base + L.tiles), max_tiles, a.ri, r->perm,
+                            r->topk_w, k, st);
     mark(1);
   }
-  const int max_tiles = (int)max_tiles_for(*shape, BM);
   if (e == hipSuccess && (stages & MOE_STAGE_GATE_UP)) {
     e = moe::launch_gateup(a, shape->w_dtype, BM, max_tiles, st);
     mark(2);

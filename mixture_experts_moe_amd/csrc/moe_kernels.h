@@ -10,10 +10,17 @@ namespace moe {
 constexpr int kMaxExperts = 512;
 constexpr int kMaxTopK = 8;
 
+// Per h row q (sorted pairs, then P + t for the shared expert): token, row of
+// the partial output, routing weight (1 for the shared expert).
+struct RowInfo {
+  int32_t* tok;
+  int32_t* prow;
+  float* w;
+};
+
 // Everything the expert kernels read or write (device pointers).
 struct ExpertArgs {
-  const int2* tiles;          // [max_tiles] (group, first row)
-  const int32_t* tile_count;  // [1]
+  const int4* tiles;          // [max_tiles] (group, first row, first h row, rows); group -1: none
   const int32_t* offsets;     // [E+1]
   const int32_t* perm;        // [P]
   const float* topk_w;        // [P]
@@ -30,6 +37,7 @@ struct ExpertArgs {
   void* h;                    // [P+T][hstride]: E4M3 codes, bf16 or fp32
   float* sh;                  // [P+T][hstride/128] E4M3 scales of h
   float* part;                // [P+T][d] weighted expert outputs
+  RowInfo ri;                 // [P+T] each
 };
 
 size_t dispatch_chunk_hist_ints(int T, int k, int E);
@@ -55,8 +63,9 @@ hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n
                                 hipStream_t st);
 // Forward preparation in one launch: E4M3 activation quantisation (when
 // xq != null) and the expert tile plan (last block).
-hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts, int E,
-                          bool has_shared, int BM, int2* tiles, int32_t* tile_count, hipStream_t st);
+hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts,
+                          const int32_t* offsets, int E, int P, bool has_shared, int BM, int4* tiles, int max_tiles,
+                          const RowInfo& ri, const int32_t* perm, const float* topk_w, int k, hipStream_t st);
 hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
 hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
