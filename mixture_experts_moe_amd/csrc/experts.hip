@@ -74,72 +74,125 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Forward preparation, one launch: the first blocks quantise the activations
-// (four 128-element groups per block, as above); the next ones write, for every
-// h row q (sorted pairs, then the shared expert's rows P + t), its token, its
-// partial-output row and its routing weight, so the expert kernels read them
-// with one load per row; the last block plans the expert tiles: tiles
-// per group = ceil(rows / BM), groups in order (routed experts 0..E-1, then the
-// shared expert with all T rows); tile i = (group, first row, its first h row,
-// rows), so an expert block finds all it needs in one load; the slots past the
-// last tile get group -1.
+// Forward preparation, one launch.
+//  * The first blocks write the block schedules of the two expert kernels (see
+//    below).
+//  * The next ones write, for every h row q (sorted pairs, then the shared
+//    expert's rows P + t), its token, its partial-output row and its routing
+//    weight, so the expert kernels read them with one load per row.
+//  * The last ones quantise the activations (four 128-element groups per
+//    block, as above).
+//  Schedules.  The
+//    tiles: per group (routed experts 0..E-1, then the shared expert with all
+//    T rows) ceil(rows / BM) tiles of BM rows, in group order; work item
+//    i = tile * n_slices + slice.  Block b of a kernel gets item i = b
+//    (identity), or, in XCD mode, item (b % 8) * L + b / 8 with L = ceil(items /
+//    8): the chip's eight XCDs (block b runs on XCD b % 8, each with its own L2)
+//    then each take one contiguous run of items, so the tiles of one expert run
+//    on one XCD close together in time and share its weight stream through that
+//    L2.  A record is (group, first row, first h row, rows | slice << 16), or
+//    group -1 for a block without work.  Each plan block recomputes the tile
+//    prefix over the groups (E + 1 counts) and fills its share of records.
 // ---------------------------------------------------------------------------
+struct PlanArgs {
+  const int32_t* counts;
+  const int32_t* offsets;
+  int E, T, P, has_shared, BM, xcd;
+  int4* sched[2];  // gate/up, down
+  int n_sched[2];  // blocks of each kernel (multiples of 8)
+  int n_slices[2];
+};
+
+constexpr int kPlanPerThread = 2;
+
+__device__ void plan_block(const PlanArgs& pa, int blk) {
+  __shared__ int32_t tstart[kMaxExperts + 2], grow[kMaxExperts + 1], gh0[kMaxExperts + 1];
+  __shared__ int32_t tmp[17];
+  constexpr int PER = (kMaxExperts + 1 + 255) / 256;  // groups per thread
+  const int E = pa.E, G = E + (pa.has_shared ? 1 : 0), BM = pa.BM;
+  int nt[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = PER * threadIdx.x + i;
+    const int rows = g < E ? pa.counts[g] : (g < G ? pa.T : 0);
+    if (g < G) {
+      grow[g] = rows;
+      gh0[g] = g < E ? pa.offsets[g] : pa.P;
+    }
+    nt[i] = (rows + BM - 1) / BM;
+    sum += nt[i];
+  }
+  int total;
+  int st = block_excl_scan<256>(sum, tmp, &total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int g = PER * threadIdx.x + i;
+    if (g < G) tstart[g] = st;
+    st += nt[i];
+  }
+  if (threadIdx.x == 0) tstart[G] = total;
+  __syncthreads();
+  for (int u = 0; u < kPlanPerThread; ++u) {
+    int e = (blk * kPlanPerThread + u) * 256 + threadIdx.x;
+    const int which = e < pa.n_sched[0] ? 0 : 1;
+    const int b = which ? e - pa.n_sched[0] : e;
+    if (b >= pa.n_sched[which]) return;
+    const int nsl = pa.n_slices[which];
+    const int n_items = total * nsl;
+    int item = b;
+    if (pa.xcd) {
+      const int L = (n_items + 7) / 8, j = b / 8;
+      item = j < L ? (b % 8) * L + j : n_items;
+    }
+    int4 rec = make_int4(-1, 0, 0, 0);
+    if (item < n_items) {
+      const int t = item / nsl, sl = item - t * nsl;
+      int lo = 0, hi = G - 1;  // the last group whose first tile is <= t (it has tiles)
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (tstart[mid] <= t) lo = mid;
+        else hi = mid - 1;
+      }
+      const int m0 = (t - tstart[lo]) * BM;
+      rec = make_int4(lo, m0, gh0[lo] + m0, min(BM, grow[lo] - m0) | (sl << 16));
+    }
+    pa.sched[which][b] = rec;
+  }
+}
+
 __global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict__ x, int64_t n_groups, int gpr,
                                                        uint8_t* __restrict__ xq, float* __restrict__ sx,
-                                                       const int32_t* __restrict__ counts,
-                                                       const int32_t* __restrict__ offsets, int E, int T, int P,
-                                                       int has_shared, int BM, int4* __restrict__ tiles, int max_tiles,
-                                                       int n_qblocks, RowInfo ri, const int32_t* __restrict__ perm,
-                                                       const float* __restrict__ topk_w, int k) {
-  if (blockIdx.x >= n_qblocks && blockIdx.x + 1 < gridDim.x) {
-    const int q = (blockIdx.x - n_qblocks) * 256 + threadIdx.x;
+                                                       int n_pblocks, int n_rblocks, RowInfo ri,
+                                                       const int32_t* __restrict__ perm,
+                                                       const float* __restrict__ topk_w, int k, PlanArgs pa) {
+  if (blockIdx.x < n_pblocks) {  // the longest blocks go first
+    plan_block(pa, blockIdx.x);
+    return;
+  }
+  if (blockIdx.x < n_pblocks + n_rblocks) {
+    const int q = (blockIdx.x - n_pblocks) * 256 + threadIdx.x, P = pa.P;
     if (q < P) {
       const int p = perm[q];
       ri.tok[q] = p >= 0 ? p / k : 0;
       ri.prow[q] = p;
       ri.w[q] = p >= 0 ? topk_w[p] : 0.f;
-    } else if (q < P + (has_shared ? T : 0)) {
+    } else if (q < P + (pa.has_shared ? pa.T : 0)) {
       ri.tok[q] = q - P;
       ri.prow[q] = q;
       ri.w[q] = 1.f;
     }
     return;
   }
-  if (blockIdx.x + 1 < gridDim.x) {
-    const int lane = threadIdx.x & 63;
-    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (g >= n_groups) return;
-    const int64_t o = (g / gpr) * (int64_t)gpr * 128 + (g % gpr) * 128 + 2 * lane;
-    const uint32_t pr = *(const uint32_t*)(x + o);
-    const float v0 = __uint_as_float(pr << 16), v1 = __uint_as_float(pr & 0xffff0000u);
-    const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-    const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-    *(uint16_t*)(xq + o) = (uint16_t)pack2_e4m3(v0 / s, v1 / s);
-    if (lane == 0) sx[g] = s;
-    return;
-  }
-  __shared__ int32_t tmp[17];
-  constexpr int PER = (kMaxExperts + 1 + 255) / 256;  // groups per thread
-  const int G = E + (has_shared ? 1 : 0);
-  int nt[PER], rows[PER], h0[PER], sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int g = PER * threadIdx.x + i;
-    rows[i] = g < E ? counts[g] : (g < G ? T : 0);
-    h0[i] = g < E ? offsets[g] : P;
-    nt[i] = (rows[i] + BM - 1) / BM;
-    sum += nt[i];
-  }
-  int total;
-  int s = block_excl_scan<256>(sum, tmp, &total);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int g = PER * threadIdx.x + i;
-    for (int j = 0; j < nt[i]; ++j)
-      tiles[s + j] = make_int4(g, j * BM, h0[i] + j * BM, min(BM, rows[i] - j * BM));
-    s += nt[i];
-  }
-  for (int i = total + threadIdx.x; i < max_tiles; i += 256) tiles[i] = make_int4(-1, 0, 0, 0);
+  const int lane = threadIdx.x & 63;
+  const int64_t g = (int64_t)(blockIdx.x - n_pblocks - n_rblocks) * 4 + (threadIdx.x >> 6);
+  if (g >= n_groups) return;
+  const int64_t o = (g / gpr) * (int64_t)gpr * 128 + (g % gpr) * 128 + 2 * lane;
+  const uint32_t pr = *(const uint32_t*)(x + o);
+  const float v0 = __uint_as_float(pr << 16), v1 = __uint_as_float(pr & 0xffff0000u);
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
+  *(uint16_t*)(xq + o) = (uint16_t)pack2_e4m3(v0 / s, v1 / s);
+  if (lane == 0) sx[g] = s;
 }
 
 // Address of the weight bytes a lane streams for one 16-row tile: in the
@@ -174,30 +227,17 @@ struct TileRows {
   bool shared;
 };
 
-// Work item of a block in a 1-D grid of n_slices x max_tiles blocks (max_tiles
-// is an upper bound: the actual tile count is only known on the device).  Items
-// run slice-fastest, so the feature slices of one tile (all reading the tile's
-// activation rows, and together one contiguous run of its expert's weights) are
-// dispatched together.  Blocks past the live tiles are idle.
-struct WorkItem {
-  int tile, slice;
-};
-inline unsigned work_grid(int n_items) { return (unsigned)n_items; }
-__device__ __forceinline__ WorkItem work_item(int n_slices) {
-  WorkItem it;
-  it.tile = blockIdx.x / n_slices;
-  it.slice = blockIdx.x % n_slices;
-  return it;
-}
-
-__device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile) {
-  const int4 td = a.tiles[tile];
+// The block's schedule record (written by the plan step): its tile's rows and
+// its feature slice.
+__device__ __forceinline__ TileRows block_rows(const ExpertArgs& a, int& slice) {
+  const int4 rec = a.sched[blockIdx.x];
   TileRows r;
-  r.g = td.x;
-  r.m0 = td.y;
-  r.hrow0 = td.z;
-  r.rows = td.w;
-  r.shared = td.x == a.E;
+  r.g = rec.x;
+  r.m0 = rec.y;
+  r.hrow0 = rec.z;
+  r.rows = rec.w & 0xffff;
+  r.shared = rec.x == a.E;
+  slice = rec.w >> 16;
   return r;
 }
 
@@ -211,29 +251,28 @@ __device__ __forceinline__ TileRows tile_rows(const ExpertArgs& a, int tile) {
 //   WT = 1: bf16 weights and activations, 16x16x32 MFMA accumulating in fp32;
 //           h stored as bf16.
 // Block = 8 waves covering one 128-feature group nb of h for one tile (see
-// work_item).  Wave w owns h features nb*128 + w*16 + [0, 16): one 16-row
+// block_rows).  Wave w owns h features nb*128 + w*16 + [0, 16): one 16-row
 // tile of W_gate and the same rows of W_up, so g and u of a feature meet in one
 // lane.  32 weight rows per wave keeps many short streams in flight, which the
 // HBM prefers to a few long ones.
 // ---------------------------------------------------------------------------
 constexpr int kGateUpWaves = 8;
 
-template <int BM, int WT>
+template <int BM, int WT, bool XB>
 __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertArgs a) {
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;  // bytes per element
   constexpr int NT = kGateUpWaves * 64;
-  const WorkItem it = work_item(a.n_slices);
-  const int tile = it.tile;
-  const TileRows tr = tile_rows(a, tile);
+  constexpr bool XBF = WT == 1 || XB;  // activations in LDS as bf16 (else E4M3 codes)
+  int nb;
+  const TileRows tr = block_rows(a, nb);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int nb = it.slice;
   if (nb * 128 >= Fg) return;
 
   const int RB = a.d * EB;        // bytes per activation / weight row in HBM
   const int nbb = RB / 128;       // 128-byte K blocks of a weight row
-  const int xstride = a.d * 2 + 16;  // padded LDS row: the activations as bf16
+  const int xstride = (XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* xs = smem;
   float* sxs = (float*)(smem + (BM + 1) * xstride);     // [BM][d/128] (FP8 only)
@@ -316,7 +355,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       const v4i z = {0, 0, 0, 0};
       const v4i x = live ? v[u] : z;
       uint8_t* dst = xs + (i < nch ? r : BM) * xstride;
-      if constexpr (WT == 2) {  // E4M3 codes -> bf16 once per block (exact)
+      if constexpr (WT == 2 && XB) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
         e4m3x16_to_bf16(x, lo, hi);
         *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
@@ -343,11 +382,20 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if constexpr (WT == 2) {
-          // bf16 activations of K block bb in the weight codes' K order: codes
-          // 16*(lane/16) + [0,16) of each 64-element half
-          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 256 + 2 * lk;
-          const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 16), *(const v4i*)(bp + 128),
-                            *(const v4i*)(bp + 144)};
+          v4i b[4];
+          if constexpr (XB) {
+            // bf16 activations of K block bb in the weight codes' K order: codes
+            // 16*(lane/16) + [0,16) of each 64-element half
+            const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 256 + 2 * lk;
+            b[0] = *(const v4i*)bp;
+            b[1] = *(const v4i*)(bp + 16);
+            b[2] = *(const v4i*)(bp + 128);
+            b[3] = *(const v4i*)(bp + 144);
+          } else {  // codes, decoded here
+            const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
+            e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
+            e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[2], b[3]);
+          }
           const float cs = sxs[(c * 16 + lr) * nbb + bb] * (r == 0 ? sgp[bb] : sup[bb]);
           acc[r][c] += kblock_e4m3_exact(wlo[r][j], whi[r][j], b) * cs;
         } else {
@@ -427,7 +475,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 // Down projection on the matrix cores; epilogue multiplies by the pair's
 // routing weight (1 for the shared expert) and writes the fp32 partial row of
 // pair p (or P + t).  A block takes one tile and one slice of 64*RT output
-// features (see work_item); wave w owns RT 16-row tiles (features nb*64*RT + w*16*RT + 16 r).
+// features (see block_rows); wave w owns RT 16-row tiles (features nb*64*RT + w*16*RT + 16 r).
 // RT = 2 for short tiles, RT = 4 for tall ones (a tile's h rows are staged once
 // per 256 features); RT = 1 when a row's K does not fit one stage.
 // ---------------------------------------------------------------------------
@@ -436,11 +484,9 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;
   constexpr int KG = RT == 1 ? 10 : 5;  // K blocks requested per stage
-  const WorkItem it = work_item(a.n_slices);
-  const int tile = it.tile;
-  const TileRows tr = tile_rows(a, tile);
+  int nb;
+  const TileRows tr = block_rows(a, nb);
   if (tr.g < 0) return;
-  const int nb = it.slice;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int RB = Fg * EB;          // bytes per h row / W_down row
   const int nbb = RB / 128;
@@ -608,12 +654,12 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 // ---------------------------------------------------------------------------
 template <int BM>
 __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
-  const int tile = blockIdx.y;
-  const TileRows tr = tile_rows(a, tile);
+  int sl;
+  const TileRows tr = block_rows(a, sl);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int f = blockIdx.x * 64 + (threadIdx.x & 63);
-  if (blockIdx.x * 64 >= Fg) return;
+  const int f = sl * 64 + (threadIdx.x & 63);
+  if (sl * 64 >= Fg) return;
   extern __shared__ __align__(16) uint8_t smem[];
   float* xs = (float*)smem;  // [BM][d]
   const int tid = threadIdx.x;
@@ -645,11 +691,11 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
 
 template <int BM>
 __global__ __launch_bounds__(256) void down_f32_kernel(ExpertArgs a) {
-  const int tile = blockIdx.y;
-  const TileRows tr = tile_rows(a, tile);
+  int sl;
+  const TileRows tr = block_rows(a, sl);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int n = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int n = sl * 64 + (threadIdx.x & 63);
   extern __shared__ __align__(16) uint8_t smem[];
   float* hs = (float*)smem;  // [BM][Fg]
   const int tid = threadIdx.x;
@@ -724,16 +770,30 @@ hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n
   return hipGetLastError();
 }
 
-hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts,
-                          const int32_t* offsets, int E, int P, bool has_shared, int BM, int4* tiles, int max_tiles,
-                          const RowInfo& ri, const int32_t* perm, const float* topk_w, int k, hipStream_t st) {
+hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const RowInfo& ri,
+                          const int32_t* perm, const float* topk_w, int k, const Plan& plan, const int32_t* counts,
+                          const int32_t* offsets, int E, int P, bool has_shared, hipStream_t st) {
   const int gpr = d / 128;
   const int64_t ng = xq ? (int64_t)T * gpr : 0;
   const int64_t nqb = (ng + 3) / 4;
   const int64_t nrb = ((int64_t)P + (has_shared ? T : 0) + 255) / 256;
-  prepare_kernel<<<(unsigned)(nqb + nrb + 1), 256, 0, st>>>((const uint16_t*)x, ng, gpr, xq, sx, counts, offsets, E,
-                                                            T, P, has_shared ? 1 : 0, BM, tiles, max_tiles, (int)nqb,
-                                                            ri, perm, topk_w, k);
+  PlanArgs pa;
+  pa.counts = counts;
+  pa.offsets = offsets;
+  pa.E = E;
+  pa.T = T;
+  pa.P = P;
+  pa.has_shared = has_shared ? 1 : 0;
+  pa.BM = plan.BM;
+  pa.xcd = plan.xcd ? 1 : 0;
+  for (int w = 0; w < 2; ++w) {
+    pa.sched[w] = plan.sched[w];
+    pa.n_sched[w] = plan.n_sched[w];
+    pa.n_slices[w] = plan.n_slices[w];
+  }
+  const int64_t npb = ((int64_t)plan.n_sched[0] + plan.n_sched[1] + 256 * kPlanPerThread - 1) / (256 * kPlanPerThread);
+  prepare_kernel<<<(unsigned)(nqb + nrb + npb), 256, 0, st>>>((const uint16_t*)x, ng, gpr, xq, sx, (int)npb, (int)nrb,
+                                                              ri, perm, topk_w, k, pa);
   return hipGetLastError();
 }
 
@@ -748,9 +808,13 @@ static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, co
   return hipGetLastError();
 }
 
+// Activations in LDS as bf16 for 16-row tiles; taller tiles keep the E4M3 codes
+// (decoded per use) so that two blocks fit a CU.
+static bool gateup_x_bf16(int BM, int wmode) { return wmode == 1 || BM <= 16; }
+
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
-  size_t b = (size_t)(BM + 1) * (d * 2 + 16);  // activations as bf16, plus a spare row
+  size_t b = (size_t)(BM + 1) * ((gateup_x_bf16(BM, wmode) ? d * 2 : d) + 16);  // plus a spare row
   if (wmode == 2) b += (size_t)BM * (d / 128) * 4;
   return b + kGateUpWaves * BM * 4;
 }
@@ -762,37 +826,48 @@ size_t down_lds_bytes(int BM, int wmode, int Fg) {
   return b + BM * 4 + BM * 4;
 }
 
-hipError_t launch_gateup(const ExpertArgs& a0, int wmode, int BM, int max_tiles, hipStream_t st) {
-  ExpertArgs a = a0;
-  const int Fmax = a.F > a.Fs ? a.F : a.Fs;
-  if (wmode == 0)
-    return launch_dyn(gateup_f32_kernel<16>, dim3((Fmax + 63) / 64, max_tiles), gateup_lds_bytes(16, 0, a.d), st, a);
-  a.max_tiles = max_tiles;
-  a.n_slices = Fmax / 128;
-  const dim3 grid(work_grid(a.n_slices * max_tiles));
-  const size_t lds = gateup_lds_bytes(BM, wmode, a.d);
-  const int nt = kGateUpWaves * 64;
-  if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2>, grid, lds, st, a, nt);
-  if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2>, grid, lds, st, a, nt);
-  if (wmode == 2 && BM == 64) return launch_dyn(gateup_mfma_kernel<64, 2>, grid, lds, st, a, nt);
-  if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1>, grid, lds, st, a, nt);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_down(const ExpertArgs& a0, int wmode, int BM, int max_tiles, hipStream_t st) {
-  ExpertArgs a = a0;
-  const int Fmax = a.F > a.Fs ? a.F : a.Fs;
-  if (wmode == 0)
-    return launch_dyn(down_f32_kernel<16>, dim3((a.d + 63) / 64, max_tiles), down_lds_bytes(16, 0, Fmax), st, a);
-  const size_t lds = down_lds_bytes(BM, wmode, Fmax);
+// Tiles, slices and schedule sizes of one forward call.
+int down_rows_per_wave(int BM, int wmode, int Fmax, int d) {
   // RT 16-row weight tiles per wave (RT > 1 needs a row's whole K in one stage):
   // 2 for short tiles, 4 for tall ones, whose h rows are then staged once per
   // 256 output features
+  if (wmode == 0) return 1;
   const bool one_stage = Fmax * (wmode == 2 ? 1 : 2) <= 5 * 128;
-  const int RT = !one_stage ? 1 : (BM == 16 ? (a.d % 128 == 0 ? 2 : 1) : (a.d % 256 == 0 ? 4 : 1));
-  a.max_tiles = max_tiles;
-  a.n_slices = (a.d + 64 * RT - 1) / (64 * RT);
-  const dim3 grid(work_grid(a.n_slices * max_tiles));
+  return !one_stage ? 1 : (BM == 16 ? (d % 128 == 0 ? 2 : 1) : (d % 256 == 0 ? 4 : 1));
+}
+
+void plan_sizes(int wmode, int BM, int max_tiles, int Fmax, int d, int& nsl_gu, int& nsl_dn, int& n_gu, int& n_dn) {
+  const int RT = down_rows_per_wave(BM, wmode, Fmax, d);
+  nsl_gu = wmode == 0 ? (Fmax + 63) / 64 : Fmax / 128;
+  nsl_dn = (d + 64 * RT - 1) / (64 * RT);
+  n_gu = (max_tiles * nsl_gu + 7) / 8 * 8;
+  n_dn = (max_tiles * nsl_dn + 7) / 8 * 8;
+}
+
+hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipStream_t st) {
+  ExpertArgs a = a0;
+  a.sched = plan.sched[0];
+  const dim3 grid(plan.n_sched[0]);
+  const int BM = plan.BM;
+  if (wmode == 0) return launch_dyn(gateup_f32_kernel<16>, grid, gateup_lds_bytes(16, 0, a.d), st, a);
+  const size_t lds = gateup_lds_bytes(BM, wmode, a.d);
+  const int nt = kGateUpWaves * 64;
+  if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2, true>, grid, lds, st, a, nt);
+  if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2, false>, grid, lds, st, a, nt);
+  if (wmode == 2 && BM == 64) return launch_dyn(gateup_mfma_kernel<64, 2, false>, grid, lds, st, a, nt);
+  if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1, true>, grid, lds, st, a, nt);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_down(const ExpertArgs& a0, int wmode, const Plan& plan, hipStream_t st) {
+  ExpertArgs a = a0;
+  a.sched = plan.sched[1];
+  const dim3 grid(plan.n_sched[1]);
+  const int BM = plan.BM;
+  const int Fmax = a.F > a.Fs ? a.F : a.Fs;
+  if (wmode == 0) return launch_dyn(down_f32_kernel<16>, grid, down_lds_bytes(16, 0, Fmax), st, a);
+  const size_t lds = down_lds_bytes(BM, wmode, Fmax);
+  const int RT = down_rows_per_wave(BM, wmode, Fmax, a.d);
   if (wmode == 2 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2>, grid, lds, st, a);
   if (wmode == 2 && RT == 4 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
   if (wmode == 2 && RT == 4 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 4>, grid, lds, st, a);

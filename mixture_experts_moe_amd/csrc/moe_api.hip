@@ -14,7 +14,7 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, rpart, chunk_hist, local_rank, tiles, rinfo, xq, sx, h, sh, part, total;
+  size_t logits, rpart, chunk_hist, local_rank, sched_gu, sched_dn, rinfo, xq, sx, h, sh, part, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -44,7 +44,11 @@ Layout layout(const moe_shape& s) {
   L.rpart = seg(moe::router_part_floats(s.T, s.top_k, s.d_model, s.n_experts, s.act_dtype == MOE_BF16) * 4);
   L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
   L.local_rank = seg(P * 4);
-  L.tiles = seg((size_t)max_tiles_for(s, 16) * sizeof(int4));
+  {  // block schedules, sized for the largest case (16-row tiles, 64-feature slices)
+    const size_t mt = (size_t)max_tiles_for(s, 16);
+    L.sched_gu = seg((mt * ((Fmax + 63) / 64) + 7) / 8 * 8 * sizeof(int4));
+    L.sched_dn = seg((mt * ((d + 63) / 64) + 7) / 8 * 8 * sizeof(int4));
+  }
   L.rinfo = seg((P + T) * 12);
   L.xq = seg(fp8 ? T * d : 0);
   L.sx = seg(fp8 ? T * (d / 128) * 4 : 0);
@@ -73,7 +77,7 @@ int validate_shape(const moe_shape* s) {
   const int Fmax = s->d_ffn > s->d_ffn_shared ? s->d_ffn : s->d_ffn_shared;
   if (moe::gateup_lds_bytes(16, s->w_dtype, s->d_model) > kMaxLds) return MOE_ERR_UNSUPPORTED;
   if (moe::down_lds_bytes(16, s->w_dtype, Fmax) > kMaxLds) return MOE_ERR_UNSUPPORTED;
-  if (max_tiles_for(*s, 16) * (s->d_model / 64) > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
+  if (max_tiles_for(*s, 16) * (s->d_model / 64 + Fmax / 64 + 16) > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -181,7 +185,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   const int BM = pick_bm(*shape);
 
   ExpertArgs a;
-  a.tiles = (const int4*)(base + L.tiles);
+  a.sched = nullptr;
   a.offsets = r->offsets;
   a.perm = r->perm;
   a.topk_w = r->topk_w;
@@ -193,8 +197,6 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.Fs = shape->d_ffn_shared;
   a.P = P;
   a.hstride = a.F > a.Fs ? a.F : a.Fs;
-  a.max_tiles = 0;
-  a.n_slices = 0;
   a.w_tiled = shape->w_layout == MOE_LAYOUT_TILED;
   a.xa = fp8 ? (const void*)(base + L.xq) : x;
   a.sxa = (const float*)(base + L.sx);
@@ -221,20 +223,25 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   auto mark = [&](int i) {
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], st);
   };
-  const int max_tiles = (int)max_tiles_for(*shape, BM);
+  moe::Plan plan;
+  plan.BM = BM;
+  plan.xcd = BM > 16;  // several tiles per expert: keep an expert's tiles on one XCD
+  moe::plan_sizes(shape->w_dtype, BM, (int)max_tiles_for(*shape, BM), a.hstride, d, plan.n_slices[0],
+                  plan.n_slices[1], plan.n_sched[0], plan.n_sched[1]);
+  plan.sched[0] = (int4*)(base + L.sched_gu);
+  plan.sched[1] = (int4*)(base + L.sched_dn);
   mark(0);
   if (stages & MOE_STAGE_PREPARE) {
-    e = moe::launch_prepare(x, T, d, fp8 ? (uint8_t*)(base + L.xq) : nullptr, (float*)(base + L.sx), r->counts,
-                            r->offsets, E, P, has_shared, BM, (int4*)(base + L.tiles), max_tiles, a.ri, r->perm,
-                            r->topk_w, k, st);
+    e = moe::launch_prepare(x, T, d, fp8 ? (uint8_t*)(base + L.xq) : nullptr, (float*)(base + L.sx), a.ri, r->perm,
+                            r->topk_w, k, plan, r->counts, r->offsets, E, P, has_shared, st);
     mark(1);
   }
   if (e == hipSuccess && (stages & MOE_STAGE_GATE_UP)) {
-    e = moe::launch_gateup(a, shape->w_dtype, BM, max_tiles, st);
+    e = moe::launch_gateup(a, shape->w_dtype, plan, st);
     mark(2);
   }
   if (e == hipSuccess && (stages & MOE_STAGE_DOWN)) {
-    e = moe::launch_down(a, shape->w_dtype, BM, max_tiles, st);
+    e = moe::launch_down(a, shape->w_dtype, plan, st);
     mark(3);
   }
   if (e == hipSuccess && (stages & MOE_STAGE_COMBINE)) {

@@ -20,13 +20,12 @@ struct RowInfo {
 
 // Everything the expert kernels read or write (device pointers).
 struct ExpertArgs {
-  const int4* tiles;          // [max_tiles] (group, first row, first h row, rows); group -1: none
+  const int4* sched;          // [blocks] per block: (group, first row, first h row, rows | slice << 16); group -1: none
   const int32_t* offsets;     // [E+1]
   const int32_t* perm;        // [P]
   const float* topk_w;        // [P]
   int T, d, E, k, F, Fs, P;
   int hstride;                // elements per h row = max(F, Fs)
-  int max_tiles, n_slices;    // 1-D launch: n_slices feature slices x max_tiles tiles
   int w_tiled;                // weights in MOE_LAYOUT_TILED
   const void* xa;             // gate/up input rows: E4M3 codes, bf16 or fp32 [T][d]
   const float* sxa;           // E4M3 activation scales [T][d/128]
@@ -61,13 +60,25 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st);
 
 hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n_cols, uint8_t* codes, float* scales,
                                 hipStream_t st);
+// Block schedules of the two expert kernels ([0] gate/up, [1] down), written by
+// the preparation launch: BM rows per tile; xcd: an expert's tiles are kept on
+// one XCD (when experts have several tiles).
+struct Plan {
+  int BM;
+  bool xcd;
+  int4* sched[2];
+  int n_sched[2];   // blocks (multiples of 8)
+  int n_slices[2];  // feature slices per tile
+};
+int down_rows_per_wave(int BM, int wmode, int Fmax, int d);
+void plan_sizes(int wmode, int BM, int max_tiles, int Fmax, int d, int& nsl_gu, int& nsl_dn, int& n_gu, int& n_dn);
 // Forward preparation in one launch: E4M3 activation quantisation (when
-// xq != null) and the expert tile plan (last block).
-hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const int32_t* counts,
-                          const int32_t* offsets, int E, int P, bool has_shared, int BM, int4* tiles, int max_tiles,
-                          const RowInfo& ri, const int32_t* perm, const float* topk_w, int k, hipStream_t st);
-hipError_t launch_gateup(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
-hipError_t launch_down(const ExpertArgs& a, int wmode, int BM, int max_tiles, hipStream_t st);
+// xq != null), the per-row info and the block schedules.
+hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const RowInfo& ri,
+                          const int32_t* perm, const float* topk_w, int k, const Plan& plan, const int32_t* counts,
+                          const int32_t* offsets, int E, int P, bool has_shared, hipStream_t st);
+hipError_t launch_gateup(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
+hipError_t launch_down(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
                                hipStream_t st);
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,
