@@ -40,7 +40,7 @@ struct ExpertArgs {
 };
 
 size_t dispatch_chunk_hist_ints(int T, int k, int E);
-// Router partial sums kept between the router and top-k launches (short inputs).
+// Router partial sums kept between the router and top-k launches (bf16 activations).
 size_t router_part_floats(int T, int k, int d, int E, bool x_bf16);
 
 struct RouteLaunch {
@@ -51,7 +51,7 @@ struct RouteLaunch {
   const int32_t* forced;   // forced ids or null
   int T, d, E, k;
   float* logits;           // where the logits go (the caller's buffer or workspace)
-  float* rpart;            // [d/kslice][T][E] router partial sums (short inputs)
+  float* rpart;            // [d/kslice][T][E] router partial sums (bf16 activations)
   int32_t* idx;
   float* w;
   int32_t *chunk_hist, *local_rank, *counts, *offsets, *perm, *inv_perm, *status;

@@ -5,14 +5,16 @@
 //   [port]  "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No."
 //   [bench] "We Stopped the Kolibri Benchmark Before Scoring One Answer"
 //
-// Launch sequence of one routing call.
+// Launch sequence of one routing call.  The router (bf16 activations) is split
+// along K at every T: one block per (16 experts, K slice, token tile) writes
+// partial dot products, which top-k adds in slice order, so a token's logits
+// (and so its experts) never depend on T or on the batch around it.
 // Short inputs (T * k <= 1024 pairs, e.g. a decode batch), three launches:
-//   1. router partial logits over K slices, one block per (16 experts, K slice,
-//      token tile), so the router weights stream through many CUs at once;
+//   1. router partial sums;
 //   2. top-k, one wave per token: adds the slices, selects, softmax weights;
 //   3. the whole counting sort in one block.
-// Long inputs:
-//   1. router logits, one block per (token tile, 16 experts);
+// Long inputs, four launches:
+//   1. router partial sums;
 //   2. top-k per chunk of tokens, and the chunk's share of the dispatch;
 //   3. scan of the chunk histograms into counts and offsets;
 //   4. placement of every pair.
@@ -31,13 +33,7 @@ namespace moe {
 // already bf16, so every product x*hi, x*mid, x*lo is exact in fp32 and the
 // matrix core accumulates them in fp32.  The result is an fp32 dot product of
 // x and W_r; only the summation order differs from a scalar loop.
-//
-// Block = 16 waves over one tile of 16 experts x TT tokens; wave w takes one
-// sixteenth of the K range (whole 128-wide blocks), so each wave's loads go out
-// in one round, and the sixteen partial sums are added through LDS in wave
-// order (fixed, so the result does not depend on timing).
 // ---------------------------------------------------------------------------
-constexpr int kRouterWaves = 16;
 
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], v8bf& hi, v8bf& mid, v8bf& lo) {
 #pragma unroll
@@ -49,82 +45,6 @@ __device__ __forceinline__ void split3_bf16(const float (&w)[8], v8bf& hi, v8bf&
     hi[j] = h;
     mid[j] = m;
     lo[j] = (__bf16)r2;
-  }
-}
-
-template <int TT>
-__global__ __launch_bounds__(1024) void router_mfma_kernel(const uint16_t* __restrict__ x,
-                                                                         const float* __restrict__ W,
-                                                                         float* __restrict__ logits, int T, int d,
-                                                                         int E, int32_t* __restrict__ status) {
-  constexpr int NC = TT / 16;
-  __shared__ float red[kRouterWaves][NC][4][64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lk = (lane >> 4) * 8;
-  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * 16;
-  // wave w takes K blocks [w*pw, min((w+1)*pw, nkb)) of 128 (d is a multiple of 128)
-  const int nkb = d / 128, pw = (nkb + kRouterWaves - 1) / kRouterWaves;
-  const int k0 = min(wave * pw, nkb) * 128, kper = min((wave + 1) * pw, nkb) * 128 - k0;
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
-  const int e = e0 + lr;
-  const bool ev = e < E;
-  const float* wp = W + (size_t)(ev ? e : E - 1) * d + k0 + lk;
-  const uint16_t* xp[NC];
-  bool tv[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int t = t0 + c * 16 + lr;
-    tv[c] = t < T;
-    xp[c] = x + (size_t)(tv[c] ? t : T - 1) * d + k0 + lk;
-  }
-  v4f acc[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) acc[c] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // one K step = 32: lane l holds K = step + (l/16)*8 + [0, 8) of its expert row
-  // and of its token row (the same K map on both operands); all steps of the
-  // slice are requested before the first product
-  for (int kk = 0; kk < kper; kk += 128) {
-    float4 wa[4][2];
-    v4i xb[4][NC];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      wa[u][0] = *(const float4*)(wp + kk + 32 * u);
-      wa[u][1] = *(const float4*)(wp + kk + 32 * u + 4);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) xb[u][c] = *(const v4i*)(xp[c] + kk + 32 * u);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      float wv[8] = {wa[u][0].x, wa[u][0].y, wa[u][0].z, wa[u][0].w, wa[u][1].x, wa[u][1].y, wa[u][1].z, wa[u][1].w};
-      if (!ev) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) wv[j] = 0.f;
-      }
-      v8bf hi, mid, lo;
-      split3_bf16(wv, hi, mid, lo);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const v8bf b = tv[c] ? __builtin_bit_cast(v8bf, xb[u][c]) : v8bf{};
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[c], 0, 0, 0);
-        acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[c], 0, 0, 0);
-      }
-    }
-  }
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][c][i][lane] = acc[c][i];
-  __syncthreads();
-  // the block's 16 x TT outputs, one per thread: lane l of "wave slot" holds
-  // experts e0 + 4*(l/16) + i, token c*16 + l%16
-  for (int o = threadIdx.x; o < NC * 4 * 64; o += kRouterWaves * 64) {
-    const int c = o / 256, i = (o / 64) & 3, l = o & 63;
-    float v = red[0][c][i][l];
-#pragma unroll
-    for (int w = 1; w < kRouterWaves; ++w) v += red[w][c][i][l];
-    const int t = t0 + c * 16 + (l & 15), ee = e0 + 4 * (l >> 4) + i;
-    if (t < T && ee < E) logits[(size_t)t * E + ee] = v;
   }
 }
 
@@ -193,6 +113,153 @@ __global__ __launch_bounds__(256) void router_split_kernel(const uint16_t* __res
     const int t = t0 + c * 16 + (l & 15), ee = e0 + 4 * (l >> 4) + i;
     if (t < T && ee < E) part[((size_t)ks * T + t) * E + ee] = v;
   }
+}
+
+// ---------------------------------------------------------------------------
+// Router partial logits for long inputs (bf16 x): tiles of 64 tokens x 64
+// experts, 4 waves of 32 x 32, over one half of the K range (blockIdx.z): the
+// halves split at slice gsl (256-deep slices, the same boundary the top-k
+// kernel uses; one half when there is a single slice).  Both operands are staged in LDS per chunk of 32*NS K (two LDS
+// buffers, the chunk after next prefetched into registers); the fp32 weights
+// are split into their three exact bf16 terms while staged.  Sum order per
+// logit: per chunk a chain of 3*NS products from zero, four chunks added in
+// order into a slice, the half's slices added in order -- the K-split kernel's
+// order, so both kernels give the same logits bit for bit.
+// ---------------------------------------------------------------------------
+template <int NS>
+__global__ __launch_bounds__(256) void router_tile_kernel(const uint16_t* __restrict__ x, const float* __restrict__ W,
+                                                          float* __restrict__ part, int T, int d, int E, int gsl,
+                                                          int32_t* __restrict__ status) {
+  constexpr int TT = 64, TE = 64, KC = 32 * NS;  // tile, K per chunk
+  constexpr int XS = KC * 2 + 16;                  // LDS row stride (bytes), padded
+  constexpr int XP = TT * KC / 8;                  // x pieces (8 bf16) per chunk
+  constexpr int WP = TE * KC / 4;                  // W pieces (4 fp32) per chunk
+  constexpr int PX = XP / 256, PW = WP / 256;      // per thread
+  __shared__ __align__(16) uint8_t xs[2][TT * XS];
+  __shared__ __align__(16) uint8_t wsm[2][3 * TE * XS];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, kg = lane >> 4;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE, half = blockIdx.z;
+  const int wt = wave & 1, we = wave >> 1;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && half == 0 && tid == 0) *status = 0;
+  constexpr int cps = 4;  // chunks per slice (a slice is 4*KC deep, as in the K-split kernel)
+  const int c0 = half ? gsl * cps : 0, c1 = half ? d / KC : gsl * cps;  // a multiple of 4 chunks, >= 4
+  struct Pre {
+    v4i xv[PX];
+    float4 wv[PW];
+  };
+  auto fetch = [&](int ch, Pre& p) {
+    const int k0 = ch * KC;
+#pragma unroll
+    for (int u = 0; u < PX; ++u) {
+      const int i = tid + u * 256, r = i / (KC / 8), c = i % (KC / 8), t = min(t0 + r, T - 1);
+      p.xv[u] = *(const v4i*)(x + (size_t)t * d + k0 + c * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int i = tid + u * 256, r = i / (KC / 4), c = i % (KC / 4), e = min(e0 + r, E - 1);
+      p.wv[u] = *(const float4*)(W + (size_t)e * d + k0 + c * 4);
+    }
+  };
+  auto store = [&](int buf, const Pre& p) {
+#pragma unroll
+    for (int u = 0; u < PX; ++u) {
+      const int i = tid + u * 256, r = i / (KC / 8), c = i % (KC / 8);
+      const v4i z = {0, 0, 0, 0};
+      *(v4i*)(xs[buf] + r * XS + c * 16) = t0 + r < T ? p.xv[u] : z;
+    }
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      const int i = tid + u * 256, r = i / (KC / 4), c = i % (KC / 4);
+      const bool live = e0 + r < E;
+      uint16_t h[3][4];
+      const float w4[4] = {p.wv[u].x, p.wv[u].y, p.wv[u].z, p.wv[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {  // the split of split3_bf16, element by element
+        const float w = live ? w4[j] : 0.f;
+        const __bf16 hi = (__bf16)w;
+        const float r1 = w - (float)hi;
+        const __bf16 mi = (__bf16)r1;
+        const __bf16 lo = (__bf16)(r1 - (float)mi);
+        h[0][j] = __builtin_bit_cast(uint16_t, hi);
+        h[1][j] = __builtin_bit_cast(uint16_t, mi);
+        h[2][j] = __builtin_bit_cast(uint16_t, lo);
+      }
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp) {
+        uint2 pk;
+        pk.x = (uint32_t)h[sp][0] | ((uint32_t)h[sp][1] << 16);
+        pk.y = (uint32_t)h[sp][2] | ((uint32_t)h[sp][3] << 16);
+        *(uint2*)(wsm[buf] + (sp * TE + r) * XS + c * 8) = pk;
+      }
+    }
+  };
+  v4f tot[2][2], sl[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) tot[i][j] = sl[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, int ch) {
+    v4f cc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) cc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {  // 32-deep steps; lane holds K = 32u + 8*kg + [0, 8)
+      v8bf b[2], a[3][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) b[j] = *(const v8bf*)(xs[buf] + (wt * 32 + j * 16 + lr) * XS + u * 64 + kg * 16);
+#pragma unroll
+      for (int sp = 0; sp < 3; ++sp)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[sp][i] = *(const v8bf*)(wsm[buf] + (sp * TE + we * 32 + i * 16 + lr) * XS + u * 64 + kg * 16);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][i], b[j], cc[i][j], 0, 0, 0);
+          cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][i], b[j], cc[i][j], 0, 0, 0);
+          cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2][i], b[j], cc[i][j], 0, 0, 0);
+        }
+    }
+    const int q = (ch - c0) % cps, slice = (ch - c0) / cps;  // chunk -> slice -> half total
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        sl[i][j] = q == 0 ? cc[i][j] : sl[i][j] + cc[i][j];
+        if (q == cps - 1) tot[i][j] = slice == 0 ? sl[i][j] : tot[i][j] + sl[i][j];
+      }
+  };
+  // two register sets in a ring: the chunk after next is in flight during a
+  // chunk's products.  The chunk count is even; past the end the last chunk is
+  // fetched again (in bounds, never used), so the code stays branch-free.
+  Pre pa, pb;
+  fetch(c0, pa);
+  fetch(c0 + 1, pb);
+  store(0, pa);
+  __syncthreads();
+  for (int ch = c0; ch < c1; ch += 2) {
+    fetch(min(ch + 2, c1 - 1), pa);
+    store(1, pb);
+    compute(0, ch);
+    __syncthreads();
+    fetch(min(ch + 3, c1 - 1), pb);
+    store(0, pa);
+    compute(1, ch + 1);
+    __syncthreads();
+  }
+  float* out = part + (size_t)half * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + we * 32 + i * 16 + 4 * kg + r, t = t0 + wt * 32 + j * 16 + lr;
+        if (e < E && t < T) out[(size_t)t * E + e] = tot[i][j][r];
+      }
 }
 
 // ---------------------------------------------------------------------------
@@ -463,10 +530,55 @@ __device__ __forceinline__ void dispatch_block(const TopkArgs& a, DispatchLds& s
   }
 }
 
+// Logits of token t for the candidates e = lane + 64 j.  The router left n_parts
+// partial sums per logit, in K order; the logit is (parts [0, gs) added in
+// order) + (parts [gs, n_parts) added in order): the K-split router writes one
+// part per 256-deep slice (gs = half of them), the tiled router one part per
+// half of K (gs = 1), so both give the same sum bit for bit.  Written to
+// logits_out when given.  The parts are requested 8 at a time (all J
+// candidates at once), then added.
+template <int J>
+__device__ __forceinline__ void gather_logits(const float* __restrict__ part, int n_parts, int gs, int T, int E,
+                                              int t, int lane, float* __restrict__ logits_out, float (&lv)[J]) {
+  constexpr int QB = 8;
+  float h0[J], h1[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) h0[j] = h1[j] = 0.f;
+  for (int q0 = 0; q0 < n_parts; q0 += QB) {
+    float v[QB][J];
+#pragma unroll
+    for (int q = 0; q < QB; ++q)
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        const int e = lane + 64 * j;
+        v[q][j] = (q0 + q < n_parts && e < E) ? part[((size_t)(q0 + q) * T + t) * E + e] : 0.f;
+      }
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      const int qq = q0 + q;
+#pragma unroll
+      for (int j = 0; j < J; ++j) {
+        if (qq < gs) h0[j] = qq == 0 ? v[q][j] : h0[j] + v[q][j];
+        else if (qq < n_parts) h1[j] = qq == gs ? v[q][j] : h1[j] + v[q][j];
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) lv[j] = gs < n_parts ? h0[j] + h1[j] : h0[j];
+  if (logits_out) {
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const int e = lane + 64 * j;
+      if (e < E) logits_out[(size_t)t * E + e] = lv[j];
+    }
+  }
+}
+
 // Top-k + dispatch over chunks of `tpc` tokens (long inputs): block = 16 waves,
 // wave w takes tokens w, w+16, ... of its chunk.
 template <int J, bool FORCED>
-__global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
+__global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a, const float* __restrict__ part, int n_parts,
+                                                            int gs, float* __restrict__ logits_out) {
   __shared__ DispatchLds s;
   __shared__ int32_t ids[kMaxChunkPairs];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -480,11 +592,7 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
       continue;
     }
     float lv[J];
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = lane + 64 * j;
-      lv[j] = e < E ? a.logits[(size_t)t * E + e] : 0.f;
-    }
+    gather_logits<J>(part, n_parts, gs, T, E, t, lane, logits_out, lv);
     const int id = route_token<J, FORCED>(a, t, lv, lane);
     if (lane < k) ids[tl * k + lane] = id;
   }
@@ -499,36 +607,11 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a) {
 // the logit (written to logits_out when given), then the selection.
 template <int J, bool FORCED>
 __global__ __launch_bounds__(64) void topk_small_kernel(TopkArgs a, const float* __restrict__ part, int n_parts,
-                                                        float* __restrict__ logits_out) {
+                                                        int gs, float* __restrict__ logits_out) {
   const int t = blockIdx.x, lane = threadIdx.x;
   const int E = a.E, T = a.T;
-  // the slices are requested 8 at a time (all J candidates at once), then added in order
-  constexpr int QB = 8;
   float lv[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) lv[j] = 0.f;
-  for (int q0 = 0; q0 < n_parts; q0 += QB) {
-    float v[QB][J];
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-#pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const int e = lane + 64 * j;
-        v[q][j] = (q0 + q < n_parts && e < E) ? part[((size_t)(q0 + q) * T + t) * E + e] : 0.f;
-      }
-#pragma unroll
-    for (int q = 0; q < QB; ++q)
-#pragma unroll
-      for (int j = 0; j < J; ++j)
-        if (q0 + q < n_parts) lv[j] = (q0 + q == 0) ? v[q][j] : lv[j] + v[q][j];
-  }
-  if (logits_out) {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const int e = lane + 64 * j;
-      if (e < E) logits_out[(size_t)t * E + e] = lv[j];
-    }
-  }
+  gather_logits<J>(part, n_parts, gs, T, E, t, lane, logits_out, lv);
   route_token<J, FORCED>(a, t, lv, lane);
 }
 
@@ -614,7 +697,8 @@ size_t dispatch_chunk_hist_ints(int T, int k, int E) {
 int router_kslice(int d) { return d % 256 == 0 ? 256 : 128; }
 
 size_t router_part_floats(int T, int k, int d, int E, bool x_bf16) {
-  if (!x_bf16 || (int64_t)T * k > kMaxChunkPairs) return 0;
+  if (!x_bf16) return 0;
+  if ((int64_t)T * k > kMaxChunkPairs) return (size_t)2 * T * E;  // two halves of K
   return (size_t)(d / router_kslice(d)) * T * E;
 }
 
@@ -645,13 +729,29 @@ static TopkArgs topk_args(const RouteLaunch& L, int tpc) {
     default: return hipErrorInvalidValue;                                                \
   }
 
-// Short inputs: split router, one wave per token, one-block dispatch.
-static hipError_t launch_route_short(const RouteLaunch& L, hipStream_t st) {
-  const float* part;
-  int n_parts;
-  float* logits_out;
-  if (L.x_bf16) {
-    const int ksl = router_kslice(L.d), NS = ksl / 128, NC = L.T <= 16 ? 1 : (L.T <= 32 ? 2 : (L.T <= 48 ? 3 : 4));
+// Router launch: bf16 activations go through the K-split kernel (short inputs)
+// or the tiled kernel (long inputs), which leave partial sums that top-k adds in
+// one order, so a token's logits never depend on T; fp32 activations (small
+// layers) get plain logits.
+static hipError_t launch_router(const RouteLaunch& L, hipStream_t st, const float*& part, int& n_parts, int& gs,
+                                float*& logits_out) {
+  const bool shortin = (int64_t)L.T * L.k <= kMaxChunkPairs;
+  if (L.x_bf16 && !shortin) {  // tiles over two halves of K
+    const int ksl = router_kslice(L.d), ns = L.d / ksl, halves = ns > 1 ? 2 : 1;
+    const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64, halves);
+    if (ksl == 256)
+      router_tile_kernel<2><<<grid, 256, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
+                                                  (ns + 1) / 2, L.status);
+    else
+      router_tile_kernel<1><<<grid, 256, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
+                                                  (ns + 1) / 2, L.status);
+    part = L.rpart;
+    n_parts = halves;
+    gs = 1;
+    logits_out = L.logits;
+  } else if (L.x_bf16) {
+    const int ksl = router_kslice(L.d), NS = ksl / 128;
+    const int NC = !shortin ? 4 : (L.T <= 16 ? 1 : (L.T <= 32 ? 2 : (L.T <= 48 ? 3 : 4)));
     const dim3 grid((L.E + 15) / 16, L.d / ksl, (L.T + 16 * NC - 1) / (16 * NC));
     const uint16_t* x = (const uint16_t*)L.x;
 #define MOE_SPLIT(nc, ns) \
@@ -664,57 +764,57 @@ static hipError_t launch_route_short(const RouteLaunch& L, hipStream_t st) {
 #undef MOE_SPLIT
     part = L.rpart;
     n_parts = L.d / ksl;
+    gs = (n_parts + 1) / 2;
     logits_out = L.logits;
   } else {
-    const dim3 grid((L.T + 31) / 32, (L.E + 15) / 16);
-    router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+    if (shortin) {
+      const dim3 grid((L.T + 31) / 32, (L.E + 15) / 16);
+      router_f32_kernel<32, 16><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+    } else {
+      const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64);
+      router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
+    }
     part = L.logits;
     n_parts = 1;
+    gs = 1;
     logits_out = nullptr;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const TopkArgs a = topk_args(L, L.T);
-#define MOE_TOPK_SMALL(n)                                                                        \
-  case n:                                                                                        \
-    if (L.forced) topk_small_kernel<n, true><<<L.T, 64, 0, st>>>(a, part, n_parts, logits_out);  \
-    else topk_small_kernel<n, false><<<L.T, 64, 0, st>>>(a, part, n_parts, logits_out);          \
-    break;
-  MOE_J_SWITCH((L.E + 63) / 64, MOE_TOPK_SMALL)
-#undef MOE_TOPK_SMALL
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  dispatch_small_kernel<<<1, 1024, 0, st>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
-  if ((int64_t)L.T * L.k <= kMaxChunkPairs) return launch_route_short(L, st);
-  if (L.x_bf16) {
-    const int TT = 64;
-    const dim3 grid((L.T + TT - 1) / TT, (L.E + 15) / 16);
-    router_mfma_kernel<64><<<grid, kRouterWaves * 64, 0, st>>>((const uint16_t*)L.x, L.w_router, L.logits, L.T, L.d,
-                                                               L.E, L.status);
-  } else {
-    const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64);
-    router_f32_kernel<64, 64><<<grid, 256, 0, st>>>((const float*)L.x, L.w_router, L.logits, L.T, L.d, L.E, L.status);
-  }
-  hipError_t e = hipGetLastError();
+  const float* part;
+  int n_parts, gs;
+  float* logits_out;
+  hipError_t e = launch_router(L, st, part, n_parts, gs, logits_out);
   if (e != hipSuccess) return e;
-
+  if ((int64_t)L.T * L.k <= kMaxChunkPairs) {  // one wave per token, then a one-block dispatch
+    const TopkArgs a = topk_args(L, L.T);
+#define MOE_TOPK_SMALL(n)                                                                        \
+  case n:                                                                                        \
+    if (L.forced) topk_small_kernel<n, true><<<L.T, 64, 0, st>>>(a, part, n_parts, gs, logits_out);  \
+    else topk_small_kernel<n, false><<<L.T, 64, 0, st>>>(a, part, n_parts, gs, logits_out);          \
+    break;
+    MOE_J_SWITCH((L.E + 63) / 64, MOE_TOPK_SMALL)
+#undef MOE_TOPK_SMALL
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dispatch_small_kernel<<<1, 1024, 0, st>>>(a);
+    return hipGetLastError();
+  }
   const int P = L.T * L.k;
   const int tpc = tokens_per_chunk(L.T, L.k);
   const int n_chunks = (L.T + tpc - 1) / tpc;
   const TopkArgs a = topk_args(L, tpc);
-#define MOE_TOPK_CASE(n)                                                                \
-  case n:                                                                               \
-    if (L.forced) topk_dispatch_kernel<n, true><<<n_chunks, 1024, 0, st>>>(a);          \
-    else topk_dispatch_kernel<n, false><<<n_chunks, 1024, 0, st>>>(a);                  \
+#define MOE_TOPK_CASE(n)                                                                                        \
+  case n:                                                                                                       \
+    if (L.forced) topk_dispatch_kernel<n, true><<<n_chunks, 1024, 0, st>>>(a, part, n_parts, gs, logits_out);        \
+    else topk_dispatch_kernel<n, false><<<n_chunks, 1024, 0, st>>>(a, part, n_parts, gs, logits_out);                \
     break;
   MOE_J_SWITCH((L.E + 63) / 64, MOE_TOPK_CASE)
 #undef MOE_TOPK_CASE
   e = hipGetLastError();
-  if (e != hipSuccess || n_chunks == 1) return e;
+  if (e != hipSuccess) return e;
   dispatch_scan_kernel<<<1, 1024, 0, st>>>(L.chunk_hist, n_chunks, L.E, L.counts, L.offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

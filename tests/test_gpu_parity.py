@@ -456,3 +456,29 @@ def test_tiled_layout_matches_rowmajor(case, T):
         ys.append(y)
     torch.cuda.synchronize()
     assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
+
+
+# ------------------------------------------------------------------ batch invariance
+
+@pytest.mark.parametrize("T_big", [300, 2048])
+def test_batch_invariance(T_big):
+    """A token's logits, ids, weights and output do not depend on the batch it
+    sits in: the 32 decode tokens alone (short-batch kernels, 16-row tiles) and
+    as the first rows of a larger batch (long-batch router; at T=2048 32-row
+    tiles and the XCD schedule) give the same bits.  (The pages' port drifted
+    when only the prefill chunk size changed: "We Ported Aleph Alpha's Kolibri
+    to a MacBook. Our Own Gate Said No.", section "Taking it apart".)"""
+    small = synth.make_inputs("decode_t32")
+    big = synth.make_inputs("prefill_t2048", T=T_big)
+    s = small["shape"]
+    big = dict(big)
+    xb = big["x"].copy()
+    xb[: s.T] = small["x"]
+    big["x"] = xb
+    say(f"decode_t32 alone vs inside a T={T_big} batch")
+    g1 = run_gpu(small)
+    g2 = run_gpu(big)
+    assert np.array_equal(g1["logits"].view(np.uint32), g2["logits"][: s.T].view(np.uint32))
+    assert np.array_equal(g1["topk_idx"], g2["topk_idx"][: s.T])
+    assert np.array_equal(g1["topk_w"].view(np.uint32), g2["topk_w"][: s.T].view(np.uint32))
+    assert np.array_equal(g1["y"].view(np.uint32), g2["y"][: s.T].view(np.uint32))
