@@ -146,7 +146,7 @@ def run_workload(name, steps, warmup, rotate, layout):
 
     # attribution pass (same kernels): events around the routing call, and events
     # the library records on the stream between the forward stages
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     for i in range(steps):
         b = bound[i % len(bound)]
         ev[i][0].record(st)
@@ -154,11 +154,11 @@ def run_workload(name, steps, warmup, rotate, layout):
         ev[i][1].record(st)
         b.forward(moe.STAGE_ALL, events=ev[i][2:])
     torch.cuda.synchronize()
-    names = ("route", "prepare", "gate_up", "down", "combine")
-    pairs = ((0, 1), (2, 3), (3, 4), (4, 5), (5, 6))
+    names = ("route", "gate_up", "down", "combine")
+    pairs = ((0, 1), (2, 3), (3, 4), (4, 5))
     stage_us = {n: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)])) * 1e3
                 for n, (a, b) in zip(names, pairs)}
-    per_step = np.array([ev[i][0].elapsed_time(ev[i][6]) for i in range(steps)]) * 1e3
+    per_step = np.array([ev[i][0].elapsed_time(ev[i][5]) for i in range(steps)]) * 1e3
     pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
     counts = r.counts.cpu().numpy()
     assert r.status.item() == 0

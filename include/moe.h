@@ -116,18 +116,28 @@ typedef struct {
                           within an expert; entries past offsets[E] are -1 */
   int32_t *inv_perm;   /* [T * k] inv_perm[p] = q, or -1 for an invalid pair */
   int32_t *status;     /* [1] device status word: MOE_OK or MOE_ERR_FORCED_INDEX */
+  void *plan;          /* moe_plan_bytes() bytes: the dispatch plan the routing call
+                          writes for moe_forward (expert-kernel block schedules,
+                          per-row token/weight, and with FP8 weights the activations
+                          as E4M3 codes with per-(token, 128) scales); opaque */
 } moe_routing;
 
 /* Workspace bytes needed by moe_route, moe_route_forced and moe_forward for this
- * shape (one size serves all three).  Returns 0 for an invalid shape. */
+ * shape (one size serves all three).  Returns 0 for an invalid shape.  The
+ * workspace carries nothing from one call to the next. */
 size_t moe_workspace_bytes(const moe_shape *shape);
+
+/* Bytes of moe_routing.plan for this shape.  Returns 0 for an invalid shape. */
+size_t moe_plan_bytes(const moe_shape *shape);
 
 /* Free routing.  Router logits l = x W_r^T (fp32 accumulation); selection score
  * s = l + sel_bias (selection only); top-k of s, lowest expert index on ties;
  * weights softmax over the k chosen logits; then the dispatch: counts, offsets,
  * and the stable permutation of pairs by expert ([port] part 3 and its update:
- * the expert matmul runs over (token, expert) rows sorted by expert).
- * x is [T, d] in act_dtype.  Sets *status = MOE_OK. */
+ * the expert matmul runs over (token, expert) rows sorted by expert), and the
+ * dispatch plan in out->plan (with FP8 weights it includes the activations
+ * quantised as moe_quantize_rows does).  x is [T, d] in act_dtype.  Sets
+ * *status = MOE_OK. */
 int moe_route(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *out,
               void *ws, size_t ws_bytes, void *stream);
 
@@ -148,26 +158,26 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
  * fp32 and this order: acc = shared; acc += w_j * y_j for j = 0..k-1;
  * y = acc rounded to act_dtype (bf16: round to nearest even).
  * `r` must hold the results of moe_route / moe_route_forced for the same shape
- * and x (logits and inv_perm are not read).  y is [T, d] in act_dtype. */
+ * and x (its plan included; logits, counts, offsets, perm and inv_perm are
+ * not read).  y is [T, d] in act_dtype. */
 int moe_forward(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
                 void *ws, size_t ws_bytes, void *stream);
 
 /* Stages of moe_forward, in launch order. */
 enum {
-  MOE_STAGE_PREPARE = 1,   /* activation quantisation (FP8 weights) and the expert tile plan */
-  MOE_STAGE_GATE_UP = 2,   /* grouped gate/up projections + SwiGLU (+ h quantisation) */
-  MOE_STAGE_DOWN = 4,      /* grouped down projection, times the routing weight */
-  MOE_STAGE_COMBINE = 8,   /* fixed-order combine into y */
-  MOE_STAGE_ALL = 15
+  MOE_STAGE_GATE_UP = 1,   /* grouped gate/up projections + SwiGLU (+ h quantisation) */
+  MOE_STAGE_DOWN = 2,      /* grouped down projection, times the routing weight */
+  MOE_STAGE_COMBINE = 4,   /* fixed-order combine into y */
+  MOE_STAGE_ALL = 7
 };
 
 /* moe_forward restricted to a subset of its stages (bitmask of MOE_STAGE_*),
  * optionally timed.  Calling the stages one at a time, in order, on one stream
  * with the same arguments and workspace gives bitwise the result of
  * moe_forward; the intermediate results live in the workspace between the
- * calls.  `events` is NULL or an array of 5 hipEvent_t created by the caller:
+ * calls.  `events` is NULL or an array of 4 hipEvent_t created by the caller:
  * events[0] is recorded on `stream` before the first stage and events[i] right
- * after stage i (1 = prepare .. 4 = combine) when that stage is selected, so the
+ * after stage i (1 = gate/up .. 3 = combine) when that stage is selected, so the
  * interval between two records spans only that stage's kernels.  Unknown stage
  * bits: MOE_ERR_INVALID_ARG. */
 int moe_forward_stages(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,

@@ -25,6 +25,7 @@
 
 #include "moe_device.h"
 #include "moe_kernels.h"
+#include "moe_plan.h"
 
 namespace moe {
 
@@ -45,154 +46,15 @@ __device__ __forceinline__ v4i stream_load(const uint8_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Activation quantisation: per row and 128-element group, s = amax/448 (1 for
-// an all-zero group), code = E4M3(v/s) round-to-nearest-even, saturating.  One
-// wave per group, two elements per lane.
+// Activation quantisation on its own (moe_quantize_rows): one wave per
+// 128-element group, as in the routing call's plan step.
 // ---------------------------------------------------------------------------
 template <bool BF16IN>
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ in, int64_t n_groups, int gpr,
                                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
-  const int lane = threadIdx.x & 63;
   const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (g >= n_groups) return;
-  const int64_t row = g / gpr, col = (g % gpr) * 128 + 2 * lane;
-  const int64_t o = row * (int64_t)gpr * 128 + col;
-  float v0, v1;
-  if (BF16IN) {
-    const uint32_t pr = *(const uint32_t*)((const uint16_t*)in + o);
-    v0 = __uint_as_float(pr << 16);
-    v1 = __uint_as_float(pr & 0xffff0000u);
-  } else {
-    const float2 pr = *(const float2*)((const float*)in + o);
-    v0 = pr.x;
-    v1 = pr.y;
-  }
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-  *(uint16_t*)(codes + o) = (uint16_t)pack2_e4m3(v0 / s, v1 / s);
-  if (lane == 0) scales[g] = s;
-}
-
-// ---------------------------------------------------------------------------
-// Forward preparation, one launch.
-//  * The first blocks write the block schedules of the two expert kernels (see
-//    below).
-//  * The next ones write, for every h row q (sorted pairs, then the shared
-//    expert's rows P + t), its token, its partial-output row and its routing
-//    weight, so the expert kernels read them with one load per row.
-//  * The last ones quantise the activations (four 128-element groups per
-//    block, as above).
-//  Schedules.  The
-//    tiles: per group (routed experts 0..E-1, then the shared expert with all
-//    T rows) ceil(rows / BM) tiles of BM rows, in group order; work item
-//    i = tile * n_slices + slice.  Block b of a kernel gets item i = b
-//    (identity), or, in XCD mode, item (b % 8) * L + b / 8 with L = ceil(items /
-//    8): the chip's eight XCDs (block b runs on XCD b % 8, each with its own L2)
-//    then each take one contiguous run of items, so the tiles of one expert run
-//    on one XCD close together in time and share its weight stream through that
-//    L2.  A record is (group, first row, first h row, rows | slice << 16), or
-//    group -1 for a block without work.  Each plan block recomputes the tile
-//    prefix over the groups (E + 1 counts) and fills its share of records.
-// ---------------------------------------------------------------------------
-struct PlanArgs {
-  const int32_t* counts;
-  const int32_t* offsets;
-  int E, T, P, has_shared, BM, xcd;
-  int4* sched[2];  // gate/up, down
-  int n_sched[2];  // blocks of each kernel (multiples of 8)
-  int n_slices[2];
-};
-
-constexpr int kPlanPerThread = 2;
-
-__device__ void plan_block(const PlanArgs& pa, int blk) {
-  __shared__ int32_t tstart[kMaxExperts + 2], grow[kMaxExperts + 1], gh0[kMaxExperts + 1];
-  __shared__ int32_t tmp[17];
-  constexpr int PER = (kMaxExperts + 1 + 255) / 256;  // groups per thread
-  const int E = pa.E, G = E + (pa.has_shared ? 1 : 0), BM = pa.BM;
-  int nt[PER], sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int g = PER * threadIdx.x + i;
-    const int rows = g < E ? pa.counts[g] : (g < G ? pa.T : 0);
-    if (g < G) {
-      grow[g] = rows;
-      gh0[g] = g < E ? pa.offsets[g] : pa.P;
-    }
-    nt[i] = (rows + BM - 1) / BM;
-    sum += nt[i];
-  }
-  int total;
-  int st = block_excl_scan<256>(sum, tmp, &total);
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int g = PER * threadIdx.x + i;
-    if (g < G) tstart[g] = st;
-    st += nt[i];
-  }
-  if (threadIdx.x == 0) tstart[G] = total;
-  __syncthreads();
-  for (int u = 0; u < kPlanPerThread; ++u) {
-    int e = (blk * kPlanPerThread + u) * 256 + threadIdx.x;
-    const int which = e < pa.n_sched[0] ? 0 : 1;
-    const int b = which ? e - pa.n_sched[0] : e;
-    if (b >= pa.n_sched[which]) return;
-    const int nsl = pa.n_slices[which];
-    const int n_items = total * nsl;
-    int item = b;
-    if (pa.xcd) {
-      const int L = (n_items + 7) / 8, j = b / 8;
-      item = j < L ? (b % 8) * L + j : n_items;
-    }
-    int4 rec = make_int4(-1, 0, 0, 0);
-    if (item < n_items) {
-      const int t = item / nsl, sl = item - t * nsl;
-      int lo = 0, hi = G - 1;  // the last group whose first tile is <= t (it has tiles)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (tstart[mid] <= t) lo = mid;
-        else hi = mid - 1;
-      }
-      const int m0 = (t - tstart[lo]) * BM;
-      rec = make_int4(lo, m0, gh0[lo] + m0, min(BM, grow[lo] - m0) | (sl << 16));
-    }
-    pa.sched[which][b] = rec;
-  }
-}
-
-__global__ __launch_bounds__(256) void prepare_kernel(const uint16_t* __restrict__ x, int64_t n_groups, int gpr,
-                                                       uint8_t* __restrict__ xq, float* __restrict__ sx,
-                                                       int n_pblocks, int n_rblocks, RowInfo ri,
-                                                       const int32_t* __restrict__ perm,
-                                                       const float* __restrict__ topk_w, int k, PlanArgs pa) {
-  if (blockIdx.x < n_pblocks) {  // the longest blocks go first
-    plan_block(pa, blockIdx.x);
-    return;
-  }
-  if (blockIdx.x < n_pblocks + n_rblocks) {
-    const int q = (blockIdx.x - n_pblocks) * 256 + threadIdx.x, P = pa.P;
-    if (q < P) {
-      const int p = perm[q];
-      ri.tok[q] = p >= 0 ? p / k : 0;
-      ri.prow[q] = p;
-      ri.w[q] = p >= 0 ? topk_w[p] : 0.f;
-    } else if (q < P + (pa.has_shared ? pa.T : 0)) {
-      ri.tok[q] = q - P;
-      ri.prow[q] = q;
-      ri.w[q] = 1.f;
-    }
-    return;
-  }
-  const int lane = threadIdx.x & 63;
-  const int64_t g = (int64_t)(blockIdx.x - n_pblocks - n_rblocks) * 4 + (threadIdx.x >> 6);
-  if (g >= n_groups) return;
-  const int64_t o = (g / gpr) * (int64_t)gpr * 128 + (g % gpr) * 128 + 2 * lane;
-  const uint32_t pr = *(const uint32_t*)(x + o);
-  const float v0 = __uint_as_float(pr << 16), v1 = __uint_as_float(pr & 0xffff0000u);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-  *(uint16_t*)(xq + o) = (uint16_t)pack2_e4m3(v0 / s, v1 / s);
-  if (lane == 0) sx[g] = s;
+  quantize_group<BF16IN>(in, g, gpr, codes, scales, threadIdx.x & 63);
 }
 
 // Address of the weight bytes a lane streams for one 16-row tile: in the
@@ -230,14 +92,20 @@ struct TileRows {
 // The block's schedule record (written by the plan step): its tile's rows and
 // its feature slice.
 __device__ __forceinline__ TileRows block_rows(const ExpertArgs& a, int& slice) {
-  const int4 rec = a.sched[blockIdx.x];
+  int4 rec;
+  if (a.per_tile) {
+    rec = a.sched[blockIdx.x / a.nsl];
+    slice = blockIdx.x % a.nsl;
+  } else {
+    rec = a.sched[blockIdx.x];
+    slice = rec.w >> 16;
+  }
   TileRows r;
   r.g = rec.x;
   r.m0 = rec.y;
   r.hrow0 = rec.z;
   r.rows = rec.w & 0xffff;
   r.shared = rec.x == a.E;
-  slice = rec.w >> 16;
   return r;
 }
 
@@ -770,33 +638,6 @@ hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n
   return hipGetLastError();
 }
 
-hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const RowInfo& ri,
-                          const int32_t* perm, const float* topk_w, int k, const Plan& plan, const int32_t* counts,
-                          const int32_t* offsets, int E, int P, bool has_shared, hipStream_t st) {
-  const int gpr = d / 128;
-  const int64_t ng = xq ? (int64_t)T * gpr : 0;
-  const int64_t nqb = (ng + 3) / 4;
-  const int64_t nrb = ((int64_t)P + (has_shared ? T : 0) + 255) / 256;
-  PlanArgs pa;
-  pa.counts = counts;
-  pa.offsets = offsets;
-  pa.E = E;
-  pa.T = T;
-  pa.P = P;
-  pa.has_shared = has_shared ? 1 : 0;
-  pa.BM = plan.BM;
-  pa.xcd = plan.xcd ? 1 : 0;
-  for (int w = 0; w < 2; ++w) {
-    pa.sched[w] = plan.sched[w];
-    pa.n_sched[w] = plan.n_sched[w];
-    pa.n_slices[w] = plan.n_slices[w];
-  }
-  const int64_t npb = ((int64_t)plan.n_sched[0] + plan.n_sched[1] + 256 * kPlanPerThread - 1) / (256 * kPlanPerThread);
-  prepare_kernel<<<(unsigned)(nqb + nrb + npb), 256, 0, st>>>((const uint16_t*)x, ng, gpr, xq, sx, (int)npb, (int)nrb,
-                                                              ri, perm, topk_w, k, pa);
-  return hipGetLastError();
-}
-
 template <typename K>
 static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, const ExpertArgs& a,
                              int threads = 256) {
@@ -847,6 +688,8 @@ void plan_sizes(int wmode, int BM, int max_tiles, int Fmax, int d, int& nsl_gu, 
 hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipStream_t st) {
   ExpertArgs a = a0;
   a.sched = plan.sched[0];
+  a.per_tile = !plan.xcd;
+  a.nsl = plan.n_slices[0];
   const dim3 grid(plan.n_sched[0]);
   const int BM = plan.BM;
   if (wmode == 0) return launch_dyn(gateup_f32_kernel<16>, grid, gateup_lds_bytes(16, 0, a.d), st, a);
@@ -861,7 +704,9 @@ hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipS
 
 hipError_t launch_down(const ExpertArgs& a0, int wmode, const Plan& plan, hipStream_t st) {
   ExpertArgs a = a0;
-  a.sched = plan.sched[1];
+  a.sched = plan.xcd ? plan.sched[1] : plan.sched[0];
+  a.per_tile = !plan.xcd;
+  a.nsl = plan.n_slices[1];
   const dim3 grid(plan.n_sched[1]);
   const int BM = plan.BM;
   const int Fmax = a.F > a.Fs ? a.F : a.Fs;

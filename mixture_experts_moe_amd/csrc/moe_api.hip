@@ -14,7 +14,13 @@ constexpr size_t kMaxLds = 160 * 1024;  // LDS per workgroup on gfx950
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t logits, rpart, chunk_hist, local_rank, sched_gu, sched_dn, rinfo, xq, sx, h, sh, part, total;
+  size_t logits, rpart, chunk_hist, local_rank, h, sh, part, total;
+};
+
+// Segments of the dispatch plan (moe_routing.plan), written by the routing call
+// and read by the forward call.
+struct PlanLayout {
+  size_t sched_gu, sched_dn, rinfo, xq, sx, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -27,8 +33,9 @@ int64_t max_tiles_for(const moe_shape& s, int BM) {
 }
 
 // Workspace segments (256-byte aligned).  Routing uses logits (when the caller
-// passes none), the router partial sums, chunk_hist and local_rank; the forward pass
-// uses the rest.  Nothing is carried from one call to the next.
+// passes none), the router partial sums, chunk_hist and local_rank; the forward
+// pass uses the rest.  Nothing is carried from one call to the next: what the
+// forward pass needs from routing travels in moe_routing (plan included).
 Layout layout(const moe_shape& s) {
   const size_t T = s.T, d = s.d_model, E = s.n_experts, P = T * s.top_k;
   const size_t Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
@@ -44,17 +51,31 @@ Layout layout(const moe_shape& s) {
   L.rpart = seg(moe::router_part_floats(s.T, s.top_k, s.d_model, s.n_experts, s.act_dtype == MOE_BF16) * 4);
   L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
   L.local_rank = seg(P * 4);
-  {  // block schedules, sized for the largest case (16-row tiles, 64-feature slices)
-    const size_t mt = (size_t)max_tiles_for(s, 16);
-    L.sched_gu = seg((mt * ((Fmax + 63) / 64) + 7) / 8 * 8 * sizeof(int4));
-    L.sched_dn = seg((mt * ((d + 63) / 64) + 7) / 8 * 8 * sizeof(int4));
-  }
-  L.rinfo = seg((P + T) * 12);
-  L.xq = seg(fp8 ? T * d : 0);
-  L.sx = seg(fp8 ? T * (d / 128) * 4 : 0);
   L.h = seg((P + T) * Fmax * h_elem_bytes(s.w_dtype));
   L.sh = seg(fp8 ? (P + T) * (Fmax / 128) * 4 : 0);
   L.part = seg((P + T) * d * 4);
+  L.total = o;
+  return L;
+}
+
+PlanLayout plan_layout(const moe_shape& s) {
+  const size_t T = s.T, d = s.d_model, P = T * s.top_k;
+  const size_t Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
+  const bool fp8 = s.w_dtype == MOE_FP8E4M3_B128;
+  PlanLayout L;
+  size_t o = 0;
+  auto seg = [&](size_t bytes) {
+    size_t at = o;
+    o += align256(bytes);
+    return at;
+  };
+  // block schedules, sized for the largest case (16-row tiles, 64-feature slices)
+  const size_t mt = (size_t)max_tiles_for(s, 16);
+  L.sched_gu = seg((mt * ((Fmax + 63) / 64) + 7) / 8 * 8 * sizeof(int4));
+  L.sched_dn = seg((mt * ((d + 63) / 64) + 7) / 8 * 8 * sizeof(int4));
+  L.rinfo = seg((P + T) * 12);
+  L.xq = seg(fp8 ? T * d : 0);
+  L.sx = seg(fp8 ? T * (d / 128) * 4 : 0);
   L.total = o;
   return L;
 }
@@ -97,9 +118,44 @@ int pick_bm(const moe_shape& s) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 int check_routing_out(const moe_routing* r) {
-  if (!r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm || !r->status)
+  if (!r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm || !r->status ||
+      !r->plan)
     return MOE_ERR_INVALID_ARG;
   return MOE_OK;
+}
+
+// The plan of one call: tile height, schedule sizes and where its parts sit in
+// the plan buffer (the same for the routing call that writes it and the forward
+// call that reads it).
+struct PlanView {
+  moe::Plan plan;
+  moe::RowInfo ri;
+  uint8_t* xq;
+  float* sx;
+};
+
+PlanView plan_view(const moe_shape& s, void* plan_buf) {
+  const PlanLayout pl = plan_layout(s);
+  char* base = (char*)plan_buf;
+  const int P = s.T * s.top_k;
+  const int Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
+  PlanView v;
+  v.plan.BM = pick_bm(s);
+  v.plan.xcd = v.plan.BM > 16;  // several tiles per expert: keep an expert's tiles on one XCD
+  moe::plan_sizes(s.w_dtype, v.plan.BM, (int)max_tiles_for(s, v.plan.BM), Fmax, s.d_model, v.plan.n_slices[0],
+                  v.plan.n_slices[1], v.plan.n_sched[0], v.plan.n_sched[1]);
+  v.plan.max_tiles = (int)max_tiles_for(s, v.plan.BM);
+  if (!v.plan.xcd)  // blocks take the tiles in order from one tile list
+    for (int i = 0; i < 2; ++i) v.plan.n_sched[i] = v.plan.max_tiles * v.plan.n_slices[i];
+  v.plan.sched[0] = (int4*)(base + pl.sched_gu);
+  v.plan.sched[1] = (int4*)(base + pl.sched_dn);
+  v.ri.tok = (int32_t*)(base + pl.rinfo);
+  v.ri.prow = v.ri.tok + (P + s.T);
+  v.ri.w = (float*)(v.ri.prow + (P + s.T));
+  const bool fp8 = s.w_dtype == MOE_FP8E4M3_B128;
+  v.xq = fp8 ? (uint8_t*)(base + pl.xq) : nullptr;
+  v.sx = fp8 ? (float*)(base + pl.sx) : nullptr;
+  return v;
 }
 
 int route_common(const moe_shape* shape, const moe_weights* w, const void* x, const int32_t* forced,
@@ -133,6 +189,29 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   R.perm = out->perm;
   R.inv_perm = out->inv_perm;
   R.status = out->status;
+  const PlanView v = plan_view(*shape, out->plan);
+  moe::PlanCtx& pc = R.plan;
+  pc.pa.counts = out->counts;
+  pc.pa.offsets = out->offsets;
+  pc.pa.E = shape->n_experts;
+  pc.pa.T = shape->T;
+  pc.pa.P = shape->T * shape->top_k;
+  pc.pa.has_shared = shape->d_ffn_shared > 0 ? 1 : 0;
+  pc.pa.BM = v.plan.BM;
+  pc.pa.xcd = v.plan.xcd ? 1 : 0;
+  for (int i = 0; i < 2; ++i) {
+    pc.pa.sched[i] = v.plan.sched[i];
+    pc.pa.n_sched[i] = v.plan.n_sched[i];
+    pc.pa.n_slices[i] = v.plan.n_slices[i];
+  }
+  pc.pa.max_tiles = v.plan.max_tiles;
+  pc.ri = v.ri;
+  pc.x = (const uint16_t*)x;
+  pc.xq = v.xq;
+  pc.sx = v.sx;
+  pc.gpr = shape->d_model / 128;
+  pc.n_groups = v.xq ? (int64_t)shape->T * pc.gpr : 0;
+  pc.k = shape->top_k;
   return hip_status(moe::launch_route(R, (hipStream_t)stream));
 }
 
@@ -143,6 +222,11 @@ extern "C" {
 size_t moe_workspace_bytes(const moe_shape* shape) {
   if (validate_shape(shape) != MOE_OK) return 0;
   return layout(*shape).total;
+}
+
+size_t moe_plan_bytes(const moe_shape* shape) {
+  if (validate_shape(shape) != MOE_OK) return 0;
+  return plan_layout(*shape).total;
 }
 
 int moe_route(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* out, void* ws,
@@ -166,7 +250,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   if (stages & ~(uint32_t)MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
   int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
-  if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm)
+  if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->plan)
     return MOE_ERR_INVALID_ARG;
   const bool fp8 = shape->w_dtype == MOE_FP8E4M3_B128;
   const bool has_shared = shape->d_ffn_shared > 0;
@@ -182,7 +266,6 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
   const int T = shape->T, d = shape->d_model, E = shape->n_experts, k = shape->top_k, P = T * k;
-  const int BM = pick_bm(*shape);
 
   ExpertArgs a;
   a.sched = nullptr;
@@ -198,8 +281,9 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.P = P;
   a.hstride = a.F > a.Fs ? a.F : a.Fs;
   a.w_tiled = shape->w_layout == MOE_LAYOUT_TILED;
-  a.xa = fp8 ? (const void*)(base + L.xq) : x;
-  a.sxa = (const float*)(base + L.sx);
+  const PlanView v = plan_view(*shape, r->plan);
+  a.xa = fp8 ? (const void*)v.xq : x;
+  a.sxa = v.sx;
   a.wg = w->w_gate;
   a.wu = w->w_up;
   a.wd = w->w_down;
@@ -215,38 +299,25 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.h = base + L.h;
   a.sh = (float*)(base + L.sh);
   a.part = (float*)(base + L.part);
-  a.ri.tok = (int32_t*)(base + L.rinfo);
-  a.ri.prow = a.ri.tok + (P + T);
-  a.ri.w = (float*)(a.ri.prow + (P + T));
+  a.ri = v.ri;
 
   hipError_t e = hipSuccess;
   auto mark = [&](int i) {
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], st);
   };
-  moe::Plan plan;
-  plan.BM = BM;
-  plan.xcd = BM > 16;  // several tiles per expert: keep an expert's tiles on one XCD
-  moe::plan_sizes(shape->w_dtype, BM, (int)max_tiles_for(*shape, BM), a.hstride, d, plan.n_slices[0],
-                  plan.n_slices[1], plan.n_sched[0], plan.n_sched[1]);
-  plan.sched[0] = (int4*)(base + L.sched_gu);
-  plan.sched[1] = (int4*)(base + L.sched_dn);
+  const moe::Plan& plan = v.plan;
   mark(0);
-  if (stages & MOE_STAGE_PREPARE) {
-    e = moe::launch_prepare(x, T, d, fp8 ? (uint8_t*)(base + L.xq) : nullptr, (float*)(base + L.sx), a.ri, r->perm,
-                            r->topk_w, k, plan, r->counts, r->offsets, E, P, has_shared, st);
-    mark(1);
-  }
-  if (e == hipSuccess && (stages & MOE_STAGE_GATE_UP)) {
+  if (stages & MOE_STAGE_GATE_UP) {
     e = moe::launch_gateup(a, shape->w_dtype, plan, st);
-    mark(2);
+    mark(1);
   }
   if (e == hipSuccess && (stages & MOE_STAGE_DOWN)) {
     e = moe::launch_down(a, shape->w_dtype, plan, st);
-    mark(3);
+    mark(2);
   }
   if (e == hipSuccess && (stages & MOE_STAGE_COMBINE)) {
     e = moe::launch_combine(a.part, r->topk_idx, T, k, d, E, P, has_shared, y, shape->act_dtype == MOE_BF16, st);
-    mark(4);
+    mark(3);
   }
   return hip_status(e);
 }

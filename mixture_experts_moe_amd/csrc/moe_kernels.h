@@ -18,9 +18,36 @@ struct RowInfo {
   float* w;
 };
 
+// Schedule parameters of the dispatch plan (see moe_plan.h).
+struct PlanArgs {
+  const int32_t* counts;   // [E] pairs per expert
+  const int32_t* offsets;  // [E] first sorted pair of each expert
+  int E, T, P, has_shared, BM, xcd;
+  int4* sched[2];          // gate/up, down (xcd: one record per block; else sched[0] is the tile list)
+  int n_sched[2];          // blocks of each kernel
+  int n_slices[2];
+  int max_tiles;           // entries of the tile list
+};
+
+// Where the routing call's last launch writes the dispatch plan, and the
+// activations it quantises.
+struct PlanCtx {
+  PlanArgs pa;
+  RowInfo ri;
+  const uint16_t* x;  // bf16 activations [T][d] (quantised when xq != null)
+  uint8_t* xq;
+  float* sx;
+  int64_t n_groups;   // T * d / 128 when quantising, else 0
+  int gpr;            // d / 128
+  int k;
+};
+
 // Everything the expert kernels read or write (device pointers).
 struct ExpertArgs {
-  const int4* sched;          // [blocks] per block: (group, first row, first h row, rows | slice << 16); group -1: none
+  const int4* sched;          // per_tile: tile list (group, first row, first h row, rows), block b takes tile
+                              // b / nsl and slice b % nsl; else one record per block with rows | slice << 16;
+                              // group -1: no work
+  int per_tile, nsl;          // set per launch
   const int32_t* offsets;     // [E+1]
   const int32_t* perm;        // [P]
   const float* topk_w;        // [P]
@@ -55,28 +82,26 @@ struct RouteLaunch {
   int32_t* idx;
   float* w;
   int32_t *chunk_hist, *local_rank, *counts, *offsets, *perm, *inv_perm, *status;
+  PlanCtx plan;            // the dispatch plan the last launch writes
 };
 hipError_t launch_route(const RouteLaunch& L, hipStream_t st);
 
 hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n_cols, uint8_t* codes, float* scales,
                                 hipStream_t st);
 // Block schedules of the two expert kernels ([0] gate/up, [1] down), written by
-// the preparation launch: BM rows per tile; xcd: an expert's tiles are kept on
-// one XCD (when experts have several tiles).
+// the routing call: BM rows per tile.  xcd (experts with several tiles): one
+// record per block, an expert's tiles kept on one XCD; otherwise the blocks
+// take the tiles in order, slice fastest, from one shared tile list (sched[0]).
 struct Plan {
   int BM;
   bool xcd;
   int4* sched[2];
-  int n_sched[2];   // blocks (multiples of 8)
+  int n_sched[2];   // blocks of each kernel
   int n_slices[2];  // feature slices per tile
+  int max_tiles;
 };
 int down_rows_per_wave(int BM, int wmode, int Fmax, int d);
 void plan_sizes(int wmode, int BM, int max_tiles, int Fmax, int d, int& nsl_gu, int& nsl_dn, int& n_gu, int& n_dn);
-// Forward preparation in one launch: E4M3 activation quantisation (when
-// xq != null), the per-row info and the block schedules.
-hipError_t launch_prepare(const void* x, int T, int d, uint8_t* xq, float* sx, const RowInfo& ri,
-                          const int32_t* perm, const float* topk_w, int k, const Plan& plan, const int32_t* counts,
-                          const int32_t* offsets, int E, int P, bool has_shared, hipStream_t st);
 hipError_t launch_gateup(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
 hipError_t launch_down(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,

@@ -20,6 +20,7 @@
 //   4. placement of every pair.
 #include "moe_device.h"
 #include "moe_kernels.h"
+#include "moe_plan.h"
 
 namespace moe {
 
@@ -463,7 +464,8 @@ __device__ __forceinline__ int route_token(const TopkArgs& a, int t, const float
 
 // LDS of the block-wide dispatch step.
 struct DispatchLds {
-  int32_t hist[kMaxExperts];
+  int32_t hist[kMaxExperts];  // whole sort: offsets at the end
+  int32_t cnt[kMaxExperts];   // whole sort: counts
   int32_t wave_cnt[16 * kMaxExperts];
   int32_t tmp[17];
 };
@@ -475,8 +477,8 @@ struct DispatchLds {
 // counts scanned in wave order).  `whole`: the block holds every pair, so the
 // counting sort is finished here (counts, offsets, perm, inv_perm); otherwise
 // the block's histogram and ranks go to chunk_hist / local_rank.
-__device__ __forceinline__ void dispatch_block(const TopkArgs& a, DispatchLds& s, int e, int p, bool live,
-                                               bool whole) {
+__device__ __forceinline__ int dispatch_block(const TopkArgs& a, DispatchLds& s, int e, int p, bool live,
+                                              bool whole) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   uint64_t peers = __ballot(1);
@@ -506,7 +508,7 @@ __device__ __forceinline__ void dispatch_block(const TopkArgs& a, DispatchLds& s
   if (!whole) {
     if (live) a.local_rank[p] = rank;
     for (int i = tid; i < E; i += 1024) a.chunk_hist[(size_t)blockIdx.x * E + i] = s.hist[i];
-    return;
+    return -1;
   }
   const int cnt = tid < E ? s.hist[tid] : 0;
   int total;
@@ -515,12 +517,14 @@ __device__ __forceinline__ void dispatch_block(const TopkArgs& a, DispatchLds& s
     a.counts[tid] = cnt;
     a.offsets[tid] = off;
     s.hist[tid] = off;
+    s.cnt[tid] = cnt;
   }
   if (tid == 0) a.offsets[E] = total;
   __syncthreads();
+  int q = -1;
   if (live) {
     if (e >= 0) {
-      const int q = s.hist[e] + rank;
+      q = s.hist[e] + rank;
       a.perm[q] = p;
       a.inv_perm[p] = q;
     } else {
@@ -528,6 +532,7 @@ __device__ __forceinline__ void dispatch_block(const TopkArgs& a, DispatchLds& s
     }
     if (p >= total) a.perm[p] = -1;
   }
+  return q;
 }
 
 // Logits of token t for the candidates e = lane + 64 j.  The router left n_parts
@@ -615,13 +620,39 @@ __global__ __launch_bounds__(64) void topk_small_kernel(TopkArgs a, const float*
   route_token<J, FORCED>(a, t, lv, lane);
 }
 
-// Short inputs, step 3: the whole counting sort in one block (T * k <= 1024).
-__global__ __launch_bounds__(1024) void dispatch_small_kernel(TopkArgs a) {
+// Short inputs, step 3: block 0 does the whole counting sort (T * k <= 1024)
+// and then the dispatch plan (per-row info, block schedules, see moe_plan.h);
+// the other blocks quantise the activations (FP8 weights), 16 groups each.
+__global__ __launch_bounds__(1024) void dispatch_small_kernel(TopkArgs a, PlanCtx pc) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (blockIdx.x > 0) {
+    const int64_t g = (int64_t)(blockIdx.x - 1) * 16 + (tid >> 6);
+    if (g < pc.n_groups) quantize_group<true>(pc.x, g, pc.gpr, pc.xq, pc.sx, lane);
+    return;
+  }
   __shared__ DispatchLds s;
-  const int P = a.T * a.k, p = threadIdx.x;
+  __shared__ PlanLds pl;
+  const int T = a.T, P = T * a.k, p = tid;
   const bool live = p < P;
   const int e = live ? a.idx[p] : -1;
-  dispatch_block(a, s, e, p, live, true);
+  const float wp = a.w[live ? p : 0];  // requested with the ids: one round trip for both
+  const int q = dispatch_block(a, s, e, p, live, true);
+  if (q >= 0) {
+    pc.ri.tok[q] = p / a.k;
+    pc.ri.prow[q] = p;
+    pc.ri.w[q] = wp;
+  }
+  if (pc.pa.has_shared)
+    for (int t = tid; t < T; t += 1024) {
+      pc.ri.tok[P + t] = t;
+      pc.ri.prow[P + t] = P + t;
+      pc.ri.w[P + t] = 1.f;
+    }
+  PlanArgs pa = pc.pa;
+  pa.counts = s.cnt;
+  pa.offsets = s.hist;
+  const int total = plan_tables<1024>(pa, pl);
+  plan_scatter<1024>(pa, pl, total);
 }
 
 // Several chunks: per expert, an exclusive scan of the chunk histograms in chunk
@@ -658,24 +689,57 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict
   if (e == 0) offsets[E] = total;
 }
 
-// Placement: q = offsets[e] + (pairs of e in earlier chunks) + rank in the chunk.
+// Long inputs, step 4, one launch: placement of every pair, q = offsets[e] +
+// (pairs of e in earlier chunks) + rank in the chunk, with the per-row info of
+// the placed pairs (blocks [0, npl)); the shared expert's rows (next nsr
+// blocks); the block schedules (next npb blocks, kPlanEntries entries each);
+// the activation quantisation (the rest, four groups each).
+constexpr int kPlanEntries = 512;
+
 __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int P, int E, int np,
                                                               const int32_t* __restrict__ chunk_prefix,
                                                               const int32_t* __restrict__ local_rank,
                                                               const int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ perm,
-                                                              int32_t* __restrict__ inv_perm) {
-  const int p = blockIdx.x * 256 + threadIdx.x;
-  if (p >= P) return;
-  const int e = idx[p];
-  if (e >= 0 && e < E) {
-    const int q = offsets[e] + chunk_prefix[(size_t)(p / np) * E + e] + local_rank[p];
-    perm[q] = p;
-    inv_perm[p] = q;
-  } else {
-    inv_perm[p] = -1;
+                                                              int32_t* __restrict__ inv_perm,
+                                                              const float* __restrict__ topk_w, PlanCtx pc,
+                                                              int npl, int nsr, int npb) {
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  if (blk < npl) {
+    const int p = blk * 256 + tid;
+    if (p >= P) return;
+    const int e = idx[p];
+    if (e >= 0 && e < E) {
+      const int q = offsets[e] + chunk_prefix[(size_t)(p / np) * E + e] + local_rank[p];
+      perm[q] = p;
+      inv_perm[p] = q;
+      pc.ri.tok[q] = p / pc.k;
+      pc.ri.prow[q] = p;
+      pc.ri.w[q] = topk_w[p];
+    } else {
+      inv_perm[p] = -1;
+    }
+    if (p >= offsets[E]) perm[p] = -1;
+    return;
   }
-  if (p >= offsets[E]) perm[p] = -1;
+  if (blk < npl + nsr) {
+    const int t = (blk - npl) * 256 + tid;
+    if (t < pc.pa.T) {
+      pc.ri.tok[P + t] = t;
+      pc.ri.prow[P + t] = P + t;
+      pc.ri.w[P + t] = 1.f;
+    }
+    return;
+  }
+  if (blk < npl + nsr + npb) {
+    __shared__ PlanLds pl;
+    const int total = plan_tables<256>(pc.pa, pl);
+    const int e0 = (blk - npl - nsr) * kPlanEntries, ne = plan_n_entries(pc.pa);
+    for (int i = tid; i < kPlanEntries && e0 + i < ne; i += 256) plan_any_entry(pc.pa, pl, total, e0 + i);
+    return;
+  }
+  const int64_t g = (int64_t)(blk - npl - nsr - npb) * 4 + (tid >> 6);
+  if (g < pc.n_groups) quantize_group<true>(pc.x, g, pc.gpr, pc.xq, pc.sx, tid & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -799,7 +863,8 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
 #undef MOE_TOPK_SMALL
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dispatch_small_kernel<<<1, 1024, 0, st>>>(a);
+    const int nqb = (int)((L.plan.n_groups + 15) / 16);
+    dispatch_small_kernel<<<1 + nqb, 1024, 0, st>>>(a, L.plan);
     return hipGetLastError();
   }
   const int P = L.T * L.k;
@@ -818,8 +883,11 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
   dispatch_scan_kernel<<<1, 1024, 0, st>>>(L.chunk_hist, n_chunks, L.E, L.counts, L.offsets);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dispatch_place_kernel<<<(P + 255) / 256, 256, 0, st>>>(L.idx, P, L.E, tpc * L.k, L.chunk_hist, L.local_rank,
-                                                         L.offsets, L.perm, L.inv_perm);
+  const int npl = (P + 255) / 256, nsr = L.plan.pa.has_shared ? (L.T + 255) / 256 : 0;
+  const int npb = (plan_n_entries(L.plan.pa) + kPlanEntries - 1) / kPlanEntries;
+  const int64_t nqb = (L.plan.n_groups + 3) / 4;
+  dispatch_place_kernel<<<(unsigned)(npl + nsr + npb + nqb), 256, 0, st>>>(
+      L.idx, P, L.E, tpc * L.k, L.chunk_hist, L.local_rank, L.offsets, L.perm, L.inv_perm, L.w, L.plan, npl, nsr, npb);
   return hipGetLastError();
 }
 #undef MOE_J_SWITCH

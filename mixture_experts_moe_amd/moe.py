@@ -20,10 +20,11 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 
 # Every function the header declares (checked against include/moe.h by the tests).
-ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
+ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
                  "moe_quantize_rows", "moe_pack_weights", "moe_status_string")
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
-STAGE_PREPARE, STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 8, 15
+STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
+N_STAGE_EVENTS = 4
 
 
 class MoeError(RuntimeError):
@@ -45,7 +46,7 @@ class Weights(C.Structure):
     _fields_ = [(n, C.c_void_p) for n in _WEIGHT_FIELDS]
 
 
-_ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "status")
+_ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "status", "plan")
 
 
 class RoutingStruct(C.Structure):
@@ -66,6 +67,8 @@ def lib() -> C.CDLL:
         p, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
         L.moe_workspace_bytes.restype = C.c_size_t
         L.moe_workspace_bytes.argtypes = [p]
+        L.moe_plan_bytes.restype = C.c_size_t
+        L.moe_plan_bytes.argtypes = [p]
         L.moe_route.argtypes = [p, p, p, p, p, C.c_size_t, p]
         L.moe_route_forced.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
         L.moe_forward.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
@@ -122,6 +125,7 @@ class Routing:
     perm: torch.Tensor
     inv_perm: torch.Tensor
     status: torch.Tensor
+    plan: torch.Tensor  # opaque dispatch plan (moe_plan_bytes bytes)
 
     def struct(self) -> RoutingStruct:
         return RoutingStruct(*[_ptr(getattr(self, n)) for n in _ROUTING_FIELDS])
@@ -134,11 +138,16 @@ def alloc_routing(shape: Shape, device="cuda", with_logits=True) -> Routing:
         logits=torch.empty((T, E), dtype=torch.float32, device=device) if with_logits else None,
         topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
         counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
-        perm=torch.empty(T * k, **i32), inv_perm=torch.empty(T * k, **i32), status=torch.empty(1, **i32))
+        perm=torch.empty(T * k, **i32), inv_perm=torch.empty(T * k, **i32), status=torch.empty(1, **i32),
+        plan=torch.empty(max(plan_bytes(shape), 256), dtype=torch.uint8, device=device))
 
 
 def workspace_bytes(shape: Shape) -> int:
     return int(lib().moe_workspace_bytes(C.byref(shape)))
+
+
+def plan_bytes(shape: Shape) -> int:
+    return int(lib().moe_plan_bytes(C.byref(shape)))
 
 
 def alloc_workspace(shape: Shape, device="cuda") -> torch.Tensor:
@@ -173,14 +182,14 @@ def forward(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor,
 
 
 def _events(events):
-    """torch.cuda.Event list -> hipEvent_t[5] (or None)."""
+    """torch.cuda.Event list -> hipEvent_t[N_STAGE_EVENTS] (or None)."""
     if events is None:
         return None
-    assert len(events) == 5
+    assert len(events) == N_STAGE_EVENTS
     for ev in events:
         if ev.cuda_event == 0:  # torch creates the HIP event lazily
             ev.record()
-    return (C.c_void_p * 5)(*[ev.cuda_event for ev in events])
+    return (C.c_void_p * N_STAGE_EVENTS)(*[ev.cuda_event for ev in events])
 
 
 def forward_stages(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor, ws: torch.Tensor,

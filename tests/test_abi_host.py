@@ -61,10 +61,9 @@ FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below returns before
 
 
 def _routing_struct(**null):
-    vals = {n: 0x2000 for n in ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm", "inv_perm", "status")}
+    vals = {n: 0x2000 for n in moe._ROUTING_FIELDS}
     vals.update({k: None for k in null})
-    return moe.RoutingStruct(*[vals[n] for n in ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm",
-                                                 "inv_perm", "status")])
+    return moe.RoutingStruct(*[vals[n] for n in moe._ROUTING_FIELDS])
 
 
 def _weights_struct(**null):
@@ -90,6 +89,7 @@ def test_route_host_validation():
     assert _route(good, w=_weights_struct(w_router=1)) == moe.MOE_ERR_INVALID_ARG
     assert _route(good, r=_routing_struct(perm=1)) == moe.MOE_ERR_INVALID_ARG
     assert _route(good, r=_routing_struct(status=1)) == moe.MOE_ERR_INVALID_ARG
+    assert _route(good, r=_routing_struct(plan=1)) == moe.MOE_ERR_INVALID_ARG
     assert _route(good, x=None) == moe.MOE_ERR_INVALID_ARG
     assert _route(good, ws_bytes=moe.workspace_bytes(good) - 1) == moe.MOE_ERR_WORKSPACE
     assert _route(good, ws=None) == moe.MOE_ERR_INVALID_ARG
@@ -117,6 +117,7 @@ def _forward(shape, w=None, r=None, y=FAKE, ws_bytes=1 << 40):
 
 def test_forward_host_validation():
     fp8 = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    assert _forward(fp8, r=_routing_struct(plan=1)) == moe.MOE_ERR_INVALID_ARG
     assert _forward(fp8, w=_weights_struct(s_gate=1)) == moe.MOE_ERR_INVALID_ARG
     assert _forward(fp8, w=_weights_struct(ss_down=1)) == moe.MOE_ERR_INVALID_ARG
     assert _forward(fp8, w=_weights_struct(sh_up=1)) == moe.MOE_ERR_INVALID_ARG
@@ -164,3 +165,16 @@ def test_layout_field_validation():
     assert _forward(bad) == moe.MOE_ERR_INVALID_ARG
     f32 = moe.make_shape(32, 2048, 384, 6, 640, 640, act="f32", w="f32", layout="tiled")
     assert _forward(f32) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_plan_bytes():
+    _lib()
+    s32 = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    s2k = moe.make_shape(2048, 2048, 384, 6, 640, 640)
+    n32, n2k = moe.plan_bytes(s32), moe.plan_bytes(s2k)
+    # at least the E4M3 activations, their scales and the per-row info
+    assert n32 >= 32 * 2048 + 32 * 16 * 4 + (32 * 7) * 12
+    assert n2k >= 2048 * 2048 + 2048 * 16 * 4 + (2048 * 7) * 12 and n2k > n32
+    bf = moe.make_shape(32, 2048, 384, 6, 640, 640, act="bf16", w="bf16")
+    assert moe.plan_bytes(bf) < n32  # no activation codes with bf16 weights
+    assert moe.plan_bytes(moe.make_shape(32, 2048, 384, 9, 640, 640)) == 0

@@ -362,7 +362,8 @@ def test_invalid_forced_ids_flag_status_and_stay_in_bounds():
                                                   ("status", 1, torch.int32), ("logits", T * E, torch.float32))}
     r = moe.Routing(logits=bufs["logits"][1].view(T, E), topk_idx=bufs["topk_idx"][1].view(T, k),
                     topk_w=bufs["topk_w"][1].view(T, k), counts=bufs["counts"][1], offsets=bufs["offsets"][1],
-                    perm=bufs["perm"][1], inv_perm=bufs["inv_perm"][1], status=bufs["status"][1])
+                    perm=bufs["perm"][1], inv_perm=bufs["inv_perm"][1], status=bufs["status"][1],
+                    plan=torch.empty(moe.plan_bytes(shape), dtype=torch.uint8, device=DEV))
     g = run_gpu(inp, forced=bad, routing=r)
     for n, (full, _) in bufs.items():
         tail = full[-guard:].cpu().numpy()
@@ -406,12 +407,12 @@ def test_forward_stages_match_forward():
     moe.route(shape, dev, dev["x"], r, ws)
     moe.forward(shape, dev, dev["x"], r, y1, ws)
     b = moe.Bound(shape, dev, dev["x"], r, y2, ws)
-    for st in (moe.STAGE_PREPARE, moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE):
+    for st in (moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE):
         b.forward(st)
     torch.cuda.synchronize()
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
     with pytest.raises(moe.MoeError):
-        b.forward(16)
+        b.forward(8)
 
 
 # ------------------------------------------------------------------ tiled weight layout
