@@ -604,16 +604,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int q = d / 4;
   if (gid >= (int64_t)T * q) return;
   const int t = (int)(gid / q), n = (int)(gid - (int64_t)t * q) * 4;
+  // every slot's row is requested together with the ids (the rows of invalid
+  // slots are in bounds and skipped), so the call costs one round trip
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   if (has_shared) acc = *(const float4*)(part + (size_t)(P + t) * d + n);
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[(size_t)t * k + j];
-    if (e < 0 || e >= E) continue;
-    const float4 v = *(const float4*)(part + ((size_t)t * k + j) * d + n);
-    acc.x = acc.x + v.x;
-    acc.y = acc.y + v.y;
-    acc.z = acc.z + v.z;
-    acc.w = acc.w + v.w;
+  float4 v[kMaxTopK];
+  int ev[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j)
+    if (j < k) {
+      ev[j] = idx[(size_t)t * k + j];
+      v[j] = *(const float4*)(part + ((size_t)t * k + j) * d + n);
+    }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j >= k || ev[j] < 0 || ev[j] >= E) continue;
+    acc.x = acc.x + v[j].x;
+    acc.y = acc.y + v[j].y;
+    acc.z = acc.z + v[j].z;
+    acc.w = acc.w + v[j].w;
   }
   if (BF16OUT) {
     uint2 pk;

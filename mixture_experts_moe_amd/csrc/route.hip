@@ -655,43 +655,54 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(TopkArgs a, PlanCt
   plan_scatter<1024>(pa, pl, total);
 }
 
-// Several chunks: per expert, an exclusive scan of the chunk histograms in chunk
-// order (in place: entry [c][e] becomes the pairs of e in chunks before c), the
-// expert totals and their exclusive scan.  One block, one thread per expert.
-__global__ __launch_bounds__(1024) void dispatch_scan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks, int E,
-                                                              int32_t* __restrict__ counts,
-                                                              int32_t* __restrict__ offsets) {
+// Several chunks, step 3: one block per expert e scans e's chunk histogram
+// entries in chunk order, in place (entry [c][e] becomes the pairs of e in
+// chunks before c), and writes counts[e].  Each thread takes a run of chunks.
+__global__ __launch_bounds__(256) void dispatch_scan_kernel(int32_t* __restrict__ chunk_hist, int n_chunks, int E,
+                                                             int32_t* __restrict__ counts) {
   __shared__ int32_t tmp[17];
-  const int e = threadIdx.x;
-  int run = 0;
-  if (e < E) {
-    int c = 0;
-    for (; c + 4 <= n_chunks; c += 4) {
-      int32_t* h = chunk_hist + (size_t)c * E + e;
-      const int v0 = h[0], v1 = h[E], v2 = h[2 * E], v3 = h[3 * E];
-      h[0] = run;
-      h[E] = run + v0;
-      h[2 * E] = run + v0 + v1;
-      h[3 * E] = run + v0 + v1 + v2;
-      run += v0 + v1 + v2 + v3;
-    }
-    for (; c < n_chunks; ++c) {
-      int32_t* h = chunk_hist + (size_t)c * E + e;
-      const int v = *h;
-      *h = run;
-      run += v;
-    }
-    counts[e] = run;
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int per = (n_chunks + 255) / 256, c0 = min(tid * per, n_chunks), c1 = min(c0 + per, n_chunks);
+  int sum = 0;
+  for (int c = c0; c < c1; ++c) sum += chunk_hist[(size_t)c * E + e];
+  int total;
+  int run = block_excl_scan<256>(sum, tmp, &total);
+  for (int c = c0; c < c1; ++c) {
+    int32_t* h = chunk_hist + (size_t)c * E + e;
+    const int v = *h;
+    *h = run;
+    run += v;
+  }
+  if (tid == 0) counts[e] = total;
+}
+
+// Exclusive scan of counts[0..E) into offs[0..E] (LDS) by a 256-thread block.
+__device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts, int E, int32_t* offs,
+                                              int32_t* tmp) {
+  constexpr int PER = (kMaxExperts + 255) / 256;
+  int v[PER], sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = PER * threadIdx.x + i;
+    v[i] = e < E ? counts[e] : 0;
+    sum += v[i];
   }
   int total;
-  const int off = block1024_excl_scan(e < E ? run : 0, tmp, &total);
-  if (e < E) offsets[e] = off;
-  if (e == 0) offsets[E] = total;
+  int run = block_excl_scan<256>(sum, tmp, &total);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = PER * threadIdx.x + i;
+    if (e < E) offs[e] = run;
+    run += v[i];
+  }
+  if (threadIdx.x == 0) offs[E] = total;
+  __syncthreads();
 }
 
 // Long inputs, step 4, one launch: placement of every pair, q = offsets[e] +
 // (pairs of e in earlier chunks) + rank in the chunk, with the per-row info of
-// the placed pairs (blocks [0, npl)); the shared expert's rows (next nsr
+// the placed pairs (blocks [0, npl); each derives the expert offsets from the
+// counts, block 0 also stores them); the shared expert's rows (next nsr
 // blocks); the block schedules (next npb blocks, kPlanEntries entries each);
 // the activation quantisation (the rest, four groups each).
 constexpr int kPlanEntries = 512;
@@ -699,18 +710,24 @@ constexpr int kPlanEntries = 512;
 __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int P, int E, int np,
                                                               const int32_t* __restrict__ chunk_prefix,
                                                               const int32_t* __restrict__ local_rank,
-                                                              const int32_t* __restrict__ offsets,
+                                                              const int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
                                                               int32_t* __restrict__ perm,
                                                               int32_t* __restrict__ inv_perm,
                                                               const float* __restrict__ topk_w, PlanCtx pc,
                                                               int npl, int nsr, int npb) {
   const int tid = threadIdx.x, blk = blockIdx.x;
+  __shared__ int32_t offs[kMaxExperts + 1], tmp[17];
   if (blk < npl) {
-    const int p = blk * 256 + tid;
-    if (p >= P) return;
+    const int p = min(blk * 256 + tid, P - 1);
     const int e = idx[p];
+    const int cp = (e >= 0 && e < E) ? chunk_prefix[(size_t)(p / np) * E + e] + local_rank[p] : 0;
+    block_offsets(counts, E, offs, tmp);
+    if (blk == 0)
+      for (int i = tid; i <= E; i += 256) offsets[i] = offs[i];
+    if (blk * 256 + tid >= P) return;
     if (e >= 0 && e < E) {
-      const int q = offsets[e] + chunk_prefix[(size_t)(p / np) * E + e] + local_rank[p];
+      const int q = offs[e] + cp;
       perm[q] = p;
       inv_perm[p] = q;
       pc.ri.tok[q] = p / pc.k;
@@ -719,7 +736,7 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
     } else {
       inv_perm[p] = -1;
     }
-    if (p >= offsets[E]) perm[p] = -1;
+    if (p >= offs[E]) perm[p] = -1;
     return;
   }
   if (blk < npl + nsr) {
@@ -733,9 +750,12 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
   }
   if (blk < npl + nsr + npb) {
     __shared__ PlanLds pl;
-    const int total = plan_tables<256>(pc.pa, pl);
+    block_offsets(counts, E, offs, tmp);
+    PlanArgs pa = pc.pa;
+    pa.offsets = offs;
+    const int total = plan_tables<256>(pa, pl);
     const int e0 = (blk - npl - nsr) * kPlanEntries, ne = plan_n_entries(pc.pa);
-    for (int i = tid; i < kPlanEntries && e0 + i < ne; i += 256) plan_any_entry(pc.pa, pl, total, e0 + i);
+    for (int i = tid; i < kPlanEntries && e0 + i < ne; i += 256) plan_any_entry(pa, pl, total, e0 + i);
     return;
   }
   const int64_t g = (int64_t)(blk - npl - nsr - npb) * 4 + (tid >> 6);
@@ -746,10 +766,10 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 // Launchers
 // ---------------------------------------------------------------------------
 // Tokens per top-k block: all of them when their pairs fit one block, else 16
-// (64 for long inputs, to keep the chunk count and the scan short).
+// (one token per wave; the per-expert scan of the chunk histograms is parallel).
 int tokens_per_chunk(int T, int k) {
   if (T * k <= kMaxChunkPairs) return T > 0 ? T : 1;
-  return T <= 4096 ? 16 : 64;
+  return 16;
 }
 
 size_t dispatch_chunk_hist_ints(int T, int k, int E) {
@@ -880,14 +900,15 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
 #undef MOE_TOPK_CASE
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dispatch_scan_kernel<<<1, 1024, 0, st>>>(L.chunk_hist, n_chunks, L.E, L.counts, L.offsets);
+  dispatch_scan_kernel<<<L.E, 256, 0, st>>>(L.chunk_hist, n_chunks, L.E, L.counts);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int npl = (P + 255) / 256, nsr = L.plan.pa.has_shared ? (L.T + 255) / 256 : 0;
   const int npb = (plan_n_entries(L.plan.pa) + kPlanEntries - 1) / kPlanEntries;
   const int64_t nqb = (L.plan.n_groups + 3) / 4;
   dispatch_place_kernel<<<(unsigned)(npl + nsr + npb + nqb), 256, 0, st>>>(
-      L.idx, P, L.E, tpc * L.k, L.chunk_hist, L.local_rank, L.offsets, L.perm, L.inv_perm, L.w, L.plan, npl, nsr, npb);
+      L.idx, P, L.E, tpc * L.k, L.chunk_hist, L.local_rank, L.counts, L.offsets, L.perm, L.inv_perm, L.w, L.plan, npl, nsr,
+      npb);
   return hipGetLastError();
 }
 #undef MOE_J_SWITCH
