@@ -478,7 +478,8 @@ struct DispatchLds {
 // counting sort is finished here (counts, offsets, perm, inv_perm); otherwise
 // the block's histogram and ranks go to chunk_hist / local_rank.
 __device__ __forceinline__ int dispatch_block(const TopkArgs& a, DispatchLds& s, int e, int p, bool live,
-                                              bool whole) {
+                                              bool whole, int n_pairs) {
+  const int nw = (n_pairs + 63) / 64;  // waves that hold pairs (threads past n_pairs have e = -1)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int E = a.E;
   uint64_t peers = __ballot(1);
@@ -490,13 +491,13 @@ __device__ __forceinline__ int dispatch_block(const TopkArgs& a, DispatchLds& s,
   const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
   const int in_wave = __popcll(peers & below);
   const bool leader = (peers & below) == 0;  // lowest lane of its id group
-  for (int i = tid; i < 16 * E; i += 1024) s.wave_cnt[i] = 0;
+  for (int i = tid; i < nw * E; i += 1024) s.wave_cnt[i] = 0;
   __syncthreads();
   if (leader && e >= 0) s.wave_cnt[wave * E + e] = __popcll(peers);
   __syncthreads();
   for (int i = tid; i < E; i += 1024) {  // exclusive scan over waves, in wave order; totals -> hist
     int run = 0;
-    for (int w = 0; w < 16; ++w) {
+    for (int w = 0; w < nw; ++w) {
       const int c = s.wave_cnt[w * E + i];
       s.wave_cnt[w * E + i] = run;
       run += c;
@@ -604,7 +605,7 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a, const f
   __syncthreads();
   const int np = a.tpc * k, p = blockIdx.x * np + tid;
   const bool live = tid < np && p < T * k;
-  dispatch_block(a, s, tid < np ? ids[tid] : -1, p, live, gridDim.x == 1);
+  dispatch_block(a, s, tid < np ? ids[tid] : -1, p, live, gridDim.x == 1, np);
 }
 
 // Short inputs, step 2: one wave per token.  The router left n_parts partial
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(1024) void dispatch_small_kernel(TopkArgs a, PlanCt
   const bool live = p < P;
   const int e = live ? a.idx[p] : -1;
   const float wp = a.w[live ? p : 0];  // requested with the ids: one round trip for both
-  const int q = dispatch_block(a, s, e, p, live, true);
+  const int q = dispatch_block(a, s, e, p, live, true, P);
   if (q >= 0) {
     pc.ri.tok[q] = p / a.k;
     pc.ri.prow[q] = p;
