@@ -49,8 +49,8 @@ FORCED = {"prefill_t2048"}
 KERNEL_SOURCES = ("mixture_experts_moe_amd/csrc/experts.hip", "mixture_experts_moe_amd/csrc/moe_device.h",
                   "mixture_experts_moe_amd/csrc/moe_kernels.h", "mixture_experts_moe_amd/csrc/moe_api.hip")
 TRAFFIC = {  # workload -> counters of the gate/up kernel, tiled layout
-    "decode_t32": {"sources_sha256": "3133c18c23e7a95715a22fdb140ea150e8ee2acc90b38cc0d8fbea8a5fae2777",
-                   "fetch_bytes": 405766421, "write_bytes": 176379},
+    "decode_t32": {"sources_sha256": "272ec6650286742c015401aa395a4b81a5b73234521bf81bc308e0d8f57fd993",
+                   "fetch_bytes": 405712661, "write_bytes": 176821},
 }
 
 
