@@ -29,20 +29,24 @@
 
 namespace moe {
 
-#ifndef MOE_NT_LOADS
-#define MOE_NT_LOADS 0
-#endif
 #ifndef MOE_GU_KG
 #define MOE_GU_KG 4  // K blocks per weight stage in the gate/up stream
 #endif
 
-// Streaming load of 16 weight bytes (non-temporal: read once per call).
+// Load of 16 weight bytes.  NT: non-temporal, for launches that read each
+// expert's weights once (FP8 weights in 16-row tiles: identity block schedule,
+// chosen when experts average at most 12 rows, so one tile per expert in the
+// usual case).  Measured on MI355X at decode, the streaming hint
+// keeps the weight stream from evicting the small outputs the kernels write
+// (h codes, fp32 partials) and the activations they re-read, whose dirty lines
+// otherwise go back to HBM in the middle of the stream: gate/up -3 us, down
+// -4.5 us per launch.  Taller tiles (XCD schedules) read an expert's weights
+// once per row tile and rely on L2 keeping them between the tiles, so they use
+// ordinary loads.
+template <bool NT>
 __device__ __forceinline__ v4i stream_load(const uint8_t* p) {
-#if MOE_NT_LOADS
-  return __builtin_nontemporal_load((const v4i*)p);
-#else
-  return *(const v4i*)p;
-#endif
+  if constexpr (NT) return __builtin_nontemporal_load((const v4i*)p);
+  else return *(const v4i*)p;
 }
 
 // ---------------------------------------------------------------------------
@@ -182,8 +186,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
     for (int j = 0; j < KG; ++j) {
       const int kb = min(q * KG + j, nbb - 1);
       const uint8_t* p = ws[r].p + (size_t)kb * ws[r].kb_stride;
-      wlo[r][j] = stream_load(p);
-      whi[r][j] = stream_load(p + ws[r].hi_off);
+      wlo[r][j] = stream_load<WT == 2 && BM == 16>(p);
+      whi[r][j] = stream_load<WT == 2 && BM == 16>(p + ws[r].hi_off);
     }
   };
   // Staging.  Loads complete in issue order as far as the wait counter goes,
@@ -388,8 +392,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 #pragma unroll
     for (int j = 0; j < KG; ++j) {  // unconditional: past the row's end the last K block is read again
       const uint8_t* p = ws.p + r * tile_step + (size_t)min(q0 + j, nbb - 1) * ws.kb_stride;
-      wlo[slot][j] = stream_load(p);
-      whi[slot][j] = stream_load(p + ws.hi_off);
+      wlo[slot][j] = stream_load<WT == 2 && BM == 16>(p);
+      whi[slot][j] = stream_load<WT == 2 && BM == 16>(p + ws.hi_off);
     }
   };
   // Staging, in pinned issue order (loads complete in issue order as far as
