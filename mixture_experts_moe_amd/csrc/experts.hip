@@ -43,6 +43,12 @@ namespace moe {
 // -4.5 us per launch.  Taller tiles (XCD schedules) read an expert's weights
 // once per row tile and rely on L2 keeping them between the tiles, so they use
 // ordinary loads.
+// A compile-time integer as a value (register-slot and run selectors).
+template <int N>
+struct Ic {
+  static constexpr int value = N;
+};
+
 template <bool NT>
 __device__ __forceinline__ v4i stream_load(const uint8_t* p) {
   if constexpr (NT) return __builtin_nontemporal_load((const v4i*)p);
@@ -148,7 +154,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
   extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* xs = smem;
   float* sxs = (float*)(smem + (BM + 1) * xstride);     // [BM][d/128] (FP8 only)
-  float* red = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [waves][BM]
+  float* wsc = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [2][d/128] gate, up block scales (FP8 only)
+  float* red = wsc + (WT == 2 ? 2 * (a.d / 128) : 0);   // [waves][BM]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
@@ -172,27 +179,41 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[r][c] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Weight stream: stage = one 16-row tile (r = 0 gate, 1 up) across KG
-  // consecutive K blocks (q-th group); slot r holds tile r, two stages in
-  // flight.  The loop body issues its loads unconditionally (a short last group
-  // re-reads the final K block, in bounds and in cache) and the last group is
-  // peeled, so the memory-counter waits stay exact and nothing is fetched twice
-  // in the steady state.
+  // Weight stream.  Stage = KG consecutive K blocks of one 16-row tile (gate
+  // or up); two register slots, two stages in flight.
+  //  * 16-row tiles (SEQ): the wave reads its gate tile over all of K, then its
+  //    up tile -- one long run after the other streams faster than the two
+  //    interleaved (measured).  Stage st < nq is gate group st, otherwise up
+  //    group st - nq; the slots take alternate stages.
+  //  * Taller tiles: gate and up interleaved, slot 0 = gate, slot 1 = up,
+  //    stage st = (group st / 2, tile st % 2); the sequential order spills there.
+  // The loop bodies issue their loads unconditionally (a short last group
+  // re-reads the final K block, in bounds and in cache) and the last pair of
+  // stages is peeled, so the memory-counter waits stay exact and nothing is
+  // fetched twice in the steady state.  Slots and tiles are template constants
+  // (Ic), so the register arrays are never indexed at run time.
+  constexpr bool SEQ = BM == 16;
   constexpr int KG = MOE_GU_KG;
-  const int nq = (nbb + KG - 1) / KG;
+  const int nq = (nbb + KG - 1) / KG, ns = 2 * nq;
   v4i wlo[2][KG], whi[2][KG];
-  auto load = [&](int r, int q) {
+  auto load = [&](auto S, int st) {
+    constexpr int sl = decltype(S)::value;
+    const bool up = SEQ ? st >= nq : sl == 1;
+    const int q = SEQ ? (up ? st - nq : st) : st / 2;
+    const uint8_t* base = up ? ws[1].p : ws[0].p;
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       const int kb = min(q * KG + j, nbb - 1);
-      const uint8_t* p = ws[r].p + (size_t)kb * ws[r].kb_stride;
-      wlo[r][j] = stream_load<WT == 2 && BM == 16>(p);
-      whi[r][j] = stream_load<WT == 2 && BM == 16>(p + ws[r].hi_off);
+      const uint8_t* p = base + (size_t)kb * ws[0].kb_stride;
+      wlo[sl][j] = stream_load<WT == 2 && BM == 16>(p);
+      whi[sl][j] = stream_load<WT == 2 && BM == 16>(p + ws[0].hi_off);
     }
   };
   // Staging.  Loads complete in issue order as far as the wait counter goes,
   // so the order is pinned: the token of each row this thread stages (perm),
-  // then the weight stream, then the activation rows (which need the tokens).
+  // the activation and weight block scales, then the weight stream, then the
+  // activation rows (which need the tokens).  The scales go to LDS, so the
+  // product loop reads no global memory besides the weight stream.
   // All loads are unconditional (clamped addresses, zero by select) and the
   // chunks past the tile land in a spare LDS row, so the code is straight-line
   // and every wait is exact.  The first batch of SB chunks per thread covers a
@@ -206,12 +227,15 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
     int tk[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / cpr);
-    float sv = 0.f;
-    if (WT == 2 && first) sv = a.sxa[(size_t)row_token(tid / nkb) * nkb + tid % nkb];
+    float sv = 0.f, wv = 0.f;
+    if (WT == 2 && first) {
+      sv = a.sxa[(size_t)row_token(tid / nkb) * nkb + tid % nkb];
+      wv = tid < nkb ? sgp[tid] : sup[min(tid - nkb, nkb - 1)];  // the slice's weight block scales
+    }
     if (first) {
       __builtin_amdgcn_sched_barrier(0);
-      load(0, 0);
-      load(1, 0);
+      load(Ic<0>{}, 0);
+      load(Ic<1>{}, 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     v4i v[SB];
@@ -237,6 +261,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       }
     }
     if (WT == 2 && first && tid < BM * nkb) sxs[tid] = tid / nkb <= rlast ? sv : 0.f;
+    if (WT == 2 && first && tid < 2 * nkb) wsc[tid] = wv;
   };
   stage(tid, true);
   for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
@@ -246,7 +271,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
   }
   __syncthreads();
 
-  auto compute = [&](int r, int q) {
+  auto compute_run = [&](auto R, auto S, int q) {
+    constexpr int r = decltype(R)::value, sl = decltype(S)::value;
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       const int bb = q * KG + j;
@@ -268,26 +294,32 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
             e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
             e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[2], b[3]);
           }
-          const float cs = sxs[(c * 16 + lr) * nbb + bb] * (r == 0 ? sgp[bb] : sup[bb]);
-          acc[r][c] += kblock_e4m3_exact(wlo[r][j], whi[r][j], b) * cs;
+          const float cs = sxs[(c * 16 + lr) * nbb + bb] * wsc[r * nbb + bb];
+          acc[r][c] += kblock_e4m3_exact(wlo[sl][j], whi[sl][j], b) * cs;
         } else {
           const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
           const v4i blo = *(const v4i*)bp;
           const v4i bhi = *(const v4i*)(bp + 64);
-          acc[r][c] = mfma_bf16(wlo[r][j], blo, acc[r][c]);
-          acc[r][c] = mfma_bf16(whi[r][j], bhi, acc[r][c]);
+          acc[r][c] = mfma_bf16(wlo[sl][j], blo, acc[r][c]);
+          acc[r][c] = mfma_bf16(whi[sl][j], bhi, acc[r][c]);
         }
       }
     }
   };
-  for (int q = 0; q + 1 < nq; ++q) {
-    compute(0, q);
-    load(0, q + 1);
-    compute(1, q);
-    load(1, q + 1);
+  auto compute = [&](auto S, int st) {
+    if constexpr (!SEQ) compute_run(S, S, st / 2);
+    else if (st < nq) compute_run(Ic<0>{}, S, st);
+    else compute_run(Ic<1>{}, S, st - nq);
+  };
+  int st = 0;
+  for (; st + 2 < ns; st += 2) {  // ns is even: both loads of the body are in range
+    compute(Ic<0>{}, st);
+    load(Ic<0>{}, st + 2);
+    compute(Ic<1>{}, st + 1);
+    load(Ic<1>{}, st + 3);
   }
-  compute(0, nq - 1);
-  compute(1, nq - 1);
+  compute(Ic<0>{}, st);
+  compute(Ic<1>{}, st + 1);
 
   // Epilogue: h = silu(g) * u for features f0 + 4*(lane/16) + i, row c*16 + lane%16.
   float h[NC][4];
@@ -669,7 +701,7 @@ static bool gateup_x_bf16(int BM, int wmode) { return wmode == 1 || BM <= 16; }
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
   size_t b = (size_t)(BM + 1) * ((gateup_x_bf16(BM, wmode) ? d * 2 : d) + 16);  // plus a spare row
-  if (wmode == 2) b += (size_t)BM * (d / 128) * 4;
+  if (wmode == 2) b += (size_t)BM * (d / 128) * 4 + 2 * (d / 128) * 4;
   return b + kGateUpWaves * BM * 4;
 }
 
@@ -710,7 +742,6 @@ hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipS
   const int nt = kGateUpWaves * 64;
   if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2, true>, grid, lds, st, a, nt);
   if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2, false>, grid, lds, st, a, nt);
-  if (wmode == 2 && BM == 64) return launch_dyn(gateup_mfma_kernel<64, 2, false>, grid, lds, st, a, nt);
   if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1, true>, grid, lds, st, a, nt);
   return hipErrorInvalidValue;
 }
@@ -728,11 +759,9 @@ hipError_t launch_down(const ExpertArgs& a0, int wmode, const Plan& plan, hipStr
   const int RT = down_rows_per_wave(BM, wmode, Fmax, a.d);
   if (wmode == 2 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2>, grid, lds, st, a);
   if (wmode == 2 && RT == 4 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
-  if (wmode == 2 && RT == 4 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 4>, grid, lds, st, a);
   if (RT != 1) return hipErrorInvalidValue;
   if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 1>, grid, lds, st, a);
   if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 1>, grid, lds, st, a);
-  if (wmode == 2 && BM == 64) return launch_dyn(down_mfma_kernel<64, 2, 1>, grid, lds, st, a);
   if (wmode == 1 && BM == 16) return launch_dyn(down_mfma_kernel<16, 1, 1>, grid, lds, st, a);
   return hipErrorInvalidValue;
 }
