@@ -44,7 +44,9 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape or dtype combination */
   MOE_ERR_WORKSPACE = -3,    /* ws_bytes below moe_workspace_bytes() */
   MOE_ERR_HIP = -4,          /* a HIP launch failed */
-  MOE_ERR_FORCED_INDEX = -5  /* (device status) a forced expert id was outside [0, E) */
+  MOE_ERR_FORCED_INDEX = -5, /* (device status) a forced expert id was outside [0, E) */
+  MOE_ERR_DEVICE_SYNC = -6   /* (device status) inside moe_forward, a block's bounded wait for
+                                another block's results ran out; y is not valid */
 } moe_status;
 
 typedef enum {
@@ -115,11 +117,13 @@ typedef struct {
   int32_t *perm;       /* [T * k] perm[q] = p: pairs sorted by expert, ascending p
                           within an expert; entries past offsets[E] are -1 */
   int32_t *inv_perm;   /* [T * k] inv_perm[p] = q, or -1 for an invalid pair */
-  int32_t *status;     /* [1] device status word: MOE_OK or MOE_ERR_FORCED_INDEX */
+  int32_t *status;     /* [1] device status word: MOE_OK, MOE_ERR_FORCED_INDEX (routing)
+                          or MOE_ERR_DEVICE_SYNC (forward) */
   void *plan;          /* moe_plan_bytes() bytes: the dispatch plan the routing call
                           writes for moe_forward (expert-kernel block schedules,
-                          per-row token/weight, and with FP8 weights the activations
-                          as E4M3 codes with per-(token, 128) scales); opaque */
+                          per-row token/weight, with FP8 weights the activations
+                          as E4M3 codes with per-(token, 128) scales, and per-tile
+                          counters the forward's blocks synchronise on); opaque */
 } moe_routing;
 
 /* Workspace bytes needed by moe_route, moe_route_forced and moe_forward for this
@@ -159,7 +163,12 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
  * y = acc rounded to act_dtype (bf16: round to nearest even).
  * `r` must hold the results of moe_route / moe_route_forced for the same shape
  * and x (its plan included; logits, counts, offsets, perm and inv_perm are
- * not read).  y is [T, d] in act_dtype. */
+ * not read).  y is [T, d] in act_dtype.  With FP8 weights in 16-row tiles the
+ * two projections run as one launch whose down blocks wait on per-tile
+ * counters in the plan (reset before the launch ends): a plan serves any
+ * number of forward calls, one at a time; forward calls that overlap on one
+ * plan race.  If such a wait runs out (it cannot when blocks start in order),
+ * *r->status becomes MOE_ERR_DEVICE_SYNC. */
 int moe_forward(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
                 void *ws, size_t ws_bytes, void *stream);
 
@@ -178,8 +187,10 @@ enum {
  * calls.  `events` is NULL or an array of 4 hipEvent_t created by the caller:
  * events[0] is recorded on `stream` before the first stage and events[i] right
  * after stage i (1 = gate/up .. 3 = combine) when that stage is selected, so the
- * interval between two records spans only that stage's kernels.  Unknown stage
- * bits: MOE_ERR_INVALID_ARG. */
+ * interval between two records spans only that stage's kernels.  When gate/up
+ * and down are both selected and run as one launch (see moe_forward), events[1]
+ * and events[2] are both recorded after it.  Unknown stage bits:
+ * MOE_ERR_INVALID_ARG. */
 int moe_forward_stages(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
                        void *ws, size_t ws_bytes, uint32_t stages, void *const *events, void *stream);
 

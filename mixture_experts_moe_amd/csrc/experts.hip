@@ -23,6 +23,7 @@
 // LDS for the whole K loop.
 #include <limits.h>
 
+#include "moe.h"
 #include "moe_device.h"
 #include "moe_kernels.h"
 #include "moe_plan.h"
@@ -101,13 +102,13 @@ struct TileRows {
 
 // The block's schedule record (written by the plan step): its tile's rows and
 // its feature slice.
-__device__ __forceinline__ TileRows block_rows(const ExpertArgs& a, int& slice) {
+__device__ __forceinline__ TileRows block_rows(const ExpertArgs& a, int b, int& slice) {
   int4 rec;
   if (a.per_tile) {
-    rec = a.sched[blockIdx.x / a.nsl];
-    slice = blockIdx.x % a.nsl;
+    rec = a.sched[b / a.nsl];
+    slice = b % a.nsl;
   } else {
-    rec = a.sched[blockIdx.x];
+    rec = a.sched[b];
     slice = rec.w >> 16;
   }
   TileRows r;
@@ -136,22 +137,34 @@ __device__ __forceinline__ TileRows block_rows(const ExpertArgs& a, int& slice) 
 // ---------------------------------------------------------------------------
 constexpr int kGateUpWaves = 8;
 
-template <int BM, int WT, bool XB>
-__global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertArgs a) {
+// Device-coherent 32-bit store and load (agent-scope relaxed atomics: written
+// through to, and read from, the point where all XCDs see the same data), for
+// results one block hands to blocks on other XCDs within one launch.
+__device__ __forceinline__ void store_coherent(void* p, uint32_t v) {
+  __hip_atomic_store((uint32_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_coherent(const void* p) {
+  return __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The work of gate/up block b (smem: the block's dynamic LDS).  Returns false
+// for a block without work.  COH: h codes and scales are stored coherently
+// (the fused expert launch).
+template <int BM, int WT, bool XB, bool COH = false>
+__device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t* smem) {
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;  // bytes per element
   constexpr int NT = kGateUpWaves * 64;
   constexpr bool XBF = WT == 1 || XB;  // activations in LDS as bf16 (else E4M3 codes)
   int nb;
-  const TileRows tr = block_rows(a, nb);
-  if (tr.g < 0) return;
+  const TileRows tr = block_rows(a, b, nb);
+  if (tr.g < 0) return false;
   const int Fg = tr.shared ? a.Fs : a.F;
-  if (nb * 128 >= Fg) return;
+  if (nb * 128 >= Fg) return false;
 
   const int RB = a.d * EB;        // bytes per activation / weight row in HBM
   const int nbb = RB / 128;       // 128-byte K blocks of a weight row
   const int xstride = (XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
-  extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* xs = smem;
   float* sxs = (float*)(smem + (BM + 1) * xstride);     // [BM][d/128] (FP8 only)
   float* wsc = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [2][d/128] gate, up block scales (FP8 only)
@@ -354,9 +367,15 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       const float sc = amax > 0.f ? amax / 448.0f : 1.0f;
       if (rr < tr.rows) {
         const size_t row = (size_t)(hrow0 + rr);
-        *(uint32_t*)(hq + row * a.hstride + fcol) =
-            pack4_e4m3(h[c][0] / sc, h[c][1] / sc, h[c][2] / sc, h[c][3] / sc);
-        if (wave == 0 && lane < 16) a.sh[row * gpr + nb] = sc;
+        const uint32_t hv = pack4_e4m3(h[c][0] / sc, h[c][1] / sc, h[c][2] / sc, h[c][3] / sc);
+        uint8_t* hp = hq + row * a.hstride + fcol;
+        if constexpr (COH) {
+          store_coherent(hp, hv);
+          if (wave == 0 && lane < 16) store_coherent(&a.sh[row * gpr + nb], __float_as_uint(sc));
+        } else {
+          *(uint32_t*)hp = hv;
+          if (wave == 0 && lane < 16) a.sh[row * gpr + nb] = sc;
+        }
       }
     }
   } else {
@@ -373,30 +392,38 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
       }
     }
   }
+  return true;
+}
+
+template <int BM, int WT, bool XB>
+__global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  gateup_block<BM, WT, XB>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
 // Down projection on the matrix cores; epilogue multiplies by the pair's
 // routing weight (1 for the shared expert) and writes the fp32 partial row of
-// pair p (or P + t).  A block takes one tile and one slice of 64*RT output
-// features (see block_rows); wave w owns RT 16-row tiles (features nb*64*RT + w*16*RT + 16 r).
-// RT = 2 for short tiles, RT = 4 for tall ones (a tile's h rows are staged once
-// per 256 features); RT = 1 when a row's K does not fit one stage.
+// pair p (or P + t).  A block of NW waves takes one tile and one slice of
+// NW*16*RT output features (see block_rows); wave w owns RT 16-row tiles
+// (features (nb*NW + w)*16*RT + 16 r).  RT = 2 for short tiles, RT = 4 for
+// tall ones (a tile's h rows are staged once per 256 features); RT = 1 when a
+// row's K does not fit one stage.
 // ---------------------------------------------------------------------------
-template <int BM, int WT, int RT>
-__global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
+template <int BM, int WT, int RT, int NW, bool COH = false>
+__device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* smem) {
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;
   constexpr int KG = RT == 1 ? 10 : 5;  // K blocks requested per stage
+  constexpr int NT = NW * 64;
   int nb;
-  const TileRows tr = block_rows(a, nb);
+  const TileRows tr = block_rows(a, b, nb);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int RB = Fg * EB;          // bytes per h row / W_down row
   const int nbb = RB / 128;
   const int hstride_b = a.hstride * EB;
   const int lstride = Fg * 2 + 16;  // padded LDS row: h as bf16
-  extern __shared__ __align__(16) uint8_t smem[];
   uint8_t* hs = smem;
   float* shs = (float*)(smem + (BM + 1) * lstride);          // [BM][Fg/128] (FP8)
   float* wrow = shs + (WT == 2 ? BM * (Fg / 128) : 0);       // [BM] routing weight
@@ -405,16 +432,18 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
-  const int n0 = (nb * 4 + wave) * 16 * RT;
+  const int n0 = (nb * NW + wave) * 16 * RT;
   const bool wave_live = n0 < a.d;  // d is a multiple of 16*RT here: whole waves are live or not
   const uint8_t* wd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * a.d * RB;
   const int nl = wave_live ? n0 : 0;
   const WeightStream ws = weight_stream(wd, RB, nl, a.w_tiled, lane);
   // 16-row tile r of the wave starts 16*r rows (tiled: r tiles) further on
   const size_t tile_step = a.w_tiled ? (size_t)nbb * 2048 : (size_t)16 * RB;
-  // W_down block scales of the block's 64*RT rows (one or two 128-row scale
+  // W_down block scales of the block's NW*16*RT rows (one or two 128-row scale
   // blocks), staged in LDS with h; the wave's row of them
-  const int nsr = RT == 4 ? 2 : 1, srow0 = nb * 64 * RT / 128;
+  constexpr int nsr = NW * 16 * RT > 128 ? NW * 16 * RT / 128 : 1;
+  static_assert(nsr <= 2, "LDS holds two rows of W_down scales");
+  const int srow0 = nb * NW * 16 * RT / 128;
   const float* sdp = wsd + (nl / 128 - srow0) * (Fg / 128);
   // The weight stream depends only on the tile's expert and feature slice:
   // request it before the h rows are staged.  A stage = KG K blocks of one
@@ -441,21 +470,30 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   const int o = a.ri.prow[hrow0 + min(tid, rlast)];
   float sv = 0.f, dv = 0.f;
   if (WT == 2) {
-    sv = a.sh[(size_t)(hrow0 + min(tid / nkb, rlast)) * gpr + tid % nkb];
+    const float* shp = a.sh + (size_t)(hrow0 + min(tid / nkb, rlast)) * gpr + tid % nkb;
+    sv = COH ? __uint_as_float(load_coherent(shp)) : *shp;
     const float* sd = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)srow0 * nkb;
     dv = sd[min(tid, nsr * nkb - 1)];
   }
   auto stage_load = [&](int i0, v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * 256, r = min(i / cpr, rlast), c = i % cpr;
-      v[u] = *(const v4i*)(hsrc + (size_t)(hrow0 + r) * hstride_b + c * 16);
+      const int i = i0 + u * NT, r = min(i / cpr, rlast), c = i % cpr;
+      const uint8_t* hp = hsrc + (size_t)(hrow0 + r) * hstride_b + c * 16;
+      if constexpr (COH) {  // coherent loads skip the L2: fetch only chunks of live rows
+        v[u] = v4i{0, 0, 0, 0};
+        if (i < nch && i / cpr <= rlast)
+          v[u] = v4i{(int)load_coherent(hp), (int)load_coherent(hp + 4), (int)load_coherent(hp + 8),
+                     (int)load_coherent(hp + 12)};
+      } else {
+        v[u] = *(const v4i*)hp;
+      }
     }
   };
   auto stage_store = [&](int i0, const v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * 256, r = i / cpr, c = i % cpr;
+      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
       const bool live = i < nch && r <= rlast;
       const v4i z = {0, 0, 0, 0};
       const v4i x = live ? v[u] : z;
@@ -478,14 +516,16 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   const float wt = a.ri.w[hrow0 + min(tid, rlast)];
   stage_store(tid, hv);
-  for (int i0 = tid + 256 * SB; i0 < nch; i0 += 256 * SB) {  // tall tiles or wide rows only
+  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) {  // tall tiles or wide rows only
     stage_load(i0, hv);
     stage_store(i0, hv);
   }
   if (WT == 2) {
     if (tid < BM * nkb) shs[tid] = tid / nkb <= rlast ? sv : 0.f;
-    for (int i = tid + 256; i < BM * nkb; i += 256)  // tall tiles or wide rows only
-      shs[i] = i / nkb <= rlast ? a.sh[(size_t)(hrow0 + i / nkb) * gpr + i % nkb] : 0.f;
+    for (int i = tid + NT; i < BM * nkb; i += NT) {  // tall tiles or wide rows only
+      const float* shp = a.sh + (size_t)(hrow0 + min(i / nkb, rlast)) * gpr + i % nkb;
+      shs[i] = i / nkb <= rlast ? (COH ? __uint_as_float(load_coherent(shp)) : *shp) : 0.f;
+    }
     if (tid < nsr * nkb) wsd[tid] = dv;
   }
   if (tid < BM) {
@@ -552,6 +592,74 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
     }
 }
 
+template <int BM, int WT, int RT>
+__global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  down_block<BM, WT, RT, 4>(a, blockIdx.x, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up and down in one launch (FP8 weights, 16-row tiles, tile-list
+// schedule).  Blocks [0, n_gu) do the gate/up work; the rest are 8-wave down
+// blocks (256 output features each).  A gate/up block stores its h codes and
+// scales coherently (agent-scope atomic stores, written through to where every
+// XCD reads them), waits until each of its waves' stores has completed, and
+// then counts itself in ready[tile]; a down block of that tile waits until the
+// count reaches the tile's gate/up slices and reads h and its scales with
+// coherent loads issued after that.  No cache-wide writeback or invalidation
+// is needed: device-scope fences (one L2 writeback or invalidation per block)
+// cost more than the launch gap they remove.  The down blocks start while the
+// last gate/up blocks are still streaming, which fills the launch's last,
+// partly empty round of blocks, and the kernel boundary between the two
+// projections disappears.
+//
+// Forward progress: blocks are dispatched in block order, so every gate/up
+// block a down block waits for was dispatched before it, holds its own slot
+// and never waits itself.  The wait is bounded all the same: past kSpinLimit
+// polls the block sets the routing status word to MOE_ERR_DEVICE_SYNC and goes
+// on (its output is then not valid).  The routing call zeroes ready[] and
+// done[] with the plan; the last down block of a tile zeroes them again, so the
+// plan can serve any number of forward calls (one at a time).
+// ---------------------------------------------------------------------------
+constexpr int kSpinLimit = 1 << 22;  // polls of about 64 cycles each: far beyond any real wait
+
+__global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(ExpertArgs gu, ExpertArgs dn, int n_gu,
+                                                                          int32_t* __restrict__ ready,
+                                                                          int32_t* __restrict__ done,
+                                                                          int32_t* __restrict__ status) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int b = blockIdx.x;
+  if (b < n_gu) {
+    if (gateup_block<16, 2, true, true>(gu, b, smem)) {
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent stores have completed ...
+      __syncthreads();                // ... and so have every other wave's
+      if (threadIdx.x == 0) atomicAdd(&ready[b / gu.nsl], 1);
+    }
+    return;
+  }
+  const int bd = b - n_gu, tile = bd / dn.nsl;
+  const int4 rec = dn.sched[tile];
+  if (rec.x < 0) return;
+  const int need = (rec.x == dn.E ? dn.Fs : dn.F) / 128;  // gate/up slices of the tile
+  if (threadIdx.x == 0) {
+    int polls = 0;
+    while (__hip_atomic_load(&ready[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++polls == kSpinLimit) {
+        *status = MOE_ERR_DEVICE_SYNC;
+        break;
+      }
+    }
+  }
+  __syncthreads();  // h is read below, with coherent loads, after the count was seen
+  down_block<16, 2, 2, kGateUpWaves, true>(dn, bd, smem);
+  __syncthreads();
+  if (threadIdx.x == 0 && atomicAdd(&done[tile], 1) == dn.nsl - 1) {  // the tile's last down block
+    atomicExch(&ready[tile], 0);
+    atomicExch(&done[tile], 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // fp32 expert projections (fp32 activations and weights): plain fp32
 // multiply-add, one output feature per thread.  blockIdx.x = 64-feature slice.
@@ -559,7 +667,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 template <int BM>
 __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
   int sl;
-  const TileRows tr = block_rows(a, sl);
+  const TileRows tr = block_rows(a, blockIdx.x, sl);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int f = sl * 64 + (threadIdx.x & 63);
@@ -596,7 +704,7 @@ __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
 template <int BM>
 __global__ __launch_bounds__(256) void down_f32_kernel(ExpertArgs a) {
   int sl;
-  const TileRows tr = block_rows(a, sl);
+  const TileRows tr = block_rows(a, blockIdx.x, sl);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int n = sl * 64 + (threadIdx.x & 63);
@@ -744,6 +852,32 @@ hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipS
   if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2, false>, grid, lds, st, a, nt);
   if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1, true>, grid, lds, st, a, nt);
   return hipErrorInvalidValue;
+}
+
+bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d) {
+  return wmode == 2 && plan.BM == 16 && !plan.xcd && plan.sync && down_rows_per_wave(16, 2, Fmax, d) == 2 &&
+         d % (kGateUpWaves * 32) == 0;
+}
+
+hipError_t launch_experts_fused(const ExpertArgs& a0, const Plan& plan, int32_t* status, hipStream_t st) {
+  ExpertArgs gu = a0, dn = a0;
+  gu.sched = dn.sched = plan.sched[0];
+  gu.per_tile = dn.per_tile = 1;
+  gu.nsl = plan.n_slices[0];
+  dn.nsl = a0.d / (kGateUpWaves * 32);  // 8 waves x 2 tiles x 16 features per down block
+  const int Fmax = a0.F > a0.Fs ? a0.F : a0.Fs;
+  const int n_gu = plan.max_tiles * gu.nsl, n_dn = plan.max_tiles * dn.nsl;
+  size_t lds = gateup_lds_bytes(16, 2, a0.d);
+  const size_t ldn = down_lds_bytes(16, 2, Fmax);
+  if (ldn > lds) lds = ldn;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)experts_fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  experts_fused_kernel<<<n_gu + n_dn, kGateUpWaves * 64, lds, st>>>(gu, dn, n_gu, plan.sync,
+                                                                     plan.sync + plan.max_tiles, status);
+  return hipGetLastError();
 }
 
 hipError_t launch_down(const ExpertArgs& a0, int wmode, const Plan& plan, hipStream_t st) {

@@ -20,7 +20,7 @@ struct Layout {
 // Segments of the dispatch plan (moe_routing.plan), written by the routing call
 // and read by the forward call.
 struct PlanLayout {
-  size_t sched_gu, sched_dn, rinfo, xq, sx, total;
+  size_t sched_gu, sched_dn, rinfo, xq, sx, sync, total;
 };
 
 int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
@@ -76,6 +76,7 @@ PlanLayout plan_layout(const moe_shape& s) {
   L.rinfo = seg((P + T) * 12);
   L.xq = seg(fp8 ? T * d : 0);
   L.sx = seg(fp8 ? T * (d / 128) * 4 : 0);
+  L.sync = seg(2 * mt * 4);  // per tile: gate/up slices done, down blocks done (fused expert launch)
   L.total = o;
   return L;
 }
@@ -149,6 +150,7 @@ PlanView plan_view(const moe_shape& s, void* plan_buf) {
     for (int i = 0; i < 2; ++i) v.plan.n_sched[i] = v.plan.max_tiles * v.plan.n_slices[i];
   v.plan.sched[0] = (int4*)(base + pl.sched_gu);
   v.plan.sched[1] = (int4*)(base + pl.sched_dn);
+  v.plan.sync = v.plan.xcd ? nullptr : (int32_t*)(base + pl.sync);
   v.ri.tok = (int32_t*)(base + pl.rinfo);
   v.ri.prow = v.ri.tok + (P + s.T);
   v.ri.w = (float*)(v.ri.prow + (P + s.T));
@@ -205,6 +207,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
     pc.pa.n_slices[i] = v.plan.n_slices[i];
   }
   pc.pa.max_tiles = v.plan.max_tiles;
+  pc.pa.sync = v.plan.sync;
   pc.ri = v.ri;
   pc.x = (const uint16_t*)x;
   pc.xq = v.xq;
@@ -306,12 +309,19 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
     if (events && e == hipSuccess) e = hipEventRecord((hipEvent_t)events[i], st);
   };
   const moe::Plan& plan = v.plan;
+  const int Fmax = a.F > a.Fs ? a.F : a.Fs;
+  const bool fused = (stages & MOE_STAGE_GATE_UP) && (stages & MOE_STAGE_DOWN) && r->status &&
+                     moe::experts_fusable(shape->w_dtype, plan, Fmax, d);
   mark(0);
-  if (stages & MOE_STAGE_GATE_UP) {
+  if (fused) {  // both projections in one launch: events 1 and 2 mark its end
+    e = moe::launch_experts_fused(a, plan, r->status, st);
+    mark(1);
+    mark(2);
+  } else if (stages & MOE_STAGE_GATE_UP) {
     e = moe::launch_gateup(a, shape->w_dtype, plan, st);
     mark(1);
   }
-  if (e == hipSuccess && (stages & MOE_STAGE_DOWN)) {
+  if (e == hipSuccess && !fused && (stages & MOE_STAGE_DOWN)) {
     e = moe::launch_down(a, shape->w_dtype, plan, st);
     mark(2);
   }
@@ -353,6 +363,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace smaller than moe_workspace_bytes()";
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
     case MOE_ERR_FORCED_INDEX: return "MOE_ERR_FORCED_INDEX: a forced expert id was outside [0, n_experts)";
+    case MOE_ERR_DEVICE_SYNC: return "MOE_ERR_DEVICE_SYNC: a forward block's wait for another block timed out";
     default: return "unknown moe status";
   }
 }

@@ -27,6 +27,7 @@ struct PlanArgs {
   int n_sched[2];          // blocks of each kernel
   int n_slices[2];
   int max_tiles;           // entries of the tile list
+  int32_t* sync;           // [2][max_tiles] tile-list schedules: counters of the fused expert launch, zeroed here
 };
 
 // Where the routing call's last launch writes the dispatch plan, and the
@@ -99,11 +100,15 @@ struct Plan {
   int n_sched[2];   // blocks of each kernel
   int n_slices[2];  // feature slices per tile
   int max_tiles;
+  int32_t* sync;    // [2][max_tiles] per-tile counters (tile-list schedules only, else null)
 };
 int down_rows_per_wave(int BM, int wmode, int Fmax, int d);
 void plan_sizes(int wmode, int BM, int max_tiles, int Fmax, int d, int& nsl_gu, int& nsl_dn, int& n_gu, int& n_dn);
 hipError_t launch_gateup(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
 hipError_t launch_down(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
+// Gate/up and down as one launch (FP8 weights, 16-row tiles, tile-list plan).
+bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d);
+hipError_t launch_experts_fused(const ExpertArgs& a, const Plan& plan, int32_t* status, hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
                                hipStream_t st);
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,

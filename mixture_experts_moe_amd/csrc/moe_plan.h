@@ -14,6 +14,8 @@
 //    partial-output row and routing weight.
 //  * With FP8 weights, the activations as E4M3 codes with per-(token, 128)
 //    scales.
+//  * For tile-list plans, two counters per tile that the fused expert launch
+//    synchronises on (zeroed here; the launch leaves them zero).
 #pragma once
 
 #include "moe_device.h"
@@ -83,6 +85,7 @@ __device__ int plan_tables(const PlanArgs& pa, PlanLds& L) {
 // Tile-list entry t (identity schedules) of a plan with `total` tiles.
 __device__ __forceinline__ void plan_tile_entry(const PlanArgs& pa, const PlanLds& L, int total, int t) {
   if (t >= pa.max_tiles) return;
+  if (pa.sync) pa.sync[t] = pa.sync[pa.max_tiles + t] = 0;
   int4 rec = make_int4(-1, 0, 0, 0);
   if (t < total) {
     const int G = pa.E + (pa.has_shared ? 1 : 0);
@@ -159,6 +162,8 @@ __device__ void plan_scatter(const PlanArgs& pa, const PlanLds& L, int total) {
         pa.sched[0][t0 + j] = make_int4(g, j * BM, L.gh0[g] + j * BM, min(BM, L.grow[g] - j * BM));
     }
     for (int t = total + threadIdx.x; t < pa.max_tiles; t += NT) pa.sched[0][t] = make_int4(-1, 0, 0, 0);
+    if (pa.sync)
+      for (int t = threadIdx.x; t < 2 * pa.max_tiles; t += NT) pa.sync[t] = 0;
     return;
   }
   for (int which = 0; which < 2; ++which) {

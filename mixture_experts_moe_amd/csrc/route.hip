@@ -36,17 +36,36 @@ namespace moe {
 // x and W_r; only the summation order differs from a scalar loop.
 // ---------------------------------------------------------------------------
 
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// The split of two weights at once: each bf16 rounding (to nearest even) is
+// one packed conversion of the pair, the remainders exact fp32 differences.
+// Results as packed pairs (element 0 in the low half).
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+  const v2f w = {a, b};
+  const v2bf h = __builtin_convertvector(w, v2bf);
+  const v2f r1 = w - __builtin_convertvector(h, v2f);
+  const v2bf m = __builtin_convertvector(r1, v2bf);
+  const v2f r2 = r1 - __builtin_convertvector(m, v2f);
+  hi = __builtin_bit_cast(uint32_t, h);
+  mid = __builtin_bit_cast(uint32_t, m);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r2, v2bf));
+}
+
 __device__ __forceinline__ void split3_bf16(const float (&w)[8], v8bf& hi, v8bf& mid, v8bf& lo) {
+  v4i h, m, l;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 h = (__bf16)w[j];
-    const float r1 = w[j] - (float)h;
-    const __bf16 m = (__bf16)r1;
-    const float r2 = r1 - (float)m;
-    hi[j] = h;
-    mid[j] = m;
-    lo[j] = (__bf16)r2;
+  for (int j = 0; j < 4; ++j) {
+    uint32_t a, b, c;
+    split3_pair(w[2 * j], w[2 * j + 1], a, b, c);
+    h[j] = (int)a;
+    m[j] = (int)b;
+    l[j] = (int)c;
   }
+  hi = __builtin_bit_cast(v8bf, h);
+  mid = __builtin_bit_cast(v8bf, m);
+  lo = __builtin_bit_cast(v8bf, l);
 }
 
 // Router partial logits for short inputs, split along K: block (16 experts,
@@ -118,7 +137,9 @@ __global__ __launch_bounds__(256) void router_split_kernel(const uint16_t* __res
 
 // ---------------------------------------------------------------------------
 // Router partial logits for long inputs (bf16 x): tiles of 64 tokens x 64
-// experts, 4 waves of 32 x 32, over one half of the K range (blockIdx.z): the
+// experts over one half of the K range (blockIdx.z), NW waves: 8 waves of 32
+// tokens x 16 experts for 64-deep chunks, 4 waves of 32 x 32 for 32-deep ones
+// (so every thread stages one piece of x and two of W per chunk); the
 // halves split at slice gsl (256-deep slices, the same boundary the top-k
 // kernel uses; one half when there is a single slice).  Both operands are staged in LDS per chunk of 32*NS K (two LDS
 // buffers, the chunk after next prefetched into registers); the fp32 weights
@@ -127,15 +148,19 @@ __global__ __launch_bounds__(256) void router_split_kernel(const uint16_t* __res
 // order into a slice, the half's slices added in order -- the K-split kernel's
 // order, so both kernels give the same logits bit for bit.
 // ---------------------------------------------------------------------------
-template <int NS>
-__global__ __launch_bounds__(256) void router_tile_kernel(const uint16_t* __restrict__ x, const float* __restrict__ W,
-                                                          float* __restrict__ part, int T, int d, int E, int gsl,
-                                                          int32_t* __restrict__ status) {
+template <int NS, int NW>
+__global__ __launch_bounds__(NW * 64) void router_tile_kernel(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ W, float* __restrict__ part,
+                                                              int T, int d, int E, int gsl,
+                                                              int32_t* __restrict__ status) {
   constexpr int TT = 64, TE = 64, KC = 32 * NS;  // tile, K per chunk
+  constexpr int NT = NW * 64;                      // threads
+  constexpr int IT = 8 / NW;                       // 16-expert tiles per wave (waves: 2 along tokens)
   constexpr int XS = KC * 2 + 16;                  // LDS row stride (bytes), padded
   constexpr int XP = TT * KC / 8;                  // x pieces (8 bf16) per chunk
   constexpr int WP = TE * KC / 4;                  // W pieces (4 fp32) per chunk
-  constexpr int PX = XP / 256, PW = WP / 256;      // per thread
+  constexpr int PX = XP / NT, PW = WP / NT;        // per thread
+  static_assert(PX * NT == XP && PW * NT == WP && IT * 16 * (NW / 2) == TE, "tile shape");
   __shared__ __align__(16) uint8_t xs[2][TT * XS];
   __shared__ __align__(16) uint8_t wsm[2][3 * TE * XS];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, kg = lane >> 4;
@@ -152,71 +177,56 @@ __global__ __launch_bounds__(256) void router_tile_kernel(const uint16_t* __rest
     const int k0 = ch * KC;
 #pragma unroll
     for (int u = 0; u < PX; ++u) {
-      const int i = tid + u * 256, r = i / (KC / 8), c = i % (KC / 8), t = min(t0 + r, T - 1);
+      const int i = tid + u * NT, r = i / (KC / 8), c = i % (KC / 8), t = min(t0 + r, T - 1);
       p.xv[u] = *(const v4i*)(x + (size_t)t * d + k0 + c * 8);
     }
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
-      const int i = tid + u * 256, r = i / (KC / 4), c = i % (KC / 4), e = min(e0 + r, E - 1);
+      const int i = tid + u * NT, r = i / (KC / 4), c = i % (KC / 4), e = min(e0 + r, E - 1);
       p.wv[u] = *(const float4*)(W + (size_t)e * d + k0 + c * 4);
     }
   };
   auto store = [&](int buf, const Pre& p) {
+    // Rows past T or E hold a clamped copy of the last row (fetch); the
+    // outputs they feed are never stored, so they need no zeroing.
 #pragma unroll
     for (int u = 0; u < PX; ++u) {
-      const int i = tid + u * 256, r = i / (KC / 8), c = i % (KC / 8);
-      const v4i z = {0, 0, 0, 0};
-      *(v4i*)(xs[buf] + r * XS + c * 16) = t0 + r < T ? p.xv[u] : z;
+      const int i = tid + u * NT, r = i / (KC / 8), c = i % (KC / 8);
+      *(v4i*)(xs[buf] + r * XS + c * 16) = p.xv[u];
     }
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
-      const int i = tid + u * 256, r = i / (KC / 4), c = i % (KC / 4);
-      const bool live = e0 + r < E;
-      uint16_t h[3][4];
-      const float w4[4] = {p.wv[u].x, p.wv[u].y, p.wv[u].z, p.wv[u].w};
+      const int i = tid + u * NT, r = i / (KC / 4), c = i % (KC / 4);
+      uint2 pk[3];
+      split3_pair(p.wv[u].x, p.wv[u].y, pk[0].x, pk[1].x, pk[2].x);
+      split3_pair(p.wv[u].z, p.wv[u].w, pk[0].y, pk[1].y, pk[2].y);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {  // the split of split3_bf16, element by element
-        const float w = live ? w4[j] : 0.f;
-        const __bf16 hi = (__bf16)w;
-        const float r1 = w - (float)hi;
-        const __bf16 mi = (__bf16)r1;
-        const __bf16 lo = (__bf16)(r1 - (float)mi);
-        h[0][j] = __builtin_bit_cast(uint16_t, hi);
-        h[1][j] = __builtin_bit_cast(uint16_t, mi);
-        h[2][j] = __builtin_bit_cast(uint16_t, lo);
-      }
-#pragma unroll
-      for (int sp = 0; sp < 3; ++sp) {
-        uint2 pk;
-        pk.x = (uint32_t)h[sp][0] | ((uint32_t)h[sp][1] << 16);
-        pk.y = (uint32_t)h[sp][2] | ((uint32_t)h[sp][3] << 16);
-        *(uint2*)(wsm[buf] + (sp * TE + r) * XS + c * 8) = pk;
-      }
+      for (int sp = 0; sp < 3; ++sp) *(uint2*)(wsm[buf] + (sp * TE + r) * XS + c * 8) = pk[sp];
     }
   };
-  v4f tot[2][2], sl[2][2];
+  v4f tot[IT][2], sl[IT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) tot[i][j] = sl[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   auto compute = [&](int buf, int ch) {
-    v4f cc[2][2];
+    v4f cc[IT][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) cc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < NS; ++u) {  // 32-deep steps; lane holds K = 32u + 8*kg + [0, 8)
-      v8bf b[2], a[3][2];
+      v8bf b[2], a[3][IT];
 #pragma unroll
       for (int j = 0; j < 2; ++j) b[j] = *(const v8bf*)(xs[buf] + (wt * 32 + j * 16 + lr) * XS + u * 64 + kg * 16);
 #pragma unroll
       for (int sp = 0; sp < 3; ++sp)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          a[sp][i] = *(const v8bf*)(wsm[buf] + (sp * TE + we * 32 + i * 16 + lr) * XS + u * 64 + kg * 16);
+        for (int i = 0; i < IT; ++i)
+          a[sp][i] = *(const v8bf*)(wsm[buf] + (sp * TE + we * 16 * IT + i * 16 + lr) * XS + u * 64 + kg * 16);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < IT; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][i], b[j], cc[i][j], 0, 0, 0);
@@ -226,39 +236,44 @@ __global__ __launch_bounds__(256) void router_tile_kernel(const uint16_t* __rest
     }
     const int q = (ch - c0) % cps, slice = (ch - c0) / cps;  // chunk -> slice -> half total
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < IT; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         sl[i][j] = q == 0 ? cc[i][j] : sl[i][j] + cc[i][j];
         if (q == cps - 1) tot[i][j] = slice == 0 ? sl[i][j] : tot[i][j] + sl[i][j];
       }
   };
-  // two register sets in a ring: the chunk after next is in flight during a
-  // chunk's products.  The chunk count is even; past the end the last chunk is
-  // fetched again (in bounds, never used), so the code stays branch-free.
-  Pre pa, pb;
-  fetch(c0, pa);
-  fetch(c0 + 1, pb);
-  store(0, pa);
+  // Four register sets in a ring: while chunk ch is multiplied (LDS buffer
+  // ch % 2), chunk ch + 1 is moved from registers to the other buffer and chunks
+  // ch + 2 and ch + 3 are in flight, so a load has two chunks of products to
+  // arrive.  Each half is a whole number of 4-chunk slices, so the loop is
+  // unrolled by 4 and every ring index is a constant; past the end the last
+  // chunk is fetched again (in bounds, never used) and the code stays
+  // branch-free.
+  Pre pr[4];
+  fetch(c0, pr[0]);
+  fetch(c0 + 1, pr[1]);
+  fetch(c0 + 2, pr[2]);
+  store(0, pr[0]);
   __syncthreads();
-  for (int ch = c0; ch < c1; ch += 2) {
-    fetch(min(ch + 2, c1 - 1), pa);
-    store(1, pb);
-    compute(0, ch);
-    __syncthreads();
-    fetch(min(ch + 3, c1 - 1), pb);
-    store(0, pa);
-    compute(1, ch + 1);
-    __syncthreads();
+  for (int ch = c0; ch < c1; ch += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      fetch(min(ch + u + 3, c1 - 1), pr[(u + 3) & 3]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the new loads ahead of the waits for older ones
+      store((u + 1) & 1, pr[(u + 1) & 3]);
+      compute(u & 1, ch + u);
+      __syncthreads();
+    }
   }
   float* out = part + (size_t)half * T * E;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < IT; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int e = e0 + we * 32 + i * 16 + 4 * kg + r, t = t0 + wt * 32 + j * 16 + lr;
+        const int e = e0 + we * 16 * IT + i * 16 + 4 * kg + r, t = t0 + wt * 32 + j * 16 + lr;
         if (e < E && t < T) out[(size_t)t * E + e] = tot[i][j][r];
       }
 }
@@ -825,11 +840,11 @@ static hipError_t launch_router(const RouteLaunch& L, hipStream_t st, const floa
     const int ksl = router_kslice(L.d), ns = L.d / ksl, halves = ns > 1 ? 2 : 1;
     const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64, halves);
     if (ksl == 256)
-      router_tile_kernel<2><<<grid, 256, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
-                                                  (ns + 1) / 2, L.status);
+      router_tile_kernel<2, 8><<<grid, 512, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
+                                                     (ns + 1) / 2, L.status);
     else
-      router_tile_kernel<1><<<grid, 256, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
-                                                  (ns + 1) / 2, L.status);
+      router_tile_kernel<1, 4><<<grid, 256, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
+                                                     (ns + 1) / 2, L.status);
     part = L.rpart;
     n_parts = halves;
     gs = 1;

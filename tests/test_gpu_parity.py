@@ -415,6 +415,33 @@ def test_forward_stages_match_forward():
         b.forward(8)
 
 
+def test_forward_repeats_on_one_plan():
+    """With FP8 weights in 16-row tiles the two projections run as one launch
+    that synchronises on per-tile counters in the plan and leaves them at zero:
+    one routing call serves repeated forward calls and any split of the stages,
+    bitwise, and the status word stays MOE_OK."""
+    inp = synth.make_inputs("decode_t32")
+    s = inp["shape"]
+    say("decode_t32: five forward calls on one plan (whole, whole, and three stage splits)")
+    shape = moe.shape_of(s)
+    dev = gpu_inputs(inp)
+    r = moe.alloc_routing(shape, DEV)
+    ws = moe.alloc_workspace(shape, DEV)
+    moe.route(shape, dev, dev["x"], r, ws)
+    G, D, C = moe.STAGE_GATE_UP, moe.STAGE_DOWN, moe.STAGE_COMBINE
+    ys = []
+    for seq in ([G | D | C], [G | D | C], [G | D, C], [G, D | C], [G | D | C]):
+        y = torch.full((s.T, s.d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        b = moe.Bound(shape, dev, dev["x"], r, y, ws)
+        for st in seq:
+            b.forward(st)
+        ys.append(y)
+    torch.cuda.synchronize()
+    assert r.status.item() == 0
+    for y in ys[1:]:
+        assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+
+
 # ------------------------------------------------------------------ tiled weight layout
 
 def test_pack_weights_layout():
