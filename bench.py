@@ -10,10 +10,12 @@ timed region) and rotate over several device copies so every step streams
 them from HBM rather than from the 256 MB last-level cache.
 
 Prints one JSON line.  `value` is tokens/s of the whole step; `roofline` is
-for the dominant kernel (the grouped gate/up projection), from its average
-launch duration (back-to-back launches between two HIP events on the stream it
-runs on); `stage_us` attributes the step to its stages with events between
-them, which add a few microseconds each; `cpu_baseline` is
+for the dominant kernel (at decode the fused expert kernel: grouped gate/up,
+SwiGLU and down projections in one launch), from its average launch duration
+(back-to-back launches between two HIP events on the stream it runs on);
+`stage_us` attributes the step to its stages with events between them, which
+add a few microseconds each (with the fused kernel, `gate_up` holds both
+projections and `down` is empty); `cpu_baseline` is
 the CPU oracle timed on a bounded sample of the same workload.
 """
 import argparse
@@ -43,16 +45,16 @@ DESCRIPTION = {
 }
 FORCED = {"prefill_t2048"}
 
-# HBM bytes per launch of the gate/up kernel on the default workload, from two
+# HBM bytes per launch of the fused expert kernel on the default workload, from two
 # rocprofv3 --pmc passes over this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch), each scaled by what the counter reads for the 480 MiB weight copies
 # the same run makes (fetch x2.0, write x1.0).  Valid only for the kernel sources
 # they were taken on: any change to them makes `traffic` null until re-measured.
 KERNEL_SOURCES = ("mixture_experts_moe_amd/csrc/experts.hip", "mixture_experts_moe_amd/csrc/moe_device.h",
                   "mixture_experts_moe_amd/csrc/moe_kernels.h", "mixture_experts_moe_amd/csrc/moe_api.hip")
-TRAFFIC = {  # workload -> counters of the gate/up kernel, tiled layout
-    "decode_t32": {"sources_sha256": "49e06e769c5a0ec4d4488c472de2b46737d3af329e373da674d8ea2427d69318",
-                   "fetch_bytes": 404783787, "write_bytes": 174867},
+TRAFFIC = {  # workload -> counters of the fused expert kernel, tiled layout
+    "decode_t32": {"sources_sha256": "936b7d4ce75e3fb3e689bbe8285bace5859e373fa515b68579dca03b599a7d32",
+                   "fetch_bytes": 607309919, "write_bytes": 2227087},
 }
 
 
@@ -163,20 +165,23 @@ def run_workload(name, steps, warmup, rotate, layout):
     per_step = np.array([ev[i][0].elapsed_time(ev[i][5]) for i in range(steps)]) * 1e3
     pct = {f"p{q}": float(np.percentile(per_step, q)) for q in (10, 50, 90)}
 
-    # launch duration of the dominant kernel: back-to-back launches of the
-    # gate/up stage (one kernel) on the routing above, rotating over the weight
-    # copies, between two events on the same stream.  The stage events above add
-    # a few microseconds to each stage; this is the figure rocprofv3 reports.
+    # launch duration of the expert projections (gate/up + down: one fused
+    # kernel for FP8 weights in 16-row tiles, e.g. decode; two kernels
+    # otherwise): back-to-back launches on the routing above, rotating over the
+    # weight copies, between two events on the same stream.  The stage events
+    # above add a few microseconds to each stage; this is the figure rocprofv3
+    # reports for the kernel.
     n_l = max(20, steps // 2)
+    experts = moe.STAGE_GATE_UP | moe.STAGE_DOWN
     for i in range(3):
-        bound[i % len(bound)].forward(moe.STAGE_GATE_UP)
+        bound[i % len(bound)].forward(experts)
     l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     l0.record(st)
     for i in range(n_l):
-        bound[i % len(bound)].forward(moe.STAGE_GATE_UP)
+        bound[i % len(bound)].forward(experts)
     l1.record(st)
     torch.cuda.synchronize()
-    stage_us["gate_up_launch"] = l0.elapsed_time(l1) * 1e3 / n_l
+    stage_us["experts_launch"] = l0.elapsed_time(l1) * 1e3 / n_l
     counts = r.counts.cpu().numpy()
     assert r.status.item() == 0
     return s, wall, stage_us, algorithmic(s, counts), counts, pct
@@ -217,8 +222,8 @@ def main():
         sys.exit(1)
     s, wall, st_us, alg, counts, pct = run_workload(a.workload, a.steps, a.warmup, a.rotate, a.layout)
     t_step = wall
-    gu_s = st_us["gate_up_launch"] * 1e-6
-    achieved = alg["gateup_bytes"] / gu_s / 1e9
+    ex_bytes = alg["gateup_bytes"] + alg["down_bytes"]
+    achieved = ex_bytes / (st_us["experts_launch"] * 1e-6) / 1e9
     out = {
         "metric": METRIC, "value": s.T / t_step, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": t_step * 1e3, "higher_is_better": True, "scaling": "weak",
@@ -226,10 +231,12 @@ def main():
         "config": {"workload": f"{a.workload}: {DESCRIPTION[a.workload]}", "T": s.T, "d_model": s.d,
                    "n_experts": s.E, "top_k": s.k, "d_ffn": s.F, "d_ffn_shared": s.Fs,
                    "weight_copies_rotated": a.rotate, "weight_layout": a.layout},
-        "roofline": {"bound": "hbm", "kernel": "gateup_mfma_kernel (grouped gate/up + SwiGLU + h quantisation)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "experts_fused_kernel (grouped gate/up + SwiGLU + h quantisation + down x routing "
+                               "weight, one launch)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": measured_traffic(a.workload) if a.layout == "tiled" else None,
-                     "bytes_per_launch": alg["gateup_bytes"], "avg_launch_us": st_us["gate_up_launch"]},
+                     "bytes_per_launch": ex_bytes, "avg_launch_us": st_us["experts_launch"]},
         "stage_us": st_us,
         "step_us_event_percentiles": pct,
         "step_roofline": {"B_alg_bytes": alg["B_alg"], "distinct_experts": alg["U"],
@@ -244,7 +251,8 @@ def main():
                                                            a.rotate, a.layout)
         extra[name] = {"tokens_per_s": s2.T / wall2, "ms_per_step": wall2 * 1e3, "stage_us": st2,
                        "step_us_event_percentiles": pct2,
-                       "gateup_GBs": alg2["gateup_bytes"] / (st2["gate_up_launch"] * 1e-6) / 1e9,
+                       "experts_GBs": (alg2["gateup_bytes"] + alg2["down_bytes"]) / (st2["experts_launch"] * 1e-6)
+                       / 1e9,
                        "hbm_frac": alg2["B_alg"] / wall2 / (HBM_PEAK_GBS * 1e9),
                        "fp8_mfma_frac": alg2["F_mm"] / wall2 / (FP8_PEAK_TFLOPS * 1e12),
                        "roofline_frac": max(alg2["B_alg"] / (HBM_PEAK_GBS * 1e9),
