@@ -26,6 +26,9 @@ per-layer inputs):
                     is an exact multiple of 1/64 and top-k ties are common.
 * ``ties_t256_bf16w`` the same, with bf16 expert weights rounded from the
                     same base draws instead of FP8 codes.
+* ``decode_t32_w8a16`` the decode batch with the same FP8 weights used as
+                    W8A16: activations enter both projections in bf16,
+                    unquantised.
 
 Per-layer shapes are the large Kolibri-style layer of "We Ported Aleph
 Alpha's Kolibri to a MacBook. Our Own Gate Said No." (section "The gate":
@@ -53,7 +56,7 @@ class LayerShape:
     F: int
     Fs: int
     act: str  # "f32" | "bf16"
-    w: str  # "f32" | "bf16" | "fp8"
+    w: str  # "f32" | "bf16" | "fp8" | "fp8a16" (the same FP8 weights, activations not quantised)
 
     @property
     def P(self) -> int:
@@ -70,6 +73,7 @@ CASES = {
     "prefill_t2048": ("big", 2048, "bf16", "fp8", "normal", "normal", False),
     "skew_t8192": ("big", 8192, "bf16", "fp8", "normal", "normal", True),
     "ties_t256": ("big", 256, "bf16", "fp8", "int3", "grid64", False),
+    "decode_t32_w8a16": ("big", 32, "bf16", "fp8a16", "normal", "normal", False),
     "ties_t256_bf16w": ("big", 256, "bf16", "bf16", "int3", "grid64", False),
 }
 
@@ -212,7 +216,7 @@ def make_inputs(case: str, T: int | None = None, seed: int = 0) -> dict:
         sel_bias = (-1.1 * np.log(ranks.astype(np.float64))).astype(np.float32)
 
     out = dict(shape=shape, x=x, w_router=np.ascontiguousarray(w_router), sel_bias=sel_bias)
-    out.update(_expert_weights(layer, seed, w_dtype))
+    out.update(_expert_weights(layer, seed, "fp8" if w_dtype == "fp8a16" else w_dtype))
     return out
 
 

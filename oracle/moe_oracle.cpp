@@ -71,7 +71,11 @@ enum Mutant {
 int g_mutant = MUT_NONE;
 
 enum { ACT_F32 = 0, ACT_BF16 = 1 };
-enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2 };
+// W_FP8_A16: the same FP8 weights (codes and 128x128 block scales), with the
+// activations entering both projections unquantised (W8A16): the CPU runtime of
+// [cache] decodes the FP8 weights and runs its matmuls on the activations as
+// they are.  Neither x nor h is quantised; everything else is as for W_FP8.
+enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP8_A16 = 3 };
 enum { OK = 0, ERR_INVALID = -1, ERR_FORCED_INDEX = -5 };
 
 // ---- number formats --------------------------------------------------------
@@ -145,7 +149,7 @@ float quant_group(const float* v, int n, float* deq) {
 struct Shape {
   int32_t T, d, E, k, F, Fs;
   int32_t act_dtype;  // ACT_F32 | ACT_BF16
-  int32_t w_dtype;    // W_F32 | W_BF16 | W_FP8
+  int32_t w_dtype;    // W_F32 | W_BF16 | W_FP8 | W_FP8_A16
 };
 
 struct Weights {
@@ -258,7 +262,9 @@ void activation_row(const Shape& s, const void* x, int t, float* row) {
 
 int check_shape(const Shape* s) {
   if (!s || s->T < 0 || s->d <= 0 || s->E <= 0 || s->k < 1 || s->k > s->E || s->F <= 0 || s->Fs < 0) return ERR_INVALID;
-  if (s->w_dtype == W_FP8 && (s->d % 128 || s->F % 128 || s->Fs % 128)) return ERR_INVALID;
+  if (s->w_dtype < W_F32 || s->w_dtype > W_FP8_A16) return ERR_INVALID;
+  if ((s->w_dtype == W_FP8 || s->w_dtype == W_FP8_A16) && (s->d % 128 || s->F % 128 || s->Fs % 128))
+    return ERR_INVALID;
   return OK;
 }
 

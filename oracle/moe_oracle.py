@@ -14,7 +14,7 @@ import numpy as np
 from . import build as _build
 
 ACT = {"f32": 0, "bf16": 1}
-WDT = {"f32": 0, "bf16": 1, "fp8": 2}
+WDT = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3}
 OK, ERR_INVALID, ERR_FORCED_INDEX = 0, -1, -5
 
 MUTANTS = {

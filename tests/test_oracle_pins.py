@@ -483,3 +483,60 @@ def test_skew_workload_is_skewed():
     _, _, idx, _ = O.route(L, tok)
     counts = np.bincount(idx.ravel(), minlength=384)
     assert counts.max() > 10 * counts.mean()
+
+
+# ---------------------------------------------------------------- W8A16 (FP8 weights, bf16 activations)
+
+def _small_fp8_layer(w_mode, T=16, seed=7):
+    """A small layer with block-scaled E4M3 weights (d=256, E=8, k=2, F=Fs=128),
+    as the given weight mode: "fp8" / "fp8a16" (codes and scales) or "f32"
+    (the same weights decoded by torch: decode(code) * scale in fp32)."""
+    rng = np.random.default_rng(seed)
+    d, E, k, F, Fs = 256, 8, 2, 128, 128
+    x = synth.bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    inp = dict(shape=synth.LayerShape(T=T, d=d, E=E, k=k, F=F, Fs=Fs, act="bf16", w=w_mode),
+               x=x, w_router=(rng.standard_normal((E, d), dtype=np.float32) * 0.05).astype(np.float32),
+               sel_bias=None)
+    for pre, sp, dims, n in (("w_", "s_", (F, d, d, F), E), ("sh_", "ss_", (Fs, d, d, Fs), None)):
+        for name, (r, c) in (("gate", dims[:2]), ("up", dims[:2]), ("down", dims[2:])):
+            ws = [rng.standard_normal((r, c), dtype=np.float32) * np.float32(0.02) for _ in range(n or 1)]
+            blocks = [synth._fp8_blocks(w) for w in ws]
+            if w_mode == "f32":
+                vals = [_dequant_weight(cq, sq) for cq, sq in blocks]
+                inp[pre + name] = np.stack(vals) if n else vals[0]
+            else:
+                inp[pre + name] = np.stack([b[0] for b in blocks]) if n else blocks[0][0]
+                inp[sp + name] = np.stack([b[1] for b in blocks]) if n else blocks[0][1]
+    return inp, O.Layer(inp)
+
+
+def test_w8a16_equals_f32_mode_on_decoded_weights():
+    """W8A16 is the FP8 weights' exact values, unquantised activations and h:
+    bitwise the oracle's fp32-weight mode run on the same weights decoded by
+    torch (each element decode(code) * scale, one fp32 multiply)."""
+    a16, La = _small_fp8_layer("fp8a16")
+    f32, Lf = _small_fp8_layer("f32")
+    _, la, ia, wa = O.route(La)
+    _, lf, i_f, wf = O.route(Lf)
+    assert np.array_equal(la.view(np.uint32), lf.view(np.uint32))
+    assert np.array_equal(ia, i_f) and np.array_equal(wa.view(np.uint32), wf.view(np.uint32))
+    ya, acc_a = O.forward(La, ia, wa)
+    yf, acc_f = O.forward(Lf, i_f, wf)
+    assert np.array_equal(acc_a.view(np.uint32), acc_f.view(np.uint32))
+    assert np.array_equal(ya, yf)
+    # and it is not the FP8 mode, whose activations and h are quantised
+    q, Lq = _small_fp8_layer("fp8")
+    _, acc_q = O.forward(Lq, ia, wa)
+    assert np.max(np.abs(acc_q - acc_a)) > 1e-4 * np.sqrt(np.mean(acc_a.astype(np.float64) ** 2))
+
+
+def test_w8a16_expert_ffn_vs_textbook():
+    """One expert in W8A16: the activation row enters as the bf16 values
+    themselves, and the FFN is the float64 textbook SwiGLU on torch-decoded
+    block-scaled weights."""
+    inp, L = _small_fp8_layer("fp8a16")
+    for e, t in ((-1, 3), (0, 5), (6, 11)):
+        xu, y = O.expert_ffn(L, e, t)
+        assert np.array_equal(xu.view(np.uint32), _x_f32(inp)[t].view(np.uint32))
+        ref = _swiglu64(*_fp8_expert_weights(inp, e), xu)
+        assert np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref ** 2)) <= 1e-6
