@@ -52,11 +52,17 @@ typedef enum {
 typedef enum {
   MOE_F32 = 0,           /* float32 */
   MOE_BF16 = 1,          /* bfloat16 */
-  MOE_FP8E4M3_B128 = 2   /* OCP FP8 E4M3 codes, value = decode(code) * scale of its
-                            128 x 128 block (fp32 scales); weights only */
+  MOE_FP8E4M3_B128 = 2,  /* OCP FP8 E4M3 codes, value = decode(code) * scale of its
+                            128 x 128 block (fp32 scales); weights only.  The activations
+                            entering each projection are quantised to E4M3 (see moe_forward) */
+  MOE_FP8E4M3_B128_A16 = 3 /* the same weights as W8A16: activations enter both
+                              projections in bf16, unquantised, and h stays bf16
+                              ([cache]: the CPU runtime decodes the FP8 weights for its
+                              matmuls on bf16 activations); weights only */
 } moe_dtype;
 
-/* Supported (act_dtype, w_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8E4M3_B128).
+/* Supported (act_dtype, w_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8E4M3_B128),
+ * (BF16, FP8E4M3_B128_A16).
  * Limits: 1 <= top_k <= 8, top_k <= n_experts <= 512, d_model and d_ffn multiples
  * of 128 with d_model <= 8192 and d_ffn <= 4096, d_ffn_shared 0 (no shared expert)
  * or a multiple of 128 <= 4096, T * top_k < 2^31. */
@@ -77,11 +83,12 @@ typedef struct {
   int32_t act_dtype;     /* moe_dtype of x and y: MOE_F32 or MOE_BF16 */
   int32_t w_dtype;       /* moe_dtype of the expert weights */
   int32_t w_layout;      /* moe_layout of w_gate, w_up, w_down, sh_gate, sh_up, sh_down;
-                            MOE_LAYOUT_TILED needs w_dtype BF16 or FP8E4M3_B128 */
+                            MOE_LAYOUT_TILED needs w_dtype BF16 or an FP8 one */
 } moe_shape;
 
 /* Layer weights.  Expert matrices are (out, in) row-major and stacked by expert.
- * Scales are required for MOE_FP8E4M3_B128 and ignored otherwise.
+ * Scales are required for MOE_FP8E4M3_B128 and MOE_FP8E4M3_B128_A16 and ignored
+ * otherwise.
  *   [port] "The gate": a router scores the experts for every token and a shared
  *   expert serves every token; part 1 of "Taking it apart": selection uses the
  *   router score plus a per-expert selection bias; part 3: the router runs in
@@ -155,16 +162,18 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
                      const moe_routing *out, void *ws, size_t ws_bytes, void *stream);
 
 /* Expert FFNs and combine.  For every routed pair and for the shared expert:
- * SwiGLU h = silu(W_gate x) * (W_up x), y_e = W_down h.  With FP8 weights the
- * activations entering each projection are quantised per token and per
- * 128-element group to E4M3 with scale amax/448 (round to nearest even,
- * saturating), and the block scales are applied in fp32.  Combine per token, in
+ * SwiGLU h = silu(W_gate x) * (W_up x), y_e = W_down h.  With MOE_FP8E4M3_B128
+ * weights the activations entering each projection are quantised per token and
+ * per 128-element group to E4M3 with scale amax/448 (round to nearest even,
+ * saturating); with MOE_FP8E4M3_B128_A16 they enter as bf16 (h rounded to bf16).
+ * With either, each 128 x 128 block's products are summed exactly in fp32 and
+ * the block scales applied in fp32.  Combine per token, in
  * fp32 and this order: acc = shared; acc += w_j * y_j for j = 0..k-1;
  * y = acc rounded to act_dtype (bf16: round to nearest even).
  * `r` must hold the results of moe_route / moe_route_forced for the same shape
  * and x (its plan included; logits, counts, offsets, perm and inv_perm are
- * not read).  y is [T, d] in act_dtype.  With FP8 weights in 16-row tiles the
- * two projections run as one launch whose down blocks wait on per-tile
+ * not read).  y is [T, d] in act_dtype.  With MOE_FP8E4M3_B128 weights in
+ * 16-row tiles the two projections run as one launch whose down blocks wait on per-tile
  * counters in the plan (reset before the launch ends): a plan serves any
  * number of forward calls, one at a time; forward calls that overlap on one
  * plan race.  If such a wait runs out (it cannot when blocks start in order),

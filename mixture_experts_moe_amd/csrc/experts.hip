@@ -149,11 +149,15 @@ __device__ __forceinline__ uint32_t load_coherent(const void* p) {
 
 // The work of gate/up block b (smem: the block's dynamic LDS).  Returns false
 // for a block without work.  COH: h codes and scales are stored coherently
-// (the fused expert launch).
-template <int BM, int WT, bool XB, bool COH = false>
+// (the fused expert launch).  A16 (with WT = 2): W8A16 -- the activation rows
+// are bf16 (not quantised, unit scales) and h is stored as bf16.
+template <int BM, int WT, bool XB, bool COH = false, bool A16 = false>
 __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t* smem) {
+  static_assert(!A16 || (WT == 2 && XB), "W8A16 stages bf16 activations for FP8 weights");
+  constexpr bool XQ = WT == 2 && !A16;  // activations as E4M3 codes with scales, h quantised
   constexpr int NC = BM / 16;
-  constexpr int EB = WT == 2 ? 1 : 2;  // bytes per element
+  constexpr int EB = WT == 2 ? 1 : 2;   // bytes per weight element
+  constexpr int EX = XQ ? 1 : 2;        // bytes per activation element in HBM
   constexpr int NT = kGateUpWaves * 64;
   constexpr bool XBF = WT == 1 || XB;  // activations in LDS as bf16 (else E4M3 codes)
   int nb;
@@ -162,7 +166,8 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   const int Fg = tr.shared ? a.Fs : a.F;
   if (nb * 128 >= Fg) return false;
 
-  const int RB = a.d * EB;        // bytes per activation / weight row in HBM
+  const int RB = a.d * EB;        // bytes per weight row in HBM
+  const int RX = a.d * EX;        // bytes per activation row in HBM
   const int nbb = RB / 128;       // 128-byte K blocks of a weight row
   const int xstride = (XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
   uint8_t* xs = smem;
@@ -232,7 +237,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   // and every wait is exact.  The first batch of SB chunks per thread covers a
   // 16-row tile at d = 2048.
   constexpr int SB = 4;
-  const int cpr = RB / 16, nch = BM * cpr, nkb = a.d / 128;
+  const int cpr = RX / 16, nch = BM * cpr, nkb = a.d / 128;
   const uint8_t* xa = (const uint8_t*)a.xa;
   const int rlast = tr.rows - 1;
   auto row_token = [&](int r) { return a.ri.tok[tr.hrow0 + min(r, rlast)]; };  // token of tile row r (clamped)
@@ -242,7 +247,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / cpr);
     float sv = 0.f, wv = 0.f;
     if (WT == 2 && first) {
-      sv = a.sxa[(size_t)row_token(tid / nkb) * nkb + tid % nkb];
+      sv = XQ ? a.sxa[(size_t)row_token(tid / nkb) * nkb + tid % nkb] : 1.0f;
       wv = tid < nkb ? sgp[tid] : sup[min(tid - nkb, nkb - 1)];  // the slice's weight block scales
     }
     if (first) {
@@ -255,7 +260,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
       const int i = i0 + u * NT, c = i % cpr;
-      v[u] = *(const v4i*)(xa + (size_t)tk[u] * RB + c * 16);
+      v[u] = *(const v4i*)(xa + (size_t)tk[u] * RX + c * 16);
     }
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
@@ -264,7 +269,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       const v4i z = {0, 0, 0, 0};
       const v4i x = live ? v[u] : z;
       uint8_t* dst = xs + (i < nch ? r : BM) * xstride;
-      if constexpr (WT == 2 && XB) {  // E4M3 codes -> bf16 once per block (exact)
+      if constexpr (XQ && XB) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
         e4m3x16_to_bf16(x, lo, hi);
         *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
@@ -280,7 +285,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
   if (WT == 2) {
     for (int i = tid + NT; i < BM * nkb; i += NT)  // tall tiles or wide rows only
-      sxs[i] = i / nkb <= rlast ? a.sxa[(size_t)row_token(i / nkb) * nkb + i % nkb] : 0.f;
+      sxs[i] = i / nkb <= rlast ? (XQ ? a.sxa[(size_t)row_token(i / nkb) * nkb + i % nkb] : 1.0f) : 0.f;
   }
   __syncthreads();
 
@@ -345,7 +350,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     }
   const int hrow0 = tr.hrow0;
   const int fcol = f0 + 4 * (lane >> 4);
-  if constexpr (WT == 2) {
+  if constexpr (XQ) {  // h quantised per (row, 128 features); else stored as bf16
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       float m = 0.f;
@@ -395,10 +400,10 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   return true;
 }
 
-template <int BM, int WT, bool XB>
+template <int BM, int WT, bool XB, bool A16 = false>
 __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  gateup_block<BM, WT, XB>(a, blockIdx.x, smem);
+  gateup_block<BM, WT, XB, false, A16>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -410,19 +415,23 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 // tall ones (a tile's h rows are staged once per 256 features); RT = 1 when a
 // row's K does not fit one stage.
 // ---------------------------------------------------------------------------
-template <int BM, int WT, int RT, int NW, bool COH = false>
+// A16 (with WT = 2): W8A16 -- h rows are bf16 with unit scales.
+template <int BM, int WT, int RT, int NW, bool COH = false, bool A16 = false>
 __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* smem) {
+  static_assert(!A16 || (WT == 2 && !COH), "W8A16 reads bf16 h rows for FP8 weights");
+  constexpr bool HQ = WT == 2 && !A16;  // h as E4M3 codes with scales
   constexpr int NC = BM / 16;
-  constexpr int EB = WT == 2 ? 1 : 2;
+  constexpr int EB = WT == 2 ? 1 : 2;   // bytes per weight element
+  constexpr int EH = HQ ? 1 : 2;        // bytes per h element
   constexpr int KG = RT == 1 ? 10 : 5;  // K blocks requested per stage
   constexpr int NT = NW * 64;
   int nb;
   const TileRows tr = block_rows(a, b, nb);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int RB = Fg * EB;          // bytes per h row / W_down row
+  const int RB = Fg * EB;          // bytes per W_down row
   const int nbb = RB / 128;
-  const int hstride_b = a.hstride * EB;
+  const int hstride_b = a.hstride * EH;
   const int lstride = Fg * 2 + 16;  // padded LDS row: h as bf16
   uint8_t* hs = smem;
   float* shs = (float*)(smem + (BM + 1) * lstride);          // [BM][Fg/128] (FP8)
@@ -465,13 +474,13 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   // code is straight-line and every wait is exact.
   constexpr int SB = 4;
   const int hrow0 = tr.hrow0, rlast = tr.rows - 1;
-  const int cpr = RB / 16, nch = BM * cpr, nkb = Fg / 128, gpr = a.hstride / 128;
+  const int cpr = Fg * EH / 16, nch = BM * cpr, nkb = Fg / 128, gpr = a.hstride / 128;
   const uint8_t* hsrc = (const uint8_t*)a.h;
   const int o = a.ri.prow[hrow0 + min(tid, rlast)];
   float sv = 0.f, dv = 0.f;
   if (WT == 2) {
     const float* shp = a.sh + (size_t)(hrow0 + min(tid / nkb, rlast)) * gpr + tid % nkb;
-    sv = COH ? __uint_as_float(load_coherent(shp)) : *shp;
+    sv = !HQ ? 1.0f : COH ? __uint_as_float(load_coherent(shp)) : *shp;
     const float* sd = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)srow0 * nkb;
     dv = sd[min(tid, nsr * nkb - 1)];
   }
@@ -498,7 +507,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
       const v4i z = {0, 0, 0, 0};
       const v4i x = live ? v[u] : z;
       uint8_t* dst = hs + (i < nch ? r : BM) * lstride;
-      if constexpr (WT == 2) {  // E4M3 codes -> bf16 once per block (exact)
+      if constexpr (HQ) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
         e4m3x16_to_bf16(x, lo, hi);
         *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
@@ -524,7 +533,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
     if (tid < BM * nkb) shs[tid] = tid / nkb <= rlast ? sv : 0.f;
     for (int i = tid + NT; i < BM * nkb; i += NT) {  // tall tiles or wide rows only
       const float* shp = a.sh + (size_t)(hrow0 + min(i / nkb, rlast)) * gpr + i % nkb;
-      shs[i] = i / nkb <= rlast ? (COH ? __uint_as_float(load_coherent(shp)) : *shp) : 0.f;
+      shs[i] = i / nkb <= rlast ? (!HQ ? 1.0f : COH ? __uint_as_float(load_coherent(shp)) : *shp) : 0.f;
     }
     if (tid < nsr * nkb) wsd[tid] = dv;
   }
@@ -592,10 +601,10 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
     }
 }
 
-template <int BM, int WT, int RT>
+template <int BM, int WT, int RT, bool A16 = false>
 __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
-  down_block<BM, WT, RT, 4>(a, blockIdx.x, smem);
+  down_block<BM, WT, RT, 4, false, A16>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -804,19 +813,20 @@ static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, co
 
 // Activations in LDS as bf16 for 16-row tiles; taller tiles keep the E4M3 codes
 // (decoded per use) so that two blocks fit a CU.
-static bool gateup_x_bf16(int BM, int wmode) { return wmode == 1 || BM <= 16; }
+static bool gateup_x_bf16(int BM, int wmode) { return wmode != 2 || BM <= 16; }
 
+// wmode: the moe_dtype of the weights (0 f32, 1 bf16, 2 FP8, 3 FP8 as W8A16).
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
   size_t b = (size_t)(BM + 1) * ((gateup_x_bf16(BM, wmode) ? d * 2 : d) + 16);  // plus a spare row
-  if (wmode == 2) b += (size_t)BM * (d / 128) * 4 + 2 * (d / 128) * 4;
+  if (wmode >= 2) b += (size_t)BM * (d / 128) * 4 + 2 * (d / 128) * 4;
   return b + kGateUpWaves * BM * 4;
 }
 
 size_t down_lds_bytes(int BM, int wmode, int Fg) {
   if (wmode == 0) return (size_t)BM * Fg * 4;
   size_t b = (size_t)(BM + 1) * (Fg * 2 + 16);  // h as bf16, plus a spare row
-  if (wmode == 2) b += (size_t)BM * (Fg / 128) * 4 + 2 * (Fg / 128) * 4;
+  if (wmode >= 2) b += (size_t)BM * (Fg / 128) * 4 + 2 * (Fg / 128) * 4;
   return b + BM * 4 + BM * 4;
 }
 
@@ -826,7 +836,7 @@ int down_rows_per_wave(int BM, int wmode, int Fmax, int d) {
   // 2 for short tiles, 4 for tall ones, whose h rows are then staged once per
   // 256 output features
   if (wmode == 0) return 1;
-  const bool one_stage = Fmax * (wmode == 2 ? 1 : 2) <= 5 * 128;
+  const bool one_stage = Fmax * (wmode >= 2 ? 1 : 2) <= 5 * 128;
   return !one_stage ? 1 : (BM == 16 ? (d % 128 == 0 ? 2 : 1) : (d % 256 == 0 ? 4 : 1));
 }
 
@@ -851,6 +861,7 @@ hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipS
   if (wmode == 2 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2, true>, grid, lds, st, a, nt);
   if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2, false>, grid, lds, st, a, nt);
   if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1, true>, grid, lds, st, a, nt);
+  if (wmode == 3 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2, true, true>, grid, lds, st, a, nt);
   return hipErrorInvalidValue;
 }
 
@@ -892,11 +903,13 @@ hipError_t launch_down(const ExpertArgs& a0, int wmode, const Plan& plan, hipStr
   const size_t lds = down_lds_bytes(BM, wmode, Fmax);
   const int RT = down_rows_per_wave(BM, wmode, Fmax, a.d);
   if (wmode == 2 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2>, grid, lds, st, a);
+  if (wmode == 3 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2, true>, grid, lds, st, a);
   if (wmode == 2 && RT == 4 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
   if (RT != 1) return hipErrorInvalidValue;
   if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 1>, grid, lds, st, a);
   if (wmode == 2 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 1>, grid, lds, st, a);
   if (wmode == 1 && BM == 16) return launch_dyn(down_mfma_kernel<16, 1, 1>, grid, lds, st, a);
+  if (wmode == 3 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 1, true>, grid, lds, st, a);
   return hipErrorInvalidValue;
 }
 

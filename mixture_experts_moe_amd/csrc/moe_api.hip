@@ -23,7 +23,7 @@ struct PlanLayout {
   size_t sched_gu, sched_dn, rinfo, xq, sx, sync, total;
 };
 
-int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_BF16 ? 2 : 4); }
+int h_elem_bytes(int w_dtype) { return w_dtype == MOE_FP8E4M3_B128 ? 1 : (w_dtype == MOE_F32 ? 4 : 2); }
 
 int64_t max_tiles_for(const moe_shape& s, int BM) {
   const int64_t P = (int64_t)s.T * s.top_k;
@@ -90,7 +90,8 @@ int validate_shape(const moe_shape* s) {
   if ((int64_t)s->T * s->top_k > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
   const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
-                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128);
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128_A16);
   if (!combo) return MOE_ERR_UNSUPPORTED;
   if (s->w_layout != MOE_LAYOUT_ROWMAJOR && s->w_layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (s->w_layout == MOE_LAYOUT_TILED && s->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
@@ -255,12 +256,13 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   if (rc != MOE_OK) return rc;
   if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->plan)
     return MOE_ERR_INVALID_ARG;
-  const bool fp8 = shape->w_dtype == MOE_FP8E4M3_B128;
+  const bool fp8 = shape->w_dtype == MOE_FP8E4M3_B128;                  // activations quantised
+  const bool scaled = fp8 || shape->w_dtype == MOE_FP8E4M3_B128_A16;  // block-scaled FP8 weights
   const bool has_shared = shape->d_ffn_shared > 0;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
-  if (fp8 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+  if (scaled && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
   if (has_shared && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_INVALID_ARG;
-  if (has_shared && fp8 && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_INVALID_ARG;
+  if (has_shared && scaled && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_INVALID_ARG;
   if (shape->T == 0) return MOE_OK;
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);

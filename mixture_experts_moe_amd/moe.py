@@ -16,8 +16,9 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP, MOE_ERR_FORCED_INDEX = 0, -1, -2, -3, -4, -5
-DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_FORCED_INDEX, MOE_ERR_DEVICE_SYNC = -5, -6  # device status word
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3}
 
 # Every function the header declares (checked against include/moe.h by the tests).
 ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",

@@ -34,7 +34,7 @@ def test_exports_every_declared_function():
 
 def test_status_strings():
     _lib()
-    for rc in (0, -1, -2, -3, -4, -5):
+    for rc in (0, -1, -2, -3, -4, -5, -6):
         assert moe.status_string(rc).startswith("MOE_")
     assert "unknown" in moe.status_string(7)
 
@@ -178,3 +178,22 @@ def test_plan_bytes():
     bf = moe.make_shape(32, 2048, 384, 6, 640, 640, act="bf16", w="bf16")
     assert moe.plan_bytes(bf) < n32  # no activation codes with bf16 weights
     assert moe.plan_bytes(moe.make_shape(32, 2048, 384, 9, 640, 640)) == 0
+
+
+def test_w8a16_shape_and_scales():
+    """(bf16 activations, FP8 weights as W8A16) is a supported pair; like the FP8
+    mode it needs the block scales, and with no activation codes its workspace
+    and plan are those of a layer whose h is bf16."""
+    _lib()
+    a16 = moe.make_shape(32, 2048, 384, 6, 640, 640, act="bf16", w="fp8a16")
+    assert moe.workspace_bytes(a16) > moe.workspace_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640))
+    assert moe.workspace_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640, act="f32", w="fp8a16")) == 0
+    assert moe.plan_bytes(a16) < moe.plan_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640))  # no x codes
+    assert moe.plan_bytes(a16) > 0
+    L = _lib()
+    r = _routing_struct()
+    y = FAKE
+    for null in ("s_gate", "s_up", "s_down", "ss_gate"):
+        w = _weights_struct(**{null: None})
+        rc = L.moe_forward(C.byref(a16), C.byref(w), FAKE, C.byref(r), y, FAKE, 1 << 40, None)
+        assert rc == moe.MOE_ERR_INVALID_ARG, null

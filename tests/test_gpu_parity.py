@@ -274,6 +274,38 @@ def test_prefill_forced_full_size():
     check_y(g["y"][tok], acc_ref)
 
 
+# ------------------------------------------------------------------ W8A16 weight mode
+
+@pytest.mark.parametrize("T", [32, 300])
+def test_w8a16_free(T):
+    """The FP8 weights used as W8A16 (bf16 activations into both projections,
+    unquantised; h in bf16) against the oracle's W8A16 mode: the decode batch
+    in full, and a 300-token batch (long routing path, 16-row tiles) on sampled
+    tokens."""
+    inp = synth.make_inputs("decode_t32_w8a16", T=T)
+    s = inp["shape"]
+    say(f"decode_t32_w8a16 T={s.T}: W8A16 against the oracle")
+    g = run_gpu(inp)
+    assert g["status"][0] == 0
+    check_dispatch_properties(g, s.E)
+    L = O.Layer(inp)
+    tok = np.arange(s.T) if s.T <= 32 else np.unique(np.concatenate([np.arange(0, s.T, 11), [s.T - 1]]))
+    _, lg, idx, w = O.route(L, tok)
+    check_logits(g["logits"][tok], lg)
+    bad, ex = route_agreement(g["topk_idx"][tok], idx, selection_scores(inp, lg), s.k)
+    say(f"  ids on {len(tok)} tokens: {bad} mismatches, {ex} exempt")
+    assert bad == 0
+    same = (g["topk_idx"][tok] == idx).all(axis=1)
+    assert np.max(np.abs(g["topk_w"][tok][same] - w[same])) <= W_ABS
+    _, acc_ref = O.forward(L, idx[same], w[same], tok[same])
+    check_y(g["y"][tok[same]], acc_ref)
+    # and it is a different computation from the FP8 mode on the same layer, x and experts
+    q_inp = dict(synth.make_inputs("decode_t32", T=T))
+    q_inp["x"] = inp["x"]
+    q = run_gpu(q_inp, forced=g["topk_idx"])
+    assert not np.array_equal(q["y"].view(np.uint32), g["y"].view(np.uint32))
+
+
 # ------------------------------------------------------------------ skewed load, free routing
 
 def test_skew_free_full_size():
@@ -465,7 +497,8 @@ def test_pack_weights_layout():
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("case,T", [("decode_t32", None), ("prefill_t2048", 700), ("ties_t256_bf16w", None)])
+@pytest.mark.parametrize("case,T", [("decode_t32", None), ("prefill_t2048", 700), ("ties_t256_bf16w", None),
+                                    ("decode_t32_w8a16", None)])
 def test_tiled_layout_matches_rowmajor(case, T):
     """The same layer with packed weights gives the same bits as with row-major ones."""
     inp = synth.make_inputs(case, T=T)
