@@ -55,8 +55,8 @@ FORCED = {"prefill_t2048"}
 KERNEL_SOURCES = ("mixture_experts_moe_amd/csrc/experts.hip", "mixture_experts_moe_amd/csrc/moe_device.h",
                   "mixture_experts_moe_amd/csrc/moe_kernels.h", "mixture_experts_moe_amd/csrc/moe_api.hip")
 TRAFFIC = {  # workload -> counters of the fused expert kernel, tiled layout
-    "decode_t32": {"sources_sha256": "936b7d4ce75e3fb3e689bbe8285bace5859e373fa515b68579dca03b599a7d32",
-                   "fetch_bytes": 607309919, "write_bytes": 2227087},
+    "decode_t32": {"sources_sha256": "5e59f858f13afbe4403dd75e4c2a9d29dacf39d69f1f3717d8bb09de179880ff",
+                   "fetch_bytes": 607259410, "write_bytes": 2227087},
 }
 
 

@@ -172,7 +172,7 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
  * y = acc rounded to act_dtype (bf16: round to nearest even).
  * `r` must hold the results of moe_route / moe_route_forced for the same shape
  * and x (its plan included; logits, counts, offsets, perm and inv_perm are
- * not read).  y is [T, d] in act_dtype.  With MOE_FP8E4M3_B128 weights in
+ * not read).  y is [T, d] in act_dtype.  With FP8 weights (either mode) in
  * 16-row tiles the two projections run as one launch whose down blocks wait on per-tile
  * counters in the plan (reset before the launch ends): a plan serves any
  * number of forward calls, one at a time; forward calls that overlap on one

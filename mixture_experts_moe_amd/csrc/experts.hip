@@ -393,7 +393,13 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
         uint2 pk;
         pk.x = (uint32_t)f32_to_bf16(h[c][0]) | ((uint32_t)f32_to_bf16(h[c][1]) << 16);
         pk.y = (uint32_t)f32_to_bf16(h[c][2]) | ((uint32_t)f32_to_bf16(h[c][3]) << 16);
-        *(uint2*)(hb + row * a.hstride + fcol) = pk;
+        uint16_t* hp = hb + row * a.hstride + fcol;
+        if constexpr (COH) {
+          store_coherent(hp, pk.x);
+          store_coherent(hp + 2, pk.y);
+        } else {
+          *(uint2*)hp = pk;
+        }
       }
     }
   }
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void gateup_mfma_kernel(ExpertAr
 // A16 (with WT = 2): W8A16 -- h rows are bf16 with unit scales.
 template <int BM, int WT, int RT, int NW, bool COH = false, bool A16 = false>
 __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* smem) {
-  static_assert(!A16 || (WT == 2 && !COH), "W8A16 reads bf16 h rows for FP8 weights");
+  static_assert(!A16 || WT == 2, "W8A16 reads bf16 h rows for FP8 weights");
   constexpr bool HQ = WT == 2 && !A16;  // h as E4M3 codes with scales
   constexpr int NC = BM / 16;
   constexpr int EB = WT == 2 ? 1 : 2;   // bytes per weight element
@@ -608,10 +614,10 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up and down in one launch (FP8 weights, 16-row tiles, tile-list
-// schedule).  Blocks [0, n_gu) do the gate/up work; the rest are 8-wave down
-// blocks (256 output features each).  A gate/up block stores its h codes and
-// scales coherently (agent-scope atomic stores, written through to where every
+// Gate/up and down in one launch (FP8 weights with E4M3 or, A16, bf16
+// activations; 16-row tiles, tile-list schedule).  Blocks [0, n_gu) do the
+// gate/up work; the rest are 8-wave down blocks (256 output features each).  A
+// gate/up block stores its h rows (and their scales) coherently (agent-scope atomic stores, written through to where every
 // XCD reads them), waits until each of its waves' stores has completed, and
 // then counts itself in ready[tile]; a down block of that tile waits until the
 // count reaches the tile's gate/up slices and reads h and its scales with
@@ -632,6 +638,7 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 22;  // polls of about 64 cycles each: far beyond any real wait
 
+template <bool A16>
 __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(ExpertArgs gu, ExpertArgs dn, int n_gu,
                                                                           int32_t* __restrict__ ready,
                                                                           int32_t* __restrict__ done,
@@ -639,7 +646,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(Expert
   extern __shared__ __align__(16) uint8_t smem[];
   const int b = blockIdx.x;
   if (b < n_gu) {
-    if (gateup_block<16, 2, true, true>(gu, b, smem)) {
+    if (gateup_block<16, 2, true, true, A16>(gu, b, smem)) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent stores have completed ...
       __syncthreads();                // ... and so have every other wave's
       if (threadIdx.x == 0) atomicAdd(&ready[b / gu.nsl], 1);
@@ -661,7 +668,7 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(Expert
     }
   }
   __syncthreads();  // h is read below, with coherent loads, after the count was seen
-  down_block<16, 2, 2, kGateUpWaves, true>(dn, bd, smem);
+  down_block<16, 2, 2, kGateUpWaves, true, A16>(dn, bd, smem);
   __syncthreads();
   if (threadIdx.x == 0 && atomicAdd(&done[tile], 1) == dn.nsl - 1) {  // the tile's last down block
     atomicExch(&ready[tile], 0);
@@ -866,11 +873,12 @@ hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipS
 }
 
 bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d) {
-  return wmode == 2 && plan.BM == 16 && !plan.xcd && plan.sync && down_rows_per_wave(16, 2, Fmax, d) == 2 &&
-         d % (kGateUpWaves * 32) == 0;
+  return (wmode == 2 || wmode == 3) && plan.BM == 16 && !plan.xcd && plan.sync &&
+         down_rows_per_wave(16, wmode, Fmax, d) == 2 && d % (kGateUpWaves * 32) == 0;
 }
 
-hipError_t launch_experts_fused(const ExpertArgs& a0, const Plan& plan, int32_t* status, hipStream_t st) {
+hipError_t launch_experts_fused(const ExpertArgs& a0, int wmode, const Plan& plan, int32_t* status,
+                                hipStream_t st) {
   ExpertArgs gu = a0, dn = a0;
   gu.sched = dn.sched = plan.sched[0];
   gu.per_tile = dn.per_tile = 1;
@@ -878,16 +886,15 @@ hipError_t launch_experts_fused(const ExpertArgs& a0, const Plan& plan, int32_t*
   dn.nsl = a0.d / (kGateUpWaves * 32);  // 8 waves x 2 tiles x 16 features per down block
   const int Fmax = a0.F > a0.Fs ? a0.F : a0.Fs;
   const int n_gu = plan.max_tiles * gu.nsl, n_dn = plan.max_tiles * dn.nsl;
-  size_t lds = gateup_lds_bytes(16, 2, a0.d);
-  const size_t ldn = down_lds_bytes(16, 2, Fmax);
+  size_t lds = gateup_lds_bytes(16, wmode, a0.d);
+  const size_t ldn = down_lds_bytes(16, wmode, Fmax);
   if (ldn > lds) lds = ldn;
+  auto kernel = wmode == 3 ? experts_fused_kernel<true> : experts_fused_kernel<false>;
   if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)experts_fused_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  experts_fused_kernel<<<n_gu + n_dn, kGateUpWaves * 64, lds, st>>>(gu, dn, n_gu, plan.sync,
-                                                                     plan.sync + plan.max_tiles, status);
+  kernel<<<n_gu + n_dn, kGateUpWaves * 64, lds, st>>>(gu, dn, n_gu, plan.sync, plan.sync + plan.max_tiles, status);
   return hipGetLastError();
 }
 

@@ -316,7 +316,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
                      moe::experts_fusable(shape->w_dtype, plan, Fmax, d);
   mark(0);
   if (fused) {  // both projections in one launch: events 1 and 2 mark its end
-    e = moe::launch_experts_fused(a, plan, r->status, st);
+    e = moe::launch_experts_fused(a, shape->w_dtype, plan, r->status, st);
     mark(1);
     mark(2);
   } else if (stages & MOE_STAGE_GATE_UP) {

@@ -108,7 +108,8 @@ hipError_t launch_gateup(const ExpertArgs& a, int wmode, const Plan& plan, hipSt
 hipError_t launch_down(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
 // Gate/up and down as one launch (FP8 weights, 16-row tiles, tile-list plan).
 bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d);
-hipError_t launch_experts_fused(const ExpertArgs& a, const Plan& plan, int32_t* status, hipStream_t st);
+hipError_t launch_experts_fused(const ExpertArgs& a, int wmode, const Plan& plan, int32_t* status,
+                                hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
                                hipStream_t st);
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,
