@@ -29,6 +29,11 @@ per-layer inputs):
 * ``decode_t32_w8a16`` the decode batch with the same FP8 weights used as
                     W8A16: activations enter both projections in bf16,
                     unquantised.
+* ``decode_t32_u4`` the decode batch with 4-bit weights: the same base draws
+                    quantised per row and group of 64 columns as
+                    round((w - min) / scale) with scale = (max - min) / 15 and
+                    bias = min (both bf16), two codes to a byte, the even column
+                    in the low nibble; activations enter in bf16.
 
 Per-layer shapes are the large Kolibri-style layer of "We Ported Aleph
 Alpha's Kolibri to a MacBook. Our Own Gate Said No." (section "The gate":
@@ -56,7 +61,7 @@ class LayerShape:
     F: int
     Fs: int
     act: str  # "f32" | "bf16"
-    w: str  # "f32" | "bf16" | "fp8" | "fp8a16" (the same FP8 weights, activations not quantised)
+    w: str  # "f32" | "bf16" | "fp8" | "fp8a16" (the same FP8 weights, activations not quantised) | "u4"
 
     @property
     def P(self) -> int:
@@ -74,6 +79,7 @@ CASES = {
     "skew_t8192": ("big", 8192, "bf16", "fp8", "normal", "normal", True),
     "ties_t256": ("big", 256, "bf16", "fp8", "int3", "grid64", False),
     "decode_t32_w8a16": ("big", 32, "bf16", "fp8a16", "normal", "normal", False),
+    "decode_t32_u4": ("big", 32, "bf16", "u4", "normal", "normal", False),
     "ties_t256_bf16w": ("big", 256, "bf16", "bf16", "int3", "grid64", False),
 }
 
@@ -117,6 +123,23 @@ def _fp8_blocks(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     return codes, scale
 
 
+def u4_groups(w: np.ndarray) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Quantise a [R, C] fp32 weight (C a multiple of 64) to 4-bit affine groups:
+    per row and group of 64 columns, scale = bf16((max - min) / 15) and bias =
+    bf16(min); q = clip(round((w - bias) / scale), 0, 15), two codes to a byte
+    with the even column in the low nibble.  Returns (codes [R, C/2] uint8,
+    scales and biases [R, C/64] as bf16 bits); weight ~= scale * q + bias."""
+    R, C = w.shape
+    g = w.reshape(R, C // 64, 64)
+    lo, hi = g.min(axis=2), g.max(axis=2)
+    scale_b = bf16_bits(np.maximum((hi - lo) / np.float32(15.0), np.float32(1e-8)))
+    bias_b = bf16_bits(lo)
+    sc, bi = bf16_bits_to_f32(scale_b), bf16_bits_to_f32(bias_b)
+    q = np.clip(np.rint((g - bi[:, :, None]) / sc[:, :, None]), 0, 15).astype(np.uint8).reshape(R, C)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    return codes, scale_b, bias_b
+
+
 _layer_cache: dict = {}
 _layer_lock = threading.Lock()
 
@@ -140,39 +163,51 @@ def _expert_weights(layer: str, seed: int, w_dtype: str) -> dict:
         wdt, sh = np.float32, None
     elif w_dtype == "bf16":
         wdt, sh = np.uint16, None
-    elif w_dtype == "fp8":
+    elif w_dtype in ("fp8", "u4"):
         wdt = np.uint8
     else:
         raise ValueError(w_dtype)
-    out["w_gate"] = np.empty((E, F, d), wdt)
-    out["w_up"] = np.empty((E, F, d), wdt)
-    out["w_down"] = np.empty((E, d, F), wdt)
+    cdiv = 2 if w_dtype == "u4" else 1  # 4-bit codes: two to a byte
+    out["w_gate"] = np.empty((E, F, d // cdiv), wdt)
+    out["w_up"] = np.empty((E, F, d // cdiv), wdt)
+    out["w_down"] = np.empty((E, d, F // cdiv), wdt)
     if w_dtype == "fp8":
         out["s_gate"] = np.empty((E, F // 128, d // 128), np.float32)
         out["s_up"] = np.empty((E, F // 128, d // 128), np.float32)
         out["s_down"] = np.empty((E, d // 128, F // 128), np.float32)
+    if w_dtype == "u4":
+        for p in ("s_", "b_"):
+            out[p + "gate"] = np.empty((E, F, d // 64), np.uint16)
+            out[p + "up"] = np.empty((E, F, d // 64), np.uint16)
+            out[p + "down"] = np.empty((E, d, F // 64), np.uint16)
 
     def convert(w: np.ndarray):
         if w_dtype == "f32":
-            return w, None
+            return w, None, None
         if w_dtype == "bf16":
-            return bf16_bits(w), None
-        return _fp8_blocks(w)
+            return bf16_bits(w), None, None
+        if w_dtype == "u4":
+            return u4_groups(w)
+        return (*_fp8_blocks(w), None)
 
     def one(e: int):
         for name, tensor, shape in (("gate", _T_GATE, (F, d)), ("up", _T_UP, (F, d)), ("down", _T_DOWN, (d, F))):
-            c, s = convert(draw(tensor, e, shape))
+            c, s, b = convert(draw(tensor, e, shape))
             out["w_" + name][e] = c
             if s is not None:
                 out["s_" + name][e] = s
+            if b is not None:
+                out["b_" + name][e] = b
 
     with ThreadPoolExecutor(max_workers=min(16, max(1, torch.get_num_threads()))) as ex:
         list(ex.map(one, range(E)))
 
     for name, tensor, shape in (("gate", _T_GATE, (Fs, d)), ("up", _T_UP, (Fs, d)), ("down", _T_DOWN, (d, Fs))):
-        c, s = convert(draw(tensor, _SHARED, shape))
+        c, s, b = convert(draw(tensor, _SHARED, shape))
         out["sh_" + name] = c
         out["ss_" + name] = s
+        if b is not None:
+            out["sb_" + name] = b
     with _layer_lock:
         _layer_cache[key] = out
     return out
@@ -185,9 +220,11 @@ def make_inputs(case: str, T: int | None = None, seed: int = 0) -> dict:
     ``w_router`` ([E,d] float32), ``sel_bias`` ([E] float32 or None),
     ``w_gate``/``w_up`` ([E,F,d]), ``w_down`` ([E,d,F]) as float32, uint16 bf16
     bits or uint8 E4M3 codes, ``s_gate``/``s_up`` ([E,F/128,d/128]) and
-    ``s_down`` ([E,d/128,F/128]) fp32 block scales (FP8 only, else absent),
+    ``s_down`` ([E,d/128,F/128]) fp32 block scales (FP8 only, else absent);
+    4-bit weights: ``w_*`` codes [E,F,d/2] / [E,d,F/2] uint8 and bf16-bit
+    group scales ``s_*`` and biases ``b_*`` ([E,F,d/64] / [E,d,F/64]),
     ``sh_gate``/``sh_up`` ([Fs,d]), ``sh_down`` ([d,Fs]) and their scales
-    ``ss_*`` for the shared expert.  Rows of ``x`` for a smaller ``T`` are a
+    ``ss_*`` (and 4-bit biases ``sb_*``) for the shared expert.  Rows of ``x`` for a smaller ``T`` are a
     prefix of those for a larger one.
     """
     layer, T0, act, w_dtype, x_recipe, r_recipe, with_bias = CASES[case]

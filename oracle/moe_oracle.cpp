@@ -66,7 +66,10 @@ enum Mutant {
   MUT_WEIGHTS_BIASED = 10,   // weights from the biased score instead of the logit
   MUT_SILU_SIGN = 11,        // silu(z) = z / (1 + exp(z))
   MUT_GATE_UP_SWAP = 12,     // silu applied to the up projection
-  MUT_COMBINE_NO_WEIGHT = 13 // routed outputs added without their weights
+  MUT_COMBINE_NO_WEIGHT = 13, // routed outputs added without their weights
+  MUT_U4_NIBBLE_SWAP = 14,   // 4-bit codes: even columns read from the high nibble
+  MUT_U4_NO_BIAS = 15,       // 4-bit groups: the bias term dropped
+  MUT_U4_GROUP128 = 16       // 4-bit groups: parameters indexed per 128 columns
 };
 int g_mutant = MUT_NONE;
 
@@ -75,7 +78,17 @@ enum { ACT_F32 = 0, ACT_BF16 = 1 };
 // activations entering both projections unquantised (W8A16): the CPU runtime of
 // [cache] decodes the FP8 weights and runs its matmuls on the activations as
 // they are.  Neither x nor h is quantised; everything else is as for W_FP8.
-enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP8_A16 = 3 };
+//
+// W_U4: 4-bit weights, the analogue of the port's 4-bit (K4) build ([bench]
+// "The gate, forced": an 8-bit and a 4-bit conversion, both run under MLX;
+// "What this means if you want Kolibri on a Mac": the 4-bit build decodes
+// faster).  The pages do not give the 4-bit format.  Reading: MLX's default
+// affine group quantisation -- groups of 64 consecutive columns of a row,
+// element value = scale * q + bias with q the unsigned 4-bit code and scale,
+// bias bf16 per (row, group); codes two to a byte, the even column in the low
+// nibble.  Activations and h stay unquantised, as in W_FP8_A16.
+enum { W_F32 = 0, W_BF16 = 1, W_FP8 = 2, W_FP8_A16 = 3, W_U4 = 4 };
+constexpr int kU4Group = 64;
 enum { OK = 0, ERR_INVALID = -1, ERR_FORCED_INDEX = -5 };
 
 // ---- number formats --------------------------------------------------------
@@ -149,7 +162,7 @@ float quant_group(const float* v, int n, float* deq) {
 struct Shape {
   int32_t T, d, E, k, F, Fs;
   int32_t act_dtype;  // ACT_F32 | ACT_BF16
-  int32_t w_dtype;    // W_F32 | W_BF16 | W_FP8 | W_FP8_A16
+  int32_t w_dtype;    // W_F32 | W_BF16 | W_FP8 | W_FP8_A16 | W_U4
 };
 
 struct Weights {
@@ -167,12 +180,21 @@ struct Weights {
   const float* ss_gate;   // [Fs/128, d/128]
   const float* ss_up;
   const float* ss_down;   // [d/128, Fs/128]
+  // W_U4: the s_* and ss_* pointers above hold bf16 group scales
+  // [rows, cols/64] per matrix, and these the bf16 group biases
+  const uint16_t* b_gate;   // [E, F, d/64]
+  const uint16_t* b_up;     // [E, F, d/64]
+  const uint16_t* b_down;   // [E, d, F/64]
+  const uint16_t* sb_gate;  // [Fs, d/64]
+  const uint16_t* sb_up;
+  const uint16_t* sb_down;  // [d, Fs/64]
 };
 
 // One row-major weight matrix [rows, cols] in its storage format.
 struct Mat {
   const void* data;
-  const float* scale;  // [rows/128, cols/128] for FP8
+  const void* scale;    // FP8: fp32 [rows/128, cols/128]; U4: bf16 [rows, cols/64]
+  const uint16_t* bias; // U4: bf16 [rows, cols/64]
   int rows, cols, w_dtype;
 };
 
@@ -187,15 +209,27 @@ const float* e4m3_table() {
   return table;
 }
 
-// Element (r, c) of a weight matrix, decoded to fp32.
-float mat_at(const Mat& m, int r, int c) {
+// Element (r, c) of a weight matrix, decoded.  FP8: decode(code) * scale, one
+// fp32 multiply.  U4: scale * q + bias, exact in double (a 4-bit integer times
+// a bf16 value plus a bf16 value of similar size needs far fewer than 53 bits).
+double mat_at(const Mat& m, int r, int c) {
   size_t i = (size_t)r * m.cols + c;
   if (m.w_dtype == W_F32) return ((const float*)m.data)[i];
   if (m.w_dtype == W_BF16) return bf16_to_f32(((const uint16_t*)m.data)[i]);
+  if (m.w_dtype == W_U4) {
+    const uint8_t byte = ((const uint8_t*)m.data)[i / 2];
+    const bool high = (c % 2 == 1) != (g_mutant == MUT_U4_NIBBLE_SWAP);
+    const int q = high ? byte >> 4 : byte & 0xF;
+    const int group = g_mutant == MUT_U4_GROUP128 ? c / 128 : c / kU4Group;
+    const size_t gi = (size_t)r * (m.cols / kU4Group) + group;
+    const double scale = bf16_to_f32(((const uint16_t*)m.scale)[gi]);
+    const double bias = g_mutant == MUT_U4_NO_BIAS ? 0.0 : bf16_to_f32(m.bias[gi]);
+    return scale * q + bias;
+  }
   int nrb = m.rows / 128, ncb = m.cols / 128;
   int si = (r / 128) * ncb + (c / 128);
   if (g_mutant == MUT_SCALE_TRANSPOSED) si = (c / 128) * nrb + (r / 128);
-  return e4m3_table()[((const uint8_t*)m.data)[i]] * m.scale[si];
+  return e4m3_table()[((const uint8_t*)m.data)[i]] * ((const float*)m.scale)[si];
 }
 
 float act_at(const Shape& s, const void* x, int t, int i) {
@@ -207,7 +241,7 @@ float act_at(const Shape& s, const void* x, int t, int i) {
 void matvec(const Mat& m, const float* v, float* out) {
   for (int r = 0; r < m.rows; ++r) {
     double acc = 0.0;
-    for (int c = 0; c < m.cols; ++c) acc += (double)mat_at(m, r, c) * (double)v[c];
+    for (int c = 0; c < m.cols; ++c) acc += mat_at(m, r, c) * (double)v[c];
     out[r] = (float)acc;
   }
 }
@@ -224,16 +258,28 @@ void expert_ffn(const Shape& s, const Weights& w, int expert, const float* xin, 
   int F = expert < 0 ? s.Fs : s.F;
   Mat g, u, dn;
   if (expert < 0) {
-    g = Mat{w.sh_gate, w.ss_gate, F, s.d, s.w_dtype};
-    u = Mat{w.sh_up, w.ss_up, F, s.d, s.w_dtype};
-    dn = Mat{w.sh_down, w.ss_down, s.d, F, s.w_dtype};
+    g = Mat{w.sh_gate, w.ss_gate, w.sb_gate, F, s.d, s.w_dtype};
+    u = Mat{w.sh_up, w.ss_up, w.sb_up, F, s.d, s.w_dtype};
+    dn = Mat{w.sh_down, w.ss_down, w.sb_down, s.d, F, s.w_dtype};
+  } else if (s.w_dtype == W_U4) {
+    const size_t cb = (size_t)F * s.d / 2;         // code bytes per matrix
+    const size_t ng = (size_t)F * s.d / kU4Group;  // groups per matrix
+    const uint16_t* sg = (const uint16_t*)w.s_gate;
+    const uint16_t* su = (const uint16_t*)w.s_up;
+    const uint16_t* sd = (const uint16_t*)w.s_down;
+    g = Mat{(const char*)w.w_gate + expert * cb, sg + expert * ng, w.b_gate + expert * ng, F, s.d, s.w_dtype};
+    u = Mat{(const char*)w.w_up + expert * cb, su + expert * ng, w.b_up + expert * ng, F, s.d, s.w_dtype};
+    dn = Mat{(const char*)w.w_down + expert * cb, sd + expert * ng, w.b_down + expert * ng, s.d, F, s.w_dtype};
   } else {
     size_t esz = (size_t)F * s.d;
     size_t el = s.w_dtype == W_F32 ? 4 : (s.w_dtype == W_BF16 ? 2 : 1);
     size_t sgz = (size_t)(F / 128) * (s.d / 128);
-    g = Mat{(const char*)w.w_gate + expert * esz * el, w.s_gate ? w.s_gate + expert * sgz : nullptr, F, s.d, s.w_dtype};
-    u = Mat{(const char*)w.w_up + expert * esz * el, w.s_up ? w.s_up + expert * sgz : nullptr, F, s.d, s.w_dtype};
-    dn = Mat{(const char*)w.w_down + expert * esz * el, w.s_down ? w.s_down + expert * sgz : nullptr, s.d, F, s.w_dtype};
+    g = Mat{(const char*)w.w_gate + expert * esz * el, w.s_gate ? w.s_gate + expert * sgz : nullptr, nullptr, F, s.d,
+            s.w_dtype};
+    u = Mat{(const char*)w.w_up + expert * esz * el, w.s_up ? w.s_up + expert * sgz : nullptr, nullptr, F, s.d,
+            s.w_dtype};
+    dn = Mat{(const char*)w.w_down + expert * esz * el, w.s_down ? w.s_down + expert * sgz : nullptr, nullptr, s.d, F,
+             s.w_dtype};
   }
   std::vector<float> gv(F), uv(F), h(F), hq(F);
   matvec(g, xin, gv.data());
@@ -262,9 +308,10 @@ void activation_row(const Shape& s, const void* x, int t, float* row) {
 
 int check_shape(const Shape* s) {
   if (!s || s->T < 0 || s->d <= 0 || s->E <= 0 || s->k < 1 || s->k > s->E || s->F <= 0 || s->Fs < 0) return ERR_INVALID;
-  if (s->w_dtype < W_F32 || s->w_dtype > W_FP8_A16) return ERR_INVALID;
+  if (s->w_dtype < W_F32 || s->w_dtype > W_U4) return ERR_INVALID;
   if ((s->w_dtype == W_FP8 || s->w_dtype == W_FP8_A16) && (s->d % 128 || s->F % 128 || s->Fs % 128))
     return ERR_INVALID;
+  if (s->w_dtype == W_U4 && (s->d % kU4Group || s->F % kU4Group || s->Fs % kU4Group)) return ERR_INVALID;
   return OK;
 }
 

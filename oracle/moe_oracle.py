@@ -14,13 +14,14 @@ import numpy as np
 from . import build as _build
 
 ACT = {"f32": 0, "bf16": 1}
-WDT = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3}
+WDT = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3, "u4": 4}
 OK, ERR_INVALID, ERR_FORCED_INDEX = 0, -1, -5
 
 MUTANTS = {
     "select_unbiased": 1, "router_bf16": 2, "logits_bf16": 3, "tie_highest": 4, "softmax_all": 5,
     "no_shared": 6, "scale_transposed": 7, "reversed_order": 8, "no_h_quant": 9, "weights_biased": 10,
-    "silu_sign": 11, "gate_up_swap": 12, "combine_no_weight": 13,
+    "silu_sign": 11, "gate_up_swap": 12, "combine_no_weight": 13, "u4_nibble_swap": 14, "u4_no_bias": 15,
+    "u4_group128": 16,
 }
 
 
@@ -28,10 +29,13 @@ class _Shape(C.Structure):
     _fields_ = [(n, C.c_int32) for n in ("T", "d", "E", "k", "F", "Fs", "act_dtype", "w_dtype")]
 
 
+_WEIGHT_FIELDS = ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                  "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down",
+                  "b_gate", "b_up", "b_down", "sb_gate", "sb_up", "sb_down")
+
+
 class _Weights(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in (
-        "w_router", "sel_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-        "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")]
+    _fields_ = [(n, C.c_void_p) for n in _WEIGHT_FIELDS]
 
 
 _lib = None
@@ -84,9 +88,7 @@ class Layer:
         if inp.get("sel_bias") is None:
             self._keep.pop("sel_bias", None)
         self.shape = _Shape(s.T, s.d, s.E, s.k, s.F, s.Fs, ACT[s.act], WDT[s.w])
-        self.weights = _Weights(*[_ptr(self._keep.get(n)) for n in (
-            "w_router", "sel_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-            "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")])
+        self.weights = _Weights(*[_ptr(self._keep.get(n)) for n in _WEIGHT_FIELDS])
         self.x = self._keep["x"]
 
     def _args(self):

@@ -540,3 +540,89 @@ def test_w8a16_expert_ffn_vs_textbook():
         assert np.array_equal(xu.view(np.uint32), _x_f32(inp)[t].view(np.uint32))
         ref = _swiglu64(*_fp8_expert_weights(inp, e), xu)
         assert np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref ** 2)) <= 1e-6
+
+
+# ---------------------------------------------------------------- 4-bit weights
+
+def _u4_dequant(codes, scales, biases):
+    """scale * q + bias per (row, group of 64 columns), unpacked with numpy bit
+    operations (the even column in the low nibble) and computed in float64;
+    asserted exact in fp32 so that the fp32-weight mode sees the same values."""
+    codes = np.asarray(codes, np.uint8)
+    R, half = codes.shape
+    q = np.empty((R, 2 * half), np.float64)
+    q[:, 0::2] = codes & 0x0F
+    q[:, 1::2] = codes >> 4
+    s = np.repeat(synth.bf16_bits_to_f32(scales).astype(np.float64), 64, axis=1)
+    b = np.repeat(synth.bf16_bits_to_f32(biases).astype(np.float64), 64, axis=1)
+    w = s * q + b
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+    return w.astype(np.float32)
+
+
+def _small_u4_layer(w_mode, T=16, seed=11, unit=False):
+    """A small layer with 4-bit group-quantised weights (d=256, E=8, k=2,
+    F=Fs=128) as "u4" (codes, scales, biases) or "f32" (the same weights
+    dequantised by _u4_dequant).  unit: every scale 1 and bias 0, so the weights
+    are the integer codes themselves."""
+    rng = np.random.default_rng(seed)
+    d, E, k, F, Fs = 256, 8, 2, 128, 128
+    x = synth.bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    inp = dict(shape=synth.LayerShape(T=T, d=d, E=E, k=k, F=F, Fs=Fs, act="bf16", w=w_mode),
+               x=x, w_router=(rng.standard_normal((E, d), dtype=np.float32) * 0.05).astype(np.float32),
+               sel_bias=None)
+    for pre, sp, bp, dims, n in (("w_", "s_", "b_", (F, d, d, F), E), ("sh_", "ss_", "sb_", (Fs, d, d, Fs), None)):
+        for name, (r, c) in (("gate", dims[:2]), ("up", dims[:2]), ("down", dims[2:])):
+            mats = []
+            for _ in range(n or 1):
+                codes, sc, bi = synth.u4_groups(rng.standard_normal((r, c), dtype=np.float32) * np.float32(0.02))
+                if unit:
+                    sc = np.full_like(sc, 0x3F80)  # bf16 1.0
+                    bi = np.zeros_like(bi)
+                mats.append((codes, sc, bi))
+            if w_mode == "f32":
+                vals = [_u4_dequant(*m) for m in mats]
+                inp[pre + name] = np.stack(vals) if n else vals[0]
+            else:
+                for key, j in ((pre, 0), (sp, 1), (bp, 2)):
+                    inp[key + name] = np.stack([m[j] for m in mats]) if n else mats[0][j]
+    return inp, O.Layer(inp)
+
+
+@pytest.mark.parametrize("unit", [False, True])
+def test_u4_equals_f32_mode_on_dequantised_weights(unit):
+    """The 4-bit mode is the layer on the weights scale * q + bias: bitwise the
+    oracle's fp32-weight mode on the same weights dequantised independently
+    (numpy bit operations, float64, exact in fp32).  With unit scales and zero
+    biases the weights are the integer codes.  Each planted 4-bit mistake (the
+    nibbles swapped, the bias dropped, groups of 128) breaks the equality."""
+    u4, Lu = _small_u4_layer("u4", unit=unit)
+    f32, Lf = _small_u4_layer("f32", unit=unit)
+    _, lu, iu, wu = O.route(Lu)
+    _, lf, i_f, wf = O.route(Lf)
+    assert np.array_equal(lu.view(np.uint32), lf.view(np.uint32)) and np.array_equal(iu, i_f)
+    yu, acc_u = O.forward(Lu, iu, wu)
+    yf, acc_f = O.forward(Lf, i_f, wf)
+    assert np.array_equal(acc_u.view(np.uint32), acc_f.view(np.uint32))
+    assert np.array_equal(yu, yf)
+    rms = np.sqrt(np.mean(acc_f.astype(np.float64) ** 2))
+    for m in ("u4_nibble_swap",) + (() if unit else ("u4_group128", "u4_no_bias")):  # unit: all groups alike
+        with O.mutant(m):
+            _, acc_m = O.forward(Lu, iu, wu)
+        assert np.max(np.abs(acc_m - acc_f)) > 1e-3 * rms, m
+
+
+def test_u4_expert_ffn_vs_textbook():
+    """One expert with 4-bit weights: the activation row enters as its bf16
+    values, and the FFN is the float64 textbook SwiGLU on the dequantised
+    weights."""
+    inp, L = _small_u4_layer("u4")
+    for e, t in ((-1, 2), (0, 7), (5, 13)):
+        xu, y = O.expert_ffn(L, e, t)
+        assert np.array_equal(xu.view(np.uint32), _x_f32(inp)[t].view(np.uint32))
+        if e < 0:
+            ws = [_u4_dequant(inp["sh_" + n], inp["ss_" + n], inp["sb_" + n]) for n in ("gate", "up", "down")]
+        else:
+            ws = [_u4_dequant(inp["w_" + n][e], inp["s_" + n][e], inp["b_" + n][e]) for n in ("gate", "up", "down")]
+        ref = _swiglu64(*ws, xu)
+        assert np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref ** 2)) <= 1e-6
