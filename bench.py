@@ -44,6 +44,8 @@ DESCRIPTION = {
     "ties_t256_bf16w": "near-tie batch, T=256, bf16 expert weights, free routing",
     "decode_t32_w8a16": "decode batch, T=32, the same FP8 weights used as W8A16 (bf16 activations into both "
                         "projections, unquantised), free routing",
+    "decode_t32_u4": "decode batch, T=32, the same layer with 4-bit affine group-quantised expert weights (bf16 "
+                     "scale and bias per row and 64 columns), bf16 activations, free routing",
 }
 FORCED = {"prefill_t2048"}
 
@@ -84,21 +86,23 @@ def parse():
     ap.add_argument("--rotate", type=int, default=4, help="device copies of the expert weights")
     ap.add_argument("--layout", default="tiled", choices=("tiled", "rowmajor"), help="expert-weight layout")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0: skip)")
-    ap.add_argument("--also", default="prefill_t2048,skew_t8192,decode_t32_w8a16", help="extra workloads timed after the main one (comma list)")
+    ap.add_argument("--also", default="prefill_t2048,skew_t8192,decode_t32_w8a16,decode_t32_u4", help="extra workloads timed after the main one (comma list)")
     return ap.parse_args()
 
 
 def algorithmic(s, counts):
     """Algorithmic bytes and flops (what the method must move / compute)."""
-    bw = {"fp8": 1, "fp8a16": 1, "bf16": 2, "f32": 4}[s.w]
+    bw = {"fp8": 1, "fp8a16": 1, "bf16": 2, "f32": 4, "u4": 0.5}[s.w]
     ba = {"bf16": 2, "f32": 4}[s.act]
     U = int((counts > 0).sum())
     P = s.T * s.k
     fp8 = s.w == "fp8"                # activations and h quantised to E4M3
     scaled = s.w in ("fp8", "fp8a16")  # block-scaled FP8 weights
-    nb = lambda r, c: (r // 128) * (c // 128) * 4 if scaled else 0  # block-scale bytes
-    gu_w = U * 2 * (s.F * s.d * bw + nb(s.F, s.d)) + 2 * (s.Fs * s.d * bw + nb(s.Fs, s.d))
-    dn_w = U * (s.d * s.F * bw + nb(s.d, s.F)) + (s.d * s.Fs * bw + nb(s.d, s.Fs))
+
+    def nb(r, c):  # scale bytes: fp32 per 128x128 block, or a bf16 scale and bias per row and 64 columns
+        return (r // 128) * (c // 128) * 4 if scaled else (r * (c // 64) * 4 if s.w == "u4" else 0)
+    gu_w = int(U * 2 * (s.F * s.d * bw + nb(s.F, s.d)) + 2 * (s.Fs * s.d * bw + nb(s.Fs, s.d)))
+    dn_w = int(U * (s.d * s.F * bw + nb(s.d, s.F)) + (s.d * s.Fs * bw + nb(s.d, s.Fs)))
     act_in = s.T * s.d + s.T * (s.d // 128) * 4 if fp8 else s.T * s.d * ba
     h_rows = P + s.T
     h_bytes = h_rows * s.F * (1 if fp8 else 2) + (h_rows * (s.F // 128) * 4 if fp8 else 0)
@@ -122,7 +126,7 @@ def run_workload(name, steps, warmup, rotate, layout):
     if layout == "tiled":
         dev = moe.pack_layer_weights(dev)
     shape = moe.shape_of(s, layout=layout)
-    wkeys = ("w_gate", "w_up", "w_down")
+    wkeys = ("w_gate", "w_up", "w_down") + (("s_gate", "s_up", "s_down") if s.w == "u4" else ())
     copies = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, rotate - 1))]
     r = moe.alloc_routing(shape, "cuda:0")
     ws = moe.alloc_workspace(shape, "cuda:0")

@@ -55,14 +55,20 @@ typedef enum {
   MOE_FP8E4M3_B128 = 2,  /* OCP FP8 E4M3 codes, value = decode(code) * scale of its
                             128 x 128 block (fp32 scales); weights only.  The activations
                             entering each projection are quantised to E4M3 (see moe_forward) */
-  MOE_FP8E4M3_B128_A16 = 3 /* the same weights as W8A16: activations enter both
+  MOE_FP8E4M3_B128_A16 = 3, /* the same weights as W8A16: activations enter both
                               projections in bf16, unquantised, and h stays bf16
                               ([cache]: the CPU runtime decodes the FP8 weights for its
                               matmuls on bf16 activations); weights only */
+  MOE_U4_G64 = 4           /* 4-bit affine groups: per row and group of 64 consecutive
+                              columns a bf16 scale and bias, value = scale * q + bias
+                              with q the unsigned 4-bit code (the 4-bit build of [bench]
+                              "The gate, forced", read as MLX's default group
+                              quantisation); activations enter in bf16, unquantised,
+                              and h stays bf16; weights only, MOE_LAYOUT_TILED only */
 } moe_dtype;
 
 /* Supported (act_dtype, w_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8E4M3_B128),
- * (BF16, FP8E4M3_B128_A16).
+ * (BF16, FP8E4M3_B128_A16), (BF16, U4_G64).
  * Limits: 1 <= top_k <= 8, top_k <= n_experts <= 512, d_model and d_ffn multiples
  * of 128 with d_model <= 8192 and d_ffn <= 4096, d_ffn_shared 0 (no shared expert)
  * or a multiple of 128 <= 4096, T * top_k < 2^31. */
@@ -70,7 +76,9 @@ typedef enum {
 typedef enum {
   MOE_LAYOUT_ROWMAJOR = 0,   /* [rows][cols] row-major, as documented per tensor */
   MOE_LAYOUT_TILED = 1       /* the same bytes regrouped by moe_pack_weights into 2 KB
-                                tiles of 16 rows x 128 bytes (bf16: 64 columns) */
+                                tiles of 16 rows x 128 bytes (bf16: 64 columns); 4-bit
+                                weights: the codes and group parameters as
+                                moe_pack_weights_u4 writes them */
 } moe_layout;
 
 typedef struct {
@@ -83,11 +91,15 @@ typedef struct {
   int32_t act_dtype;     /* moe_dtype of x and y: MOE_F32 or MOE_BF16 */
   int32_t w_dtype;       /* moe_dtype of the expert weights */
   int32_t w_layout;      /* moe_layout of w_gate, w_up, w_down, sh_gate, sh_up, sh_down;
-                            MOE_LAYOUT_TILED needs w_dtype BF16 or an FP8 one */
+                            MOE_LAYOUT_TILED needs w_dtype BF16, an FP8 one or U4_G64;
+                            U4_G64 needs MOE_LAYOUT_TILED */
 } moe_shape;
 
 /* Layer weights.  Expert matrices are (out, in) row-major and stacked by expert.
- * Scales are required for MOE_FP8E4M3_B128 and MOE_FP8E4M3_B128_A16 and ignored
+ * Scales are required for MOE_FP8E4M3_B128 and MOE_FP8E4M3_B128_A16 (fp32 block
+ * scales, shapes below) and for MOE_U4_G64 (each s_* / ss_* then points to the
+ * group parameters moe_pack_weights_u4 wrote for that matrix stack, 4 bytes per
+ * row and 64-column group, and w_* / sh_* to its packed codes), and ignored
  * otherwise.
  *   [port] "The gate": a router scores the experts for every token and a shared
  *   expert serves every token; part 1 of "Taking it apart": selection uses the
@@ -100,15 +112,15 @@ typedef struct {
   const void *w_gate;     /* [E, F, d] */
   const void *w_up;       /* [E, F, d] */
   const void *w_down;     /* [E, d, F] */
-  const float *s_gate;    /* [E, F/128, d/128] block scales */
-  const float *s_up;      /* [E, F/128, d/128] */
-  const float *s_down;    /* [E, d/128, F/128] */
+  const void *s_gate;     /* [E, F/128, d/128] block scales */
+  const void *s_up;       /* [E, F/128, d/128] */
+  const void *s_down;     /* [E, d/128, F/128] */
   const void *sh_gate;    /* shared expert [Fs, d] (ignored when Fs == 0) */
   const void *sh_up;      /* [Fs, d] */
   const void *sh_down;    /* [d, Fs] */
-  const float *ss_gate;   /* [Fs/128, d/128] */
-  const float *ss_up;     /* [Fs/128, d/128] */
-  const float *ss_down;   /* [d/128, Fs/128] */
+  const void *ss_gate;    /* [Fs/128, d/128] */
+  const void *ss_up;      /* [Fs/128, d/128] */
+  const void *ss_down;    /* [d/128, Fs/128] */
 } moe_weights;
 
 /* Routing results (written by moe_route / moe_route_forced, read by moe_forward).
@@ -167,7 +179,10 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
  * per 128-element group to E4M3 with scale amax/448 (round to nearest even,
  * saturating); with MOE_FP8E4M3_B128_A16 they enter as bf16 (h rounded to bf16).
  * With either, each 128 x 128 block's products are summed exactly in fp32 and
- * the block scales applied in fp32.  Combine per token, in
+ * the block scales applied in fp32.  With MOE_U4_G64 x and h (rounded to bf16)
+ * enter as bf16 and each weight is scale * q + bias of its (row, 64-column
+ * group), summed per group in fp32 as scale * sum(x * q) + bias * sum(x).
+ * Combine per token, in
  * fp32 and this order: acc = shared; acc += w_j * y_j for j = 0..k-1;
  * y = acc rounded to act_dtype (bf16: round to nearest even).
  * `r` must hold the results of moe_route / moe_route_forced for the same shape
@@ -225,6 +240,22 @@ int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const v
  * matrices with n_mats = 1; scales, router and bias keep their layout.  This
  * is a data-layout choice of this library, not something the method needs. */
 int moe_pack_weights(int64_t n_mats, int32_t rows, int32_t row_bytes, const void *in, void *out, void *stream);
+
+/* 4-bit weights (MOE_U4_G64) into MOE_LAYOUT_TILED.  Input, per matrix of the
+ * n_mats stacked [rows][cols] matrices (rows a multiple of 16, cols of 128):
+ * codes [rows][cols/2] bytes, column c of a row in byte c/2, the even column in
+ * the low nibble; scales and biases [rows][cols/64] bf16 (group g = columns
+ * 64g .. 64g+63).  Output: codes_out (same size as codes) and params_out
+ * ([rows][cols/64] x 4 bytes).  Codes: tile (rt, kb) -- rows 16*rt .. 16*rt+15,
+ * columns 128*kb .. 128*kb+127 -- is 1 KB at 1024*(rt*(cols/128) + kb); its
+ * 32-bit word 4*l + m holds row 16*rt + l%16 and columns 128*kb + 32*m +
+ * 8*(l/16) + [0, 8), the even column 2j of those 8 in bits 4j..4j+3 and the
+ * odd column 2j+1 in bits 16+4j..19+4j.  Group parameters: 8 bytes at
+ * 8*(16*(rt*(cols/128) + kb) + r) for row 16*rt + r: the bf16 scale and bias of
+ * group 2*kb, then those of group 2*kb + 1.  Inputs and outputs must not
+ * overlap.  This regrouping is a data-layout choice of this library. */
+int moe_pack_weights_u4(int64_t n_mats, int32_t rows, int32_t cols, const void *codes, const uint16_t *scales,
+                        const uint16_t *biases, void *codes_out, void *params_out, void *stream);
 
 /* Static description of a status code. */
 const char *moe_status_string(int status);

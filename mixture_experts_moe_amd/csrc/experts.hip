@@ -614,8 +614,381 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up and down in one launch (FP8 weights with E4M3 or, A16, bf16
-// activations; 16-row tiles, tile-list schedule).  Blocks [0, n_gu) do the
+// 4-bit weights (MOE_U4_G64): element value = scale * q + bias per (row, group
+// of 64 columns), bf16 activations and h.  The codes arrive in
+// MOE_LAYOUT_TILED as moe_pack_weights_u4 writes them: per 16-row tile and
+// 128-column block 1 KB, in which lane l's 16 bytes (at 16*l) belong to row
+// l%16 and word m of them to columns 128*kb + 32*m + 8*(l/16) + [0, 8), nibble
+// order (0, 2, 4, 6 | 1, 3, 5, 7), so that (w >> 4i) & 0x000F000F isolates
+// columns 2i and 2i+1 in the two 16-bit halves.  OR-ing 0x4300 into a half
+// makes it the bf16 value 128 + q exactly, and the matrix cores sum
+// x * (128 + q) exactly-multiplied in fp32 over each 32-column step.  A group
+// is two whole steps, so per group
+//     sum_i x_i * (scale * q_i + bias) = scale * S + (bias - 128 * scale) * X
+// with S the group's matrix-core sum and X = sum_i x_i (added up once per row
+// while the rows are staged).  The weights are the B operand: a lane's output
+// column is its own weight row, so it needs one (scale, bias) pair per group,
+// and the packed group parameters give it 8 bytes per 128-column block (the
+// scale and bias of its row's two groups).  Output lanes hold rows 4*(l/16) + v
+// of one column; a 4x4 transpose inside each quad of lanes turns that into four
+// consecutive columns of one row for the stores.
+// ---------------------------------------------------------------------------
+
+// Eight 4-bit codes (one packed word) as eight bf16 values 128 + q.
+__device__ __forceinline__ v4i u4_word_to_bf16(uint32_t w) {
+  v4i r;
+  r[0] = (int)((w & 0x000F000Fu) | 0x43004300u);
+  r[1] = (int)(((w >> 4) & 0x000F000Fu) | 0x43004300u);
+  r[2] = (int)(((w >> 8) & 0x000F000Fu) | 0x43004300u);
+  r[3] = (int)(((w >> 12) & 0x000F000Fu) | 0x43004300u);
+  return r;
+}
+
+// Sum of the eight bf16 values of a 16-byte chunk, then over the eight
+// consecutive lanes that hold one 64-column group (all lanes must call it).
+__device__ __forceinline__ float group_sum_bf16x8(v4i x) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    s += __uint_as_float((uint32_t)x[j] << 16) + __uint_as_float((uint32_t)x[j] & 0xffff0000u);
+  s += __shfl_xor(s, 1, kWave);
+  s += __shfl_xor(s, 2, kWave);
+  s += __shfl_xor(s, 4, kWave);
+  return s;
+}
+
+// One 64-column group's contribution to a lane's four outputs: S is the
+// matrix-core sum of x * (128 + q), pv the group's bf16 scale (low half) and
+// bias (high half), X the four rows' sums of x over the group.
+__device__ __forceinline__ v4f u4_group_term(v4f S, uint32_t pv, v4f X) {
+  const float sc = __uint_as_float(pv << 16), bi = __uint_as_float(pv & 0xffff0000u);
+  return sc * S + fmaf(-128.0f, sc, bi) * X;
+}
+
+// 4x4 transpose inside each quad of lanes: lane i of a quad holds column i of
+// a 4x4 block (a[v] = C[v][i]); afterwards it holds row i (a[v] = C[i][v]).
+// All lanes must call it.
+__device__ __forceinline__ v4f quad_transpose(v4f a) {
+  const int i = threadIdx.x & 3;
+  const bool odd = i & 1, upper = i & 2;
+  float s0 = odd ? a[0] : a[1], s1 = odd ? a[2] : a[3];
+  float r0 = __shfl_xor(s0, 1, kWave), r1 = __shfl_xor(s1, 1, kWave);
+  if (odd) {
+    a[0] = r0;
+    a[2] = r1;
+  } else {
+    a[1] = r0;
+    a[3] = r1;
+  }
+  s0 = upper ? a[0] : a[2];
+  s1 = upper ? a[1] : a[3];
+  r0 = __shfl_xor(s0, 2, kWave);
+  r1 = __shfl_xor(s1, 2, kWave);
+  if (upper) {
+    a[0] = r0;
+    a[1] = r1;
+  } else {
+    a[2] = r0;
+    a[3] = r1;
+  }
+  return a;
+}
+
+// Gate/up with 4-bit weights: 16-row tiles, 8 waves, one 128-feature group nb
+// of h per block (as for FP8 weights); wave w owns features nb*128 + 16w +
+// [0, 16) of W_gate and W_up, streamed gate run first, then up run, KG blocks
+// of 128 columns per stage, two stages in flight.  COH: h stored coherently
+// (the fused expert launch).
+template <bool COH>
+__device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint8_t* smem) {
+  constexpr int BM = 16, NT = kGateUpWaves * 64, KG = 4, SB = 4;
+  int nb;
+  const TileRows tr = block_rows(a, b, nb);
+  if (tr.g < 0) return false;
+  const int Fg = tr.shared ? a.Fs : a.F;
+  if (nb * 128 >= Fg) return false;
+  const int d = a.d, nkb = d / 128, ng = d / 64;
+  const int xstride = d * 2 + 16;                     // padded LDS row of bf16 activations
+  uint8_t* xs = smem;                                 // [BM + 1][xstride] (a spare row)
+  float* xsum = (float*)(smem + (BM + 1) * xstride);  // [d/64][BM] group sums of each row
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+  const size_t cbytes = (size_t)a.F * d / 2, pbytes = (size_t)a.F * ng * 4;  // one routed matrix
+  const uint8_t* cg = tr.shared ? (const uint8_t*)a.shg : (const uint8_t*)a.wg + (size_t)tr.g * cbytes;
+  const uint8_t* cu = tr.shared ? (const uint8_t*)a.shu : (const uint8_t*)a.wu + (size_t)tr.g * cbytes;
+  const uint8_t* pg = tr.shared ? (const uint8_t*)a.ssg : (const uint8_t*)a.sg + (size_t)tr.g * pbytes;
+  const uint8_t* pu = tr.shared ? (const uint8_t*)a.ssu : (const uint8_t*)a.su + (size_t)tr.g * pbytes;
+  const int f0 = nb * 128 + wave * 16;
+  const size_t t0 = (size_t)(f0 / 16) * nkb;  // the wave's first tile block
+  const uint8_t* cs[2] = {cg + t0 * 1024 + lane * 16, cu + t0 * 1024 + lane * 16};
+  const uint8_t* ps[2] = {pg + t0 * 128 + lr * 8, pu + t0 * 128 + lr * 8};
+
+  // Stage st < nq: gate blocks [st*KG, st*KG + KG); else up blocks of st - nq.
+  // Loads are unconditional (a short last stage re-reads the final block).
+  const int nq = (nkb + KG - 1) / KG, ns = 2 * nq;
+  v4i wc[2][KG];
+  uint2 wp[2][KG];
+  auto load = [&](auto S, int st) {
+    constexpr int sl = decltype(S)::value;
+    const bool up = st >= nq;
+    const int q = up ? st - nq : st;
+    const uint8_t* c = up ? cs[1] : cs[0];
+    const uint8_t* p = up ? ps[1] : ps[0];
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const int kb = min(q * KG + j, nkb - 1);
+      wc[sl][j] = stream_load<true>(c + (size_t)kb * 1024);
+      wp[sl][j] = *(const uint2*)(p + (size_t)kb * 128);
+    }
+  };
+
+  // Staging, in pinned issue order: row tokens, the weight stream, then the
+  // activation rows (bf16, zero past the tile) and their per-group sums.
+  const int cpr = d / 8, nch = BM * cpr;  // 16-byte chunks per row / per tile
+  const uint8_t* xa = (const uint8_t*)a.xa;
+  const int rlast = tr.rows - 1;
+  auto stage = [&](int i0, bool first) {
+    int tk[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) tk[u] = a.ri.tok[tr.hrow0 + min((i0 + u * NT) / cpr, rlast)];
+    if (first) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(Ic<0>{}, 0);
+      load(Ic<1>{}, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    v4i v[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) v[u] = *(const v4i*)(xa + (size_t)tk[u] * d * 2 + ((i0 + u * NT) % cpr) * 16);
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
+      const v4i z = {0, 0, 0, 0};
+      const v4i x = i < nch && r <= rlast ? v[u] : z;
+      *(v4i*)(xs + (i < nch ? r : BM) * xstride + (i < nch ? c : 0) * 16) = x;
+      const float s = group_sum_bf16x8(x);  // the group's 8 chunks sit in 8 consecutive lanes
+      if ((tid & 7) == 0 && i < nch) xsum[(c / 8) * BM + r] = s;
+    }
+  };
+  stage(tid, true);
+  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
+  __syncthreads();
+
+  v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  auto compute_run = [&](auto R, auto S, int q) {
+    constexpr int r = decltype(R)::value, sl = decltype(S)::value;
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const int kb = q * KG + j;
+      if (kb >= nkb) break;
+      const uint8_t* xp = xs + lr * xstride + kb * 256 + q4 * 16;  // columns 128 kb + 32 m + 8 q4
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4f S = {0.f, 0.f, 0.f, 0.f};
+        S = mfma_bf16(*(const v4i*)(xp + 128 * h), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h]), S);
+        S = mfma_bf16(*(const v4i*)(xp + 128 * h + 64), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h + 1]), S);
+        const v4f X = *(const v4f*)(xsum + (2 * kb + h) * BM + 4 * q4);
+        acc[r] += u4_group_term(S, h ? wp[sl][j].y : wp[sl][j].x, X);
+      }
+    }
+  };
+  auto compute = [&](auto S, int st) {
+    if (st < nq) compute_run(Ic<0>{}, S, st);
+    else compute_run(Ic<1>{}, S, st - nq);
+  };
+  int st = 0;
+  for (; st + 2 < ns; st += 2) {  // ns is even: both loads of the body are in range
+    compute(Ic<0>{}, st);
+    load(Ic<0>{}, st + 2);
+    compute(Ic<1>{}, st + 1);
+    load(Ic<1>{}, st + 3);
+  }
+  compute(Ic<0>{}, st);
+  compute(Ic<1>{}, st + 1);
+
+  // h = silu(g) * u for rows 4*q4 + v of feature f0 + lr, then transposed to
+  // row 4*q4 + lane%4, features f0 + 4*((lane/4)%4) + v.
+  v4f hv;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float gv = acc[0][v], uv = acc[1][v];
+    hv[v] = gv / (1.0f + expf(-gv)) * uv;
+  }
+  hv = quad_transpose(hv);
+  const int rr = 4 * q4 + (lane & 3);
+  if (rr < tr.rows) {
+    uint2 pk;
+    pk.x = (uint32_t)f32_to_bf16(hv[0]) | ((uint32_t)f32_to_bf16(hv[1]) << 16);
+    pk.y = (uint32_t)f32_to_bf16(hv[2]) | ((uint32_t)f32_to_bf16(hv[3]) << 16);
+    uint16_t* hp = (uint16_t*)a.h + (size_t)(tr.hrow0 + rr) * a.hstride + f0 + 4 * ((lane >> 2) & 3);
+    if constexpr (COH) {
+      store_coherent(hp, pk.x);
+      store_coherent(hp + 2, pk.y);
+    } else {
+      *(uint2*)hp = pk;
+    }
+  }
+  return true;
+}
+
+template <bool COH>
+__global__ __launch_bounds__(kGateUpWaves * 64) void gateup_u4_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  gateup_block_u4<COH>(a, blockIdx.x, smem);
+}
+
+// Down projection with 4-bit weights: NW waves, each owning RT 16-row tiles
+// of W_down (features (nb*NW + w)*16*RT + 16 r).  RT = 2 holds both tiles'
+// whole rows in registers (F <= 640: up to 5 blocks of 128 columns each);
+// RT = 1 streams one tile's row in stages of 4 blocks, two in flight.  The
+// epilogue multiplies by the pair's routing weight and writes fp32 partials.
+template <int RT, int NW, bool COH>
+__device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_t* smem) {
+  constexpr int BM = 16, NT = NW * 64, SB = 4;
+  constexpr int KG = RT == 2 ? 5 : 4;  // 128-column blocks per register slot
+  int nb;
+  const TileRows tr = block_rows(a, b, nb);
+  if (tr.g < 0) return;
+  const int Fg = tr.shared ? a.Fs : a.F;
+  const int nkb = Fg / 128, ng = Fg / 64;
+  const int lstride = Fg * 2 + 16;
+  uint8_t* hs = smem;                                 // [BM + 1][lstride] bf16 h rows
+  float* hsum = (float*)(smem + (BM + 1) * lstride);  // [Fg/64][BM] group sums of each row
+  float* wrow = hsum + ng * BM;                       // [BM] routing weight
+  int* orow = (int*)(wrow + BM);                      // [BM] partial-output row
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+  const int n0 = (nb * NW + wave) * 16 * RT;
+  const bool wave_live = n0 < a.d;  // d is a multiple of 16*RT: whole waves are live or not
+  const int nl = wave_live ? n0 : 0;
+  const size_t cbytes = (size_t)a.d * a.F / 2, pbytes = (size_t)a.d * (a.F / 64) * 4;  // one routed matrix
+  const uint8_t* cd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * cbytes;
+  const uint8_t* pd = tr.shared ? (const uint8_t*)a.ssd : (const uint8_t*)a.sd + (size_t)tr.g * pbytes;
+  const size_t t0 = (size_t)(nl / 16) * nkb;
+  const uint8_t* cs = cd + t0 * 1024 + lane * 16;  // tile r of the wave: + r * nkb blocks
+  const uint8_t* ps = pd + t0 * 128 + lr * 8;
+
+  v4i wc[2][KG];
+  uint2 wp[2][KG];
+  auto load = [&](auto S, int r, int q) {  // blocks [q*KG, q*KG + KG) of tile r (clamped: re-reads in bounds)
+    constexpr int sl = decltype(S)::value;
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const size_t kb = (size_t)r * nkb + min(q * KG + j, nkb - 1);
+      wc[sl][j] = stream_load<true>(cs + kb * 1024);
+      wp[sl][j] = *(const uint2*)(ps + kb * 128);
+    }
+  };
+
+  // Staging, in pinned issue order: h rows, the weight stream, the rows'
+  // routing weights and output rows; then h to LDS with its group sums.
+  const int hrow0 = tr.hrow0, rlast = tr.rows - 1;
+  const int cpr = Fg / 8, nch = BM * cpr;
+  const uint8_t* hsrc = (const uint8_t*)a.h;
+  const int o = a.ri.prow[hrow0 + min(tid, rlast)];
+  auto stage_load = [&](int i0, v4i (&v)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * NT, r = min(i / cpr, rlast), c = i % cpr;
+      const uint8_t* hp = hsrc + ((size_t)(hrow0 + r) * a.hstride + c * 8) * 2;
+      if constexpr (COH) {  // coherent loads skip the L2: fetch only chunks of live rows
+        v[u] = v4i{0, 0, 0, 0};
+        if (i < nch && i / cpr <= rlast)
+          v[u] = v4i{(int)load_coherent(hp), (int)load_coherent(hp + 4), (int)load_coherent(hp + 8),
+                     (int)load_coherent(hp + 12)};
+      } else {
+        v[u] = *(const v4i*)hp;
+      }
+    }
+  };
+  auto stage_store = [&](int i0, const v4i (&v)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
+      const v4i z = {0, 0, 0, 0};
+      const v4i x = i < nch && r <= rlast ? v[u] : z;
+      *(v4i*)(hs + (i < nch ? r : BM) * lstride + (i < nch ? c : 0) * 16) = x;
+      const float s = group_sum_bf16x8(x);
+      if ((tid & 7) == 0 && i < nch) hsum[(c / 8) * BM + r] = s;
+    }
+  };
+  v4i hv[SB];
+  stage_load(tid, hv);
+  __builtin_amdgcn_sched_barrier(0);
+  load(Ic<0>{}, 0, 0);
+  if (RT == 2) load(Ic<1>{}, 1, 0);
+  else load(Ic<1>{}, 0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+  const float wt = a.ri.w[hrow0 + min(tid, rlast)];
+  stage_store(tid, hv);
+  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) {
+    stage_load(i0, hv);
+    stage_store(i0, hv);
+  }
+  if (tid < BM) {
+    orow[tid] = tid <= rlast ? o : -1;
+    wrow[tid] = tid <= rlast ? wt : 0.f;
+  }
+  __syncthreads();
+  if (!wave_live) return;
+
+  v4f acc[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](auto R, auto S, int q) {
+    constexpr int r = decltype(R)::value, sl = decltype(S)::value;
+#pragma unroll
+    for (int j = 0; j < KG; ++j) {
+      const int kb = q * KG + j;
+      if (kb >= nkb) break;
+      const uint8_t* xp = hs + lr * lstride + kb * 256 + q4 * 16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        v4f S = {0.f, 0.f, 0.f, 0.f};
+        S = mfma_bf16(*(const v4i*)(xp + 128 * h), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h]), S);
+        S = mfma_bf16(*(const v4i*)(xp + 128 * h + 64), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h + 1]), S);
+        const v4f X = *(const v4f*)(hsum + (2 * kb + h) * BM + 4 * q4);
+        acc[r] += u4_group_term(S, h ? wp[sl][j].y : wp[sl][j].x, X);
+      }
+    }
+  };
+  if constexpr (RT == 2) {  // whole rows in registers (nkb <= KG)
+    compute(Ic<0>{}, Ic<0>{}, 0);
+    compute(Ic<1>{}, Ic<1>{}, 0);
+  } else {
+    const int nq = (nkb + KG - 1) / KG;
+    int q = 0;
+    for (; q + 2 < nq; q += 2) {
+      compute(Ic<0>{}, Ic<0>{}, q);
+      load(Ic<0>{}, 0, q + 2);
+      compute(Ic<0>{}, Ic<1>{}, q + 1);
+      load(Ic<1>{}, 0, q + 3);
+    }
+    compute(Ic<0>{}, Ic<0>{}, q);
+    if (q + 1 < nq) compute(Ic<0>{}, Ic<1>{}, q + 1);
+  }
+
+  const int rr = 4 * q4 + (lane & 3);
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    const v4f v = quad_transpose(acc[r]) * wrow[rr];
+    if (rr < tr.rows)
+      *(float4*)(a.part + (size_t)orow[rr] * a.d + n0 + r * 16 + 4 * ((lane >> 2) & 3)) =
+          make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <int RT>
+__global__ __launch_bounds__(256) void down_u4_kernel(ExpertArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  down_block_u4<RT, 4, false>(a, blockIdx.x, smem);
+}
+
+// ---------------------------------------------------------------------------
+// Gate/up and down in one launch (FP8 weights with E4M3 or bf16 activations,
+// or 4-bit weights; 16-row tiles, tile-list schedule).  Blocks [0, n_gu) do the
 // gate/up work; the rest are 8-wave down blocks (256 output features each).  A
 // gate/up block stores its h rows (and their scales) coherently (agent-scope atomic stores, written through to where every
 // XCD reads them), waits until each of its waves' stores has completed, and
@@ -638,7 +1011,8 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kSpinLimit = 1 << 22;  // polls of about 64 cycles each: far beyond any real wait
 
-template <bool A16>
+// WM: the weight mode -- 2 FP8, 3 FP8 as W8A16, 4 4-bit groups.
+template <int WM>
 __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(ExpertArgs gu, ExpertArgs dn, int n_gu,
                                                                           int32_t* __restrict__ ready,
                                                                           int32_t* __restrict__ done,
@@ -646,7 +1020,10 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(Expert
   extern __shared__ __align__(16) uint8_t smem[];
   const int b = blockIdx.x;
   if (b < n_gu) {
-    if (gateup_block<16, 2, true, true, A16>(gu, b, smem)) {
+    bool worked;
+    if constexpr (WM == 4) worked = gateup_block_u4<true>(gu, b, smem);
+    else worked = gateup_block<16, 2, true, true, WM == 3>(gu, b, smem);
+    if (worked) {
       __builtin_amdgcn_s_waitcnt(0);  // this wave's coherent stores have completed ...
       __syncthreads();                // ... and so have every other wave's
       if (threadIdx.x == 0) atomicAdd(&ready[b / gu.nsl], 1);
@@ -668,7 +1045,8 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(Expert
     }
   }
   __syncthreads();  // h is read below, with coherent loads, after the count was seen
-  down_block<16, 2, 2, kGateUpWaves, true, A16>(dn, bd, smem);
+  if constexpr (WM == 4) down_block_u4<2, kGateUpWaves, true>(dn, bd, smem);
+  else down_block<16, 2, 2, kGateUpWaves, true, WM == 3>(dn, bd, smem);
   __syncthreads();
   if (threadIdx.x == 0 && atomicAdd(&done[tile], 1) == dn.nsl - 1) {  // the tile's last down block
     atomicExch(&ready[tile], 0);
@@ -822,9 +1200,11 @@ static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, co
 // (decoded per use) so that two blocks fit a CU.
 static bool gateup_x_bf16(int BM, int wmode) { return wmode != 2 || BM <= 16; }
 
-// wmode: the moe_dtype of the weights (0 f32, 1 bf16, 2 FP8, 3 FP8 as W8A16).
+// wmode: the moe_dtype of the weights (0 f32, 1 bf16, 2 FP8, 3 FP8 as W8A16,
+// 4 4-bit groups).
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
+  if (wmode == 4) return (size_t)(BM + 1) * (d * 2 + 16) + (size_t)(d / 64) * BM * 4;
   size_t b = (size_t)(BM + 1) * ((gateup_x_bf16(BM, wmode) ? d * 2 : d) + 16);  // plus a spare row
   if (wmode >= 2) b += (size_t)BM * (d / 128) * 4 + 2 * (d / 128) * 4;
   return b + kGateUpWaves * BM * 4;
@@ -832,6 +1212,7 @@ size_t gateup_lds_bytes(int BM, int wmode, int d) {
 
 size_t down_lds_bytes(int BM, int wmode, int Fg) {
   if (wmode == 0) return (size_t)BM * Fg * 4;
+  if (wmode == 4) return (size_t)(BM + 1) * (Fg * 2 + 16) + (size_t)(Fg / 64) * BM * 4 + BM * 4 + BM * 4;
   size_t b = (size_t)(BM + 1) * (Fg * 2 + 16);  // h as bf16, plus a spare row
   if (wmode >= 2) b += (size_t)BM * (Fg / 128) * 4 + 2 * (Fg / 128) * 4;
   return b + BM * 4 + BM * 4;
@@ -843,6 +1224,7 @@ int down_rows_per_wave(int BM, int wmode, int Fmax, int d) {
   // 2 for short tiles, 4 for tall ones, whose h rows are then staged once per
   // 256 output features
   if (wmode == 0) return 1;
+  if (wmode == 4) return Fmax <= 5 * 128 ? 2 : 1;
   const bool one_stage = Fmax * (wmode >= 2 ? 1 : 2) <= 5 * 128;
   return !one_stage ? 1 : (BM == 16 ? (d % 128 == 0 ? 2 : 1) : (d % 256 == 0 ? 4 : 1));
 }
@@ -869,11 +1251,12 @@ hipError_t launch_gateup(const ExpertArgs& a0, int wmode, const Plan& plan, hipS
   if (wmode == 2 && BM == 32) return launch_dyn(gateup_mfma_kernel<32, 2, false>, grid, lds, st, a, nt);
   if (wmode == 1 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 1, true>, grid, lds, st, a, nt);
   if (wmode == 3 && BM == 16) return launch_dyn(gateup_mfma_kernel<16, 2, true, true>, grid, lds, st, a, nt);
+  if (wmode == 4 && BM == 16) return launch_dyn(gateup_u4_kernel<false>, grid, lds, st, a, nt);
   return hipErrorInvalidValue;
 }
 
 bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d) {
-  return (wmode == 2 || wmode == 3) && plan.BM == 16 && !plan.xcd && plan.sync &&
+  return wmode >= 2 && wmode <= 4 && plan.BM == 16 && !plan.xcd && plan.sync &&
          down_rows_per_wave(16, wmode, Fmax, d) == 2 && d % (kGateUpWaves * 32) == 0;
 }
 
@@ -889,7 +1272,7 @@ hipError_t launch_experts_fused(const ExpertArgs& a0, int wmode, const Plan& pla
   size_t lds = gateup_lds_bytes(16, wmode, a0.d);
   const size_t ldn = down_lds_bytes(16, wmode, Fmax);
   if (ldn > lds) lds = ldn;
-  auto kernel = wmode == 3 ? experts_fused_kernel<true> : experts_fused_kernel<false>;
+  auto kernel = wmode == 4 ? experts_fused_kernel<4> : wmode == 3 ? experts_fused_kernel<3> : experts_fused_kernel<2>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -911,6 +1294,8 @@ hipError_t launch_down(const ExpertArgs& a0, int wmode, const Plan& plan, hipStr
   const int RT = down_rows_per_wave(BM, wmode, Fmax, a.d);
   if (wmode == 2 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2>, grid, lds, st, a);
   if (wmode == 3 && RT == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 2, true>, grid, lds, st, a);
+  if (wmode == 4 && RT == 2 && BM == 16) return launch_dyn(down_u4_kernel<2>, grid, lds, st, a);
+  if (wmode == 4 && RT == 1 && BM == 16) return launch_dyn(down_u4_kernel<1>, grid, lds, st, a);
   if (wmode == 2 && RT == 4 && BM == 32) return launch_dyn(down_mfma_kernel<32, 2, 4>, grid, lds, st, a);
   if (RT != 1) return hipErrorInvalidValue;
   if (wmode == 2 && BM == 16) return launch_dyn(down_mfma_kernel<16, 2, 1>, grid, lds, st, a);
@@ -944,6 +1329,66 @@ hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const vo
   const int64_t n_slots = n_mats * rows * (int64_t)row_bytes / 16;
   const int64_t blocks = (n_slots + 255) / 256;
   pack_weights_kernel<<<(unsigned)blocks, 256, 0, st>>>((const uint8_t*)in, (uint8_t*)out, n_slots, rows, row_bytes);
+  return hipGetLastError();
+}
+
+// 4-bit weights into MOE_LAYOUT_TILED.  Codes: one thread per 4-byte output
+// word -- word m of slot l in tile (rt, kb) holds row 16*rt + l%16, columns
+// 128*kb + 32*m + 8*(l/16) + [0, 8), nibble j < 4 the even column 2j of them
+// and nibble 4 + j the odd column 2j + 1.  Group parameters: one thread per
+// (tile, block, row) entry of 8 bytes -- bf16 (scale, bias) of group 2*kb, then
+// of group 2*kb + 1.
+__global__ __launch_bounds__(256) void pack_u4_codes_kernel(const uint8_t* __restrict__ in,
+                                                            uint32_t* __restrict__ out, int64_t n_words, int rows,
+                                                            int cols) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n_words) return;
+  const int nkb = cols / 128;
+  const int64_t mat_words = (int64_t)rows * cols / 8;
+  const int64_t m = i / mat_words, r = i - m * mat_words;
+  const int64_t blk = r / 256;  // 1 KB = 256 words per tile block
+  const int w = (int)(r % 256), l = w / 4, word = w % 4;
+  const int rt = (int)(blk / nkb), kb = (int)(blk % nkb);
+  const int row = rt * 16 + (l & 15), col = kb * 128 + 32 * word + 8 * (l >> 4);
+  const uint8_t* src = in + (m * rows + row) * (int64_t)(cols / 2) + col / 2;
+  uint32_t o = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {  // source byte j: column col + 2j (low nibble), col + 2j + 1 (high)
+    const uint32_t byte = src[j];
+    o |= (byte & 0xFu) << (4 * j);
+    o |= (byte >> 4) << (16 + 4 * j);
+  }
+  out[i] = o;
+}
+
+__global__ __launch_bounds__(256) void pack_u4_params_kernel(const uint16_t* __restrict__ scales,
+                                                             const uint16_t* __restrict__ biases,
+                                                             uint2* __restrict__ out, int64_t n, int rows, int cols) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int nkb = cols / 128, ng = cols / 64;
+  const int64_t per_mat = (int64_t)rows * nkb;
+  const int64_t m = i / per_mat, e = i - m * per_mat;
+  const int r = (int)(e % 16);
+  const int64_t tb = e / 16;
+  const int rt = (int)(tb / nkb), kb = (int)(tb % nkb);
+  const int64_t src = (m * rows + rt * 16 + r) * (int64_t)ng + 2 * kb;
+  uint2 v;
+  v.x = (uint32_t)scales[src] | ((uint32_t)biases[src] << 16);
+  v.y = (uint32_t)scales[src + 1] | ((uint32_t)biases[src + 1] << 16);
+  out[i] = v;
+}
+
+hipError_t launch_pack_u4(int64_t n_mats, int rows, int cols, const void* codes, const void* scales,
+                          const void* biases, void* codes_out, void* params_out, hipStream_t st) {
+  const int64_t n_words = n_mats * rows * (int64_t)cols / 8;
+  const int64_t n_par = n_mats * rows * (int64_t)(cols / 128);
+  pack_u4_codes_kernel<<<(unsigned)((n_words + 255) / 256), 256, 0, st>>>((const uint8_t*)codes,
+                                                                          (uint32_t*)codes_out, n_words, rows, cols);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  pack_u4_params_kernel<<<(unsigned)((n_par + 255) / 256), 256, 0, st>>>(
+      (const uint16_t*)scales, (const uint16_t*)biases, (uint2*)params_out, n_par, rows, cols);
   return hipGetLastError();
 }
 

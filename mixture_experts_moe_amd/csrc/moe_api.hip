@@ -91,10 +91,12 @@ int validate_shape(const moe_shape* s) {
   const bool combo = (s->act_dtype == MOE_F32 && s->w_dtype == MOE_F32) ||
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_BF16) ||
                      (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128) ||
-                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128_A16);
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_FP8E4M3_B128_A16) ||
+                     (s->act_dtype == MOE_BF16 && s->w_dtype == MOE_U4_G64);
   if (!combo) return MOE_ERR_UNSUPPORTED;
   if (s->w_layout != MOE_LAYOUT_ROWMAJOR && s->w_layout != MOE_LAYOUT_TILED) return MOE_ERR_INVALID_ARG;
   if (s->w_layout == MOE_LAYOUT_TILED && s->w_dtype == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  if (s->w_layout != MOE_LAYOUT_TILED && s->w_dtype == MOE_U4_G64) return MOE_ERR_UNSUPPORTED;
   if (s->d_model % 128 || s->d_ffn % 128 || s->d_ffn_shared % 128) return MOE_ERR_UNSUPPORTED;
   if (s->d_model > 8192 || s->d_ffn > 4096 || s->d_ffn_shared > 4096) return MOE_ERR_UNSUPPORTED;
   const int Fmax = s->d_ffn > s->d_ffn_shared ? s->d_ffn : s->d_ffn_shared;
@@ -257,7 +259,8 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->plan)
     return MOE_ERR_INVALID_ARG;
   const bool fp8 = shape->w_dtype == MOE_FP8E4M3_B128;                  // activations quantised
-  const bool scaled = fp8 || shape->w_dtype == MOE_FP8E4M3_B128_A16;  // block-scaled FP8 weights
+  const bool scaled = fp8 || shape->w_dtype == MOE_FP8E4M3_B128_A16 ||  // block-scaled FP8 weights
+                      shape->w_dtype == MOE_U4_G64;                       // or 4-bit group parameters
   const bool has_shared = shape->d_ffn_shared > 0;
   if (!w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
   if (scaled && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
@@ -292,15 +295,15 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   a.wg = w->w_gate;
   a.wu = w->w_up;
   a.wd = w->w_down;
-  a.sg = w->s_gate;
-  a.su = w->s_up;
-  a.sd = w->s_down;
+  a.sg = (const float*)w->s_gate;
+  a.su = (const float*)w->s_up;
+  a.sd = (const float*)w->s_down;
   a.shg = w->sh_gate;
   a.shu = w->sh_up;
   a.shd = w->sh_down;
-  a.ssg = w->ss_gate;
-  a.ssu = w->ss_up;
-  a.ssd = w->ss_down;
+  a.ssg = (const float*)w->ss_gate;
+  a.ssu = (const float*)w->ss_up;
+  a.ssd = (const float*)w->ss_down;
   a.h = base + L.h;
   a.sh = (float*)(base + L.sh);
   a.part = (float*)(base + L.part);
@@ -355,6 +358,25 @@ int moe_pack_weights(int64_t n_mats, int32_t rows, int32_t row_bytes, const void
   if (i0 < o0 + bytes && o0 < i0 + bytes) return MOE_ERR_INVALID_ARG;  // overlap
   if (bytes / 16 / 256 >= (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;
   return hip_status(moe::launch_pack_weights(n_mats, rows, row_bytes, in, out, (hipStream_t)stream));
+}
+
+int moe_pack_weights_u4(int64_t n_mats, int32_t rows, int32_t cols, const void* codes, const uint16_t* scales,
+                        const uint16_t* biases, void* codes_out, void* params_out, void* stream) {
+  if (n_mats < 0 || rows <= 0 || cols <= 0) return MOE_ERR_INVALID_ARG;
+  if (rows % 16 || cols % 128) return MOE_ERR_UNSUPPORTED;
+  if (n_mats == 0) return MOE_OK;
+  if (!codes || !scales || !biases || !codes_out || !params_out) return MOE_ERR_INVALID_ARG;
+  const int64_t cbytes = n_mats * rows * (int64_t)cols / 2, pbytes = n_mats * rows * (int64_t)(cols / 64) * 4;
+  auto overlap = [](const void* a, int64_t na, const void* b, int64_t nb) {
+    const char *a0 = (const char*)a, *b0 = (const char*)b;
+    return a0 < b0 + nb && b0 < a0 + na;
+  };
+  if (overlap(codes, cbytes, codes_out, cbytes) || overlap(codes_out, cbytes, params_out, pbytes) ||
+      overlap(scales, pbytes / 2, params_out, pbytes) || overlap(biases, pbytes / 2, params_out, pbytes))
+    return MOE_ERR_INVALID_ARG;
+  if (cbytes / 4 / 256 >= (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;
+  return hip_status(
+      moe::launch_pack_u4(n_mats, rows, cols, codes, scales, biases, codes_out, params_out, (hipStream_t)stream));
 }
 
 const char* moe_status_string(int status) {

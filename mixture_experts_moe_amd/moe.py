@@ -18,11 +18,11 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_ERR_FORCED_INDEX, MOE_ERR_DEVICE_SYNC = -5, -6  # device status word
-DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3}
+DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3, "u4": 4}
 
 # Every function the header declares (checked against include/moe.h by the tests).
 ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
-                 "moe_quantize_rows", "moe_pack_weights", "moe_status_string")
+                 "moe_quantize_rows", "moe_pack_weights", "moe_pack_weights_u4", "moe_status_string")
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 N_STAGE_EVENTS = 4
@@ -76,6 +76,7 @@ def lib() -> C.CDLL:
         L.moe_forward_stages.argtypes = [p, p, p, p, p, p, C.c_size_t, C.c_uint32, p, p]
         L.moe_quantize_rows.argtypes = [i64, i32, i32, p, p, p, p]
         L.moe_pack_weights.argtypes = [i64, i32, i32, p, p, p]
+        L.moe_pack_weights_u4.argtypes = [i64, i32, i32, p, p, p, p, p, p]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         _lib = L
@@ -90,9 +91,13 @@ def make_shape(T, d, E, k, F, Fs, act="bf16", w="fp8", layout="rowmajor") -> Sha
     return Shape(int(T), int(d), int(E), int(k), int(F), int(Fs), DTYPES[act], DTYPES[w], LAYOUTS[layout])
 
 
-def shape_of(layer_shape, T=None, layout="rowmajor") -> Shape:
-    """Shape from any object with attributes T, d, E, k, F, Fs, act, w."""
+def shape_of(layer_shape, T=None, layout=None) -> Shape:
+    """Shape from any object with attributes T, d, E, k, F, Fs, act, w.  The
+    layout defaults to row-major, and to tiled for 4-bit weights (their only
+    layout)."""
     s = layer_shape
+    if layout is None:
+        layout = "tiled" if s.w == "u4" else "rowmajor"
     return make_shape(s.T if T is None else T, s.d, s.E, s.k, s.F, s.Fs, s.act, s.w, layout)
 
 
@@ -216,9 +221,36 @@ def pack_weights(w: torch.Tensor, stream=None) -> torch.Tensor:
     return out
 
 
+def pack_weights_u4(codes: torch.Tensor, scales: torch.Tensor, biases: torch.Tensor, stream=None):
+    """MOE_LAYOUT_TILED codes and group parameters of [n, rows, cols/2] (or
+    [rows, cols/2]) 4-bit codes with [.., rows, cols/64] bf16 scales and biases."""
+    t = codes if codes.dim() == 3 else codes.unsqueeze(0)
+    n, rows, half = t.shape
+    if scales.dtype != torch.bfloat16 or biases.dtype != torch.bfloat16:
+        raise ValueError("moe: 4-bit group scales and biases must be bfloat16")
+    if scales.shape != biases.shape or scales.numel() != n * rows * (2 * half // 64):
+        raise ValueError("moe: 4-bit group parameters do not match the codes")
+    out = torch.empty_like(codes)
+    params = torch.empty(scales.numel() * 4, dtype=torch.uint8, device=codes.device)
+    rc = lib().moe_pack_weights_u4(n, rows, 2 * half, _ptr(codes), _ptr(scales), _ptr(biases), _ptr(out),
+                                   _ptr(params), _stream(stream))
+    _check(rc, "moe_pack_weights_u4")
+    return out, params
+
+
 def pack_layer_weights(w: dict, stream=None) -> dict:
-    """The weight dict with every expert matrix packed (scales, router, x untouched)."""
+    """The weight dict with every expert matrix packed (scales, router, x
+    untouched).  4-bit weights (recognised by their biases b_*): codes and group
+    parameters packed together, the parameters taking the scales' place."""
     out = dict(w)
+    if w.get("b_gate") is not None:
+        for c, sc, b in (("w_gate", "s_gate", "b_gate"), ("w_up", "s_up", "b_up"), ("w_down", "s_down", "b_down"),
+                         ("sh_gate", "ss_gate", "sb_gate"), ("sh_up", "ss_up", "sb_up"),
+                         ("sh_down", "ss_down", "sb_down")):
+            if w.get(c) is not None:
+                out[c], out[sc] = pack_weights_u4(w[c], w[sc], w[b], stream)
+            out.pop(b, None)
+        return out
     for k in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
         if w.get(k) is not None:
             out[k] = pack_weights(w[k], stream)

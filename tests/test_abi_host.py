@@ -197,3 +197,32 @@ def test_w8a16_shape_and_scales():
         w = _weights_struct(**{null: None})
         rc = L.moe_forward(C.byref(a16), C.byref(w), FAKE, C.byref(r), y, FAKE, 1 << 40, None)
         assert rc == moe.MOE_ERR_INVALID_ARG, null
+
+
+def test_u4_shape_layout_and_params():
+    """(bf16 activations, 4-bit weights) is supported in the tiled layout only;
+    the group parameters are required; moe_pack_weights_u4 checks its sizes and
+    overlaps before any launch."""
+    L = _lib()
+    u4 = moe.make_shape(32, 2048, 384, 6, 640, 640, act="bf16", w="u4", layout="tiled")
+    assert moe.workspace_bytes(u4) > 0 and moe.plan_bytes(u4) > 0
+    assert moe.workspace_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640, act="bf16", w="u4")) == 0  # row-major
+    assert moe.workspace_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640, act="f32", w="u4", layout="tiled")) == 0
+    assert moe.plan_bytes(u4) < moe.plan_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640))  # no x codes
+    r = _routing_struct()
+    for null in ("s_gate", "s_up", "s_down", "ss_down"):
+        w = _weights_struct(**{null: None})
+        rc = L.moe_forward(C.byref(u4), C.byref(w), FAKE, C.byref(r), FAKE, FAKE, 1 << 40, None)
+        assert rc == moe.MOE_ERR_INVALID_ARG, null
+    P = L.moe_pack_weights_u4
+    assert P(1, 24, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED  # rows % 16
+    assert P(1, 16, 64, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED   # cols % 128
+    assert P(-1, 16, 128, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert P(1, 16, 128, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert P(0, 16, 128, None, None, None, None, None, None) == moe.MOE_OK
+    buf = (C.c_uint8 * 8192)()
+    a = C.addressof(buf)
+    # 16 x 128 codes = 1 KB at a; params 512 B placed inside the codes' output
+    assert P(1, 16, 128, FAKE, FAKE, FAKE, C.c_void_p(a), C.c_void_p(a + 512), None) == moe.MOE_ERR_INVALID_ARG
+    assert P(1, 16, 128, C.c_void_p(a), FAKE, FAKE, C.c_void_p(a + 256), C.c_void_p(a + 4096), None) == \
+        moe.MOE_ERR_INVALID_ARG

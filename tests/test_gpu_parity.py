@@ -28,7 +28,7 @@ Y_REL = 2e-2
 
 _weights_dev: dict = {}
 _WKEYS = ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
-          "ss_gate", "ss_up", "ss_down")
+          "ss_gate", "ss_up", "ss_down", "b_gate", "b_up", "b_down", "sb_gate", "sb_up", "sb_down")
 
 
 def say(*a):
@@ -40,7 +40,10 @@ def gpu_inputs(inp):
     once per process and shared by every workload of the same layer."""
     key = id(inp["w_gate"])
     if key not in _weights_dev:
-        _weights_dev[key] = synth.to_device({k: inp[k] for k in _WKEYS if inp.get(k) is not None}, DEV)
+        w = synth.to_device({k: inp[k] for k in _WKEYS if inp.get(k) is not None}, DEV)
+        if inp["shape"].w == "u4":  # 4-bit weights exist only in the tiled layout
+            w = moe.pack_layer_weights(w)
+        _weights_dev[key] = w
     d = dict(_weights_dev[key])
     d.update(synth.to_device({k: inp[k] for k in ("x", "w_router", "sel_bias") if inp.get(k) is not None}, DEV))
     return d
