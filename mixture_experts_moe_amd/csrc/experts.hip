@@ -634,13 +634,25 @@ __global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
 // consecutive columns of one row for the stores.
 // ---------------------------------------------------------------------------
 
-// Eight 4-bit codes (one packed word) as eight bf16 values 128 + q.
-__device__ __forceinline__ v4i u4_word_to_bf16(uint32_t w) {
+// Eight 4-bit codes (one packed word) as eight bf16 values 128 + q.  The two
+// constants are passed in registers (made opaque to the compiler) so that each
+// half-word pair costs one shift and one and-or instead of a shift, an and and
+// an or with literal operands.
+struct U4Consts {
+  uint32_t mask, high;
+};
+__device__ __forceinline__ U4Consts u4_consts() {
+  U4Consts k{0x000F000Fu, 0x43004300u};
+  asm volatile("" : "+s"(k.mask));
+  asm volatile("" : "+v"(k.high));
+  return k;
+}
+__device__ __forceinline__ v4i u4_word_to_bf16(uint32_t w, U4Consts k) {
   v4i r;
-  r[0] = (int)((w & 0x000F000Fu) | 0x43004300u);
-  r[1] = (int)(((w >> 4) & 0x000F000Fu) | 0x43004300u);
-  r[2] = (int)(((w >> 8) & 0x000F000Fu) | 0x43004300u);
-  r[3] = (int)(((w >> 12) & 0x000F000Fu) | 0x43004300u);
+  r[0] = (int)((w & k.mask) | k.high);
+  r[1] = (int)(((w >> 4) & k.mask) | k.high);
+  r[2] = (int)(((w >> 8) & k.mask) | k.high);
+  r[3] = (int)(((w >> 12) & k.mask) | k.high);
   return r;
 }
 
@@ -657,12 +669,15 @@ __device__ __forceinline__ float group_sum_bf16x8(v4i x) {
   return s;
 }
 
-// One 64-column group's contribution to a lane's four outputs: S is the
-// matrix-core sum of x * (128 + q), pv the group's bf16 scale (low half) and
-// bias (high half), X the four rows' sums of x over the group.
-__device__ __forceinline__ v4f u4_group_term(v4f S, uint32_t pv, v4f X) {
+// acc plus one 64-column group's contribution to a lane's four outputs: S is
+// the matrix-core sum of x * (128 + q), pv the group's bf16 scale (low half)
+// and bias (high half), X the four rows' sums of x over the group.
+__device__ __forceinline__ v4f u4_group_add(v4f acc, v4f S, uint32_t pv, v4f X) {
   const float sc = __uint_as_float(pv << 16), bi = __uint_as_float(pv & 0xffff0000u);
-  return sc * S + fmaf(-128.0f, sc, bi) * X;
+  const float b128 = fmaf(-128.0f, sc, bi);
+#pragma unroll
+  for (int v = 0; v < 4; ++v) acc[v] = fmaf(sc, S[v], fmaf(b128, X[v], acc[v]));
+  return acc;
 }
 
 // 4x4 transpose inside each quad of lanes: lane i of a quad holds column i of
@@ -696,12 +711,16 @@ __device__ __forceinline__ v4f quad_transpose(v4f a) {
 
 // Gate/up with 4-bit weights: 16-row tiles, 8 waves, one 128-feature group nb
 // of h per block (as for FP8 weights); wave w owns features nb*128 + 16w +
-// [0, 16) of W_gate and W_up, streamed gate run first, then up run, KG blocks
-// of 128 columns per stage, two stages in flight.  COH: h stored coherently
-// (the fused expert launch).
+// [0, 16) of W_gate and W_up.  A stage is KG blocks of 128 columns of both
+// matrices (gate blocks, then the same up blocks), two stages in flight, so
+// that each activation chunk and group sum read from LDS serves both.  COH: h
+// stored coherently (the fused expert launch).
+#ifndef MOE_U4_KG
+#define MOE_U4_KG 2  // 128-column blocks of each matrix per stage
+#endif
 template <bool COH>
 __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint8_t* smem) {
-  constexpr int BM = 16, NT = kGateUpWaves * 64, KG = 4, SB = 4;
+  constexpr int BM = 16, NT = kGateUpWaves * 64, KG = MOE_U4_KG, SB = 4;
   int nb;
   const TileRows tr = block_rows(a, b, nb);
   if (tr.g < 0) return false;
@@ -721,26 +740,24 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
   const uint8_t* pu = tr.shared ? (const uint8_t*)a.ssu : (const uint8_t*)a.su + (size_t)tr.g * pbytes;
   const int f0 = nb * 128 + wave * 16;
   const size_t t0 = (size_t)(f0 / 16) * nkb;  // the wave's first tile block
-  const uint8_t* cs[2] = {cg + t0 * 1024 + lane * 16, cu + t0 * 1024 + lane * 16};
-  const uint8_t* ps[2] = {pg + t0 * 128 + lr * 8, pu + t0 * 128 + lr * 8};
+  const uint8_t* const cs[2] = {cg + t0 * 1024 + lane * 16, cu + t0 * 1024 + lane * 16};
+  const uint8_t* const ps[2] = {pg + t0 * 128 + lr * 8, pu + t0 * 128 + lr * 8};
 
-  // Stage st < nq: gate blocks [st*KG, st*KG + KG); else up blocks of st - nq.
-  // Loads are unconditional (a short last stage re-reads the final block).
-  const int nq = (nkb + KG - 1) / KG, ns = 2 * nq;
-  v4i wc[2][KG];
-  uint2 wp[2][KG];
-  auto load = [&](auto S, int st) {
+  // Stage q: blocks [q*KG, q*KG + KG) of W_gate, then of W_up.  Loads are
+  // unconditional (a short last stage re-reads the final block, in bounds).
+  const int ns = (nkb + KG - 1) / KG;
+  v4i wc[2][2][KG];
+  uint2 wp[2][2][KG];
+  auto load = [&](auto S, int q) {
     constexpr int sl = decltype(S)::value;
-    const bool up = st >= nq;
-    const int q = up ? st - nq : st;
-    const uint8_t* c = up ? cs[1] : cs[0];
-    const uint8_t* p = up ? ps[1] : ps[0];
 #pragma unroll
-    for (int j = 0; j < KG; ++j) {
-      const int kb = min(q * KG + j, nkb - 1);
-      wc[sl][j] = stream_load<true>(c + (size_t)kb * 1024);
-      wp[sl][j] = *(const uint2*)(p + (size_t)kb * 128);
-    }
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int j = 0; j < KG; ++j) {
+        const int kb = min(q * KG + j, nkb - 1);
+        wc[sl][m][j] = stream_load<true>(cs[m] + (size_t)kb * 1024);
+        wp[sl][m][j] = *(const uint2*)(ps[m] + (size_t)kb * 128);
+      }
   };
 
   // Staging, in pinned issue order: row tokens, the weight stream, then the
@@ -776,8 +793,9 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
   __syncthreads();
 
   v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  auto compute_run = [&](auto R, auto S, int q) {
-    constexpr int r = decltype(R)::value, sl = decltype(S)::value;
+  const U4Consts kc = u4_consts();
+  auto compute = [&](auto S, int q) {
+    constexpr int sl = decltype(S)::value;
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
       const int kb = q * KG + j;
@@ -785,27 +803,27 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
       const uint8_t* xp = xs + lr * xstride + kb * 256 + q4 * 16;  // columns 128 kb + 32 m + 8 q4
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        v4f S = {0.f, 0.f, 0.f, 0.f};
-        S = mfma_bf16(*(const v4i*)(xp + 128 * h), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h]), S);
-        S = mfma_bf16(*(const v4i*)(xp + 128 * h + 64), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h + 1]), S);
+        const v4i x0 = *(const v4i*)(xp + 128 * h), x1 = *(const v4i*)(xp + 128 * h + 64);
         const v4f X = *(const v4f*)(xsum + (2 * kb + h) * BM + 4 * q4);
-        acc[r] += u4_group_term(S, h ? wp[sl][j].y : wp[sl][j].x, X);
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          v4f S = {0.f, 0.f, 0.f, 0.f};
+          S = mfma_bf16(x0, u4_word_to_bf16((uint32_t)wc[sl][m][j][2 * h], kc), S);
+          S = mfma_bf16(x1, u4_word_to_bf16((uint32_t)wc[sl][m][j][2 * h + 1], kc), S);
+          acc[m] = u4_group_add(acc[m], S, h ? wp[sl][m][j].y : wp[sl][m][j].x, X);
+        }
       }
     }
   };
-  auto compute = [&](auto S, int st) {
-    if (st < nq) compute_run(Ic<0>{}, S, st);
-    else compute_run(Ic<1>{}, S, st - nq);
-  };
-  int st = 0;
-  for (; st + 2 < ns; st += 2) {  // ns is even: both loads of the body are in range
-    compute(Ic<0>{}, st);
-    load(Ic<0>{}, st + 2);
-    compute(Ic<1>{}, st + 1);
-    load(Ic<1>{}, st + 3);
+  int q = 0;
+  for (; q + 2 < ns; q += 2) {
+    compute(Ic<0>{}, q);
+    load(Ic<0>{}, q + 2);
+    compute(Ic<1>{}, q + 1);
+    load(Ic<1>{}, q + 3);
   }
-  compute(Ic<0>{}, st);
-  compute(Ic<1>{}, st + 1);
+  compute(Ic<0>{}, q);
+  if (q + 1 < ns) compute(Ic<1>{}, q + 1);
 
   // h = silu(g) * u for rows 4*q4 + v of feature f0 + lr, then transposed to
   // row 4*q4 + lane%4, features f0 + 4*((lane/4)%4) + v.
@@ -937,6 +955,7 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   v4f acc[RT];
 #pragma unroll
   for (int r = 0; r < RT; ++r) acc[r] = v4f{0.f, 0.f, 0.f, 0.f};
+  const U4Consts kc = u4_consts();
   auto compute = [&](auto R, auto S, int q) {
     constexpr int r = decltype(R)::value, sl = decltype(S)::value;
 #pragma unroll
@@ -947,10 +966,10 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         v4f S = {0.f, 0.f, 0.f, 0.f};
-        S = mfma_bf16(*(const v4i*)(xp + 128 * h), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h]), S);
-        S = mfma_bf16(*(const v4i*)(xp + 128 * h + 64), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h + 1]), S);
+        S = mfma_bf16(*(const v4i*)(xp + 128 * h), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h], kc), S);
+        S = mfma_bf16(*(const v4i*)(xp + 128 * h + 64), u4_word_to_bf16((uint32_t)wc[sl][j][2 * h + 1], kc), S);
         const v4f X = *(const v4f*)(hsum + (2 * kb + h) * BM + 4 * q4);
-        acc[r] += u4_group_term(S, h ? wp[sl][j].y : wp[sl][j].x, X);
+        acc[r] = u4_group_add(acc[r], S, h ? wp[sl][j].y : wp[sl][j].x, X);
       }
     }
   };
