@@ -69,7 +69,9 @@ enum Mutant {
   MUT_COMBINE_NO_WEIGHT = 13, // routed outputs added without their weights
   MUT_U4_NIBBLE_SWAP = 14,   // 4-bit codes: even columns read from the high nibble
   MUT_U4_NO_BIAS = 15,       // 4-bit groups: the bias term dropped
-  MUT_U4_GROUP128 = 16       // 4-bit groups: parameters indexed per 128 columns
+  MUT_U4_GROUP128 = 16,      // 4-bit groups: parameters indexed per 128 columns
+  MUT_COMPARE_MIN_PAIR = 17, // routing comparison: a token's margin from its closest swapped pair
+  MUT_COMPARE_UNBIASED = 18  // routing comparison: margins from the logits without the selection bias
 };
 int g_mutant = MUT_NONE;
 
@@ -495,6 +497,82 @@ int oracle_dispatch(int32_t T, int32_t k, int32_t E, const int32_t* idx, int32_t
     perm[q] = (int32_t)p;
     inv_perm[p] = q;
   }
+  return OK;
+}
+
+// Routing compared as a distribution ([port] "Taking it apart": after forcing
+// the routing and comparing the rest closely, check the routing itself as a
+// distribution; [bench] "The gate, forced": sigma is a layer's RMS router-
+// logit error, and a disagreement is measured by the margin, in units of
+// sigma, by which the reference made the choice the other side did not;
+// [port] "What we couldn't explain": the disagreement count over (token,
+// layer) pairs against an allowed rate).  Reading:
+//   sigma^2 = mean over all T x E entries of (logits - ref_logits)^2;
+//   a token disagrees when its set of chosen experts differs from the
+//   reference's (ids outside [0, E) are ignored, slot order does not matter);
+//   its margin is the largest s[e] - s[e'] over experts e the reference chose
+//   and the other side did not, and e' the other way round, with s the
+//   reference's selection score (ref logit plus the selection bias);
+//   gap = margin / sigma (+inf when sigma = 0 and the margin is positive, 0
+//   when both are 0); agreeing tokens get gap -1.
+// Outputs: gap [T], sigma, the number of disagreeing tokens and the largest
+// gap (-1 when none disagrees).  Sums in double, in token and expert order.
+int oracle_route_compare(int32_t T, int32_t E, int32_t k, const float* logits, const float* ref_logits,
+                         const float* sel_bias, const int32_t* idx, const int32_t* ref_idx, float* gap,
+                         double* sigma, int32_t* n_disagree, float* max_gap) {
+  if (T < 0 || E < 1 || k < 1 || (T > 0 && (!logits || !ref_logits || !idx || !ref_idx || !gap))) return ERR_INVALID;
+  double ss = 0.0;
+  for (int64_t i = 0; i < (int64_t)T * E; ++i) {
+    const double dl = (double)logits[i] - (double)ref_logits[i];
+    ss += dl * dl;
+  }
+  const double sg = T > 0 ? std::sqrt(ss / ((double)T * E)) : 0.0;
+  auto chosen = [&](const int32_t* row, int e) {
+    for (int j = 0; j < k; ++j)
+      if (row[j] == e) return true;
+    return false;
+  };
+  int32_t nd = 0;
+  float mg = -1.0f;
+  for (int t = 0; t < T; ++t) {
+    const int32_t* a = idx + (size_t)t * k;
+    const int32_t* r = ref_idx + (size_t)t * k;
+    auto score = [&](int e) {
+      float v = ref_logits[(size_t)t * E + e];
+      if (sel_bias && g_mutant != MUT_COMPARE_UNBIASED) v = v + sel_bias[e];
+      return (double)v;
+    };
+    bool differ = false;
+    double margin = g_mutant == MUT_COMPARE_MIN_PAIR ? INFINITY : -INFINITY;
+    for (int i = 0; i < k; ++i) {
+      const int e = r[i];
+      if (e < 0 || e >= E || chosen(a, e)) continue;  // e: the reference's choice only
+      for (int j = 0; j < k; ++j) {
+        const int f = a[j];
+        if (f < 0 || f >= E || chosen(r, f)) continue;  // f: the other side's choice only
+        differ = true;
+        const double m = score(e) - score(f);
+        margin = g_mutant == MUT_COMPARE_MIN_PAIR ? std::fmin(margin, m) : std::fmax(margin, m);
+      }
+    }
+    // sets of different sizes (ignored ids) differ too, with no pair to measure
+    for (int i = 0; i < k && !differ; ++i) {
+      if (r[i] >= 0 && r[i] < E && !chosen(a, r[i])) differ = true;
+      if (a[i] >= 0 && a[i] < E && !chosen(r, a[i])) differ = true;
+    }
+    if (!differ) {
+      gap[t] = -1.0f;
+      continue;
+    }
+    nd += 1;
+    if (!std::isfinite(margin)) margin = 0.0;
+    const double g = sg > 0.0 ? margin / sg : (margin > 0.0 ? INFINITY : 0.0);
+    gap[t] = (float)g;
+    mg = std::fmax(mg, gap[t]);
+  }
+  if (sigma) *sigma = sg;
+  if (n_disagree) *n_disagree = nd;
+  if (max_gap) *max_gap = mg;
   return OK;
 }
 

@@ -21,7 +21,7 @@ MUTANTS = {
     "select_unbiased": 1, "router_bf16": 2, "logits_bf16": 3, "tie_highest": 4, "softmax_all": 5,
     "no_shared": 6, "scale_transposed": 7, "reversed_order": 8, "no_h_quant": 9, "weights_biased": 10,
     "silu_sign": 11, "gate_up_swap": 12, "combine_no_weight": 13, "u4_nibble_swap": 14, "u4_no_bias": 15,
-    "u4_group128": 16,
+    "u4_group128": 16, "compare_min_pair": 17, "compare_unbiased": 18,
 }
 
 
@@ -64,6 +64,7 @@ def lib():
         L.oracle_forward.argtypes = [p, p, p, p, p, p, i32, p, p]
         L.oracle_forward_dense_masked.argtypes = [p, p, p, p, p, p]
         L.oracle_expert_ffn.argtypes = [p, p, i32, p, i32, p, p]
+        L.oracle_route_compare.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, p, p]
         _lib = L
     return _lib
 
@@ -172,6 +173,27 @@ def expert_ffn(layer: Layer, expert: int, t: int):
     rc = lib().oracle_expert_ffn(sp, wp, expert, xp, t, _ptr(xu), _ptr(y))
     assert rc == OK, rc
     return xu, y
+
+
+def route_compare(logits, ref_logits, idx, ref_idx, sel_bias=None):
+    """Routing compared as a distribution. Returns (gap [T] float32, sigma,
+    number of disagreeing tokens, largest gap)."""
+    logits = _c(logits, np.float32)
+    ref_logits = _c(ref_logits, np.float32)
+    idx = _c(idx, np.int32)
+    ref_idx = _c(ref_idx, np.int32)
+    bias = _c(sel_bias, np.float32)
+    T, E = logits.shape
+    k = idx.shape[1]
+    assert ref_logits.shape == (T, E) and ref_idx.shape == (T, k)
+    gap = np.empty(T, np.float32)
+    sigma = C.c_double()
+    nd = C.c_int32()
+    mg = C.c_float()
+    rc = lib().oracle_route_compare(T, E, k, _ptr(logits), _ptr(ref_logits), _ptr(bias), _ptr(idx), _ptr(ref_idx),
+                                    _ptr(gap), C.addressof(sigma), C.addressof(nd), C.addressof(mg))
+    assert rc == OK, rc
+    return gap, sigma.value, nd.value, mg.value
 
 
 def e4m3_decode(codes) -> np.ndarray:

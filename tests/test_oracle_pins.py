@@ -626,3 +626,82 @@ def test_u4_expert_ffn_vs_textbook():
             ws = [_u4_dequant(inp["w_" + n][e], inp["s_" + n][e], inp["b_" + n][e]) for n in ("gate", "up", "down")]
         ref = _swiglu64(*ws, xu)
         assert np.max(np.abs(y - ref)) / np.sqrt(np.mean(ref ** 2)) <= 1e-6
+
+
+# ---------------------------------------------------------------- routing as a distribution
+
+def _cmp_case_basic():
+    """Four tokens, E=6, k=2, no selection bias.  The other side's logits are the
+    reference's plus +0.5 at (1, 3), +1.5 at (3, 4) and -2.0 at (3, 0), so
+    sigma^2 = (0.25 + 2.25 + 4) / 24.  Token 0 has the same set in another slot
+    order; token 1 swaps expert 2 (ref score 2.5) for 3 (2.25): margin 0.25;
+    token 2 is an all-equal row resolved the same way; token 3 swaps 0 (5.0)
+    for 4 (3.0): margin 2.0."""
+    ref = np.array([[2.0, 1.0, 0.5, 0.0, -1.0, -2.0],
+                    [0.0, 3.0, 2.5, 2.25, 1.0, 0.0],
+                    [1.0, 1.0, 1.0, 1.0, 1.0, 1.0],
+                    [5.0, 4.0, 0.0, -1.0, 3.0, 2.0]], np.float32)
+    oth = ref.copy()
+    oth[1, 3] += 0.5
+    oth[3, 4] += 1.5
+    oth[3, 0] -= 2.0
+    ref_idx = np.array([[0, 1], [1, 2], [0, 1], [0, 1]], np.int32)
+    idx = np.array([[1, 0], [1, 3], [0, 1], [4, 1]], np.int32)
+    return oth, ref, idx, ref_idx
+
+
+def test_route_compare_worked_example():
+    oth, ref, idx, ref_idx = _cmp_case_basic()
+    gap, sigma, nd, mg = O.route_compare(oth, ref, idx, ref_idx)
+    sig = np.sqrt(6.5 / 24.0)  # 0.52041650...
+    assert abs(sigma - sig) <= 1e-12
+    assert nd == 2
+    assert gap[0] == -1.0 and gap[2] == -1.0
+    assert abs(gap[1] - 0.25 / sig) <= 1e-6 and abs(gap[3] - 2.0 / sig) <= 1e-6  # 0.48038, 3.84308
+    assert abs(mg - 2.0 / sig) <= 1e-6
+
+
+def test_route_compare_bias_and_worst_pair():
+    """The margin uses the reference's selection score (logit + bias), and a
+    token with several swapped experts takes its largest margin; each planted
+    change (margins from the bare logits, the closest pair) moves the result."""
+    # bias: ref scores [1.0, 0.9, 0.8, 1.0, 0.1] choose {0, 3}; the other side
+    # (logit 3 lowered by 0.5) chooses {0, 1}; margin 1.0 - 0.9 = 0.1 (biased),
+    # -0.9 from the bare logits
+    ref = np.array([[1.0, 0.9, 0.8, 0.0, 0.1]], np.float32)
+    oth = ref.copy()
+    oth[0, 3] -= 0.5
+    bias = np.array([0, 0, 0, 1.0, 0], np.float32)
+    args = (oth, ref, np.array([[0, 1]], np.int32), np.array([[0, 3]], np.int32), bias)
+    sig = np.sqrt(0.25 / 5)
+    gap, sigma, nd, mg = O.route_compare(*args)
+    assert nd == 1 and abs(sigma - sig) <= 1e-12 and abs(gap[0] - 0.1 / sig) <= 1e-6
+    with O.mutant("compare_unbiased"):
+        assert O.route_compare(*args)[0][0] < 0
+    # worst pair: ref {0, 1, 2} from [3, 2, 1, 0, -1, -2]; the other side (+2.5
+    # at 3, +3.5 at 4) chooses {0, 3, 4}: pairs (1,3) 2, (1,4) 3, (2,3) 1, (2,4) 2
+    ref = np.array([[3, 2, 1, 0, -1, -2]], np.float32)
+    oth = ref + np.array([[0, 0, 0, 2.5, 3.5, 0]], np.float32)
+    args = (oth, ref, np.array([[0, 3, 4]], np.int32), np.array([[0, 1, 2]], np.int32))
+    sig = np.sqrt((2.5 ** 2 + 3.5 ** 2) / 6)
+    gap, sigma, nd, mg = O.route_compare(*args)
+    assert abs(gap[0] - 3.0 / sig) <= 1e-6 and mg == gap[0]
+    with O.mutant("compare_min_pair"):
+        assert abs(O.route_compare(*args)[0][0] - 1.0 / sig) <= 1e-6
+
+
+def test_route_compare_invariants():
+    """Identical sides: sigma 0, no disagreement.  Slot order inside a token does
+    not matter.  Scaling the logit difference by c scales sigma by c and every
+    gap by 1/c (the ids are inputs, not recomputed)."""
+    oth, ref, idx, ref_idx = _cmp_case_basic()
+    gap, sigma, nd, mg = O.route_compare(ref, ref, ref_idx, ref_idx)
+    assert sigma == 0.0 and nd == 0 and mg == -1.0 and np.all(gap == -1.0)
+    g0, s0, n0, m0 = O.route_compare(oth, ref, idx, ref_idx)
+    g1, s1, n1, m1 = O.route_compare(oth, ref, idx[:, ::-1], ref_idx[:, ::-1])
+    assert np.array_equal(g0, g1) and s0 == s1 and n0 == n1
+    oth4 = ref + 4.0 * (oth - ref)  # exact: the differences are small binary fractions
+    g4, s4, n4, m4 = O.route_compare(oth4, ref, idx, ref_idx)
+    assert abs(s4 - 4 * s0) <= 1e-12 and n4 == n0
+    d = g0 >= 0
+    assert np.allclose(g4[d], g0[d] / 4, rtol=1e-6) and np.array_equal(g4[~d], g0[~d])
