@@ -257,6 +257,33 @@ int moe_pack_weights(int64_t n_mats, int32_t rows, int32_t row_bytes, const void
 int moe_pack_weights_u4(int64_t n_mats, int32_t rows, int32_t cols, const void *codes, const uint16_t *scales,
                         const uint16_t *biases, void *codes_out, void *params_out, void *stream);
 
+/* Routing compared as a distribution: the third part of the check [port]
+ * "Taking it apart" proposes (force the routing, compare the rest closely,
+ * check the routing itself as a distribution), with sigma, a layer's RMS
+ * router-logit error, and disagreements measured by the reference's margin in
+ * units of sigma ([bench] "The gate, forced"), counted over tokens ([port]
+ * "What we couldn't explain").  Inputs (device, row-major): logits and
+ * ref_logits [T, E] fp32 (the side under test and the reference), sel_bias [E]
+ * fp32 or NULL (the reference's selection bias), idx and ref_idx [T, k] int32
+ * (each side's chosen experts, as moe_route writes them; slot order is ignored,
+ * ids outside [0, E) are ignored).  Outputs (device):
+ *   *sigma = sqrt(mean over the T x E entries of (logits - ref_logits)^2),
+ *            summed in double;
+ *   gap[t] = -1 where the two expert sets of token t agree; otherwise the
+ *            largest s[e] - s[f] over experts e only the reference chose and f
+ *            only the other side chose, s = ref_logits + sel_bias (fp32, then
+ *            the difference in double; 0 when no such pair exists), divided by
+ *            sigma (+inf for sigma = 0 and a positive margin, 0 for both 0);
+ *   *n_disagree = the number of tokens whose sets differ; *max_gap = the
+ *            largest gap (-1 when none differs).
+ * The disagreement rate is *n_disagree / T.  Results are bitwise repeatable.
+ * ws: moe_route_compare_workspace_bytes(T) bytes.  T == 0 returns MOE_OK and
+ * writes nothing.  Limits: 1 <= k <= 8, k <= E. */
+size_t moe_route_compare_workspace_bytes(int32_t T);
+int moe_route_compare(int32_t T, int32_t E, int32_t k, const float *logits, const float *ref_logits,
+                      const float *sel_bias, const int32_t *idx, const int32_t *ref_idx, float *gap, double *sigma,
+                      int32_t *n_disagree, float *max_gap, void *ws, size_t ws_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *moe_status_string(int status);
 

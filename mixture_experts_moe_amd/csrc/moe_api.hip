@@ -379,6 +379,22 @@ int moe_pack_weights_u4(int64_t n_mats, int32_t rows, int32_t cols, const void* 
       moe::launch_pack_u4(n_mats, rows, cols, codes, scales, biases, codes_out, params_out, (hipStream_t)stream));
 }
 
+size_t moe_route_compare_workspace_bytes(int32_t T) { return T < 0 ? 0 : moe::route_compare_ws_bytes(T); }
+
+int moe_route_compare(int32_t T, int32_t E, int32_t k, const float* logits, const float* ref_logits,
+                      const float* sel_bias, const int32_t* idx, const int32_t* ref_idx, float* gap, double* sigma,
+                      int32_t* n_disagree, float* max_gap, void* ws, size_t ws_bytes, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E) return MOE_ERR_INVALID_ARG;
+  if (k > moe::kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  if (!logits || !ref_logits || !idx || !ref_idx || !gap || !sigma || !n_disagree || !max_gap)
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!ws) return MOE_ERR_INVALID_ARG;
+  if (ws_bytes < moe::route_compare_ws_bytes(T)) return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route_compare(T, E, k, logits, ref_logits, sel_bias, idx, ref_idx, gap, sigma,
+                                              n_disagree, max_gap, ws, (hipStream_t)stream));
+}
+
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "MOE_OK: success";

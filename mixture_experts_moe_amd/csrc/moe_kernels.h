@@ -112,6 +112,10 @@ hipError_t launch_experts_fused(const ExpertArgs& a, int wmode, const Plan& plan
                                 hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
                                hipStream_t st);
+size_t route_compare_ws_bytes(int T);
+hipError_t launch_route_compare(int T, int E, int k, const float* logits, const float* ref_logits, const float* bias,
+                                const int32_t* idx, const int32_t* ref_idx, float* gap, double* sigma,
+                                int32_t* n_differ, float* max_gap, void* ws, hipStream_t st);
 hipError_t launch_pack_u4(int64_t n_mats, int rows, int cols, const void* codes, const void* scales,
                           const void* biases, void* codes_out, void* params_out, hipStream_t st);
 hipError_t launch_combine(const float* part, const int32_t* idx, int T, int k, int d, int E, int P, bool has_shared,

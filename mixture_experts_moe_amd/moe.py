@@ -22,7 +22,8 @@ DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3, "u4": 4}
 
 # Every function the header declares (checked against include/moe.h by the tests).
 ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
-                 "moe_quantize_rows", "moe_pack_weights", "moe_pack_weights_u4", "moe_status_string")
+                 "moe_quantize_rows", "moe_pack_weights", "moe_pack_weights_u4", "moe_route_compare_workspace_bytes",
+                 "moe_route_compare", "moe_status_string")
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 N_STAGE_EVENTS = 4
@@ -77,6 +78,9 @@ def lib() -> C.CDLL:
         L.moe_quantize_rows.argtypes = [i64, i32, i32, p, p, p, p]
         L.moe_pack_weights.argtypes = [i64, i32, i32, p, p, p]
         L.moe_pack_weights_u4.argtypes = [i64, i32, i32, p, p, p, p, p, p]
+        L.moe_route_compare_workspace_bytes.restype = C.c_size_t
+        L.moe_route_compare_workspace_bytes.argtypes = [i32]
+        L.moe_route_compare.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, p, p, p, C.c_size_t, p]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         _lib = L
@@ -255,6 +259,46 @@ def pack_layer_weights(w: dict, stream=None) -> dict:
         if w.get(k) is not None:
             out[k] = pack_weights(w[k], stream)
     return out
+
+
+@dataclasses.dataclass
+class RouteComparison:
+    """Device results of moe_route_compare."""
+    gap: torch.Tensor         # [T] float32: -1 where the expert sets agree
+    sigma: torch.Tensor       # [1] float64
+    n_disagree: torch.Tensor  # [1] int32
+    max_gap: torch.Tensor     # [1] float32
+
+
+class RouteCompare:
+    """moe_route_compare with its output and workspace buffers allocated once
+    for T tokens (each call is then a single ctypes call)."""
+
+    def __init__(self, T: int, device="cuda"):
+        self.T = int(T)
+        self.out = RouteComparison(gap=torch.empty(max(self.T, 1), dtype=torch.float32, device=device),
+                                   sigma=torch.empty(1, dtype=torch.float64, device=device),
+                                   n_disagree=torch.empty(1, dtype=torch.int32, device=device),
+                                   max_gap=torch.empty(1, dtype=torch.float32, device=device))
+        self.ws = torch.empty(max(int(lib().moe_route_compare_workspace_bytes(self.T)), 256), dtype=torch.uint8,
+                              device=device)
+
+    def __call__(self, logits: torch.Tensor, ref_logits: torch.Tensor, idx: torch.Tensor, ref_idx: torch.Tensor,
+                 sel_bias: torch.Tensor | None = None, stream=None) -> RouteComparison:
+        T, E = logits.shape
+        k = idx.shape[1]
+        if T != self.T or ref_logits.shape != (T, E) or ref_idx.shape != (T, k):
+            raise ValueError("moe_route_compare: mismatched shapes")
+        o = self.out
+        rc = lib().moe_route_compare(T, E, k, _ptr(logits), _ptr(ref_logits), _ptr(sel_bias), _ptr(idx),
+                                     _ptr(ref_idx), _ptr(o.gap), _ptr(o.sigma), _ptr(o.n_disagree), _ptr(o.max_gap),
+                                     _ptr(self.ws), self.ws.numel(), _stream(stream))
+        _check(rc, "moe_route_compare")
+        return o
+
+
+def route_compare(logits, ref_logits, idx, ref_idx, sel_bias=None, stream=None) -> RouteComparison:
+    return RouteCompare(logits.shape[0], logits.device)(logits, ref_logits, idx, ref_idx, sel_bias, stream)
 
 
 def raw_call(name: str, *args):

@@ -226,3 +226,20 @@ def test_u4_shape_layout_and_params():
     assert P(1, 16, 128, FAKE, FAKE, FAKE, C.c_void_p(a), C.c_void_p(a + 512), None) == moe.MOE_ERR_INVALID_ARG
     assert P(1, 16, 128, C.c_void_p(a), FAKE, FAKE, C.c_void_p(a + 256), C.c_void_p(a + 4096), None) == \
         moe.MOE_ERR_INVALID_ARG
+
+
+def test_route_compare_host_validation():
+    L = _lib()
+    f = L.moe_route_compare
+    ws = L.moe_route_compare_workspace_bytes(100)
+    assert ws >= 100 * 20 and L.moe_route_compare_workspace_bytes(-1) == 0
+    args = lambda T, E, k, **kw: [T, E, k] + [kw.get(n, FAKE) for n in (
+        "lg", "rl", "bias", "idx", "ridx", "gap", "sigma", "nd", "mg", "ws")] + [kw.get("wsb", 1 << 30), None]
+    assert f(*args(100, 8, 9)) == moe.MOE_ERR_INVALID_ARG           # k > E
+    assert f(*args(100, 16, 9)) == moe.MOE_ERR_UNSUPPORTED          # k > 8
+    assert f(*args(-1, 8, 2)) == moe.MOE_ERR_INVALID_ARG
+    assert f(*args(100, 8, 2, lg=None)) == moe.MOE_ERR_INVALID_ARG
+    assert f(*args(100, 8, 2, sigma=None)) == moe.MOE_ERR_INVALID_ARG
+    assert f(*args(100, 8, 2, wsb=ws - 1)) == moe.MOE_ERR_WORKSPACE
+    assert f(*args(0, 8, 2, ws=None)) == moe.MOE_OK
+    assert f(*args(100, 8, 2, ws=None)) == moe.MOE_ERR_INVALID_ARG
