@@ -57,8 +57,8 @@ FORCED = {"prefill_t2048"}
 KERNEL_SOURCES = ("mixture_experts_moe_amd/csrc/experts.hip", "mixture_experts_moe_amd/csrc/moe_device.h",
                   "mixture_experts_moe_amd/csrc/moe_kernels.h", "mixture_experts_moe_amd/csrc/moe_api.hip")
 TRAFFIC = {  # workload -> counters of the fused expert kernel, tiled layout
-    "decode_t32": {"sources_sha256": "5e59f858f13afbe4403dd75e4c2a9d29dacf39d69f1f3717d8bb09de179880ff",
-                   "fetch_bytes": 607259410, "write_bytes": 2227087},
+    "decode_t32": {"sources_sha256": "ea03760317e42b4dad90524dfbe5eced5c714671d55bac4a2449871859aedb01",
+                   "fetch_bytes": 607130412, "write_bytes": 2227087},
 }
 
 
