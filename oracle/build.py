@@ -1,4 +1,5 @@
-"""Compile the plain C++ oracle into oracle/libmoe_oracle.so (test infrastructure).
+"""Compile the plain C++ oracles (the layer, and the attention ops next to it)
+into oracle/libmoe_oracle.so (test infrastructure).
 
 -ffp-contract=off keeps every fp32 operation exactly as written (no fused
 multiply-add), and no -ffast-math: the oracle's arithmetic is IEEE as stated.
@@ -8,14 +9,14 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "moe_oracle.cpp")
+SRCS = [os.path.join(HERE, "moe_oracle.cpp"), os.path.join(HERE, "attn_oracle.cpp")]
 LIB = os.path.join(HERE, "libmoe_oracle.so")
 
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, SRC]
+           "-Wall", "-Wextra", "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
