@@ -33,6 +33,7 @@ import numpy as np  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix
 METRIC = "MoE-layer tokens/s (decode T=32, prefill T=2048); % HBM BW / % FP8 MFMA peak"
 
 DESCRIPTION = {
@@ -85,6 +86,7 @@ def parse():
     ap.add_argument("--workload", default="decode_t32", choices=sorted(DESCRIPTION))
     ap.add_argument("--rotate", type=int, default=4, help="device copies of the expert weights")
     ap.add_argument("--layout", default="tiled", choices=("tiled", "rowmajor"), help="expert-weight layout")
+    ap.add_argument("--attention", type=int, default=1, help="time the attention ops next to the layer (0: skip)")
     ap.add_argument("--compare", default="skew_t8192",
                     help="workload whose routing moe_route_compare is timed on ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0: skip)")
@@ -235,6 +237,68 @@ def run_route_compare(name, steps):
             "reference": "torch fp32 matmul router over the whole batch, ids by stable sort"}
 
 
+# The attention ops next to the layer: 16 query heads, 4 key/value heads,
+# head_dim 128, the 513-token window; a prefill chunk of 2048 tokens after 2048
+# cached ones, and one decode token after a 32768-token context.
+ATTN_CASES = {
+    "attn_swa_prefill_t2048": dict(window=513, Tq=2048, Tk=4096, q_pos0=2048),
+    "attn_nope_prefill_t2048": dict(window=0, Tq=2048, Tk=4096, q_pos0=2048),
+    "attn_nope_decode_ctx32768": dict(window=0, Tq=1, Tk=32768, q_pos0=32767),
+}
+
+
+def run_attention(steps):
+    """moe_attention on each case and moe_rope on the prefill chunk's queries
+    and keys, back to back between two events, against their rooflines
+    (prefill: the matrix cores at the bf16 peak on 4*Tq*keys*D*Hq flops; decode
+    and RoPE: HBM on the bytes they must move)."""
+    import torch
+    from mixture_experts_moe_amd import attn
+
+    Hq, Hkv, D = 16, 4, 128
+    g = torch.Generator(device="cuda:0").manual_seed(0)
+    out = {}
+    st = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(n):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for name, c in ATTN_CASES.items():
+        Tq, Tk, q0, Wn = c["Tq"], c["Tk"], c["q_pos0"], c["window"]
+        q = torch.randn((Tq, Hq, D), generator=g, device="cuda:0").to(torch.bfloat16)
+        k = torch.randn((Tk, Hkv, D), generator=g, device="cuda:0").to(torch.bfloat16)
+        v = torch.randn((Tk, Hkv, D), generator=g, device="cuda:0").to(torch.bfloat16)
+        o = torch.empty_like(q)
+        call = attn.Attention(attn.AttnShape(Hq, Hkv, D, Wn), Tq, Tk, q0)
+        us = timed(lambda: call(q, k, v, o, st), max(20, steps))
+        pos = q0 + np.arange(Tq)
+        lo = np.maximum(0, pos - Wn + 1) if Wn else np.zeros(Tq, np.int64)
+        n_keys = float(np.sum(pos - lo + 1))               # attended (query, key) pairs per head
+        flops = 4.0 * n_keys * D * Hq
+        span = int(pos[-1] + 1 - lo[0])                     # keys any query reads
+        nbytes = 2 * Tq * Hq * D * 2 + 2 * span * Hkv * D * 2  # q in, o out, k and v once
+        bound = "mfma" if flops / (BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9) else "hbm"
+        r = {"us_per_call": us, "flops": flops, "bytes": nbytes, "bound": bound,
+             "TFLOPs": flops / (us * 1e-6) / 1e12, "GBs": nbytes / (us * 1e-6) / 1e9,
+             "workspace_bytes": int(call.ws.numel()) if attn.workspace_bytes(call.shape, Tq, Tk, q0) else 0}
+        r["frac"] = r["TFLOPs"] / BF16_PEAK_TFLOPS if bound == "mfma" else r["GBs"] / HBM_PEAK_GBS
+        out[name] = r
+    x = torch.randn((2048, Hq + Hkv, D), generator=g, device="cuda:0").to(torch.bfloat16)
+    us = timed(lambda: attn.rope_(x, 2048, 10000.0, st), max(20, steps))
+    nbytes = 2 * x.numel() * 2
+    out["rope_t2048_20heads"] = {"us_per_call": us, "bytes": nbytes, "bound": "hbm", "GBs": nbytes / (us * 1e-6) / 1e9,
+                                 "frac": nbytes / (us * 1e-6) / (HBM_PEAK_GBS * 1e9)}
+    return out
+
+
 def cpu_baseline(name, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the workload."""
     from mixture_experts_moe_amd import synth
@@ -308,6 +372,8 @@ def main():
                        "max_over_mean_expert_load": float(counts2.max() / max(1e-9, counts2.mean()))}
     if a.compare:
         extra["route_compare_" + a.compare] = run_route_compare(a.compare, max(20, a.steps // 2))
+    if a.attention:
+        extra.update(run_attention(max(20, a.steps // 2)))
     if extra:
         out["also"] = extra
     if a.cpu_seconds > 0:

@@ -7,7 +7,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe.so")
-SOURCES = ["moe_api.hip", "route.hip", "experts.hip", "route_compare.hip"]
+SOURCES = ["moe_api.hip", "route.hip", "experts.hip", "route_compare.hip", "attention.hip"]
 
 # Packed fp32 VALU forms are disabled for all device code (they are not used
 # deliberately anywhere; plain fp32 arithmetic is what the kernels mean).
