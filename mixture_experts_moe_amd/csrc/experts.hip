@@ -31,7 +31,11 @@
 namespace moe {
 
 #ifndef MOE_GU_KG
-#define MOE_GU_KG 4  // K blocks per weight stage in the gate/up stream
+#define MOE_GU_KG 4  // K blocks per weight stage in the gate/up stream (16-row tiles)
+#endif
+#ifndef MOE_GU_KG_TALL
+#define MOE_GU_KG_TALL 2  // the same for taller tiles, split between gate and up (4 spills past
+                          // 128 registers: one block per CU instead of two, measured slower)
 #endif
 
 // Load of 16 weight bytes.  NT: non-temporal, for launches that read each
@@ -203,28 +207,45 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   //    up tile -- one long run after the other streams faster than the two
   //    interleaved (measured).  Stage st < nq is gate group st, otherwise up
   //    group st - nq; the slots take alternate stages.
-  //  * Taller tiles: gate and up interleaved, slot 0 = gate, slot 1 = up,
-  //    stage st = (group st / 2, tile st % 2); the sequential order spills there.
+  //  * Taller tiles: stage st = group st of KG/2 K blocks of both tiles (gate
+  //    blocks in register entries [0, KG/2), up blocks in [KG/2, KG)), so that
+  //    each activation chunk, decoded from its E4M3 codes, serves both
+  //    products; the sequential order spills there.
   // The loop bodies issue their loads unconditionally (a short last group
   // re-reads the final K block, in bounds and in cache) and the last pair of
   // stages is peeled, so the memory-counter waits stay exact and nothing is
   // fetched twice in the steady state.  Slots and tiles are template constants
   // (Ic), so the register arrays are never indexed at run time.
   constexpr bool SEQ = BM == 16;
-  constexpr int KG = MOE_GU_KG;
-  const int nq = (nbb + KG - 1) / KG, ns = 2 * nq;
+  constexpr int KG = SEQ ? MOE_GU_KG : MOE_GU_KG_TALL;
+  constexpr int KGP = KG / 2;  // blocks per tile in a taller-tile stage
+  static_assert(SEQ || (KG % 2 == 0 && WT == 2 && !XB), "taller tiles: FP8 codes, a stage split between the tiles");
+  const int nq = SEQ ? (nbb + KG - 1) / KG : (nbb + KGP - 1) / KGP;
+  const int ns = SEQ ? 2 * nq : nq;
   v4i wlo[2][KG], whi[2][KG];
   auto load = [&](auto S, int st) {
     constexpr int sl = decltype(S)::value;
-    const bool up = SEQ ? st >= nq : sl == 1;
-    const int q = SEQ ? (up ? st - nq : st) : st / 2;
-    const uint8_t* base = up ? ws[1].p : ws[0].p;
+    if constexpr (SEQ) {
+      const bool up = st >= nq;
+      const int q = up ? st - nq : st;
+      const uint8_t* base = up ? ws[1].p : ws[0].p;
 #pragma unroll
-    for (int j = 0; j < KG; ++j) {
-      const int kb = min(q * KG + j, nbb - 1);
-      const uint8_t* p = base + (size_t)kb * ws[0].kb_stride;
-      wlo[sl][j] = stream_load<WT == 2 && BM == 16>(p);
-      whi[sl][j] = stream_load<WT == 2 && BM == 16>(p + ws[0].hi_off);
+      for (int j = 0; j < KG; ++j) {
+        const int kb = min(q * KG + j, nbb - 1);
+        const uint8_t* p = base + (size_t)kb * ws[0].kb_stride;
+        wlo[sl][j] = stream_load<WT == 2>(p);
+        whi[sl][j] = stream_load<WT == 2>(p + ws[0].hi_off);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int j = 0; j < KGP; ++j) {
+          const int kb = min(st * KGP + j, nbb - 1);
+          const uint8_t* p = ws[m].p + (size_t)kb * ws[0].kb_stride;
+          wlo[sl][m * KGP + j] = stream_load<false>(p);
+          whi[sl][m * KGP + j] = stream_load<false>(p + ws[0].hi_off);
+        }
     }
   };
   // Staging.  Loads complete in issue order as far as the wait counter goes,
@@ -324,20 +345,44 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       }
     }
   };
+  // taller tiles: both tiles' blocks of group q, each activation chunk decoded once
+  auto compute_pair = [&](auto S, int q) {
+    constexpr int sl = decltype(S)::value;
+#pragma unroll
+    for (int j = 0; j < KGP; ++j) {
+      const int bb = q * KGP + j;
+      if (bb >= nbb) break;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        v4i b[4];
+        const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
+        e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
+        e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[2], b[3]);
+        const float sx = sxs[(c * 16 + lr) * nbb + bb];
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+          acc[m][c] += kblock_e4m3_exact(wlo[sl][m * KGP + j], whi[sl][m * KGP + j], b) * (sx * wsc[m * nbb + bb]);
+      }
+    }
+  };
   auto compute = [&](auto S, int st) {
-    if constexpr (!SEQ) compute_run(S, S, st / 2);
-    else if (st < nq) compute_run(Ic<0>{}, S, st);
-    else compute_run(Ic<1>{}, S, st - nq);
+    if constexpr (!SEQ) {
+      if constexpr (WT == 2 && !XB) compute_pair(S, st);
+    } else if (st < nq) {
+      compute_run(Ic<0>{}, S, st);
+    } else {
+      compute_run(Ic<1>{}, S, st - nq);
+    }
   };
   int st = 0;
-  for (; st + 2 < ns; st += 2) {  // ns is even: both loads of the body are in range
+  for (; st + 2 < ns; st += 2) {  // both loads of the body are in range
     compute(Ic<0>{}, st);
     load(Ic<0>{}, st + 2);
     compute(Ic<1>{}, st + 1);
     load(Ic<1>{}, st + 3);
   }
   compute(Ic<0>{}, st);
-  compute(Ic<1>{}, st + 1);
+  if (st + 1 < ns) compute(Ic<1>{}, st + 1);  // taller tiles: the number of groups may be odd
 
   // Epilogue: h = silu(g) * u for features f0 + 4*(lane/16) + i, row c*16 + lane%16.
   float h[NC][4];

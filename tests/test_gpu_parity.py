@@ -342,11 +342,13 @@ def _forced_random(T, k, E, seed, n_experts_used=None):
     return pool[rng.integers(0, len(pool), size=(T, k))].astype(np.int32)
 
 
-@pytest.mark.parametrize("T,kind", [(1, "free"), (37, "free"), (64, "one_expert"), (300, "few_experts"),
-                                    (5462, "forced"), (8792, "forced")])
+@pytest.mark.parametrize("T,kind", [(1, "free"), (37, "free"), (64, "one_expert"), (100, "free"), (170, "forced"),
+                                    (300, "few_experts"), (5462, "forced"), (8792, "forced")])
 def test_edge_shapes(T, kind):
     """T=1; a ragged tail; every pair on one expert (duplicate ids per token);
-    most experts empty; pair counts 32,772 and 52,752 (just above 32,768 and not
+    batches of up to 170 tokens (1024 pairs) route through the one-block
+    dispatch, longer ones per chunk; most experts empty; pair counts 32,772 and
+    52,752 (just above 32,768 and not
     a multiple of 64; and 8 x 1,099 x 6, the expert-GEMM row counts of section 3
     of "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No.")."""
     inp = synth.make_inputs("prefill_t2048", T=T)
