@@ -345,23 +345,30 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       }
     }
   };
-  // taller tiles: both tiles' blocks of group q, each activation chunk decoded once
+  // taller tiles: both tiles' blocks of group q; each activation chunk and each
+  // weight block decoded from its E4M3 codes once
   auto compute_pair = [&](auto S, int q) {
     constexpr int sl = decltype(S)::value;
 #pragma unroll
     for (int j = 0; j < KGP; ++j) {
       const int bb = q * KGP + j;
       if (bb >= nbb) break;
+      v4i b[NC][4];
+      float sx[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        v4i b[4];
         const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
-        e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
-        e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[2], b[3]);
-        const float sx = sxs[(c * 16 + lr) * nbb + bb];
+        e4m3x16_to_bf16(*(const v4i*)bp, b[c][0], b[c][1]);
+        e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[c][2], b[c][3]);
+        sx[c] = sxs[(c * 16 + lr) * nbb + bb];
+      }
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
-          acc[m][c] += kblock_e4m3_exact(wlo[sl][m * KGP + j], whi[sl][m * KGP + j], b) * (sx * wsc[m * nbb + bb]);
+      for (int m = 0; m < 2; ++m) {
+        v4i w[4];
+        kblock_decode(wlo[sl][m * KGP + j], whi[sl][m * KGP + j], w);
+        const float sw = wsc[m * nbb + bb];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[m][c] += kblock_bf16(w, b[c]) * (sx[c] * sw);
       }
     }
   };
@@ -605,6 +612,8 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
     for (int j = 0; j < KG; ++j) {
       const int bb = q0 + j;
       if (bb >= nbb) break;
+      v4i wd[4];  // the K block's weight codes decoded once for every row chunk
+      if constexpr (WT == 2) kblock_decode(wlo[slot][j], whi[slot][j], wd);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if constexpr (WT == 2) {
@@ -612,7 +621,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
           const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 16), *(const v4i*)(bp + 128),
                             *(const v4i*)(bp + 144)};
           // the wave's 16*RT <= 64 rows start at a multiple of 64: one 128-row scale block
-          acc[r][c] += kblock_e4m3_exact(wlo[slot][j], whi[slot][j], b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
+          acc[r][c] += kblock_bf16(wd, b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
         } else {
           const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 128 + lk;
           const v4i blo = *(const v4i*)bp;

@@ -156,6 +156,22 @@ __device__ __forceinline__ v4f kblock_e4m3_exact(v4i alo, v4i ahi, const v4i (&b
   return p;
 }
 
+// The same product split in two: the weight codes decoded once (a[4]), then
+// the four chained products against one row chunk's operands -- for tiles of
+// several row chunks, which would otherwise decode the same codes per chunk.
+__device__ __forceinline__ void kblock_decode(v4i alo, v4i ahi, v4i (&a)[4]) {
+  e4m3x16_to_bf16(alo, a[0], a[1]);
+  e4m3x16_to_bf16(ahi, a[2], a[3]);
+}
+__device__ __forceinline__ v4f kblock_bf16(const v4i (&a)[4], const v4i (&b)[4]) {
+  v4f p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a[i]), __builtin_bit_cast(v8bf, b[i]), p, 0, 0,
+                                                0);
+  return p;
+}
+
 // 16x16x32 bf16 matrix-core product accumulated into c.
 __device__ __forceinline__ v4f mfma_bf16(v4i a, v4i b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
