@@ -35,7 +35,7 @@ namespace moe {
 
 constexpr int kAttD = 128;    // head dimension
 constexpr int kAttKT = 64;    // keys per tile
-constexpr int kAttRows = 64;  // (query, head) rows per block
+constexpr int kAttRows = 64;  // (query, head) rows per block of 4 waves (8 waves: 128)
 constexpr int kKStride = kAttD + 8;   // bf16 elements per LDS key row
 constexpr int kVStride = kAttKT + 8;  // bf16 elements per LDS value-transposed row
 constexpr int kAttSplitMax = 512;     // key splits per row (decode)
@@ -107,9 +107,12 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int
   }
 }
 
-// One block: 64 (query, head) rows of key/value head blockIdx.y, over tile
-// range split blockIdx.z of the block's keys.
-__global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
+// One block: NW*16 (query, head) rows of key/value head blockIdx.y, over tile
+// range split blockIdx.z of the block's keys.  NW = 8 for long query batches
+// (each staged tile serves 128 rows), 4 for short ones.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64, CPT = 1024 / NT;  // threads; 16-byte chunks of K (and of V) per thread
   __shared__ __align__(16) uint16_t ks[kAttKT * kKStride];
   __shared__ __align__(16) uint16_t vts[kAttD * kVStride];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
@@ -135,21 +138,21 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
     if (live) qr[s] = *(const v4i*)(a.q + ((size_t)qi * a.Hq + head) * kAttD + 32 * s + 8 * q4);
   }
 
-  // tile staging: 64 keys x 128 d of K and of V, 16-byte chunks, 4 of each per
-  // thread.  K: chunk c is key c/16, 16-byte chunk c%16 of its row.  V: the
-  // thread takes chunk ch = c/64 of two neighbouring keys, 2 (c%32) and
-  // 2 (c%32) + 1 with c over two rounds of 512 pair slots, so that each 4-byte
-  // LDS store of the transposed tile holds one d of both keys.
-  v4i kreg[4], vreg[4];
+  // tile staging: 64 keys x 128 d of K and of V in 1024 16-byte chunks each,
+  // CPT of each per thread.  K: chunk c is key c/16, 16-byte chunk c%16 of its
+  // row.  V: the thread takes chunk ch = c/64 of two neighbouring keys,
+  // 2 (c%32) and 2 (c%32) + 1 with c over the 512 pair slots, so that each
+  // 4-byte LDS store of the transposed tile holds one d of both keys.
+  v4i kreg[CPT], vreg[CPT];
   auto fetch = [&](int tile) {
     const int k0 = k_lo + tile * kAttKT;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + u * 256;
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * NT;
       const int kk = k0 + (c >> 4);
       const size_t ko = ((size_t)min(kk, a.Tk - 1) * a.Hkv + kvh) * kAttD + (c & 15) * 8;
       kreg[u] = kk < k_hi ? *(const v4i*)(a.k + ko) : v4i{0, 0, 0, 0};
-      const int pc = tid + (u >> 1) * 256;  // pair slot
+      const int pc = tid + (u >> 1) * NT;  // pair slot
       const int kv = k0 + 2 * (pc & 31) + (u & 1);
       const size_t vo = ((size_t)min(kv, a.Tk - 1) * a.Hkv + kvh) * kAttD + (pc >> 5) * 8;
       vreg[u] = kv < k_hi ? *(const v4i*)(a.v + vo) : v4i{0, 0, 0, 0};
@@ -157,13 +160,13 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnArgs a) {
   };
   auto stage = [&]() {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int c = tid + u * 256;
+    for (int u = 0; u < CPT; ++u) {
+      const int c = tid + u * NT;
       *(v4i*)(ks + (c >> 4) * kKStride + (c & 15) * 8) = kreg[u];
     }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int pc = tid + h * 256;
+    for (int h = 0; h < CPT / 2; ++h) {
+      const int pc = tid + h * NT;
       const uint32_t* e0 = (const uint32_t*)&vreg[2 * h];      // key 2 (pc % 32), 8 d values
       const uint32_t* e1 = (const uint32_t*)&vreg[2 * h + 1];  // the next key, same d values
       uint32_t* dst = (uint32_t*)(vts + ((pc >> 5) * 8) * kVStride + 2 * (pc & 31));
@@ -341,13 +344,14 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
 // Launch plan shared by the workspace query and the launch: query blocks,
 // the largest block key range in tiles, and the split of that range.
 struct AttnPlan {
-  int qpb, q_blocks, max_tiles, n_split, tps;
+  int nw, qpb, q_blocks, max_tiles, n_split, tps;
 };
 
 AttnPlan attn_plan(const moe_attn_shape& s, int Tq, int q_pos0) {
   AttnPlan P;
   const int G = s.n_q_heads / s.n_kv_heads;
-  P.qpb = kAttRows / G;
+  P.nw = Tq >= 512 && (2 * kAttRows) % G == 0 ? 8 : 4;  // long query batches: 128-row blocks
+  P.qpb = P.nw * 16 / G;
   P.q_blocks = (Tq + P.qpb - 1) / P.qpb;
   // the widest block: a window's block spans window + qpb - 1 keys; the whole
   // context's last block spans every key up to the last query
@@ -397,7 +401,9 @@ hipError_t launch_attention(const moe_attn_shape& s, int Tq, int Tk, int q_pos0,
   a.part_o = P.n_split > 1 ? (float*)ws : nullptr;
   a.part_ml = P.n_split > 1 ? (float*)((char*)ws + ((size_t)P.n_split * rows * kAttD * 4 + 255) / 256 * 256)
                             : nullptr;
-  attention_kernel<<<dim3(P.q_blocks, s.n_kv_heads, P.n_split), 256, 0, st>>>(a);
+  const dim3 grid(P.q_blocks, s.n_kv_heads, P.n_split);
+  if (P.nw == 8) attention_kernel<8><<<grid, 512, 0, st>>>(a);
+  else attention_kernel<4><<<grid, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.n_split == 1) return e;
   attention_combine_kernel<<<(unsigned)rows, 256, 0, st>>>(a);

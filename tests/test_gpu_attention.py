@@ -98,6 +98,8 @@ def _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0, rows=None, seed=0):
     (16, 4, W, 3, 2000, 1997),      # sliding-window decode of three tokens
     (8, 8, W, 100, 700, 600),       # one query head per key/value head (64 queries a block)
     (32, 2, 0, 20, 300, 280),       # groups of 16 heads (4 queries a block)
+    (16, 4, W, 600, 1200, 600),     # a long batch: 8-wave blocks of 128 rows, ragged last block
+    (8, 8, 0, 520, 900, 380),       # long batch, one query head per group (128 queries a block)
 ])
 def test_attention_matches_oracle(Hq, Hkv, window, Tq, Tk, q_pos0):
     _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0)
