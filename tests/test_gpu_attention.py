@@ -11,8 +11,9 @@ Bars (written here):
     and takes cos, sin and the rotation in fp32, whose absolute error is below
     2^-21 (|x_j| + |x_{j+D/2}|) (one rounding each for sin or cos, the two
     products and the sum); both round once to bf16.  Bar per element:
-    |x - x_ref| <= one bf16 ulp of x_ref + 2^-20 (|x_j| + |x_{j+D/2}|), and at
-    most a share 2^-12 of the elements differ at all;
+    |x - x_ref| <= one bf16 ulp of x_ref + 2^-20 (|x_j| + |x_{j+D/2}|); and as a
+    guard against a systematic drift, at most max(4, n * 2^-10) of the n
+    elements differ at all (near-tie differences run at about 1e-4 of them);
   * attention, elementwise: |o - o_ref| <= 2^-8 |o_ref| + 2^-12 RMS(o_ref).
     The first term is the bf16 rounding of the output (half an ulp, 2^-8
     relative); the second covers the fp32 scores, exponentials and sums and the
@@ -49,7 +50,8 @@ def _rand(rng, shape, scale=1.0):
     return synth.bf16_bits((rng.standard_normal(shape) * scale).astype(np.float32))
 
 
-@pytest.mark.parametrize("T,H,D,pos0", [(64, 20, 128, 1000), (33, 4, 64, 0), (8, 16, 128, 100000)])
+@pytest.mark.parametrize("T,H,D,pos0", [(64, 20, 128, 1000), (33, 4, 64, 0), (8, 16, 128, 100000),
+                                        (5, 3, 256, 1 << 20)])
 def test_rope_matches_oracle(T, H, D, pos0):
     rng = np.random.default_rng(T + D)
     x = _rand(rng, (T, H, D))
@@ -65,7 +67,7 @@ def test_rope_matches_oracle(T, H, D, pos0):
     bound = ulp + 2.0 ** -20 * pair
     diff = np.abs(gf - rf)
     say(f"  elements differing: {(diff != 0).sum()} of {diff.size}; worst diff / bound {np.max(diff / bound):.3f}")
-    assert np.all(diff <= bound) and (diff != 0).mean() <= 2.0 ** -12
+    assert np.all(diff <= bound) and (diff != 0).sum() <= max(4, diff.size * 2.0 ** -10)
 
 
 def _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0, rows=None, seed=0):
@@ -100,6 +102,8 @@ def _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0, rows=None, seed=0):
     (32, 2, 0, 20, 300, 280),       # groups of 16 heads (4 queries a block)
     (16, 4, W, 600, 1200, 600),     # a long batch: 8-wave blocks of 128 rows, ragged last block
     (8, 8, 0, 520, 900, 380),       # long batch, one query head per group (128 queries a block)
+    (16, 1, W, 40, 45, 5),          # one key/value head for all query heads; a cache of 45 keys
+    (64, 1, 0, 2, 3, 1),            # a group of 64 heads (one query a block), three keys
 ])
 def test_attention_matches_oracle(Hq, Hkv, window, Tq, Tk, q_pos0):
     _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0)

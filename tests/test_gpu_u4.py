@@ -160,3 +160,22 @@ def test_u4_stages_match_fused():
     torch.cuda.synchronize()
     assert r.status.item() == 0
     assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+
+
+@pytest.mark.parametrize("T", [1, 64])
+def test_u4_forced(T):
+    """4-bit weights with forced routing (random ids, some repeated within a
+    token), one token and a 64-token batch, against the oracle."""
+    inp = synth.make_inputs("decode_t32_u4", T=T)
+    s = inp["shape"]
+    rng = np.random.default_rng(T)
+    forced = rng.integers(0, s.E, size=(T, s.k)).astype(np.int32)
+    forced[0, 1] = forced[0, 0]  # a duplicate id: computed twice, literally
+    say(f"decode_t32_u4 T={T}: forced routing against the oracle")
+    g = run_gpu(inp, forced=forced)
+    assert g["status"][0] == 0 and np.array_equal(g["topk_idx"], forced)
+    L = O.Layer(inp)
+    _, _, idf, wf = O.route_forced(L, forced)
+    assert np.max(np.abs(g["topk_w"] - wf)) <= W_ABS
+    _, acc_ref = O.forward(L, idf, wf)
+    check_y(g["y"], acc_ref)
