@@ -70,8 +70,12 @@ typedef enum {
 /* Supported (act_dtype, w_dtype) pairs: (F32, F32), (BF16, BF16), (BF16, FP8E4M3_B128),
  * (BF16, FP8E4M3_B128_A16), (BF16, U4_G64).
  * Limits: 1 <= top_k <= 8, top_k <= n_experts <= 512, d_model and d_ffn multiples
- * of 128 with d_model <= 8192 and d_ffn <= 4096, d_ffn_shared 0 (no shared expert)
- * or a multiple of 128 <= 4096, T * top_k < 2^31. */
+ * of 128, d_ffn_shared 0 (no shared expert) or a multiple of 128, T * top_k < 2^31.
+ * The expert kernels hold one 16-row tile's activation rows (d_model wide) and h
+ * rows (max(d_ffn, d_ffn_shared) wide) in the 160 KB of LDS of one workgroup, which
+ * bounds the widths: d_model <= 4608 for FP8E4M3_B128, FP8E4M3_B128_A16 and U4_G64
+ * weights, <= 4736 for BF16, <= 2560 for F32; d_ffn and d_ffn_shared <= 4096, and
+ * <= 2560 for F32.  Wider shapes return MOE_ERR_UNSUPPORTED. */
 /* Layouts of the expert weight matrices (moe_shape.w_layout). */
 typedef enum {
   MOE_LAYOUT_ROWMAJOR = 0,   /* [rows][cols] row-major, as documented per tensor */

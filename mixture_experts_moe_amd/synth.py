@@ -109,7 +109,7 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (b.astype(np.uint32) << 16).view(np.float32)
 
 
-def _fp8_blocks(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+def fp8_blocks(w: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """Quantise a [R, C] fp32 weight (R, C multiples of 128) to E4M3 codes plus
     one fp32 scale per 128x128 block, scale = amax(block) / 448, so that
     weight ~= decode(code) * scale."""
@@ -188,7 +188,7 @@ def _expert_weights(layer: str, seed: int, w_dtype: str) -> dict:
             return bf16_bits(w), None, None
         if w_dtype == "u4":
             return u4_groups(w)
-        return (*_fp8_blocks(w), None)
+        return (*fp8_blocks(w), None)
 
     def one(e: int):
         for name, tensor, shape in (("gate", _T_GATE, (F, d)), ("up", _T_UP, (F, d)), ("down", _T_DOWN, (d, F))):

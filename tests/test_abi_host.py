@@ -62,6 +62,21 @@ def test_workspace_bytes():
         assert moe.workspace_bytes(bad) == 0
 
 
+
+@pytest.mark.parametrize("act,w,layout,d_max,f_max", [("f32", "f32", "rowmajor", 2560, 2560),
+                                                       ("bf16", "bf16", "rowmajor", 4736, 4096),
+                                                       ("bf16", "fp8", "rowmajor", 4608, 4096),
+                                                       ("bf16", "fp8a16", "rowmajor", 4608, 4096),
+                                                       ("bf16", "u4", "tiled", 4608, 4096)])
+def test_largest_supported_widths(act, w, layout, d_max, f_max):
+    """The widths the header states as the largest supported (one 16-row tile's
+    activation and h rows in 160 KB of LDS) are accepted, one 128 step more is not."""
+    _lib()
+    ok = lambda d, F, Fs: moe.workspace_bytes(moe.make_shape(8, d, 16, 2, F, Fs, act, w, layout)) > 0
+    assert ok(d_max, 128, 128) and not ok(d_max + 128, 128, 128)
+    assert ok(256, f_max, 0) and not ok(256, f_max + 128, 0)
+    assert ok(256, 128, f_max) and not ok(256, 128, f_max + 128)
+
 FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below returns before launching
 
 

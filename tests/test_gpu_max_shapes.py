@@ -1,0 +1,90 @@
+"""The layer at the edges of the supported shape range, on the GPU through the
+C ABI, against the oracle with the parity bars of the main workloads.
+
+  * the widest FP8 layer (d_model 4608, d_ffn and d_ffn_shared 4096: one 16-row
+    tile's activation and h rows fill the LDS of a workgroup), with as many
+    experts as top_k (every token routes to every expert, so the experts hold T
+    rows each) and a ragged T;
+  * the most experts and the largest top_k (512 experts, top 8: eight candidates
+    per lane in the selection), with the one-block dispatch (800 pairs) and the
+    chunked one (2,400 pairs), free and forced.
+Layers: weights N(0, 0.02) quantised to E4M3 with 128x128 block scales, router
+weights N(0, 0.05), activations N(0, 1) in bf16 (the recipe of the main
+workloads at other sizes).
+"""
+import numpy as np
+import pytest
+
+from mixture_experts_moe_amd import synth
+from oracle import moe_oracle as O
+
+from test_gpu_parity import (DEV, W_ABS, check_dispatch, check_logits, check_y, route_agreement, run_gpu, say,
+                             selection_scores)
+
+pytestmark = pytest.mark.gpu
+
+
+def _fp8_layer(T, d, E, k, F, Fs, seed):
+    rng = np.random.default_rng(seed)
+    inp = dict(shape=synth.LayerShape(T=T, d=d, E=E, k=k, F=F, Fs=Fs, act="bf16", w="fp8"),
+               x=synth.bf16_bits(rng.standard_normal((T, d), dtype=np.float32)),
+               w_router=rng.standard_normal((E, d), dtype=np.float32) * np.float32(0.05), sel_bias=None)
+    for pre, sp, n, Fg in (("w_", "s_", E, F), ("sh_", "ss_", 0, Fs)):
+        for name, (r, c) in (("gate", (Fg, d)), ("up", (Fg, d)), ("down", (d, Fg))):
+            mats = [synth.fp8_blocks(rng.standard_normal((r, c), dtype=np.float32) * np.float32(0.02))
+                    for _ in range(max(n, 1))]
+            inp[pre + name] = np.stack([m[0] for m in mats]) if n else mats[0][0]
+            inp[sp + name] = np.stack([m[1] for m in mats]) if n else mats[0][1]
+    return inp
+
+
+def _dev(inp):
+    keys = [k for k, v in inp.items() if isinstance(v, np.ndarray)]
+    return synth.to_device({k: inp[k] for k in keys}, DEV)
+
+
+def _check(inp, g, forced=None, n_sample=None):
+    s = inp["shape"]
+    assert g["status"][0] == 0
+    L = O.Layer(inp)
+    if forced is None:
+        _, lg, idx, w = O.route(L)
+        check_logits(g["logits"], lg)
+        bad, ex = route_agreement(g["topk_idx"], idx, selection_scores(inp, lg), s.k)
+        say(f"  ids: {bad} mismatches, {ex} tokens exempt by the gap rule")
+        assert bad == 0
+        same = (g["topk_idx"] == idx).all(axis=1)
+        tok = np.nonzero(same)[0]
+    else:
+        assert np.array_equal(g["topk_idx"], forced)
+        check_dispatch(g, forced, s.E)
+        tok = np.arange(s.T)
+    if n_sample is not None:
+        tok = tok[np.unique(np.linspace(0, len(tok) - 1, n_sample).astype(int))]
+    ids = g["topk_idx"][tok]
+    _, _, idf, wf = O.route_forced(L, np.ascontiguousarray(g["topk_idx"]), tok)
+    assert np.array_equal(idf, ids)
+    assert np.max(np.abs(g["topk_w"][tok] - wf)) <= W_ABS
+    _, acc_ref = O.forward(L, idf, wf, tok)
+    check_y(g["y"][tok], acc_ref)
+
+
+def test_widest_fp8_layer():
+    T, d, E, k, F = 40, 4608, 4, 4, 4096
+    inp = _fp8_layer(T, d, E, k, F, F, seed=11)
+    say(f"widest FP8 layer T={T} d={d} E={E} k={k} F=Fs={F}")
+    g = run_gpu(inp, dev=_dev(inp))
+    _check(inp, g, n_sample=5)
+
+
+@pytest.mark.parametrize("T,kind", [(100, "free"), (100, "forced"), (300, "free"), (300, "forced")])
+def test_most_experts_top8(T, kind):
+    d, E, k, F, Fs = 256, 512, 8, 128, 128
+    inp = _fp8_layer(T, d, E, k, F, Fs, seed=12)
+    forced = None
+    if kind == "forced":
+        forced = np.random.default_rng(T).integers(0, E, size=(T, k)).astype(np.int32)
+        forced[0, :] = forced[0, 0]  # one token with every slot on one expert
+    say(f"E={E} k={k} T={T} ({T * k} pairs) {kind}")
+    g = run_gpu(inp, forced=forced, dev=_dev(inp))
+    _check(inp, g, forced=forced)

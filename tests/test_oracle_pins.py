@@ -500,7 +500,7 @@ def _small_fp8_layer(w_mode, T=16, seed=7):
     for pre, sp, dims, n in (("w_", "s_", (F, d, d, F), E), ("sh_", "ss_", (Fs, d, d, Fs), None)):
         for name, (r, c) in (("gate", dims[:2]), ("up", dims[:2]), ("down", dims[2:])):
             ws = [rng.standard_normal((r, c), dtype=np.float32) * np.float32(0.02) for _ in range(n or 1)]
-            blocks = [synth._fp8_blocks(w) for w in ws]
+            blocks = [synth.fp8_blocks(w) for w in ws]
             if w_mode == "f32":
                 vals = [_dequant_weight(cq, sq) for cq, sq in blocks]
                 inp[pre + name] = np.stack(vals) if n else vals[0]
