@@ -556,12 +556,13 @@ __device__ __forceinline__ int dispatch_block(const TopkArgs& a, DispatchLds& s,
 // order) + (parts [gs, n_parts) added in order): the K-split router writes one
 // part per 256-deep slice (gs = half of them), the tiled router one part per
 // half of K (gs = 1), so both give the same sum bit for bit.  Written to
-// logits_out when given.  The parts are requested 8 at a time (all J
-// candidates at once), then added.
-template <int J>
+// logits_out when given.  The parts are requested QB at a time (all J
+// candidates at once), then added: QB = 8 after the K-split router, 2 after the
+// tiled one (at most two parts; a larger batch would issue loads for parts
+// that do not exist, masked off but still issued).
+template <int J, int QB>
 __device__ __forceinline__ void gather_logits(const float* __restrict__ part, int n_parts, int gs, int T, int E,
                                               int t, int lane, float* __restrict__ logits_out, float (&lv)[J]) {
-  constexpr int QB = 8;
   float h0[J], h1[J];
 #pragma unroll
   for (int j = 0; j < J; ++j) h0[j] = h1[j] = 0.f;
@@ -613,7 +614,7 @@ __global__ __launch_bounds__(1024) void topk_dispatch_kernel(TopkArgs a, const f
       continue;
     }
     float lv[J];
-    gather_logits<J>(part, n_parts, gs, T, E, t, lane, logits_out, lv);
+    gather_logits<J, 2>(part, n_parts, gs, T, E, t, lane, logits_out, lv);
     const int id = route_token<J, FORCED>(a, t, lv, lane);
     if (lane < k) ids[tl * k + lane] = id;
   }
@@ -632,7 +633,7 @@ __global__ __launch_bounds__(64) void topk_small_kernel(TopkArgs a, const float*
   const int t = blockIdx.x, lane = threadIdx.x;
   const int E = a.E, T = a.T;
   float lv[J];
-  gather_logits<J>(part, n_parts, gs, T, E, t, lane, logits_out, lv);
+  gather_logits<J, 8>(part, n_parts, gs, T, E, t, lane, logits_out, lv);
   route_token<J, FORCED>(a, t, lv, lane);
 }
 
@@ -782,10 +783,16 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
 // Launchers
 // ---------------------------------------------------------------------------
 // Tokens per top-k block: all of them when their pairs fit one block, else 16
-// (one token per wave; the per-expert scan of the chunk histograms is parallel).
+// (one token per wave; the per-expert scan of the chunk histograms is parallel),
+// doubled while the blocks would outnumber the chip's 256 CUs and a chunk's
+// pairs still fit one block: the kernel holds one 16-wave block per CU, and a
+// second round of blocks costs more than a second token per wave.
+constexpr int kNumCUs = 256;
 int tokens_per_chunk(int T, int k) {
   if (T * k <= kMaxChunkPairs) return T > 0 ? T : 1;
-  return 16;
+  int tpc = 16;
+  while ((T + tpc - 1) / tpc > kNumCUs && 2 * tpc * k <= kMaxChunkPairs) tpc *= 2;
+  return tpc;
 }
 
 size_t dispatch_chunk_hist_ints(int T, int k, int E) {
