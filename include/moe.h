@@ -16,7 +16,12 @@
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers (HBM of the current HIP device),
- *     row-major, densely packed.  The caller allocates and owns every buffer,
+ *     row-major, densely packed, each 16-byte aligned (the kernels move 16 bytes
+ *     per lane; hipMalloc and torch allocations are 256-byte aligned, and every
+ *     row width the shapes allow keeps later rows aligned).  Buffers that are not
+ *     16-byte aligned return MOE_ERR_INVALID_ARG where the call checks them (the
+ *     activation rows and outputs of moe_route, moe_forward and
+ *     moe_quantize_rows); for the others behaviour is undefined.  The caller allocates and owns every buffer,
  *     including the workspace; the library never allocates or frees memory and
  *     keeps no state between calls (calls are reentrant).
  *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the default

@@ -61,15 +61,15 @@ __device__ __forceinline__ v4i stream_load(const uint8_t* p) {
 }
 
 // ---------------------------------------------------------------------------
-// Activation quantisation on its own (moe_quantize_rows): one wave per
-// 128-element group, as in the routing call's plan step.
+// Activation quantisation on its own (moe_quantize_rows): one wave per row, as
+// in the routing call's plan step.
 // ---------------------------------------------------------------------------
 template <bool BF16IN>
-__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ in, int64_t n_groups, int gpr,
+__global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restrict__ in, int64_t n_rows, int gpr,
                                                              uint8_t* __restrict__ codes, float* __restrict__ scales) {
-  const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (g >= n_groups) return;
-  quantize_group<BF16IN>(in, g, gpr, codes, scales, threadIdx.x & 63);
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  quantize_row<BF16IN>(in, row, gpr, codes, scales, threadIdx.x & 63);
 }
 
 // Address of the weight bytes a lane streams for one 16-row tile: in the
@@ -1251,10 +1251,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n_cols, uint8_t* codes, float* scales,
                                 hipStream_t st) {
   const int gpr = n_cols / 128;
-  const int64_t ng = n_rows * gpr;
-  const int64_t blocks = (ng + 3) / 4;
-  if (bf16) quantize_rows_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(in, ng, gpr, codes, scales);
-  else quantize_rows_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(in, ng, gpr, codes, scales);
+  const int64_t blocks = (n_rows + 3) / 4;
+  if (bf16) quantize_rows_kernel<true><<<(unsigned)blocks, 256, 0, st>>>(in, n_rows, gpr, codes, scales);
+  else quantize_rows_kernel<false><<<(unsigned)blocks, 256, 0, st>>>(in, n_rows, gpr, codes, scales);
   return hipGetLastError();
 }
 

@@ -121,6 +121,9 @@ int pick_bm(const moe_shape& s) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// The kernels move 16 bytes per lane through every tensor.
+bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
+
 int check_routing_out(const moe_routing* r) {
   if (!r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->inv_perm || !r->status ||
       !r->plan)
@@ -168,6 +171,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!w || !w->w_router || !x || check_routing_out(out) != MOE_OK) return MOE_ERR_INVALID_ARG;
+  if (misaligned(x)) return MOE_ERR_INVALID_ARG;
   if (shape->T == 0) return MOE_OK;
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);
@@ -216,7 +220,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   pc.xq = v.xq;
   pc.sx = v.sx;
   pc.gpr = shape->d_model / 128;
-  pc.n_groups = v.xq ? (int64_t)shape->T * pc.gpr : 0;
+  pc.n_rows = v.xq ? shape->T : 0;
   pc.k = shape->top_k;
   return hip_status(moe::launch_route(R, (hipStream_t)stream));
 }
@@ -258,6 +262,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   if (rc != MOE_OK) return rc;
   if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->plan)
     return MOE_ERR_INVALID_ARG;
+  if (misaligned(x) || misaligned(y)) return MOE_ERR_INVALID_ARG;
   const bool fp8 = shape->w_dtype == MOE_FP8E4M3_B128;                  // activations quantised
   const bool scaled = fp8 || shape->w_dtype == MOE_FP8E4M3_B128_A16 ||  // block-scaled FP8 weights
                       shape->w_dtype == MOE_U4_G64;                       // or 4-bit group parameters
@@ -343,7 +348,8 @@ int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const v
     return n_cols > 0 && n_cols % 128 ? MOE_ERR_UNSUPPORTED : MOE_ERR_INVALID_ARG;
   if (n_rows == 0) return MOE_OK;
   if (!in || !codes || !scales) return MOE_ERR_INVALID_ARG;
-  if (n_rows * (n_cols / 128) / 4 >= (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;
+  if (misaligned(in) || misaligned(codes)) return MOE_ERR_INVALID_ARG;
+  if ((n_rows + 3) / 4 * 256 > (int64_t)UINT_MAX) return MOE_ERR_UNSUPPORTED;  // one wave per row, 32-bit grid
   return hip_status(moe::launch_quantize_rows(in, act_dtype == MOE_BF16, n_rows, n_cols, codes, scales,
                                               (hipStream_t)stream));
 }

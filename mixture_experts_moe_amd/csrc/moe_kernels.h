@@ -38,7 +38,7 @@ struct PlanCtx {
   const uint16_t* x;  // bf16 activations [T][d] (quantised when xq != null)
   uint8_t* xq;
   float* sx;
-  int64_t n_groups;   // T * d / 128 when quantising, else 0
+  int n_rows;         // T when quantising, else 0
   int gpr;            // d / 128
   int k;
 };

@@ -23,27 +23,49 @@
 
 namespace moe {
 
-// Activation quantisation of one 128-element group by one wave (two elements
-// per lane): s = amax/448 (1 for an all-zero group), code = E4M3(v/s), round
-// to nearest even, saturating.  Group g = row * gpr + column group.
+// Activation quantisation of 128-element groups by one wave: per group
+// s = amax/448 (1 for an all-zero group), code = E4M3(v/s), round to nearest
+// even, saturating.  The wave takes four groups at a time, one per 16 lanes,
+// eight elements per lane (one 16-byte load, one 8-byte store): groups
+// g0 .. g0+3 of row `row` (those below gpr, the groups per row).
 template <bool BF16IN>
-__device__ __forceinline__ void quantize_group(const void* __restrict__ in, int64_t g, int gpr,
-                                               uint8_t* __restrict__ codes, float* __restrict__ scales, int lane) {
-  const int64_t o = (g / gpr) * (int64_t)gpr * 128 + (g % gpr) * 128 + 2 * lane;
-  float v0, v1;
-  if (BF16IN) {
-    const uint32_t pr = *(const uint32_t*)((const uint16_t*)in + o);
-    v0 = __uint_as_float(pr << 16);
-    v1 = __uint_as_float(pr & 0xffff0000u);
-  } else {
-    const float2 pr = *(const float2*)((const float*)in + o);
-    v0 = pr.x;
-    v1 = pr.y;
+__device__ __forceinline__ void quantize_groups4(const void* __restrict__ in, int64_t row, int g0, int gpr,
+                                                 uint8_t* __restrict__ codes, float* __restrict__ scales, int lane) {
+  const int g = g0 + (lane >> 4), l16 = lane & 15;
+  if (g < gpr) {  // whole 16-lane groups drop out together
+    const int64_t o = (row * gpr + g) * 128 + 8 * l16;
+    float v[8];
+    if (BF16IN) {
+      const v4i pr = *(const v4i*)((const uint16_t*)in + o);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = __uint_as_float((uint32_t)pr[i] << 16);
+        v[2 * i + 1] = __uint_as_float((uint32_t)pr[i] & 0xffff0000u);
+      }
+    } else {
+      const float4 a = *(const float4*)((const float*)in + o), b = *(const float4*)((const float*)in + o + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+#pragma unroll
+    for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, kWave));
+    const float s = m > 0.f ? m / 448.0f : 1.0f;
+    uint2 c;
+    c.x = pack4_e4m3(v[0] / s, v[1] / s, v[2] / s, v[3] / s);
+    c.y = pack4_e4m3(v[4] / s, v[5] / s, v[6] / s, v[7] / s);
+    *(uint2*)(codes + o) = c;
+    if (l16 == 0) scales[row * gpr + g] = s;
   }
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const float s = amax > 0.f ? amax / 448.0f : 1.0f;
-  *(uint16_t*)(codes + o) = (uint16_t)pack2_e4m3(v0 / s, v1 / s);
-  if (lane == 0) scales[g] = s;
+}
+
+// A whole row by one wave.
+template <bool BF16IN>
+__device__ __forceinline__ void quantize_row(const void* __restrict__ in, int64_t row, int gpr,
+                                             uint8_t* __restrict__ codes, float* __restrict__ scales, int lane) {
+  for (int g0 = 0; g0 < gpr; g0 += 4) quantize_groups4<BF16IN>(in, row, g0, gpr, codes, scales, lane);
 }
 
 // Group tables of one plan block: tile prefix, rows and first h row per group.

@@ -639,12 +639,13 @@ __global__ __launch_bounds__(64) void topk_small_kernel(TopkArgs a, const float*
 
 // Short inputs, step 3: block 0 does the whole counting sort (T * k <= 1024)
 // and then the dispatch plan (per-row info, block schedules, see moe_plan.h);
-// the other blocks quantise the activations (FP8 weights), 16 groups each.
+// the other blocks quantise the activations (FP8 weights), 16 chunks of 512
+// elements each (one per wave).
 __global__ __launch_bounds__(1024) void dispatch_small_kernel(TopkArgs a, PlanCtx pc) {
   const int tid = threadIdx.x, lane = tid & 63;
   if (blockIdx.x > 0) {
-    const int64_t g = (int64_t)(blockIdx.x - 1) * 16 + (tid >> 6);
-    if (g < pc.n_groups) quantize_group<true>(pc.x, g, pc.gpr, pc.xq, pc.sx, lane);
+    const int cpr = (pc.gpr + 3) / 4, u = (blockIdx.x - 1) * 16 + (tid >> 6);  // one 512-element chunk per wave
+    if (u < pc.n_rows * cpr) quantize_groups4<true>(pc.x, u / cpr, 4 * (u % cpr), pc.gpr, pc.xq, pc.sx, lane);
     return;
   }
   __shared__ DispatchLds s;
@@ -721,7 +722,7 @@ __device__ __forceinline__ void block_offsets(const int32_t* __restrict__ counts
 // the placed pairs (blocks [0, npl); each derives the expert offsets from the
 // counts, block 0 also stores them); the shared expert's rows (next nsr
 // blocks); the block schedules (next npb blocks, kPlanEntries entries each);
-// the activation quantisation (the rest, four groups each).
+// the activation quantisation (the rest, one row per wave).
 constexpr int kPlanEntries = 512;
 
 __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __restrict__ idx, int P, int E, int np,
@@ -775,8 +776,8 @@ __global__ __launch_bounds__(256) void dispatch_place_kernel(const int32_t* __re
     for (int i = tid; i < kPlanEntries && e0 + i < ne; i += 256) plan_any_entry(pa, pl, total, e0 + i);
     return;
   }
-  const int64_t g = (int64_t)(blk - npl - nsr - npb) * 4 + (tid >> 6);
-  if (g < pc.n_groups) quantize_group<true>(pc.x, g, pc.gpr, pc.xq, pc.sx, tid & 63);
+  const int row = (blk - npl - nsr - npb) * 4 + (tid >> 6);
+  if (row < pc.n_rows) quantize_row<true>(pc.x, row, pc.gpr, pc.xq, pc.sx, tid & 63);
 }
 
 // ---------------------------------------------------------------------------
@@ -906,7 +907,7 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
 #undef MOE_TOPK_SMALL
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int nqb = (int)((L.plan.n_groups + 15) / 16);
+    const int nqb = (L.plan.n_rows * ((L.plan.gpr + 3) / 4) + 15) / 16;
     dispatch_small_kernel<<<1 + nqb, 1024, 0, st>>>(a, L.plan);
     return hipGetLastError();
   }
@@ -928,7 +929,7 @@ hipError_t launch_route(const RouteLaunch& L, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int npl = (P + 255) / 256, nsr = L.plan.pa.has_shared ? (L.T + 255) / 256 : 0;
   const int npb = (plan_n_entries(L.plan.pa) + kPlanEntries - 1) / kPlanEntries;
-  const int64_t nqb = (L.plan.n_groups + 3) / 4;
+  const int nqb = (L.plan.n_rows + 3) / 4;
   dispatch_place_kernel<<<(unsigned)(npl + nsr + npb + nqb), 256, 0, st>>>(
       L.idx, P, L.E, tpc * L.k, L.chunk_hist, L.local_rank, L.counts, L.offsets, L.perm, L.inv_perm, L.w, L.plan, npl, nsr,
       npb);

@@ -160,6 +160,20 @@ def test_quantize_rows_host_validation():
     assert L.moe_quantize_rows(-1, 128, 1, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_quantize_rows(0, 128, 1, None, None, None, None) == moe.MOE_OK
     assert L.moe_quantize_rows(4, 128, 1, None, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    odd = C.c_void_p(0x1008)  # 8-byte but not 16-byte aligned
+    assert L.moe_quantize_rows(4, 128, 1, odd, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_quantize_rows(4, 128, 1, FAKE, odd, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_misaligned_activations_rejected():
+    good = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    odd = C.c_void_p(0x1008)
+    assert _route(good, x=odd) == moe.MOE_ERR_INVALID_ARG
+    L = _lib()
+    w, r = _weights_struct(), _routing_struct()
+    for x, y in ((odd, FAKE), (FAKE, odd)):
+        assert L.moe_forward(C.byref(good), C.byref(w), x, C.byref(r), y, FAKE, 1 << 40, None) == \
+            moe.MOE_ERR_INVALID_ARG
 
 
 def test_pack_weights_host_validation():
