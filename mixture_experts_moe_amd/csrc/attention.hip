@@ -109,13 +109,21 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int
 
 // One block: NW*16 (query, head) rows of key/value head blockIdx.y, over tile
 // range split blockIdx.z of the block's keys.  NW = 8 for long query batches
-// (each staged tile serves 128 rows), 4 for short ones.
-template <int NW>
-__global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
-  constexpr int NT = NW * 64, CPT = 1024 / NT;  // threads; 16-byte chunks of K (and of V) per thread
-  __shared__ __align__(16) uint16_t ks[kAttKT * kKStride];
-  __shared__ __align__(16) uint16_t vts[kAttD * kVStride];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
+// (each staged tile serves 128 rows), 4 for short ones.  KS key groups of NW
+// waves each: group g takes the tiles g, g + KS, ... of the range (its own LDS
+// buffers, the same per-tile code), and at the end the groups' running
+// (max, sum, output) states of each row are merged through LDS in group order,
+// so a long batch, whose rows alone give two waves per SIMD, gets KS times
+// as many waves to hide each tile's dependent chain.
+template <int NW, int KS>
+__global__ __launch_bounds__(NW * KS * 64) void attention_kernel(AttnArgs a) {
+  constexpr int NT = NW * 64, CPT = 1024 / NT;  // threads per group; 16-byte chunks of K (and of V) per thread
+  constexpr int kGroupLds = kAttKT * kKStride + kAttD * kVStride;  // bf16 elements: a K tile, a V^T tile
+  __shared__ __align__(16) uint16_t lds[KS * kGroupLds];
+  const int grp = __builtin_amdgcn_readfirstlane(threadIdx.x / NT);
+  uint16_t* const ks = lds + grp * kGroupLds;
+  uint16_t* const vts = ks + kAttKT * kKStride;
+  const int tid = threadIdx.x % NT, wave = tid >> 6, lane = tid & 63, lr = lane & 15, q4 = lane >> 4;
   const int kvh = blockIdx.y;
   const int qb0 = blockIdx.x * a.qpb;  // first query of the block
   // this lane's row as the B operand of S^T (and the row whose state it keeps)
@@ -188,12 +196,16 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
     return all_live && k0 + kAttKT - 1 <= p_first && (a.window == 0 || p_last - k0 < a.window);
   };
 
-  if (t_begin < t_end) fetch(t_begin);
-  for (int tile = t_begin; tile < t_end; ++tile) {
+  const int n_it = (t_end - t_begin + KS - 1) / KS;  // iterations, the same for every group
+  if (t_begin + grp < t_end) fetch(t_begin + grp);
+  for (int it = 0; it < n_it; ++it) {
+    const int tile = t_begin + it * KS + grp;
+    const bool has = tile < t_end;  // the group's last iteration may have no tile
     __syncthreads();  // the previous tile's LDS reads are done
-    stage();
+    if (has) stage();
     __syncthreads();
-    if (tile + 1 < t_end) fetch(tile + 1);
+    if (tile + KS < t_end) fetch(tile + KS);
+    if (!has) continue;
     const int k0 = k_lo + tile * kAttKT;
     // S^T: lane holds keys 16 t + 4 q4 + v of this row, t = 0..3
     v4f st[4];
@@ -270,6 +282,32 @@ __global__ __launch_bounds__(NW * 64) void attention_kernel(AttnArgs a) {
     }
   }
 
+  if constexpr (KS > 1) {
+    // merge: groups 1.. leave their states in LDS (over the tile buffers), group
+    // 0 adds them in group order: m = max, each state scaled by 2^(m_g - m)
+    static_assert(KS == 2, "one partner group");
+    static_assert((size_t)NW * 64 * 34 * 4 <= sizeof(lds), "merge buffer fits the tile buffers");
+    const int li = wave * 64 + lane;
+    float* mb = (float*)lds + (size_t)li * 32;            // this lane's 32 outputs (16-byte aligned)
+    float* ml = (float*)lds + (size_t)NW * 64 * 32 + 2 * li;  // its row's max and sum
+    __syncthreads();  // every tile read is done
+    if (grp == 1) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) *(v4f*)(mb + 4 * m) = acc[m];
+      ml[0] = mrow;
+      ml[1] = lrow;
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    const float m1 = ml[0], l1 = ml[1];
+    const float mm = fmaxf(mrow, m1);
+    const float a0 = mrow == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrow - mm);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) acc[m] = acc[m] * a0 + *(const v4f*)(mb + 4 * m) * a1;
+    lrow = lrow * a0 + l1 * a1;
+    mrow = mm;
+  }
   // lane holds O^T[d = 16 m + 4 q4 + v][row]; four lanes of a column share the row
   if (!live) return;
   const size_t orow = (size_t)qi * a.Hq + head;
@@ -344,7 +382,7 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
 // Launch plan shared by the workspace query and the launch: query blocks,
 // the largest block key range in tiles, and the split of that range.
 struct AttnPlan {
-  int nw, qpb, q_blocks, max_tiles, n_split, tps;
+  int nw, ks, qpb, q_blocks, max_tiles, n_split, tps;
 };
 
 AttnPlan attn_plan(const moe_attn_shape& s, int Tq, int q_pos0) {
@@ -363,6 +401,10 @@ AttnPlan attn_plan(const moe_attn_shape& s, int Tq, int q_pos0) {
   P.n_split = min(P.n_split, kAttSplitMax);
   P.tps = (P.max_tiles + P.n_split - 1) / P.n_split;
   P.n_split = (P.max_tiles + P.tps - 1) / P.tps;
+  // two key groups per block where a long batch's blocks span many tiles
+  // (measured: whole-context prefill chunk of 2048 queries 160 -> 146 us; a
+  // 513-key window's ~9 tiles gain nothing and pay the merge)
+  P.ks = P.nw == 8 && P.tps >= 16 ? 2 : 1;
   return P;
 }
 
@@ -402,8 +444,9 @@ hipError_t launch_attention(const moe_attn_shape& s, int Tq, int Tk, int q_pos0,
   a.part_ml = P.n_split > 1 ? (float*)((char*)ws + ((size_t)P.n_split * rows * kAttD * 4 + 255) / 256 * 256)
                             : nullptr;
   const dim3 grid(P.q_blocks, s.n_kv_heads, P.n_split);
-  if (P.nw == 8) attention_kernel<8><<<grid, 512, 0, st>>>(a);
-  else attention_kernel<4><<<grid, 256, 0, st>>>(a);
+  if (P.nw == 8 && P.ks == 2) attention_kernel<8, 2><<<grid, 1024, 0, st>>>(a);
+  else if (P.nw == 8) attention_kernel<8, 1><<<grid, 512, 0, st>>>(a);
+  else attention_kernel<4, 1><<<grid, 256, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.n_split == 1) return e;
   attention_combine_kernel<<<(unsigned)rows, 256, 0, st>>>(a);

@@ -117,6 +117,16 @@ def test_attention_full_size_sampled(window, Tq, Tk, q_pos0):
     _check_attention(16, 4, window, Tq, Tk, q_pos0, rows=rows, seed=1)
 
 
+@pytest.mark.parametrize("Tq,Tk,q_pos0", [(1024, 1100, 76), (1000, 1500, 500)])
+def test_attention_two_key_groups(Tq, Tk, q_pos0):
+    """Whole-context batches whose blocks span 16 or more key tiles without a
+    key split (32 query and 32 key/value heads: 256 blocks of 128 rows): each
+    block runs two key groups and merges their states; a ragged last block in
+    the second case.  Sampled queries (every 7th and the last)."""
+    rows = np.unique(np.concatenate([np.arange(0, Tq, 7), [Tq - 1]]))
+    _check_attention(32, 32, 0, Tq, Tk, q_pos0, rows=rows, seed=2)
+
+
 def test_window_boundary_exact():
     """Uniform attention (q = 0) of a query at position 600 over a 513-key
     window: it sees keys 88..600, so a marker at key 88 averages to 1/513 and
