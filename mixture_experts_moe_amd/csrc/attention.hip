@@ -87,6 +87,9 @@ __device__ __forceinline__ uint16_t bf16_from_double(double v) {
 // fp32's resolution), their cos and sin taken in fp32 once per token into LDS;
 // then the block rotates every head's pairs (j, j + D/2) in fp32 (about 2^-22
 // relative, against the bf16 result's 2^-8 rounding step), rounded once to bf16.
+// V pairs per thread step: 4 (8-byte loads and stores) when D/2 is a multiple
+// of 4 and x is 8-byte aligned, else 1.
+template <int V>
 __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int H, int D, int pos0,
                                                    double log2_theta) {
   __shared__ float cs[512], sn[512];
@@ -98,12 +101,32 @@ __global__ __launch_bounds__(256) void rope_kernel(uint16_t* __restrict__ x, int
   }
   __syncthreads();
   uint16_t* row0 = x + (size_t)t * H * D;
-  for (int i = tid; i < H * half; i += 256) {
-    const int h = i / half, j = i - h * half;
+  const int hv = half / V;
+  for (int i = tid; i < H * hv; i += 256) {
+    const int h = i / hv, j0 = (i - h * hv) * V;
     uint16_t* p = row0 + h * D;
-    const float a = bf16_to_f32(p[j]), b = bf16_to_f32(p[j + half]);
-    p[j] = f32_to_bf16(a * cs[j] - b * sn[j]);
-    p[j + half] = f32_to_bf16(a * sn[j] + b * cs[j]);
+    uint16_t lo[V], hi[V];
+    if constexpr (V == 4) {
+      *(uint2*)lo = *(const uint2*)(p + j0);
+      *(uint2*)hi = *(const uint2*)(p + j0 + half);
+    } else {
+      lo[0] = p[j0];
+      hi[0] = p[j0 + half];
+    }
+#pragma unroll
+    for (int u = 0; u < V; ++u) {
+      const int j = j0 + u;
+      const float a = bf16_to_f32(lo[u]), b = bf16_to_f32(hi[u]);
+      lo[u] = f32_to_bf16(a * cs[j] - b * sn[j]);
+      hi[u] = f32_to_bf16(a * sn[j] + b * cs[j]);
+    }
+    if constexpr (V == 4) {
+      *(uint2*)(p + j0) = *(const uint2*)lo;
+      *(uint2*)(p + j0 + half) = *(const uint2*)hi;
+    } else {
+      p[j0] = lo[0];
+      p[j0 + half] = hi[0];
+    }
   }
 }
 
@@ -416,7 +439,9 @@ size_t attn_ws_bytes(const moe_attn_shape& s, int Tq, int q_pos0) {
 }
 
 hipError_t launch_rope(int T, int H, int D, int pos0, float theta, void* x, hipStream_t st) {
-  rope_kernel<<<(unsigned)T, 256, 0, st>>>((uint16_t*)x, H, D, pos0, log2((double)theta));
+  const double lt = log2((double)theta);
+  if ((D / 2) % 4 == 0 && ((uintptr_t)x & 7) == 0) rope_kernel<4><<<(unsigned)T, 256, 0, st>>>((uint16_t*)x, H, D, pos0, lt);
+  else rope_kernel<1><<<(unsigned)T, 256, 0, st>>>((uint16_t*)x, H, D, pos0, lt);
   return hipGetLastError();
 }
 

@@ -51,7 +51,8 @@ def _rand(rng, shape, scale=1.0):
 
 
 @pytest.mark.parametrize("T,H,D,pos0", [(64, 20, 128, 1000), (33, 4, 64, 0), (8, 16, 128, 100000),
-                                        (5, 3, 256, 1 << 20)])
+                                        (5, 3, 256, 1 << 20),
+                                        (7, 3, 36, 17)])  # D/2 not a multiple of 4: one pair per step
 def test_rope_matches_oracle(T, H, D, pos0):
     rng = np.random.default_rng(T + D)
     x = _rand(rng, (T, H, D))
