@@ -325,7 +325,7 @@ def cpu_baseline(name, budget_s):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "the benchmark runs the layer on one GPU; --gpus must be 1 (the layer is not sharded across GPUs)", "n_gpus": a.gpus}))
         sys.exit(2)
     import torch
 
