@@ -118,14 +118,17 @@ def test_attention_full_size_sampled(window, Tq, Tk, q_pos0):
     _check_attention(16, 4, window, Tq, Tk, q_pos0, rows=rows, seed=1)
 
 
-@pytest.mark.parametrize("Tq,Tk,q_pos0", [(1024, 1100, 76), (1000, 1500, 500)])
-def test_attention_two_key_groups(Tq, Tk, q_pos0):
-    """Whole-context batches whose blocks span 16 or more key tiles without a
-    key split (32 query and 32 key/value heads: 256 blocks of 128 rows): each
-    block runs two key groups and merges their states; a ragged last block in
-    the second case.  Sampled queries (every 7th and the last)."""
+@pytest.mark.parametrize("Hq,Hkv,Tq,Tk,q_pos0", [(32, 32, 1024, 1100, 76), (32, 32, 1000, 1500, 500),
+                                                 (16, 4, 512, 8704, 8192)])
+def test_attention_two_key_groups(Hq, Hkv, Tq, Tk, q_pos0):
+    """Whole-context batches whose blocks span 16 or more key tiles: each block
+    runs two key groups and merges their states.  32 query and 32 key/value
+    heads: 256 blocks of 128 rows, no key split (a ragged last block in the
+    second case); 512 queries after 8192 cached keys: 8 key splits of 17 tiles,
+    the merged states written as split partials.  Sampled queries (every 7th
+    and the last)."""
     rows = np.unique(np.concatenate([np.arange(0, Tq, 7), [Tq - 1]]))
-    _check_attention(32, 32, 0, Tq, Tk, q_pos0, rows=rows, seed=2)
+    _check_attention(Hq, Hkv, 0, Tq, Tk, q_pos0, rows=rows, seed=2)
 
 
 def test_window_boundary_exact():
