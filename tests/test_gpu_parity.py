@@ -43,8 +43,8 @@ def gpu_inputs(inp):
         w = synth.to_device({k: inp[k] for k in _WKEYS if inp.get(k) is not None}, DEV)
         if inp["shape"].w == "u4":  # 4-bit weights exist only in the tiled layout
             w = moe.pack_layer_weights(w)
-        _weights_dev[key] = w
-    d = dict(_weights_dev[key])
+        _weights_dev[key] = (inp["w_gate"], w)  # the host array is held, so its id is never reused
+    d = dict(_weights_dev[key][1])
     d.update(synth.to_device({k: inp[k] for k in ("x", "w_router", "sel_bias") if inp.get(k) is not None}, DEV))
     return d
 
