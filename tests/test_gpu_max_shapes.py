@@ -1,10 +1,11 @@
 """The layer at the edges of the supported shape range, on the GPU through the
 C ABI, against the oracle with the parity bars of the main workloads.
 
-  * the widest FP8 layer (d_model 4608, d_ffn and d_ffn_shared 4096: one 16-row
-    tile's activation and h rows fill the LDS of a workgroup), with as many
-    experts as top_k (every token routes to every expert, so the experts hold T
-    rows each) and a ragged T;
+  * the widest layer (d_model 4608, d_ffn and d_ffn_shared 4096: one 16-row
+    tile's activation and h rows fill the LDS of a workgroup) with FP8 weights,
+    with the same weights and bf16 activations (W8A16), and with 4-bit group
+    weights; as many experts as top_k (every token routes to every expert, so
+    the experts hold T rows each) and a ragged T;
   * the most experts and the largest top_k (512 experts, top 8: eight candidates
     per lane in the selection), with the one-block dispatch (800 pairs) and the
     chunked one (2,400 pairs), free and forced.
@@ -15,7 +16,7 @@ workloads at other sizes).
 import numpy as np
 import pytest
 
-from mixture_experts_moe_amd import synth
+from mixture_experts_moe_amd import moe, synth
 from oracle import moe_oracle as O
 
 from test_gpu_parity import (DEV, W_ABS, check_dispatch, check_logits, check_y, route_agreement, run_gpu, say,
@@ -24,23 +25,31 @@ from test_gpu_parity import (DEV, W_ABS, check_dispatch, check_logits, check_y, 
 pytestmark = pytest.mark.gpu
 
 
-def _fp8_layer(T, d, E, k, F, Fs, seed):
+def _fp8_layer(T, d, E, k, F, Fs, seed, w="fp8"):
+    """A layer with FP8 block-scaled weights ("fp8", or "fp8a16": the same
+    weights with bf16 activations) or 4-bit group weights ("u4")."""
     rng = np.random.default_rng(seed)
-    inp = dict(shape=synth.LayerShape(T=T, d=d, E=E, k=k, F=F, Fs=Fs, act="bf16", w="fp8"),
+    inp = dict(shape=synth.LayerShape(T=T, d=d, E=E, k=k, F=F, Fs=Fs, act="bf16", w=w),
                x=synth.bf16_bits(rng.standard_normal((T, d), dtype=np.float32)),
                w_router=rng.standard_normal((E, d), dtype=np.float32) * np.float32(0.05), sel_bias=None)
-    for pre, sp, n, Fg in (("w_", "s_", E, F), ("sh_", "ss_", 0, Fs)):
+    quant = synth.u4_groups if w == "u4" else synth.fp8_blocks
+    parts = ("w_", "s_", "b_") if w == "u4" else ("w_", "s_")
+    for pre, n, Fg in (("", E, F), ("sh", 0, Fs)):
         for name, (r, c) in (("gate", (Fg, d)), ("up", (Fg, d)), ("down", (d, Fg))):
-            mats = [synth.fp8_blocks(rng.standard_normal((r, c), dtype=np.float32) * np.float32(0.02))
-                    for _ in range(max(n, 1))]
-            inp[pre + name] = np.stack([m[0] for m in mats]) if n else mats[0][0]
-            inp[sp + name] = np.stack([m[1] for m in mats]) if n else mats[0][1]
+            mats = [quant(rng.standard_normal((r, c), dtype=np.float32) * np.float32(0.02)) for _ in range(max(n, 1))]
+            for j, part in enumerate(parts):
+                key = (pre + part if not pre else {"w_": "sh_", "s_": "ss_", "b_": "sb_"}[part]) + name
+                inp[key] = np.stack([m[j] for m in mats]) if n else mats[0][j]
     return inp
 
 
 def _dev(inp):
-    keys = [k for k, v in inp.items() if isinstance(v, np.ndarray)]
-    return synth.to_device({k: inp[k] for k in keys}, DEV)
+    keys = [k for k, v in inp.items() if isinstance(v, np.ndarray) and k not in ("x", "w_router")]
+    w = synth.to_device({k: inp[k] for k in keys}, DEV)
+    if inp["shape"].w == "u4":  # 4-bit weights exist only in the tiled layout
+        w = moe.pack_layer_weights(w)
+    w.update(synth.to_device({k: inp[k] for k in ("x", "w_router")}, DEV))
+    return w
 
 
 def _check(inp, g, forced=None, n_sample=None):
@@ -69,10 +78,12 @@ def _check(inp, g, forced=None, n_sample=None):
     check_y(g["y"][tok], acc_ref)
 
 
-def test_widest_fp8_layer():
+@pytest.mark.parametrize("w", ["fp8", "fp8a16", "u4"])
+def test_widest_layer(w):
+    """The widest layer each weight type supports: d_model 4608, d_ffn 4096."""
     T, d, E, k, F = 40, 4608, 4, 4, 4096
-    inp = _fp8_layer(T, d, E, k, F, F, seed=11)
-    say(f"widest FP8 layer T={T} d={d} E={E} k={k} F=Fs={F}")
+    inp = _fp8_layer(T, d, E, k, F, F, seed=11, w=w)
+    say(f"widest {w} layer T={T} d={d} E={E} k={k} F=Fs={F}")
     g = run_gpu(inp, dev=_dev(inp))
     _check(inp, g, n_sample=5)
 
