@@ -105,6 +105,9 @@ def _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0, rows=None, seed=0):
     (8, 8, 0, 520, 900, 380),       # long batch, one query head per group (128 queries a block)
     (16, 1, W, 40, 45, 5),          # one key/value head for all query heads; a cache of 45 keys
     (64, 1, 0, 2, 3, 1),            # a group of 64 heads (one query a block), three keys
+    (16, 4, 1, 37, 37, 0),          # a window of one key: each query sees only itself
+    (16, 4, 65, 200, 300, 100),     # a window just over one key tile
+    (16, 4, 65, 600, 900, 300),     # the same in 8-wave blocks
 ])
 def test_attention_matches_oracle(Hq, Hkv, window, Tq, Tk, q_pos0):
     _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0)
