@@ -305,3 +305,21 @@ def test_attention_host_validation():
     assert R(4, 2, 8, -1, 10000.0, FAKE, None) == attn.ERR_INVALID_ARG
     assert R(0, 2, 8, 0, 10000.0, None, None) == attn.OK
     assert R(4, 2, 8, 0, 10000.0, None, None) == attn.ERR_INVALID_ARG
+
+
+def test_missing_library_fails_loudly():
+    """Without the built HIP library the bindings raise (no fallback path): a
+    fresh interpreter with the library path pointed at a file that does not exist."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "from mixture_experts_moe_amd import moe, attn\n"
+            "moe.LIB_PATH = '/nonexistent/libmoe.so'  # attn loads through moe\n"
+            "for f in (moe.lib, attn.lib):\n"
+            "    try:\n"
+            "        f(); print('loaded')\n"
+            "    except ImportError as e:\n"
+            "        print('ImportError', 'is not built' in str(e))\n") % root
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.stdout.split() == ["ImportError", "True", "ImportError", "True"], r.stdout + r.stderr
