@@ -43,7 +43,12 @@ def _check(logits, ref_logits, idx, ref_idx, bias=None):
     assert np.array_equal(gap < 0, gap_ref < 0)
     assert abs(sigma - sigma_ref) <= 1e-12 * max(sigma_ref, 1e-300)
     d = gap_ref >= 0
-    close = lambda a, b: (a == b) | (np.abs(a - b) <= 1e-6 * np.abs(b))  # equal also covers +inf
+    def close(a, b):  # equal (which also covers +inf), else within 1e-6 relative
+        a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+        fin = np.isfinite(a) & np.isfinite(b)
+        rel = np.zeros_like(a)
+        np.subtract(a, b, out=rel, where=fin)
+        return (a == b) | (fin & (np.abs(rel) <= 1e-6 * np.abs(b)))
     assert np.all(close(gap[d], gap_ref[d]))
     assert np.all(gap[~d] == -1.0)
     assert close(np.float32(mg), np.float32(mg_ref))
