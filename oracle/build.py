@@ -15,7 +15,7 @@ LIB = os.path.join(HERE, "libmoe_oracle.so")
 
 def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+    cmd = ["g++", "-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-pthread",
            "-Wall", "-Wextra", "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)

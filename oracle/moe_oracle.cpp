@@ -4,7 +4,9 @@
 // this file; only the tests, the smoke check and the benchmark's CPU-baseline
 // leg do.  It shares no code, header, table or helper with the HIP library.
 //
-// Plain single-threaded C++17: fp32 storage and fp32 element arithmetic, dot
+// Plain C++17, each token's arithmetic single-threaded (the *_threads drivers
+// only hand contiguous token ranges of the same per-token code to std::threads):
+// fp32 storage and fp32 element arithmetic, dot
 // products accumulated in double and rounded once to fp32 (an order-free,
 // near-correctly-rounded value of the fp32 dot product), no SIMD, no blocking,
 // no reordering beyond what each step states.  Build with -ffp-contract=off.
@@ -41,12 +43,16 @@
 // stable sort, dispatch vs numpy's stable argsort, the FFN vs a float64
 // textbook SwiGLU, exact-arithmetic FP8 cases, block-scale locality, the
 // dense all-experts-masked restatement, and planted mutants that each pin
-// must catch.  The activation-quantisation rule itself is fixed only by its
-// own definition above ("parity unpinned" by the pages).
+// must catch.  The activation-quantisation rule is fixed only by its own
+// definition above ("parity unpinned" by the pages); the pins hold the one
+// quantiser the forward runs (through oracle_expert_ffn_trace) to that
+// definition bit for bit against torch's E4M3 conversion.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <thread>
 #include <vector>
 
 namespace {
@@ -71,7 +77,9 @@ enum Mutant {
   MUT_U4_NO_BIAS = 15,       // 4-bit groups: the bias term dropped
   MUT_U4_GROUP128 = 16,      // 4-bit groups: parameters indexed per 128 columns
   MUT_COMPARE_MIN_PAIR = 17, // routing comparison: a token's margin from its closest swapped pair
-  MUT_COMPARE_UNBIASED = 18  // routing comparison: margins from the logits without the selection bias
+  MUT_COMPARE_UNBIASED = 18, // routing comparison: margins from the logits without the selection bias
+  MUT_QUANT_RECIPROCAL = 19, // activation quantisation: v * (448 / amax) instead of v / (amax / 448)
+  MUT_QUANT_TIES_AWAY = 20   // activation quantisation: E4M3 ties rounded away from zero
 };
 int g_mutant = MUT_NONE;
 
@@ -127,7 +135,8 @@ float e4m3_decode(uint8_t c) {
 
 // fp32 -> E4M3 code: nearest representable value, ties to the even code
 // (even mantissa), magnitudes beyond 448 saturate to 448, NaN -> 0x7F.
-uint8_t e4m3_encode(float v) {
+// ties_away (planted-mutant control only): ties to the larger magnitude.
+uint8_t e4m3_encode(float v, bool ties_away = false) {
   if (std::isnan(v)) return 0x7F;
   uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
   float a = std::fabs(v);
@@ -144,20 +153,47 @@ uint8_t e4m3_encode(float v) {
   if (c < 0x7E) {
     float below = e4m3_decode((uint8_t)c), above = e4m3_decode((uint8_t)(c + 1));
     float dlo = a - below, dhi = above - a;  // both exact: a and the grid are close
-    if (dhi < dlo || (dhi == dlo && (c & 1))) c += 1;
+    if (dhi < dlo || (dhi == dlo && (ties_away || (c & 1)))) c += 1;
   }
   return (uint8_t)(sign | c);
 }
 
-// Dynamic quantisation of one group: s = amax/448, codes = E4M3(v/s); an
-// all-zero group takes s = 1.  Returns s; writes the dequantised values.
-float quant_group(const float* v, int n, float* deq) {
+// Dynamic quantisation of one group of n values, the oracle's only
+// quantiser (the forward's x and h and the exported oracle_quant_groups all
+// call it): s = amax/448 (one correctly rounded fp32 division), code_i =
+// E4M3(v_i / s) rounded to nearest even and saturating; an all-zero group
+// takes s = 1 and zero codes.  Returns s.
+float quant_group(const float* v, int n, uint8_t* codes) {
   float amax = 0.0f;
   for (int i = 0; i < n; ++i) amax = std::fmax(amax, std::fabs(v[i]));
-  float s = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-  for (int i = 0; i < n; ++i) deq[i] = e4m3_decode(e4m3_encode(v[i] / s)) * s;
+  if (!(amax > 0.0f)) {
+    for (int i = 0; i < n; ++i) codes[i] = e4m3_encode(v[i]);  // zeros (signed)
+    return 1.0f;
+  }
+  const float s = amax / 448.0f;
+  const float r = 448.0f / amax;  // used only by the planted reciprocal mutant
+  for (int i = 0; i < n; ++i) {
+    const float q = g_mutant == MUT_QUANT_RECIPROCAL ? v[i] * r : v[i] / s;
+    codes[i] = e4m3_encode(q, g_mutant == MUT_QUANT_TIES_AWAY);
+  }
   return s;
 }
+
+// The values the next product sees: decode(code) * s, one fp32 multiply each.
+void dequant_group(const uint8_t* codes, int n, float s, float* deq) {
+  for (int i = 0; i < n; ++i) deq[i] = e4m3_decode(codes[i]) * s;
+}
+
+// What one expert FFN call quantised, for the pins (any pointer may be null):
+// x codes [d] and scales [d/128], h before quantisation [F], h codes [F] and
+// scales [F/128].
+struct FfnTrace {
+  uint8_t* x_codes;
+  float* x_scales;
+  float* h;
+  uint8_t* h_codes;
+  float* h_scales;
+};
 
 // ---- shapes and weights ----------------------------------------------------
 
@@ -256,7 +292,8 @@ float silu(float z) {
 // One expert's SwiGLU FFN on one activation row already in compute form
 // (FP8 mode: already quantised and dequantised).  expert = -1 is the shared
 // expert.  [port] "The gate" (routed + shared experts), part 3 (a GLU layer).
-void expert_ffn(const Shape& s, const Weights& w, int expert, const float* xin, float* y) {
+void expert_ffn(const Shape& s, const Weights& w, int expert, const float* xin, float* y,
+                const FfnTrace* trace = nullptr) {
   int F = expert < 0 ? s.Fs : s.F;
   Mat g, u, dn;
   if (expert < 0) {
@@ -284,12 +321,19 @@ void expert_ffn(const Shape& s, const Weights& w, int expert, const float* xin, 
              s.w_dtype};
   }
   std::vector<float> gv(F), uv(F), h(F), hq(F);
+  std::vector<uint8_t> hc(F);
   matvec(g, xin, gv.data());
   matvec(u, xin, uv.data());
   if (g_mutant == MUT_GATE_UP_SWAP) std::swap(gv, uv);
   for (int f = 0; f < F; ++f) h[f] = silu(gv[f]) * uv[f];
+  if (trace && trace->h) std::memcpy(trace->h, h.data(), sizeof(float) * F);
   if (s.w_dtype == W_FP8 && g_mutant != MUT_NO_H_QUANT) {
-    for (int f0 = 0; f0 < F; f0 += 128) quant_group(&h[f0], 128, &hq[f0]);
+    for (int f0 = 0; f0 < F; f0 += 128) {
+      const float sc = quant_group(&h[f0], 128, &hc[f0]);
+      dequant_group(&hc[f0], 128, sc, &hq[f0]);
+      if (trace && trace->h_scales) trace->h_scales[f0 / 128] = sc;
+    }
+    if (trace && trace->h_codes) std::memcpy(trace->h_codes, hc.data(), F);
   } else {
     hq = h;
   }
@@ -298,11 +342,17 @@ void expert_ffn(const Shape& s, const Weights& w, int expert, const float* xin, 
 
 // Token t's activation row in compute form: fp32, and in FP8 mode quantised
 // per 128-element group and dequantised.
-void activation_row(const Shape& s, const void* x, int t, float* row) {
+void activation_row(const Shape& s, const void* x, int t, float* row, const FfnTrace* trace = nullptr) {
   std::vector<float> raw(s.d);
   for (int i = 0; i < s.d; ++i) raw[i] = act_at(s, x, t, i);
   if (s.w_dtype == W_FP8) {
-    for (int i0 = 0; i0 < s.d; i0 += 128) quant_group(&raw[i0], 128, &row[i0]);
+    std::vector<uint8_t> codes(s.d);
+    for (int i0 = 0; i0 < s.d; i0 += 128) {
+      const float sc = quant_group(&raw[i0], 128, &codes[i0]);
+      dequant_group(&codes[i0], 128, sc, &row[i0]);
+      if (trace && trace->x_scales) trace->x_scales[i0 / 128] = sc;
+    }
+    if (trace && trace->x_codes) std::memcpy(trace->x_codes, codes.data(), s.d);
   } else {
     for (int i = 0; i < s.d; ++i) row[i] = raw[i];
   }
@@ -414,16 +464,10 @@ void oracle_e4m3_encode_array(const float* v, uint8_t* out, int64_t n) {
 void oracle_f32_to_bf16_array(const float* v, uint16_t* out, int64_t n) {
   for (int64_t i = 0; i < n; ++i) out[i] = f32_to_bf16(v[i]);
 }
-// Dynamic group quantisation (s = amax/448): codes and scale per group of 128.
+// Dynamic group quantisation (s = amax/448): codes and scale per group of 128,
+// through the same quant_group the forward uses for x and h.
 void oracle_quant_groups(const float* v, int64_t n_groups, uint8_t* codes, float* scales) {
-  for (int64_t g = 0; g < n_groups; ++g) {
-    const float* p = v + g * 128;
-    float amax = 0.0f;
-    for (int i = 0; i < 128; ++i) amax = std::fmax(amax, std::fabs(p[i]));
-    float s = (amax > 0.0f) ? amax / 448.0f : 1.0f;
-    scales[g] = s;
-    for (int i = 0; i < 128; ++i) codes[g * 128 + i] = e4m3_encode(p[i] / s);
-  }
+  for (int64_t g = 0; g < n_groups; ++g) scales[g] = quant_group(v + g * 128, 128, codes + g * 128);
 }
 
 // Free routing for the listed tokens (all T when token_list is null):
@@ -638,6 +682,75 @@ int oracle_forward_dense_masked(const Shape* s, const Weights* w, const void* x,
     }
     for (int c = 0; c < s->d; ++c) y_f32[(size_t)t * s->d + c] = acc[c];
   }
+  return OK;
+}
+
+// One expert on one token with what the call quantised (FP8 weights; the
+// other modes leave the code and scale outputs untouched): the x codes [d] and
+// scales [d/128] the forward uses, h before quantisation [F], its codes [F] and
+// scales [F/128], the dequantised x row [d] and the output [d].  Null outputs
+// are skipped.  The same activation_row and expert_ffn as oracle_forward.
+int oracle_expert_ffn_trace(const Shape* s, const Weights* w, int32_t expert, const void* x, int32_t t,
+                            uint8_t* x_codes, float* x_scales, float* h, uint8_t* h_codes, float* h_scales,
+                            float* x_used, float* y) {
+  if (check_shape(s) != OK || !w || !x || t < 0 || t >= s->T || expert < -1 || expert >= s->E || !y)
+    return ERR_INVALID;
+  const FfnTrace tr{x_codes, x_scales, h, h_codes, h_scales};
+  std::vector<float> xr(s->d);
+  activation_row(*s, x, t, xr.data(), &tr);
+  if (x_used) std::memcpy(x_used, xr.data(), sizeof(float) * s->d);
+  expert_ffn(*s, *w, expert, xr.data(), y, &tr);
+  return OK;
+}
+
+// The same per-token oracle code on contiguous token ranges, one std::thread
+// per range (the all-host-cores CPU baseline).  Each token's arithmetic is
+// exactly that of the single-threaded call, so the outputs are bitwise equal
+// to it.  n_threads < 1 means 1.
+int oracle_route_threads(const Shape* s, const Weights* w, const void* x, const int32_t* token_list,
+                         int32_t n_tokens, float* logits, int32_t* idx, float* wts, int32_t n_threads) {
+  if (check_shape(s) != OK || !w || !w->w_router || !x) return ERR_INVALID;
+  std::vector<int32_t> all;
+  const int n = token_list ? n_tokens : s->T;
+  const int32_t* toks = token_ids(token_list, n, all);
+  const int nt = std::max(1, std::min<int>(n_threads, std::max(n, 1)));
+  std::vector<std::thread> pool;
+  std::vector<int> rcs(nt, OK);
+  for (int i = 0; i < nt; ++i) {
+    const int a = (int)((int64_t)n * i / nt), b = (int)((int64_t)n * (i + 1) / nt);
+    pool.emplace_back([=, &rcs] {
+      rcs[i] = oracle_route(s, w, x, toks + a, b - a, logits ? logits + (size_t)a * s->E : nullptr,
+                            idx + (size_t)a * s->k, wts + (size_t)a * s->k);
+    });
+  }
+  for (auto& th : pool) th.join();
+  for (int rc : rcs)
+    if (rc != OK) return rc;
+  return OK;
+}
+
+int oracle_forward_threads(const Shape* s, const Weights* w, const void* x, const int32_t* idx, const float* wts,
+                           const int32_t* token_list, int32_t n_tokens, void* y, float* y_f32, int32_t n_threads) {
+  if (check_shape(s) != OK || !w || !x || !idx || !wts) return ERR_INVALID;
+  e4m3_table();  // filled once here, before any thread reads it
+  std::vector<int32_t> all;
+  const int n = token_list ? n_tokens : s->T;
+  const int32_t* toks = token_ids(token_list, n, all);
+  const int nt = std::max(1, std::min<int>(n_threads, std::max(n, 1)));
+  const size_t yel = s->act_dtype == ACT_F32 ? 4 : 2;
+  std::vector<std::thread> pool;
+  std::vector<int> rcs(nt, OK);
+  for (int i = 0; i < nt; ++i) {
+    const int a = (int)((int64_t)n * i / nt), b = (int)((int64_t)n * (i + 1) / nt);
+    pool.emplace_back([=, &rcs] {
+      rcs[i] = oracle_forward(s, w, x, idx + (size_t)a * s->k, wts + (size_t)a * s->k, toks + a, b - a,
+                              y ? (char*)y + (size_t)a * s->d * yel : nullptr,
+                              y_f32 ? y_f32 + (size_t)a * s->d : nullptr);
+    });
+  }
+  for (auto& th : pool) th.join();
+  for (int rc : rcs)
+    if (rc != OK) return rc;
   return OK;
 }
 

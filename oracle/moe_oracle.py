@@ -21,7 +21,8 @@ MUTANTS = {
     "select_unbiased": 1, "router_bf16": 2, "logits_bf16": 3, "tie_highest": 4, "softmax_all": 5,
     "no_shared": 6, "scale_transposed": 7, "reversed_order": 8, "no_h_quant": 9, "weights_biased": 10,
     "silu_sign": 11, "gate_up_swap": 12, "combine_no_weight": 13, "u4_nibble_swap": 14, "u4_no_bias": 15,
-    "u4_group128": 16, "compare_min_pair": 17, "compare_unbiased": 18,
+    "u4_group128": 16, "compare_min_pair": 17, "compare_unbiased": 18, "quant_reciprocal": 19,
+    "quant_ties_away": 20,
 }
 
 
@@ -64,6 +65,9 @@ def lib():
         L.oracle_forward.argtypes = [p, p, p, p, p, p, i32, p, p]
         L.oracle_forward_dense_masked.argtypes = [p, p, p, p, p, p]
         L.oracle_expert_ffn.argtypes = [p, p, i32, p, i32, p, p]
+        L.oracle_expert_ffn_trace.argtypes = [p, p, i32, p, i32, p, p, p, p, p, p, p]
+        L.oracle_route_threads.argtypes = [p, p, p, p, i32, p, p, p, i32]
+        L.oracle_forward_threads.argtypes = [p, p, p, p, p, p, i32, p, p, i32]
         L.oracle_route_compare.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, p, p]
         _lib = L
     return _lib
@@ -126,6 +130,25 @@ def route_forced(layer: Layer, forced, tokens=None):
     return rc, logits, idx, w
 
 
+def host_threads() -> int:
+    """Threads for the all-cores oracle runs: the host's cores, at most 16
+    (a GPU machine's CPU share)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def route_threads(layer: Layer, tokens=None, n_threads=None):
+    """route() over contiguous token ranges on n_threads std::threads; bitwise
+    the single-threaded result."""
+    s = layer.s
+    tl, n = _tokens(s, tokens)
+    logits = np.empty((n, s.E), np.float32)
+    idx = np.empty((n, s.k), np.int32)
+    w = np.empty((n, s.k), np.float32)
+    rc = lib().oracle_route_threads(*layer._args(), _ptr(tl), n, _ptr(logits), _ptr(idx), _ptr(w),
+                                    n_threads or host_threads())
+    return rc, logits, idx, w
+
+
 def dispatch(idx, E: int):
     idx = _c(idx, np.int32)
     T, k = idx.shape
@@ -154,6 +177,22 @@ def forward(layer: Layer, idx, w, tokens=None):
     return y, acc
 
 
+def forward_threads(layer: Layer, idx, w, tokens=None, n_threads=None):
+    """forward() over contiguous token ranges on n_threads std::threads;
+    bitwise the single-threaded result."""
+    s = layer.s
+    tl, n = _tokens(s, tokens)
+    idx = _c(idx, np.int32)
+    w = _c(w, np.float32)
+    assert idx.shape == (n, s.k) and w.shape == (n, s.k)
+    y = np.empty((n, s.d), np.float32 if s.act == "f32" else np.uint16)
+    acc = np.empty((n, s.d), np.float32)
+    rc = lib().oracle_forward_threads(*layer._args(), _ptr(idx), _ptr(w), _ptr(tl), n, _ptr(y), _ptr(acc),
+                                      n_threads or host_threads())
+    assert rc == OK, rc
+    return y, acc
+
+
 def forward_dense_masked(layer: Layer, idx, w):
     s = layer.s
     idx = _c(idx, np.int32)
@@ -173,6 +212,22 @@ def expert_ffn(layer: Layer, expert: int, t: int):
     rc = lib().oracle_expert_ffn(sp, wp, expert, xp, t, _ptr(xu), _ptr(y))
     assert rc == OK, rc
     return xu, y
+
+
+def expert_ffn_trace(layer: Layer, expert: int, t: int) -> dict:
+    """One expert (-1: shared) on token t, with what the forward quantised
+    (FP8 weights): x_codes [d] uint8, x_scales [d/128], h [F] (before
+    quantisation), h_codes [F] uint8, h_scales [F/128], x_used [d], y [d]."""
+    s = layer.s
+    F = s.Fs if expert < 0 else s.F
+    out = dict(x_codes=np.zeros(s.d, np.uint8), x_scales=np.zeros(s.d // 128, np.float32),
+               h=np.zeros(F, np.float32), h_codes=np.zeros(F, np.uint8), h_scales=np.zeros(F // 128, np.float32),
+               x_used=np.zeros(s.d, np.float32), y=np.zeros(s.d, np.float32))
+    sp, wp, xp = layer._args()
+    rc = lib().oracle_expert_ffn_trace(sp, wp, expert, xp, t, *(_ptr(out[n]) for n in (
+        "x_codes", "x_scales", "h", "h_codes", "h_scales", "x_used", "y")))
+    assert rc == OK, rc
+    return out
 
 
 def route_compare(logits, ref_logits, idx, ref_idx, sel_bias=None):

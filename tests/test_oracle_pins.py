@@ -125,6 +125,93 @@ def test_quant_groups_definition():
     # a power-of-two rescale of a group changes only its scale
     c2, s2 = O.quant_groups(v * np.float32(8.0))
     assert np.array_equal(c2, codes) and np.array_equal(s2[1:], scales[1:] * 8)
+    assert np.array_equal(codes, _quant_ref(v)[0])
+
+
+def _quant_ref(v):
+    """Per-128-group codes and scales from the quantiser's definition, computed
+    without the oracle: s = amax/448 by numpy's correctly rounded float32
+    division (1 for an all-zero group), codes = torch's float8_e4m3fn
+    conversion (round to nearest even) of the float32 quotient v/s."""
+    g = np.asarray(v, np.float32).reshape(-1, 128)
+    amax = np.abs(g).max(axis=1)
+    s = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    return _torch_f32_to_e4m3((g / s[:, None]).astype(np.float32)).ravel(), s
+
+
+def _midpoint_rows(n_rows=2, d=2048):
+    """bf16 activation rows whose every group quantises on exact E4M3 rounding
+    midpoints.  Group g has amax = 784 * 2^j (j = g - 8), so s = amax/448 =
+    1.75 * 2^j exactly, and its other values are +-m * s for midpoints
+    m = (1 + (2i+1)/16) * 2^e of the normal E4M3 range (i = 0..7, e = -6..7):
+    v/s = m exactly (m has 5 significant bits and 1.75 three, so m * s is a bf16
+    value).  Round-to-nearest-even takes the even mantissa of each tie; a
+    quantiser that rounds ties away from zero moves every midpoint with even i,
+    and one that multiplies by fl(448/amax) = fl(4/7) * 2^-j (0.75 of half an
+    ulp above 4/7) lifts the midpoints with i >= 3 over the tie, which moves
+    i = 4 and i = 6."""
+    mids = np.array([(1 + (2 * i + 1) / 16) * 2.0 ** e for e in range(-6, 8) for i in range(8)])
+    rows = np.empty((n_rows, d), np.float32)
+    for r in range(n_rows):
+        for g in range(d // 128):
+            s = 1.75 * 2.0 ** (g - 8)
+            vals = np.concatenate([mids, mids[-15:]])[:127] * s
+            sign = np.where((np.arange(127) + g + r) % 2 == 0, 1.0, -1.0)
+            rows[r, g * 128] = 448.0 * s
+            rows[r, g * 128 + 1:(g + 1) * 128] = np.roll(vals * sign, 3 * r + g)
+    assert np.array_equal(synth.bf16_bits_to_f32(synth.bf16_bits(rows)), rows)  # exact bf16 values
+    return rows
+
+
+def test_forward_quantiser_exact_on_midpoints():
+    """The forward's own activation quantisation (the codes oracle_forward
+    multiplies with, read back through oracle_expert_ffn_trace) equals the
+    definition bit for bit on groups built so that every value is an exact
+    rounding tie; each planted quantiser mistake (the reciprocal scale, ties
+    away from zero) changes codes there, and only through this one quantiser."""
+    inp, _ = _layer("decode_t32", T=4)
+    rows = _midpoint_rows()
+    x = inp["x"].copy()
+    x[:2] = synth.bf16_bits(rows)
+    L = O.Layer(dict(inp, x=x))
+    for t in (0, 1):
+        tr = O.expert_ffn_trace(L, 0, t)
+        ref_c, ref_s = _quant_ref(rows[t])
+        assert np.array_equal(tr["x_scales"].view(np.uint32), ref_s.view(np.uint32))
+        assert np.all(ref_s == (1.75 * 2.0 ** (np.arange(16) - 8)).astype(np.float32))
+        assert np.array_equal(tr["x_codes"], ref_c)
+        # the row the products see is decode(code) * s, here the tie's even neighbour exactly
+        assert np.array_equal(tr["x_used"], (_torch_e4m3_to_f32(ref_c) * np.repeat(ref_s, 128)).astype(np.float32))
+    moved = {}
+    for m in ("quant_reciprocal", "quant_ties_away"):
+        with O.mutant(m):
+            tr = O.expert_ffn_trace(L, 0, 0)
+            codes_exported, _ = O.quant_groups(rows[0])
+        moved[m] = int(np.sum(tr["x_codes"] != _quant_ref(rows[0])[0]))
+        assert moved[m] > 0, m
+        assert np.array_equal(codes_exported, tr["x_codes"]), m  # one quantiser: the same codes
+    assert moved["quant_ties_away"] > moved["quant_reciprocal"]  # even i at every exponent vs i = 4, 6
+
+
+def test_forward_quantiser_exact_on_layer_rows():
+    """On the decode layer's rows: the x codes and scales the forward uses, and
+    the h codes and scales it forms from its own h before the down projection,
+    equal the definition bit for bit (torch E4M3, numpy float32 division); the
+    products see decode(code) * s."""
+    inp, L = _layer("decode_t32", T=6)
+    xf = _x_f32(inp)
+    n_h = 0
+    for e, t in ((-1, 0), (0, 1), (200, 2), (383, 5)):
+        tr = O.expert_ffn_trace(L, e, t)
+        ref_c, ref_s = _quant_ref(xf[t])
+        assert np.array_equal(tr["x_codes"], ref_c) and np.array_equal(tr["x_scales"], ref_s)
+        assert np.array_equal(tr["x_used"], (_torch_e4m3_to_f32(ref_c) * np.repeat(ref_s, 128)).astype(np.float32))
+        h_c, h_s = _quant_ref(tr["h"])
+        assert np.array_equal(tr["h_codes"], h_c) and np.array_equal(tr["h_scales"], h_s)
+        n_h += tr["h"].size
+        _, y = O.expert_ffn(L, e, t)
+        assert np.array_equal(y, tr["y"])  # the traced call is the forward's FFN
+    assert n_h == 4 * 640
 
 
 # ---------------------------------------------------------------- router
@@ -475,6 +562,24 @@ def test_token_subset_matches_full():
     y, _ = O.forward(L, idx, w)
     y2, _ = O.forward(L, idx[tok], w[tok], tok)
     assert np.array_equal(y2, y[tok])
+
+
+def test_threaded_oracle_bitwise_equals_single_thread():
+    """The all-cores drivers run the same per-token code on contiguous token
+    ranges: logits, ids, weights and outputs are bitwise those of the
+    single-threaded calls, for any thread count (more threads than tokens too)."""
+    inp, L = _layer("decode_t32", T=13)
+    _, lg, idx, w = O.route(L)
+    y, acc = O.forward(L, idx, w)
+    for n in (1, 3, 8, 20):
+        _, lg2, idx2, w2 = O.route_threads(L, n_threads=n)
+        assert np.array_equal(lg2.view(np.uint32), lg.view(np.uint32))
+        assert np.array_equal(idx2, idx) and np.array_equal(w2.view(np.uint32), w.view(np.uint32))
+        y2, acc2 = O.forward_threads(L, idx, w, n_threads=n)
+        assert np.array_equal(y2, y) and np.array_equal(acc2.view(np.uint32), acc.view(np.uint32))
+    tok = np.array([12, 0, 7, 3, 9])
+    y3, _ = O.forward_threads(L, idx[tok], w[tok], tok, n_threads=2)
+    assert np.array_equal(y3, y[tok])
 
 
 def test_skew_workload_is_skewed():
