@@ -34,6 +34,7 @@ import numpy as np  # noqa: E402
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 FP8_PEAK_TFLOPS = 5000.0     # MI355X dense FP8 matrix
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 matrix
+FP32_PEAK_TFLOPS = 157.3     # MI355X fp32 vector
 METRIC = "MoE-layer tokens/s (decode T=32, prefill T=2048); % HBM BW / % FP8 MFMA peak"
 
 DESCRIPTION = {
@@ -47,6 +48,10 @@ DESCRIPTION = {
                         "projections, unquantised), free routing",
     "decode_t32_u4": "decode batch, T=32, the same layer with 4-bit affine group-quantised expert weights (bf16 "
                      "scale and bias per row and 64 columns), bf16 activations, free routing",
+    "tiny_f32": "tiny fp32 layer, T=64, d=256, E=16, top-2, F=Fs=128, free routing (latency-bound; no roofline "
+                "claim)",
+    "prefill_t32768": "long prefill, T=32768 tokens, same layer as decode, free routing: the only batch size of "
+                      "this layer whose matrix-core work (F_mm at the FP8 peak) outweighs its weight stream",
 }
 FORCED = {"prefill_t2048"}
 
@@ -90,7 +95,8 @@ def parse():
     ap.add_argument("--compare", default="skew_t8192",
                     help="workload whose routing moe_route_compare is timed on ('' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="CPU-baseline budget (0: skip)")
-    ap.add_argument("--also", default="prefill_t2048,skew_t8192,decode_t32_w8a16,decode_t32_u4", help="extra workloads timed after the main one (comma list)")
+    ap.add_argument("--also", default="prefill_t2048,skew_t8192,ties_t256,ties_t256_bf16w,decode_t32_w8a16,"
+                    "decode_t32_u4,tiny_f32,prefill_t32768", help="extra workloads timed after the main one (comma list)")
     return ap.parse_args()
 
 
@@ -120,6 +126,25 @@ def algorithmic(s, counts):
     }
 
 
+def step_roofline(s, alg, t_step):
+    """Step figures against the chip's peaks.  The products run on the bf16
+    matrix cores (FP8 codes and 4-bit codes are decoded exactly to bf16 in
+    registers), so the matrix-core fraction is against the dense bf16 peak;
+    fp32 layers run on the vector ALUs.  `fp8_equiv_mfma_frac` is the same work
+    against the dense FP8 peak, the figure a path on the FP8 instruction would
+    be held to; it is labelled as such and not the bound of these kernels."""
+    hbm = alg["B_alg"] / (HBM_PEAK_GBS * 1e9)
+    mm_peak = FP32_PEAK_TFLOPS if s.w == "f32" else BF16_PEAK_TFLOPS
+    mm = alg["F_mm"] / (mm_peak * 1e12)
+    return {"B_alg_bytes": alg["B_alg"], "F_mm_flops": alg["F_mm"], "distinct_experts": alg["U"],
+            "hbm_frac": hbm / t_step,
+            "mfma_frac": mm / t_step, "mfma_peak_tflops": mm_peak,
+            "mfma_unit": "fp32 vector ALU" if s.w == "f32" else "bf16 matrix cores (decoded weight codes)",
+            "fp8_equiv_mfma_frac": alg["F_mm"] / t_step / (FP8_PEAK_TFLOPS * 1e12),
+            "bound": "hbm" if hbm >= mm else "mfma",
+            "roofline_frac": max(hbm, mm) / t_step}
+
+
 def run_workload(name, steps, warmup, rotate, layout):
     import torch
     from mixture_experts_moe_amd import moe, synth
@@ -127,10 +152,15 @@ def run_workload(name, steps, warmup, rotate, layout):
     inp = synth.make_inputs(name)
     s = inp["shape"]
     dev = synth.to_device(inp, "cuda:0")
+    if s.w == "f32":
+        layout = "rowmajor"  # fp32 weights have no tiled layout
     if layout == "tiled":
         dev = moe.pack_layer_weights(dev)
     shape = moe.shape_of(s, layout=layout)
-    wkeys = ("w_gate", "w_up", "w_down") + (("s_gate", "s_up", "s_down") if s.w == "u4" else ())
+    # every weight tensor rotates: routed and shared expert matrices, their block
+    # scales or group parameters, the router and the selection bias
+    wkeys = [k for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
+                         "ss_gate", "ss_up", "ss_down", "w_router", "sel_bias") if dev.get(k) is not None]
     copies = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, rotate - 1))]
     r = moe.alloc_routing(shape, "cuda:0")
     ws = moe.alloc_workspace(shape, "cuda:0")
@@ -149,6 +179,12 @@ def run_workload(name, steps, warmup, rotate, layout):
         b.route()
         b.forward()
 
+    def check_status(what):
+        # the routing status word (reset by every routing call) and the sticky
+        # forward status (set by any forward call whose bounded wait ran out)
+        assert r.status.item() == moe.MOE_OK, f"{name} {what}: {moe.status_string(r.status.item())}"
+        assert r.forward_status.item() == moe.MOE_OK, f"{name} {what}: {moe.status_string(r.forward_status.item())}"
+
     # timed pass: one routing call and one forward call per step
     for i in range(warmup):
         step(i)
@@ -158,6 +194,7 @@ def run_workload(name, steps, warmup, rotate, layout):
         step(i)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
+    check_status("timed steps")
 
     # attribution pass (same kernels): events around the routing call, and events
     # the library records on the stream between the forward stages
@@ -169,6 +206,7 @@ def run_workload(name, steps, warmup, rotate, layout):
         ev[i][1].record(st)
         b.forward(moe.STAGE_ALL, events=ev[i][2:])
     torch.cuda.synchronize()
+    check_status("attribution steps")
     names = ("route", "gate_up", "down", "combine")
     pairs = ((0, 1), (2, 3), (3, 4), (4, 5))
     stage_us = {n: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(steps)])) * 1e3
@@ -194,7 +232,7 @@ def run_workload(name, steps, warmup, rotate, layout):
     torch.cuda.synchronize()
     stage_us["experts_launch"] = l0.elapsed_time(l1) * 1e3 / n_l
     counts = r.counts.cpu().numpy()
-    assert r.status.item() == 0
+    check_status("expert launches")
     return s, wall, stage_us, algorithmic(s, counts), counts, pct
 
 
@@ -299,27 +337,72 @@ def run_attention(steps):
     return out
 
 
+def host_cpu():
+    """The host's logical core count and CPU model (from /proc/cpuinfo)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return os.cpu_count() or 1, model
+
+
 def cpu_baseline(name, budget_s):
-    """The CPU oracle, as it stands, on a bounded sample of the workload."""
+    """The CPU oracle, as it stands, on a bounded sample of the workload: first
+    single-threaded, then its all-cores driver (the same per-token code on
+    contiguous token ranges, one std::thread each) on the host's cores, capped at
+    16 (a GPU machine's CPU share), whose results must be bitwise the
+    single-threaded ones.  `value` is the all-cores rate."""
     from mixture_experts_moe_amd import synth
     from oracle import moe_oracle as O
 
     inp = synth.make_inputs(name)
     s = inp["shape"]
     L = O.Layer(inp)
-    n_tok = min(s.T, 32)
-    tok = np.linspace(0, s.T - 1, n_tok).astype(np.int32)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        _, _, idx, w = O.route(L, tok)
-        O.forward(L, idx, w, tok)
-        done += n_tok
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    return {"value": done / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done // n_tok} passes of route + forward over {n_tok} of the workload's {s.T} tokens "
-                      f"({el:.1f} s, single-threaded C++ oracle, double-accumulated dot products)"}
+    n_cpu, model = host_cpu()
+    threads = O.host_threads()
+
+    def run(n_tok, budget, n_threads):
+        tok = np.linspace(0, s.T - 1, n_tok).astype(np.int32)
+        done, t0, res = 0, time.perf_counter(), None
+        while True:
+            if n_threads == 1:
+                _, lg, idx, w = O.route(L, tok)
+                y, acc = O.forward(L, idx, w, tok)
+            else:
+                _, lg, idx, w = O.route_threads(L, tok, n_threads)
+                y, acc = O.forward_threads(L, idx, w, tok, n_threads)
+            res = res or (lg, idx, w, y)
+            done += n_tok
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return done / el, done // n_tok, el, res
+
+    one, p1, el1, r1 = run(min(s.T, 32), budget_s / 2, 1)
+    n_all = min(s.T, 32 * threads)
+    many, p2, el2, r2 = run(n_all, budget_s / 2, threads)
+    # the first 32 sampled tokens of both runs are the same tokens only when both
+    # samples cover the whole batch; compare the all-cores run with a
+    # single-threaded pass over its own sample instead
+    tok = np.linspace(0, s.T - 1, n_all).astype(np.int32)
+    _, lg, idx, w = O.route(L, tok)
+    y, _ = O.forward(L, idx, w, tok)
+    bitwise = (np.array_equal(lg.view(np.uint32), r2[0].view(np.uint32)) and np.array_equal(idx, r2[1])
+               and np.array_equal(w.view(np.uint32), r2[2].view(np.uint32)) and np.array_equal(y, r2[3]))
+    assert bitwise, "all-cores oracle differs from the single-threaded oracle"
+    return {"value": many, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "host_logical_cpus": n_cpu, "host_cpu_model": model,
+            "single_thread": {"value": one, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{p1} passes of route + forward over 32 of the workload's {s.T} tokens "
+                                        f"({el1:.1f} s)"},
+            "all_cores_bitwise_equal_single_thread": bitwise,
+            "sample": f"{p2} passes of route + forward over {n_all} of the workload's {s.T} tokens ({el2:.1f} s) on "
+                      f"{threads} threads, contiguous token ranges, C++ oracle with double-accumulated dot "
+                      f"products"}
 
 
 def main():
@@ -351,11 +434,7 @@ def main():
                      "bytes_per_launch": ex_bytes, "avg_launch_us": st_us["experts_launch"]},
         "stage_us": st_us,
         "step_us_event_percentiles": pct,
-        "step_roofline": {"B_alg_bytes": alg["B_alg"], "distinct_experts": alg["U"],
-                          "hbm_frac": alg["B_alg"] / t_step / (HBM_PEAK_GBS * 1e9),
-                          "fp8_mfma_frac": alg["F_mm"] / t_step / (FP8_PEAK_TFLOPS * 1e12),
-                          "roofline_frac": max(alg["B_alg"] / (HBM_PEAK_GBS * 1e9),
-                                               alg["F_mm"] / (FP8_PEAK_TFLOPS * 1e12)) / t_step},
+        "step_roofline": step_roofline(s, alg, t_step),
     }
     extra = {}
     for name in [w for w in a.also.split(",") if w and w != a.workload]:
@@ -365,10 +444,7 @@ def main():
                        "step_us_event_percentiles": pct2,
                        "experts_GBs": (alg2["gateup_bytes"] + alg2["down_bytes"]) / (st2["experts_launch"] * 1e-6)
                        / 1e9,
-                       "hbm_frac": alg2["B_alg"] / wall2 / (HBM_PEAK_GBS * 1e9),
-                       "fp8_mfma_frac": alg2["F_mm"] / wall2 / (FP8_PEAK_TFLOPS * 1e12),
-                       "roofline_frac": max(alg2["B_alg"] / (HBM_PEAK_GBS * 1e9),
-                                            alg2["F_mm"] / (FP8_PEAK_TFLOPS * 1e12)) / wall2,
+                       **step_roofline(s2, alg2, wall2),
                        "max_over_mean_expert_load": float(counts2.max() / max(1e-9, counts2.mean()))}
     if a.compare:
         extra["route_compare_" + a.compare] = run_route_compare(a.compare, max(20, a.steps // 2))

@@ -47,7 +47,8 @@ typedef enum {
   MOE_OK = 0,
   MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative or inconsistent size */
   MOE_ERR_UNSUPPORTED = -2,  /* valid but unsupported shape or dtype combination */
-  MOE_ERR_WORKSPACE = -3,    /* ws_bytes below moe_workspace_bytes() */
+  MOE_ERR_WORKSPACE = -3,    /* ws_bytes below moe_workspace_bytes(), or moe_routing.plan_bytes
+                                below moe_plan_bytes() */
   MOE_ERR_HIP = -4,          /* a HIP launch failed */
   MOE_ERR_FORCED_INDEX = -5, /* (device status) a forced expert id was outside [0, E) */
   MOE_ERR_DEVICE_SYNC = -6   /* (device status) inside moe_forward, a block's bounded wait for
@@ -146,12 +147,19 @@ typedef struct {
                           within an expert; entries past offsets[E] are -1 */
   int32_t *inv_perm;   /* [T * k] inv_perm[p] = q, or -1 for an invalid pair */
   int32_t *status;     /* [1] device status word: MOE_OK, MOE_ERR_FORCED_INDEX (routing)
-                          or MOE_ERR_DEVICE_SYNC (forward) */
-  void *plan;          /* moe_plan_bytes() bytes: the dispatch plan the routing call
-                          writes for moe_forward (expert-kernel block schedules,
+                          or MOE_ERR_DEVICE_SYNC (forward); every routing call resets it */
+  void *plan;          /* at least moe_plan_bytes() bytes: the dispatch plan the routing
+                          call writes for moe_forward (expert-kernel block schedules,
                           per-row token/weight, with FP8 weights the activations
                           as E4M3 codes with per-(token, 128) scales, and per-tile
                           counters the forward's blocks synchronise on); opaque */
+  size_t plan_bytes;   /* bytes the caller allocated at plan; fewer than moe_plan_bytes()
+                          for the call's shape return MOE_ERR_WORKSPACE before any launch */
+  int32_t *forward_status; /* [1] device word, or NULL.  Sticky: moe_forward writes
+                          MOE_ERR_DEVICE_SYNC here (besides *status) when a bounded wait
+                          runs out, and no library call ever clears it, so one read
+                          after any number of route/forward calls tells whether one
+                          failed.  The caller zeroes it. */
 } moe_routing;
 
 /* Workspace bytes needed by moe_route, moe_route_forced and moe_forward for this
@@ -201,7 +209,8 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
  * counters in the plan (reset before the launch ends): a plan serves any
  * number of forward calls, one at a time; forward calls that overlap on one
  * plan race.  If such a wait runs out (it cannot when blocks start in order),
- * *r->status becomes MOE_ERR_DEVICE_SYNC. */
+ * *r->status and *r->forward_status (when given) become MOE_ERR_DEVICE_SYNC,
+ * y is not valid, and the plan must be rebuilt by a routing call. */
 int moe_forward(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
                 void *ws, size_t ws_bytes, void *stream);
 
@@ -210,10 +219,18 @@ enum {
   MOE_STAGE_GATE_UP = 1,   /* grouped gate/up projections + SwiGLU (+ h quantisation) */
   MOE_STAGE_DOWN = 2,      /* grouped down projection, times the routing weight */
   MOE_STAGE_COMBINE = 4,   /* fixed-order combine into y */
-  MOE_STAGE_ALL = 7
+  MOE_STAGE_ALL = 7,
+  /* Test hook for the error path of the one-launch expert kernel (no effect on
+     other launches): every down block waits for one gate/up block more than its
+     tile has, gives up after 16 polls and goes on, so the launch ends normally
+     with MOE_ERR_DEVICE_SYNC in *status and *forward_status and y is not valid.
+     The plan's per-tile counters may then be left non-zero: a routing call
+     must rebuild the plan before the next forward. */
+  MOE_FORWARD_TEST_WAIT_TIMEOUT = 0x100
 };
 
-/* moe_forward restricted to a subset of its stages (bitmask of MOE_STAGE_*),
+/* moe_forward restricted to a subset of its stages (bitmask of MOE_STAGE_*, plus
+ * optionally MOE_FORWARD_TEST_WAIT_TIMEOUT),
  * optionally timed.  Calling the stages one at a time, in order, on one stream
  * with the same arguments and workspace gives bitwise the result of
  * moe_forward; the intermediate results live in the workspace between the

@@ -1085,11 +1085,14 @@ __global__ __launch_bounds__(256) void down_u4_kernel(ExpertArgs a) {
 constexpr int kSpinLimit = 1 << 22;  // polls of about 64 cycles each: far beyond any real wait
 
 // WM: the weight mode -- 2 FP8, 3 FP8 as W8A16, 4 4-bit groups.
+// need_extra / spin_limit: 0 and kSpinLimit, except in the error-path test (1 and 16).
 template <int WM>
 __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(ExpertArgs gu, ExpertArgs dn, int n_gu,
                                                                           int32_t* __restrict__ ready,
                                                                           int32_t* __restrict__ done,
-                                                                          int32_t* __restrict__ status) {
+                                                                          int32_t* __restrict__ status,
+                                                                          int32_t* __restrict__ sticky,
+                                                                          int need_extra, int spin_limit) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int b = blockIdx.x;
   if (b < n_gu) {
@@ -1106,13 +1109,14 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(Expert
   const int bd = b - n_gu, tile = bd / dn.nsl;
   const int4 rec = dn.sched[tile];
   if (rec.x < 0) return;
-  const int need = (rec.x == dn.E ? dn.Fs : dn.F) / 128;  // gate/up slices of the tile
+  const int need = (rec.x == dn.E ? dn.Fs : dn.F) / 128 + need_extra;  // gate/up slices of the tile
   if (threadIdx.x == 0) {
     int polls = 0;
     while (__hip_atomic_load(&ready[tile], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
       __builtin_amdgcn_s_sleep(1);
-      if (++polls == kSpinLimit) {
+      if (++polls >= spin_limit) {
         *status = MOE_ERR_DEVICE_SYNC;
+        if (sticky) *sticky = MOE_ERR_DEVICE_SYNC;
         break;
       }
     }
@@ -1356,8 +1360,8 @@ bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d) {
          down_rows_per_wave(16, wmode, Fmax, d) == 2 && d % (kGateUpWaves * 32) == 0;
 }
 
-hipError_t launch_experts_fused(const ExpertArgs& a0, int wmode, const Plan& plan, int32_t* status,
-                                hipStream_t st) {
+hipError_t launch_experts_fused(const ExpertArgs& a0, int wmode, const Plan& plan, int32_t* status, int32_t* sticky,
+                                bool test_timeout, hipStream_t st) {
   ExpertArgs gu = a0, dn = a0;
   gu.sched = dn.sched = plan.sched[0];
   gu.per_tile = dn.per_tile = 1;
@@ -1373,7 +1377,8 @@ hipError_t launch_experts_fused(const ExpertArgs& a0, int wmode, const Plan& pla
     hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  kernel<<<n_gu + n_dn, kGateUpWaves * 64, lds, st>>>(gu, dn, n_gu, plan.sync, plan.sync + plan.max_tiles, status);
+  kernel<<<n_gu + n_dn, kGateUpWaves * 64, lds, st>>>(gu, dn, n_gu, plan.sync, plan.sync + plan.max_tiles, status,
+                                                      sticky, test_timeout ? 1 : 0, test_timeout ? 16 : kSpinLimit);
   return hipGetLastError();
 }
 

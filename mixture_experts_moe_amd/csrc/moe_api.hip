@@ -175,7 +175,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   if (shape->T == 0) return MOE_OK;
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < L.total || out->plan_bytes < plan_layout(*shape).total) return MOE_ERR_WORKSPACE;
   char* base = (char*)ws;
   moe::RouteLaunch R;
   R.x = x;
@@ -257,7 +257,8 @@ int moe_forward(const moe_shape* shape, const moe_weights* w, const void* x, con
 
 int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
                        void* ws, size_t ws_bytes, uint32_t stages, void* const* events, void* stream) {
-  if (stages & ~(uint32_t)MOE_STAGE_ALL) return MOE_ERR_INVALID_ARG;
+  if (stages & ~(uint32_t)(MOE_STAGE_ALL | MOE_FORWARD_TEST_WAIT_TIMEOUT)) return MOE_ERR_INVALID_ARG;
+  const bool test_timeout = stages & MOE_FORWARD_TEST_WAIT_TIMEOUT;
   int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!w || !x || !y || !r || !r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm || !r->plan)
@@ -274,7 +275,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   if (shape->T == 0) return MOE_OK;
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);
-  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < L.total || r->plan_bytes < plan_layout(*shape).total) return MOE_ERR_WORKSPACE;
 
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
@@ -324,7 +325,7 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
                      moe::experts_fusable(shape->w_dtype, plan, Fmax, d);
   mark(0);
   if (fused) {  // both projections in one launch: events 1 and 2 mark its end
-    e = moe::launch_experts_fused(a, shape->w_dtype, plan, r->status, st);
+    e = moe::launch_experts_fused(a, shape->w_dtype, plan, r->status, r->forward_status, test_timeout, st);
     mark(1);
     mark(2);
   } else if (stages & MOE_STAGE_GATE_UP) {

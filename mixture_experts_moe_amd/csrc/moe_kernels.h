@@ -108,8 +108,10 @@ hipError_t launch_gateup(const ExpertArgs& a, int wmode, const Plan& plan, hipSt
 hipError_t launch_down(const ExpertArgs& a, int wmode, const Plan& plan, hipStream_t st);
 // Gate/up and down as one launch (FP8 weights, 16-row tiles, tile-list plan).
 bool experts_fusable(int wmode, const Plan& plan, int Fmax, int d);
-hipError_t launch_experts_fused(const ExpertArgs& a, int wmode, const Plan& plan, int32_t* status,
-                                hipStream_t st);
+// status: the routing status word; sticky: the caller's sticky forward status
+// (or null); test_timeout: the waits target a count that never comes (error-path test).
+hipError_t launch_experts_fused(const ExpertArgs& a, int wmode, const Plan& plan, int32_t* status, int32_t* sticky,
+                                bool test_timeout, hipStream_t st);
 hipError_t launch_pack_weights(int64_t n_mats, int rows, int row_bytes, const void* in, void* out,
                                hipStream_t st);
 size_t route_compare_ws_bytes(int T);

@@ -26,6 +26,7 @@ ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_rout
                  "moe_route_compare", "moe_status_string")
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
+FORWARD_TEST_WAIT_TIMEOUT = 0x100  # error-path test hook of the one-launch expert kernel
 N_STAGE_EVENTS = 4
 
 
@@ -52,7 +53,8 @@ _ROUTING_FIELDS = ("logits", "topk_idx", "topk_w", "counts", "offsets", "perm", 
 
 
 class RoutingStruct(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in _ROUTING_FIELDS]
+    _fields_ = [(n, C.c_void_p) for n in _ROUTING_FIELDS] + [("plan_bytes", C.c_size_t),
+                                                             ("forward_status", C.c_void_p)]
 
 
 _lib = None
@@ -135,10 +137,12 @@ class Routing:
     perm: torch.Tensor
     inv_perm: torch.Tensor
     status: torch.Tensor
-    plan: torch.Tensor  # opaque dispatch plan (moe_plan_bytes bytes)
+    plan: torch.Tensor  # opaque dispatch plan (at least moe_plan_bytes bytes)
+    forward_status: torch.Tensor | None = None  # sticky: MOE_ERR_DEVICE_SYNC of any forward call, until zeroed
 
     def struct(self) -> RoutingStruct:
-        return RoutingStruct(*[_ptr(getattr(self, n)) for n in _ROUTING_FIELDS])
+        return RoutingStruct(*[_ptr(getattr(self, n)) for n in _ROUTING_FIELDS], self.plan.numel(),
+                             _ptr(self.forward_status))
 
 
 def alloc_routing(shape: Shape, device="cuda", with_logits=True) -> Routing:
@@ -149,7 +153,8 @@ def alloc_routing(shape: Shape, device="cuda", with_logits=True) -> Routing:
         topk_idx=torch.empty((T, k), **i32), topk_w=torch.empty((T, k), dtype=torch.float32, device=device),
         counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
         perm=torch.empty(T * k, **i32), inv_perm=torch.empty(T * k, **i32), status=torch.empty(1, **i32),
-        plan=torch.empty(max(plan_bytes(shape), 256), dtype=torch.uint8, device=device))
+        plan=torch.empty(max(plan_bytes(shape), 256), dtype=torch.uint8, device=device),
+        forward_status=torch.zeros(1, **i32))
 
 
 def workspace_bytes(shape: Shape) -> int:

@@ -81,6 +81,8 @@ CASES = {
     "decode_t32_w8a16": ("big", 32, "bf16", "fp8a16", "normal", "normal", False),
     "decode_t32_u4": ("big", 32, "bf16", "u4", "normal", "normal", False),
     "ties_t256_bf16w": ("big", 256, "bf16", "bf16", "int3", "grid64", False),
+    # the one batch size of this layer where the matrix-core work outweighs the weight stream
+    "prefill_t32768": ("big", 32768, "bf16", "fp8", "normal", "normal", False),
 }
 
 # Sub-stream identifiers: every tensor (and every expert of a tensor) draws from

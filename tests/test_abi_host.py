@@ -80,10 +80,10 @@ def test_largest_supported_widths(act, w, layout, d_max, f_max):
 FAKE = C.c_void_p(0x1000)  # never dereferenced: every call below returns before launching
 
 
-def _routing_struct(**null):
+def _routing_struct(plan_bytes=1 << 40, **null):
     vals = {n: 0x2000 for n in moe._ROUTING_FIELDS}
     vals.update({k: None for k in null})
-    return moe.RoutingStruct(*[vals[n] for n in moe._ROUTING_FIELDS])
+    return moe.RoutingStruct(*[vals[n] for n in moe._ROUTING_FIELDS], plan_bytes, None)
 
 
 def _weights_struct(**null):
@@ -133,6 +133,35 @@ def _forward(shape, w=None, r=None, y=FAKE, ws_bytes=1 << 40):
     w = w or _weights_struct()
     r = r or _routing_struct()
     return L.moe_forward(C.byref(shape), C.byref(w), FAKE, C.byref(r), y, FAKE, ws_bytes, None)
+
+
+def test_undersized_plan_rejected():
+    """The plan buffer's size travels with it (moe_routing.plan_bytes): one byte
+    short of moe_plan_bytes() is rejected on the host by routing and forward,
+    before any launch; T = 0 needs no plan."""
+    for s in (moe.make_shape(32, 2048, 384, 6, 640, 640), moe.make_shape(2048, 2048, 384, 6, 640, 640),
+              moe.make_shape(64, 256, 16, 2, 128, 128, act="f32", w="f32")):
+        n = moe.plan_bytes(s)
+        assert n > 0
+        assert _route(s, r=_routing_struct(plan_bytes=n - 1)) == moe.MOE_ERR_WORKSPACE
+        assert _forward(s, r=_routing_struct(plan_bytes=n - 1)) == moe.MOE_ERR_WORKSPACE
+        assert _route(s, r=_routing_struct(plan_bytes=0)) == moe.MOE_ERR_WORKSPACE
+    s0 = moe.make_shape(0, 2048, 384, 6, 640, 640)
+    assert _route(s0, ws_bytes=0, ws=None, r=_routing_struct(plan_bytes=0)) == moe.MOE_OK
+    assert _forward(s0, r=_routing_struct(plan_bytes=0)) == moe.MOE_OK
+
+
+def test_forward_stage_bits():
+    """moe_forward_stages takes the three stage bits and the error-path test bit;
+    any other bit is rejected before any launch."""
+    L = _lib()
+    s = moe.make_shape(0, 2048, 384, 6, 640, 640)
+    w, r = _weights_struct(), _routing_struct()
+    call = lambda bits: L.moe_forward_stages(C.byref(s), C.byref(w), FAKE, C.byref(r), FAKE, FAKE, 1 << 40, bits,
+                                             None, None)
+    assert call(moe.STAGE_ALL | moe.FORWARD_TEST_WAIT_TIMEOUT) == moe.MOE_OK
+    for bad in (8, 0x80, 0x200, 1 << 31):
+        assert call(moe.STAGE_ALL | bad) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_forward_host_validation():

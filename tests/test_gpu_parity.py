@@ -49,7 +49,9 @@ def gpu_inputs(inp):
     return d
 
 
-def run_gpu(inp, forced=None, dev=None, routing=None):
+def run_gpu(inp, forced=None, dev=None, routing=None, expect_status=moe.MOE_OK):
+    """One route + forward through the C ABI; asserts the device status word
+    (and the sticky forward status, when the routing carries one)."""
     s = inp["shape"]
     shape = moe.shape_of(s)
     dev = dev or gpu_inputs(inp)
@@ -67,6 +69,9 @@ def run_gpu(inp, forced=None, dev=None, routing=None):
                                                       "status")}
     out["logits"] = r.logits.cpu().numpy() if r.logits is not None else None
     out["y"] = y.float().cpu().numpy()
+    assert out["status"][0] == expect_status, moe.status_string(int(out["status"][0]))
+    if r.forward_status is not None:
+        assert r.forward_status.item() == moe.MOE_OK, moe.status_string(r.forward_status.item())
     return out
 
 
@@ -252,9 +257,8 @@ def test_ties_exact_routing(case):
     assert np.array_equal(g["topk_idx"], idx)
     check_dispatch(g, idx, s.E)
     assert np.max(np.abs(g["topk_w"] - w)) <= W_ABS
-    tok = np.arange(0, s.T, 8)
-    _, acc_ref = O.forward(L, idx[tok], w[tok], tok)
-    check_y(g["y"][tok], acc_ref)
+    _, acc_ref = O.forward_threads(L, idx, w)  # every token
+    check_y(g["y"], acc_ref)
 
 
 # ------------------------------------------------------------------ prefill, forced routing
@@ -263,18 +267,17 @@ def test_prefill_forced_full_size():
     inp = synth.make_inputs("prefill_t2048")
     s = inp["shape"]
     L = O.Layer(inp)
-    say(f"prefill_t2048: oracle free pass over T={s.T} records the ids")
-    _, lg, idx, w = O.route(L)
+    say(f"prefill_t2048: oracle free pass over T={s.T} records the ids ({O.host_threads()} threads)")
+    _, lg, idx, w = O.route_threads(L)
     g = run_gpu(inp, forced=idx)
     say("  GPU forced pass")
-    assert g["status"][0] == 0
     check_logits(g["logits"], lg)
     assert np.array_equal(g["topk_idx"], idx)
     check_dispatch(g, idx, s.E)
     assert np.max(np.abs(g["topk_w"] - w)) <= W_ABS
-    tok = np.unique(np.concatenate([np.arange(0, s.T, 64), [1, s.T - 1]]))
-    _, acc_ref = O.forward(L, idx[tok], w[tok], tok)
-    check_y(g["y"][tok], acc_ref)
+    say("  oracle forward over every token")
+    _, acc_ref = O.forward_threads(L, idx, w)
+    check_y(g["y"], acc_ref)
 
 
 # ------------------------------------------------------------------ W8A16 weight mode
@@ -321,16 +324,21 @@ def test_skew_free_full_size():
     assert counts.max() > 10 * counts.mean()
     check_dispatch_properties(g, s.E)
     L = O.Layer(inp)
-    tok = np.unique(np.concatenate([np.arange(0, s.T, 97), [s.T - 1]]))
-    _, lg, idx, w = O.route(L, tok)
+    # every 8th token, plus every token in the last 64 rows (the ragged tail
+    # tiles) of the five most loaded experts
+    heavy = np.argsort(-counts, kind="stable")[:5]
+    tail = np.concatenate([g["perm"][max(g["offsets"][e], g["offsets"][e + 1] - 64):g["offsets"][e + 1]] // s.k
+                           for e in heavy])
+    tok = np.unique(np.concatenate([np.arange(0, s.T, 8), tail, [s.T - 1]]))
+    _, lg, idx, w = O.route_threads(L, tok)
     check_logits(g["logits"][tok], lg)
     bad, ex = route_agreement(g["topk_idx"][tok], idx, selection_scores(inp, lg), s.k)
     say(f"  ids on {len(tok)} sampled tokens: {bad} mismatches, {ex} exempt")
     assert bad == 0
     same = (g["topk_idx"][tok] == idx).all(axis=1)
     assert np.max(np.abs(g["topk_w"][tok][same] - w[same])) <= W_ABS
-    ts = tok[same][::2]
-    _, acc_ref = O.forward(L, idx[same][::2], w[same][::2], ts)
+    ts = tok[same]
+    _, acc_ref = O.forward_threads(L, idx[same], w[same], ts)
     check_y(g["y"][ts], acc_ref)
 
 
@@ -401,7 +409,7 @@ def test_invalid_forced_ids_flag_status_and_stay_in_bounds():
                     topk_w=bufs["topk_w"][1].view(T, k), counts=bufs["counts"][1], offsets=bufs["offsets"][1],
                     perm=bufs["perm"][1], inv_perm=bufs["inv_perm"][1], status=bufs["status"][1],
                     plan=torch.empty(moe.plan_bytes(shape), dtype=torch.uint8, device=DEV))
-    g = run_gpu(inp, forced=bad, routing=r)
+    g = run_gpu(inp, forced=bad, routing=r, expect_status=moe.MOE_ERR_FORCED_INDEX)
     for n, (full, _) in bufs.items():
         tail = full[-guard:].cpu().numpy()
         assert (tail.view(np.int32) == SENT).all() if full.dtype == torch.int32 else \
@@ -477,6 +485,41 @@ def test_forward_repeats_on_one_plan():
     assert r.status.item() == 0
     for y in ys[1:]:
         assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
+
+
+def test_forward_wait_timeout_is_reported_and_sticky():
+    """The one-launch expert kernel's bounded wait, forced to run out from the
+    host (MOE_FORWARD_TEST_WAIT_TIMEOUT: each down block waits for one gate/up
+    block more than its tile has, 16 polls): the launch ends normally and sets
+    MOE_ERR_DEVICE_SYNC in the status word and in the sticky forward status.
+    A routing call then resets the status word and rebuilds the plan, the next
+    forward is bitwise a clean run's, and the sticky word still holds the
+    failure until the caller clears it."""
+    inp = synth.make_inputs("decode_t32")
+    s = inp["shape"]
+    say("decode_t32: fused expert launch with its waits forced to run out (16 polls), then a clean call")
+    shape = moe.shape_of(s)
+    dev = gpu_inputs(inp)
+    ref = run_gpu(inp, dev=dev)
+    r = moe.alloc_routing(shape, DEV)
+    ws = moe.alloc_workspace(shape, DEV)
+    y = torch.empty((s.T, s.d), dtype=torch.bfloat16, device=DEV)
+    b = moe.Bound(shape, dev, dev["x"], r, y, ws)
+    b.route()
+    b.forward(moe.STAGE_ALL | moe.FORWARD_TEST_WAIT_TIMEOUT)
+    torch.cuda.synchronize()
+    assert r.status.item() == moe.MOE_ERR_DEVICE_SYNC
+    assert r.forward_status.item() == moe.MOE_ERR_DEVICE_SYNC
+    b.route()
+    b.forward()
+    torch.cuda.synchronize()
+    assert r.status.item() == moe.MOE_OK
+    assert r.forward_status.item() == moe.MOE_ERR_DEVICE_SYNC  # sticky until the caller clears it
+    assert np.array_equal(y.float().cpu().numpy().view(np.uint32), ref["y"].view(np.uint32))
+    r.forward_status.zero_()
+    b.forward()
+    torch.cuda.synchronize()
+    assert r.status.item() == moe.MOE_OK and r.forward_status.item() == moe.MOE_OK
 
 
 # ------------------------------------------------------------------ tiled weight layout
