@@ -149,6 +149,7 @@ def run_workload(name, steps, warmup, rotate, layout):
     import torch
     from mixture_experts_moe_amd import moe, synth
 
+    print(f"bench: {name}: {steps} steps after {warmup} warm-up", file=sys.stderr, flush=True)
     inp = synth.make_inputs(name)
     s = inp["shape"]
     dev = synth.to_device(inp, "cuda:0")
@@ -447,12 +448,15 @@ def main():
                        **step_roofline(s2, alg2, wall2),
                        "max_over_mean_expert_load": float(counts2.max() / max(1e-9, counts2.mean()))}
     if a.compare:
+        print(f"bench: route_compare on {a.compare}", file=sys.stderr, flush=True)
         extra["route_compare_" + a.compare] = run_route_compare(a.compare, max(20, a.steps // 2))
     if a.attention:
+        print("bench: attention ops", file=sys.stderr, flush=True)
         extra.update(run_attention(max(20, a.steps // 2)))
     if extra:
         out["also"] = extra
     if a.cpu_seconds > 0:
+        print("bench: CPU baseline (the oracle)", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(a.workload, a.cpu_seconds)
     print(json.dumps(out), flush=True)
 
