@@ -51,8 +51,10 @@ typedef enum {
                                 below moe_plan_bytes() */
   MOE_ERR_HIP = -4,          /* a HIP launch failed */
   MOE_ERR_FORCED_INDEX = -5, /* (device status) a forced expert id was outside [0, E) */
-  MOE_ERR_DEVICE_SYNC = -6   /* (device status) inside moe_forward, a block's bounded wait for
+  MOE_ERR_DEVICE_SYNC = -6,  /* (device status) inside moe_forward, a block's bounded wait for
                                 another block's results ran out; y is not valid */
+  MOE_ERR_SCRATCH_LIMIT = -7 /* moe_forward_noalloc: the shape needs more than
+                                MOE_NOALLOC_SCRATCH_BYTES of scratch */
 } moe_status;
 
 typedef enum {
@@ -213,6 +215,28 @@ int moe_route_forced(const moe_shape *shape, const moe_weights *w, const void *x
  * y is not valid, and the plan must be rebuilt by a routing call. */
 int moe_forward(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
                 void *ws, size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: moe_forward
+ * with no workspace argument.  The forward's scratch (h rows, their scales, the
+ * fp32 partial outputs) lives in a static device buffer of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each device it runs on
+ * until the process ends; its address is looked up once per device (on that
+ * device's first call), and the call itself allocates and frees nothing.
+ * Scratch the shape needs, with R = T * top_k + T rows, H = max(d_ffn,
+ * d_ffn_shared), h bytes hb = 1 (MOE_FP8E4M3_B128), 4 (MOE_F32), else 2, and
+ * a256(n) = n rounded up to a multiple of 256:
+ *   a256(R * H * hb) + a256(MOE_FP8E4M3_B128 ? R * H / 128 * 4 : 0) + a256(R * d_model * 4);
+ * more than MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_SCRATCH_LIMIT before any
+ * launch (the d_model 2048, d_ffn 640, top-6 FP8 layer fits up to T = 1083).
+ * Nothing in the buffer needs to start at zero.  Every call on one device
+ * shares that device's buffer, which keeps the last call's contents: calls that
+ * overlap on one device (other streams, other host threads) race with each
+ * other.  Arguments, other errors and results are those of moe_forward with the
+ * same arguments, bitwise. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_forward_noalloc(const moe_shape *shape, const moe_weights *w, const void *x, const moe_routing *r, void *y,
+                        void *stream);
 
 /* Stages of moe_forward, in launch order. */
 enum {

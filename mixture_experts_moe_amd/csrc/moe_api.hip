@@ -1,9 +1,21 @@
 // Host side of the C ABI declared in include/moe.h: argument validation,
-// workspace layout, kernel launches on the caller's stream.  Holds no state.
+// workspace layout, kernel launches on the caller's stream.  Holds no state,
+// except the per-device address of the no-allocation forward's scratch buffer
+// (resolved once per device, then only read).
 #include <limits.h>
+
+#include <atomic>
+#include <mutex>
 
 #include "moe.h"
 #include "moe_kernels.h"
+
+// Scratch of moe_forward_noalloc: the forward's h rows, their scales and the
+// fp32 partials.  One copy per device the library runs on, held until the
+// process ends.  Host code never uses this name as an address (on the host it
+// is only a stand-in for the symbol): it asks hipGetSymbolAddress for each
+// device's copy once and passes that pointer to the kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -36,7 +48,9 @@ int64_t max_tiles_for(const moe_shape& s, int BM) {
 // passes none), the router partial sums, chunk_hist and local_rank; the forward
 // pass uses the rest.  Nothing is carried from one call to the next: what the
 // forward pass needs from routing travels in moe_routing (plan included).
-Layout layout(const moe_shape& s) {
+// forward_only: the routing segments are empty (the no-allocation forward's
+// scratch holds only the forward's segments).
+Layout layout(const moe_shape& s, bool forward_only = false) {
   const size_t T = s.T, d = s.d_model, E = s.n_experts, P = T * s.top_k;
   const size_t Fmax = s.d_ffn > s.d_ffn_shared ? s.d_ffn : s.d_ffn_shared;
   const bool fp8 = s.w_dtype == MOE_FP8E4M3_B128;
@@ -47,10 +61,11 @@ Layout layout(const moe_shape& s) {
     o += align256(bytes);
     return at;
   };
-  L.logits = seg(T * E * 4);
-  L.rpart = seg(moe::router_part_floats(s.T, s.top_k, s.d_model, s.n_experts, s.act_dtype == MOE_BF16) * 4);
-  L.chunk_hist = seg(moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
-  L.local_rank = seg(P * 4);
+  const size_t rt = forward_only ? 0 : 1;
+  L.logits = seg(rt * T * E * 4);
+  L.rpart = seg(rt * moe::router_part_floats(s.T, s.top_k, s.d_model, s.n_experts, s.act_dtype == MOE_BF16) * 4);
+  L.chunk_hist = seg(rt * moe::dispatch_chunk_hist_ints(s.T, s.top_k, s.n_experts) * 4);
+  L.local_rank = seg(rt * P * 4);
   L.h = seg((P + T) * Fmax * h_elem_bytes(s.w_dtype));
   L.sh = seg(fp8 ? (P + T) * (Fmax / 128) * 4 : 0);
   L.part = seg((P + T) * d * 4);
@@ -120,6 +135,29 @@ int pick_bm(const moe_shape& s) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Each device's address of `scratch`, looked up on the first no-allocation
+// call on that device (with that device current) and kept for the process.
+constexpr int kMaxScratchDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
+int device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxScratchDevices) return MOE_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return MOE_OK;
+}
 
 // The kernels move 16 bytes per lane through every tensor.
 bool misaligned(const void* p) { return ((uintptr_t)p & 15) != 0; }
@@ -255,8 +293,14 @@ int moe_forward(const moe_shape* shape, const moe_weights* w, const void* x, con
   return moe_forward_stages(shape, w, x, r, y, ws, ws_bytes, MOE_STAGE_ALL, nullptr, stream);
 }
 
-int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
-                       void* ws, size_t ws_bytes, uint32_t stages, void* const* events, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward_stages and moe_forward_noalloc.  noalloc: the forward's segments
+// live in this device's `scratch` (ws and ws_bytes are ignored).
+int forward_common(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
+                   void* ws, size_t ws_bytes, bool noalloc, uint32_t stages, void* const* events, void* stream) {
   if (stages & ~(uint32_t)(MOE_STAGE_ALL | MOE_FORWARD_TEST_WAIT_TIMEOUT)) return MOE_ERR_INVALID_ARG;
   const bool test_timeout = stages & MOE_FORWARD_TEST_WAIT_TIMEOUT;
   int rc = validate_shape(shape);
@@ -273,9 +317,16 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
   if (has_shared && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_INVALID_ARG;
   if (has_shared && scaled && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_INVALID_ARG;
   if (shape->T == 0) return MOE_OK;
-  if (!ws) return MOE_ERR_INVALID_ARG;
-  const Layout L = layout(*shape);
-  if (ws_bytes < L.total || r->plan_bytes < plan_layout(*shape).total) return MOE_ERR_WORKSPACE;
+  const Layout L = layout(*shape, noalloc);
+  if (noalloc) {
+    if (L.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH_LIMIT;
+    if (r->plan_bytes < plan_layout(*shape).total) return MOE_ERR_WORKSPACE;
+    const int src = device_scratch(&ws);
+    if (src != MOE_OK) return src;
+  } else {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < L.total || r->plan_bytes < plan_layout(*shape).total) return MOE_ERR_WORKSPACE;
+  }
 
   hipStream_t st = (hipStream_t)stream;
   char* base = (char*)ws;
@@ -341,6 +392,20 @@ int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void*
     mark(3);
   }
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_stages(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
+                       void* ws, size_t ws_bytes, uint32_t stages, void* const* events, void* stream) {
+  return forward_common(shape, w, x, r, y, ws, ws_bytes, false, stages, events, stream);
+}
+
+int moe_forward_noalloc(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y,
+                        void* stream) {
+  return forward_common(shape, w, x, r, y, nullptr, 0, true, MOE_STAGE_ALL, nullptr, stream);
 }
 
 int moe_quantize_rows(int64_t n_rows, int32_t n_cols, int32_t act_dtype, const void* in, uint8_t* codes,
@@ -411,6 +476,8 @@ const char* moe_status_string(int status) {
     case MOE_ERR_HIP: return "MOE_ERR_HIP: a HIP kernel launch failed";
     case MOE_ERR_FORCED_INDEX: return "MOE_ERR_FORCED_INDEX: a forced expert id was outside [0, n_experts)";
     case MOE_ERR_DEVICE_SYNC: return "MOE_ERR_DEVICE_SYNC: a forward block's wait for another block timed out";
+    case MOE_ERR_SCRATCH_LIMIT:
+      return "MOE_ERR_SCRATCH_LIMIT: the shape needs more scratch than moe_forward_noalloc's static buffer holds";
     default: return "unknown moe status";
   }
 }

@@ -21,9 +21,11 @@ MOE_ERR_FORCED_INDEX, MOE_ERR_DEVICE_SYNC = -5, -6  # device status word
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3, "u4": 4}
 
 # Every function the header declares (checked against include/moe.h by the tests).
-ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward", "moe_forward_stages",
-                 "moe_quantize_rows", "moe_pack_weights", "moe_pack_weights_u4", "moe_route_compare_workspace_bytes",
-                 "moe_route_compare", "moe_status_string")
+ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward",
+                 "moe_forward_noalloc", "moe_forward_stages", "moe_quantize_rows", "moe_pack_weights",
+                 "moe_pack_weights_u4", "moe_route_compare_workspace_bytes", "moe_route_compare", "moe_status_string")
+MOE_ERR_SCRATCH_LIMIT = -7
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
 STAGE_GATE_UP, STAGE_DOWN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
 FORWARD_TEST_WAIT_TIMEOUT = 0x100  # error-path test hook of the one-launch expert kernel
@@ -77,6 +79,7 @@ def lib() -> C.CDLL:
         L.moe_route_forced.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
         L.moe_forward.argtypes = [p, p, p, p, p, p, C.c_size_t, p]
         L.moe_forward_stages.argtypes = [p, p, p, p, p, p, C.c_size_t, C.c_uint32, p, p]
+        L.moe_forward_noalloc.argtypes = [p, p, p, p, p, p]
         L.moe_quantize_rows.argtypes = [i64, i32, i32, p, p, p, p]
         L.moe_pack_weights.argtypes = [i64, i32, i32, p, p, p]
         L.moe_pack_weights_u4.argtypes = [i64, i32, i32, p, p, p, p, p, p]
@@ -194,6 +197,13 @@ def forward(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor,
     rc = lib().moe_forward(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), C.byref(r.struct()), _ptr(y),
                            _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "moe_forward")
+
+
+def forward_noalloc(shape: Shape, w: dict, x: torch.Tensor, r: Routing, y: torch.Tensor, stream=None):
+    """moe_forward without a workspace: the library's static per-device scratch."""
+    rc = lib().moe_forward_noalloc(C.byref(shape), C.byref(weights_struct(w)), _ptr(x), C.byref(r.struct()),
+                                   _ptr(y), _stream(stream))
+    _check(rc, "moe_forward_noalloc")
 
 
 def _events(events):

@@ -39,7 +39,7 @@ def test_exports_every_declared_function():
 
 def test_status_strings():
     _lib()
-    for rc in (0, -1, -2, -3, -4, -5, -6):
+    for rc in (0, -1, -2, -3, -4, -5, -6, -7):
         assert moe.status_string(rc).startswith("MOE_")
     assert "unknown" in moe.status_string(7)
 
@@ -162,6 +162,27 @@ def test_forward_stage_bits():
     assert call(moe.STAGE_ALL | moe.FORWARD_TEST_WAIT_TIMEOUT) == moe.MOE_OK
     for bad in (8, 0x80, 0x200, 1 << 31):
         assert call(moe.STAGE_ALL | bad) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_forward_noalloc_host_validation():
+    """moe_forward_noalloc's host checks, none of which touches a GPU: the
+    scratch the shape needs against MOE_NOALLOC_SCRATCH_BYTES (the 2048 / 640 /
+    top-6 FP8 layer fits up to T = 1083), then the plan size; T = 0 is a no-op;
+    missing pointers as for moe_forward."""
+    L = _lib()
+    w = _weights_struct()
+
+    def call(shape, r=None, y=FAKE):
+        r = r or _routing_struct()
+        return L.moe_forward_noalloc(C.byref(shape), C.byref(w), FAKE, C.byref(r), y, None)
+
+    assert call(moe.make_shape(1084, 2048, 384, 6, 640, 640)) == moe.MOE_ERR_SCRATCH_LIMIT
+    assert call(moe.make_shape(8192, 2048, 384, 6, 640, 640)) == moe.MOE_ERR_SCRATCH_LIMIT
+    fits = moe.make_shape(1083, 2048, 384, 6, 640, 640)
+    assert call(fits, r=_routing_struct(plan_bytes=moe.plan_bytes(fits) - 1)) == moe.MOE_ERR_WORKSPACE
+    assert call(fits, y=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(moe.make_shape(0, 2048, 384, 6, 640, 640)) == moe.MOE_OK
+    assert call(moe.make_shape(32, 2048, 384, 9, 640, 640)) == moe.MOE_ERR_UNSUPPORTED
 
 
 def test_forward_host_validation():
