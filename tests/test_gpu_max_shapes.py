@@ -5,7 +5,8 @@ C ABI, against the oracle with the parity bars of the main workloads.
     tile's activation and h rows fill the LDS of a workgroup) with FP8 weights,
     with the same weights and bf16 activations (W8A16), and with 4-bit group
     weights; as many experts as top_k (every token routes to every expert, so
-    the experts hold T rows each) and a ragged T;
+    the experts hold T rows each) and a ragged T; with FP8 weights also with
+    ten 16-row tiles per expert;
   * the most experts and the largest top_k (512 experts, top 8: eight candidates
     per lane in the selection), with the one-block dispatch (800 pairs) and the
     chunked one (2,400 pairs), free and forced.
@@ -86,6 +87,18 @@ def test_widest_layer(w):
     say(f"widest {w} layer T={T} d={d} E={E} k={k} F=Fs={F}")
     g = run_gpu(inp, dev=_dev(inp))
     _check(inp, g, n_sample=5)
+
+
+def test_widest_layer_many_tiles():
+    """The widest FP8 layer with 150 rows per expert: past the row count that
+    picks 32-row tiles, which do not fit the LDS at this width (32 rows of h
+    4096 wide), so the kernels stay at 16-row tiles, ten per expert with a
+    ragged last one, and the down projection streams K in stages."""
+    T, d, E, k, F = 150, 4608, 4, 4, 4096
+    inp = _fp8_layer(T, d, E, k, F, F, seed=13)
+    say(f"widest fp8 layer, many 16-row tiles per expert: T={T} d={d} E={E} k={k} F=Fs={F}")
+    g = run_gpu(inp, dev=_dev(inp))
+    _check(inp, g, n_sample=6)
 
 
 @pytest.mark.parametrize("T,kind", [(100, "free"), (100, "forced"), (300, "free"), (300, "forced")])

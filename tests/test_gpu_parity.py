@@ -90,6 +90,8 @@ def check_logits(gpu, ref):
 def route_agreement(gpu_idx, ref_idx, ref_scores, k):
     """Returns (mismatches on non-exempt tokens, exempt tokens)."""
     srt = -np.sort(-ref_scores.astype(np.float64), axis=1)[:, :k + 1]
+    if srt.shape[1] == k:  # k == E: every expert is chosen, the k / k+1 gap is unbounded
+        srt = np.concatenate([srt, np.full((srt.shape[0], 1), -np.inf)], axis=1)
     gaps = srt[:, :-1] - srt[:, 1:]
     bad = exempt = 0
     for t in range(gpu_idx.shape[0]):
@@ -351,14 +353,17 @@ def _forced_random(T, k, E, seed, n_experts_used=None):
 
 
 @pytest.mark.parametrize("T,kind", [(1, "free"), (37, "free"), (64, "one_expert"), (100, "free"), (170, "forced"),
-                                    (300, "few_experts"), (5462, "forced"), (8792, "forced")])
+                                    (300, "few_experts"), (5462, "forced"), (8792, "forced"),
+                                    (8192, "few_experts")])
 def test_edge_shapes(T, kind):
     """T=1; a ragged tail; every pair on one expert (duplicate ids per token);
     batches of up to 170 tokens (1024 pairs) route through the one-block
     dispatch, longer ones per chunk; most experts empty; pair counts 32,772 and
     52,752 (just above 32,768 and not
     a multiple of 64; and 8 x 1,099 x 6, the expert-GEMM row counts of section 3
-    of "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No.")."""
+    of "We Ported Aleph Alpha's Kolibri to a MacBook. Our Own Gate Said No.");
+    the last with 49,152 pairs on three experts (over five hundred 32-row tiles
+    of one expert)."""
     inp = synth.make_inputs("prefill_t2048", T=T)
     s = inp["shape"]
     say(f"edge T={T} ({T * s.k} pairs) {kind}")
@@ -546,7 +551,7 @@ def test_pack_weights_layout():
 
 
 @pytest.mark.parametrize("case,T", [("decode_t32", None), ("prefill_t2048", 700), ("ties_t256_bf16w", None),
-                                    ("decode_t32_w8a16", None)])
+                                    ("decode_t32_w8a16", None), ("skew_t8192", 4000)])
 def test_tiled_layout_matches_rowmajor(case, T):
     """The same layer with packed weights gives the same bits as with row-major ones."""
     inp = synth.make_inputs(case, T=T)
@@ -569,12 +574,13 @@ def test_tiled_layout_matches_rowmajor(case, T):
 
 # ------------------------------------------------------------------ batch invariance
 
-@pytest.mark.parametrize("T_big", [300, 2048])
+@pytest.mark.parametrize("T_big", [300, 2048, 8192])
 def test_batch_invariance(T_big):
     """A token's logits, ids, weights and output do not depend on the batch it
     sits in: the 32 decode tokens alone (short-batch kernels, 16-row tiles) and
     as the first rows of a larger batch (long-batch router; at T=2048 32-row
-    tiles and the XCD schedule) give the same bits.  (The pages' port drifted
+    tiles and the XCD schedule, at T=8192 with many tiles per expert) give the
+    same bits.  (The pages' port drifted
     when only the prefill chunk size changed: "We Ported Aleph Alpha's Kolibri
     to a MacBook. Our Own Gate Said No.", section "Taking it apart".)"""
     small = synth.make_inputs("decode_t32")
