@@ -279,6 +279,154 @@ __global__ __launch_bounds__(NW * 64) void router_tile_kernel(const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
+// Router partial logits for batches of 4096 tokens and more, larger tiles
+// (bf16 x, d a multiple of 256): blocks of 128 tokens x 64 experts over one
+// half of K, 4 waves of 64 tokens x 32 experts (8 products per 32-deep step
+// and plane: each x fragment read from LDS feeds 2 of them, each weight
+// fragment 4, against 1 and 2 in router_tile_kernel).  Per 64-deep chunk both
+// operands go through LDS already in operand order (1 KB per 16 rows x 32 K):
+// x gathered per token, the weights split while staged into their three exact
+// bf16 planes.  Two LDS buffers, two register sets: a chunk's loads are issued
+// two chunks before it is multiplied.  Sum order per logit as in
+// router_tile_kernel and the K-split kernel (a chain of six products per chunk
+// from zero; four chunks into a slice in order; the half's slices in order),
+// so the logits are the same bit for bit.  (Weights split once at load time
+// and copied instead were measured slower: their staging registers took the
+// kernel past 256, to one wave per SIMD.)
+// ---------------------------------------------------------------------------
+template <int NJ>
+__global__ __launch_bounds__(256) void router_tile2_kernel(const uint16_t* __restrict__ x,
+                                                           const float* __restrict__ W, float* __restrict__ part,
+                                                           int T, int d, int E, int gsl,
+                                                           int32_t* __restrict__ status) {
+  constexpr int NS = 2, KC = 64, TT = 32 * NJ, TE = 64;
+  constexpr int XB = (TT / 16) * NS * 1024;  // x bytes per chunk: [token tile][step][lane]
+  constexpr int WB = 3 * 4 * NS * 1024;      // weight bytes per chunk: [plane][expert tile][step][lane]
+  constexpr int XP = XB / 16 / 256;          // 16-byte x pieces per thread per chunk
+  constexpr int WP = 4 * NS * 64 / 256;      // 8-weight slots per thread per chunk
+  static_assert(XP * 16 * 256 == XB && WP >= 1, "tile shape");
+  __shared__ __align__(16) uint8_t lds[2][XB + WB];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, kg = lane >> 4;
+  const int wt = wave & 1, we = wave >> 1;
+  const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE, half = blockIdx.z;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && half == 0 && tid == 0) *status = 0;
+  const int c0 = half ? gsl * 4 : 0, c1 = half ? d / KC : gsl * 4;  // a multiple of 4 chunks, >= 4
+  struct Set {
+    v4i xv[XP];
+    v4i wv[2 * WP];
+  };
+  auto fetch = [&](int ch, Set& S) {
+    const int ks0 = ch * NS;
+#pragma unroll
+    for (int u = 0; u < XP; ++u) {
+      const int i = tid + u * 256, tt = i / (NS * 64), ks = (i / 64) % NS, l = i % 64;
+      const int t = min(t0 + 16 * tt + (l & 15), T - 1);
+      S.xv[u] = *(const v4i*)(x + (size_t)t * d + 32 * (ks0 + ks) + 8 * (l >> 4));
+    }
+#pragma unroll
+    for (int u = 0; u < WP; ++u) {
+      const int sidx = tid + u * 256, et = sidx / (NS * 64), ks = (sidx / 64) % NS, l = sidx % 64;
+      const int e = min(e0 + 16 * et + (l & 15), E - 1);
+      const float* wp = W + (size_t)e * d + 32 * (ks0 + ks) + 8 * (l >> 4);
+      S.wv[2 * u] = *(const v4i*)wp;
+      S.wv[2 * u + 1] = *(const v4i*)(wp + 4);
+    }
+  };
+  auto store = [&](int buf, const Set& S) {
+    // Rows past T or E hold a clamped copy of the last row; the outputs they
+    // feed are never stored.
+    uint8_t* L = lds[buf];
+#pragma unroll
+    for (int u = 0; u < XP; ++u) *(v4i*)(L + (tid + u * 256) * 16) = S.xv[u];
+#pragma unroll
+    for (int u = 0; u < WP; ++u) {
+      const int sidx = tid + u * 256;
+      const v4i a = S.wv[2 * u], b = S.wv[2 * u + 1];
+      const float w[8] = {__int_as_float(a[0]), __int_as_float(a[1]), __int_as_float(a[2]), __int_as_float(a[3]),
+                          __int_as_float(b[0]), __int_as_float(b[1]), __int_as_float(b[2]), __int_as_float(b[3])};
+      v8bf hi, mid, lo;
+      split3_bf16(w, hi, mid, lo);
+      *(v8bf*)(L + XB + (0 * 4 * NS * 64 + sidx) * 16) = hi;
+      *(v8bf*)(L + XB + (1 * 4 * NS * 64 + sidx) * 16) = mid;
+      *(v8bf*)(L + XB + (2 * 4 * NS * 64 + sidx) * 16) = lo;
+    }
+  };
+  v4f tot[2][NJ], sl[2][NJ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) tot[i][j] = sl[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int buf, int ch) {
+    const uint8_t* L = lds[buf];
+    v4f cc[2][NJ];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) cc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NS; ++ks) {  // lane holds K = 32*ks + 8*kg + [0, 8)
+      v8bf b[NJ], a[3][2];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[j] = *(const v8bf*)(L + ((wt * NJ + j) * NS + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[p][i] = *(const v8bf*)(L + XB + ((p * 4 + 2 * we + i) * NS + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0][i], b[j], cc[i][j], 0, 0, 0);
+          cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1][i], b[j], cc[i][j], 0, 0, 0);
+          cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2][i], b[j], cc[i][j], 0, 0, 0);
+        }
+    }
+    const int q = (ch - c0) % 4, slice = (ch - c0) / 4;  // chunk -> slice -> half total
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        sl[i][j] = q == 0 ? cc[i][j] : sl[i][j] + cc[i][j];
+        if (q == 3) tot[i][j] = slice == 0 ? sl[i][j] : tot[i][j] + sl[i][j];
+      }
+  };
+  // Chunk c sits in register set (c - c0) % 2 from its fetch, two chunks ahead,
+  // to its store into LDS buffer (c - c0) % 2; the half is an even number of
+  // chunks, so the loop is unrolled by two and the sets are named statically.
+  Set sa, sb;
+  fetch(c0, sa);
+  fetch(c0 + 1, sb);
+  store(0, sa);
+  fetch(c0 + 2, sa);
+  __syncthreads();
+  for (int ch = c0; ch < c1; ch += 2) {
+    store(1, sb);  // chunk ch + 1 into the buffer chunk ch - 1 used
+    if (ch + 3 < c1) fetch(ch + 3, sb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the new loads ahead of the waits for older ones
+    compute(0, ch);
+    __syncthreads();
+    if (ch + 2 < c1) {
+      store(0, sa);
+      if (ch + 4 < c1) fetch(ch + 4, sa);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(1, ch + 1);
+    __syncthreads();
+  }
+  float* out = part + (size_t)half * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 32 * we + 16 * i + 4 * kg + r, t = t0 + 16 * NJ * wt + 16 * j + lr;
+        if (e < E && t < T) out[(size_t)t * E + e] = tot[i][j][r];
+      }
+}
+
+// ---------------------------------------------------------------------------
 // Router logits for fp32 activations: plain fp32 multiply-add, LDS-tiled; tiles
 // of TT tokens x TE experts, each of the 256 threads owning a (TT/16) x (TE/16)
 // register tile.
@@ -847,7 +995,11 @@ static hipError_t launch_router(const RouteLaunch& L, hipStream_t st, const floa
   if (L.x_bf16 && !shortin) {  // tiles over two halves of K
     const int ksl = router_kslice(L.d), ns = L.d / ksl, halves = ns > 1 ? 2 : 1;
     const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64, halves);
-    if (ksl == 256)
+    const uint16_t* x = (const uint16_t*)L.x;
+    if (ksl == 256 && halves == 2 && L.T >= 4096) {  // 128-token blocks once they fill the chip
+      const dim3 g2((L.T + 127) / 128, (L.E + 63) / 64, 2);
+      router_tile2_kernel<4><<<g2, 256, 0, st>>>(x, L.w_router, L.rpart, L.T, L.d, L.E, (ns + 1) / 2, L.status);
+    } else if (ksl == 256)
       router_tile_kernel<2, 8><<<grid, 512, 0, st>>>((const uint16_t*)L.x, L.w_router, L.rpart, L.T, L.d, L.E,
                                                      (ns + 1) / 2, L.status);
     else

@@ -572,6 +572,22 @@ def test_tiled_layout_matches_rowmajor(case, T):
     assert torch.equal(ys[0].view(torch.int16), ys[1].view(torch.int16))
 
 
+# ------------------------------------------------------------------ the two long-batch routers
+
+def test_long_batch_routers_agree_bitwise():
+    """From 4096 tokens the router runs in 128-token blocks of 64 x 32 products
+    per wave, below that in 64-token blocks: the same tokens give the same
+    logits, ids and weights, bit for bit, on every one of 4095 tokens."""
+    big = synth.make_inputs("skew_t8192", T=4096)
+    small = synth.make_inputs("skew_t8192", T=4095)
+    say("skew layer: 4096 tokens (128-token router blocks) vs their first 4095 (64-token blocks)")
+    g1, g2 = run_gpu(big), run_gpu(small)
+    n = 4095
+    assert np.array_equal(g1["logits"][:n].view(np.uint32), g2["logits"].view(np.uint32))
+    assert np.array_equal(g1["topk_idx"][:n], g2["topk_idx"])
+    assert np.array_equal(g1["topk_w"][:n].view(np.uint32), g2["topk_w"].view(np.uint32))
+
+
 # ------------------------------------------------------------------ batch invariance
 
 @pytest.mark.parametrize("T_big", [300, 2048, 8192])
