@@ -175,7 +175,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   const int nbb = RB / 128;       // 128-byte K blocks of a weight row
   const int xstride = (XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
   uint8_t* xs = smem;
-  float* sxs = (float*)(smem + (BM + 1) * xstride);     // [BM][d/128] (FP8 only)
+  float* sxs = (float*)(smem + (BM + 1) * xstride);     // [d/128][BM] (FP8 only): one K block's rows adjacent
   float* wsc = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [2][d/128] gate, up block scales (FP8 only)
   float* red = wsc + (WT == 2 ? 2 * (a.d / 128) : 0);   // [waves][BM]
 
@@ -268,7 +268,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / cpr);
     float sv = 0.f, wv = 0.f;
     if (WT == 2 && first) {
-      sv = XQ ? a.sxa[(size_t)row_token(tid / nkb) * nkb + tid % nkb] : 1.0f;
+      sv = XQ ? a.sxa[(size_t)row_token(tid % BM) * nkb + min(tid / BM, nkb - 1)] : 1.0f;  // clamped: in bounds
       wv = tid < nkb ? sgp[tid] : sup[min(tid - nkb, nkb - 1)];  // the slice's weight block scales
     }
     if (first) {
@@ -299,14 +299,14 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
         *(v4i*)(dst + (i < nch ? c : 0) * 16) = x;
       }
     }
-    if (WT == 2 && first && tid < BM * nkb) sxs[tid] = tid / nkb <= rlast ? sv : 0.f;
+    if (WT == 2 && first && tid < BM * nkb) sxs[tid] = tid % BM <= rlast ? sv : 0.f;
     if (WT == 2 && first && tid < 2 * nkb) wsc[tid] = wv;
   };
   stage(tid, true);
   for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
   if (WT == 2) {
     for (int i = tid + NT; i < BM * nkb; i += NT)  // tall tiles or wide rows only
-      sxs[i] = i / nkb <= rlast ? (XQ ? a.sxa[(size_t)row_token(i / nkb) * nkb + i % nkb] : 1.0f) : 0.f;
+      sxs[i] = i % BM <= rlast ? (XQ ? a.sxa[(size_t)row_token(i % BM) * nkb + i / BM] : 1.0f) : 0.f;
   }
   __syncthreads();
 
@@ -333,7 +333,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
             e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
             e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[2], b[3]);
           }
-          const float cs = sxs[(c * 16 + lr) * nbb + bb] * wsc[r * nbb + bb];
+          const float cs = sxs[bb * BM + c * 16 + lr] * wsc[r * nbb + bb];
           acc[r][c] += kblock_e4m3_exact(wlo[sl][j], whi[sl][j], b) * cs;
         } else {
           const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
@@ -360,7 +360,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
         const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
         e4m3x16_to_bf16(*(const v4i*)bp, b[c][0], b[c][1]);
         e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[c][2], b[c][3]);
-        sx[c] = sxs[(c * 16 + lr) * nbb + bb];
+        sx[c] = sxs[bb * BM + c * 16 + lr];
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
@@ -492,7 +492,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   const int hstride_b = a.hstride * EH;
   const int lstride = Fg * 2 + 16;  // padded LDS row: h as bf16
   uint8_t* hs = smem;
-  float* shs = (float*)(smem + (BM + 1) * lstride);          // [BM][Fg/128] (FP8)
+  float* shs = (float*)(smem + (BM + 1) * lstride);          // [Fg/128][BM] (FP8): one K block's rows adjacent
   float* wrow = shs + (WT == 2 ? BM * (Fg / 128) : 0);       // [BM] routing weight
   int* orow = (int*)(wrow + BM);                             // [BM] partial-output row
   float* wsd = (float*)(orow + BM);                          // [1 or 2][Fg/128] W_down block scales
@@ -537,7 +537,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   const int o = a.ri.prow[hrow0 + min(tid, rlast)];
   float sv = 0.f, dv = 0.f;
   if (WT == 2) {
-    const float* shp = a.sh + (size_t)(hrow0 + min(tid / nkb, rlast)) * gpr + tid % nkb;
+    const float* shp = a.sh + (size_t)(hrow0 + min(tid % BM, rlast)) * gpr + min(tid / BM, nkb - 1);
     sv = !HQ ? 1.0f : COH ? __uint_as_float(load_coherent(shp)) : *shp;
     const float* sd = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)srow0 * nkb;
     dv = sd[min(tid, nsr * nkb - 1)];
@@ -588,10 +588,10 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
     stage_store(i0, hv);
   }
   if (WT == 2) {
-    if (tid < BM * nkb) shs[tid] = tid / nkb <= rlast ? sv : 0.f;
+    if (tid < BM * nkb) shs[tid] = tid % BM <= rlast ? sv : 0.f;
     for (int i = tid + NT; i < BM * nkb; i += NT) {  // tall tiles or wide rows only
-      const float* shp = a.sh + (size_t)(hrow0 + min(i / nkb, rlast)) * gpr + i % nkb;
-      shs[i] = i / nkb <= rlast ? (!HQ ? 1.0f : COH ? __uint_as_float(load_coherent(shp)) : *shp) : 0.f;
+      const float* shp = a.sh + (size_t)(hrow0 + min(i % BM, rlast)) * gpr + i / BM;
+      shs[i] = i % BM <= rlast ? (!HQ ? 1.0f : COH ? __uint_as_float(load_coherent(shp)) : *shp) : 0.f;
     }
     if (tid < nsr * nkb) wsd[tid] = dv;
   }
@@ -621,7 +621,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
           const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 16), *(const v4i*)(bp + 128),
                             *(const v4i*)(bp + 144)};
           // the wave's 16*RT <= 64 rows start at a multiple of 64: one 128-row scale block
-          acc[r][c] += kblock_bf16(wd, b) * (shs[(c * 16 + lr) * nbb + bb] * sdp[bb]);
+          acc[r][c] += kblock_bf16(wd, b) * (shs[bb * BM + c * 16 + lr] * sdp[bb]);
         } else {
           const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 128 + lk;
           const v4i blo = *(const v4i*)bp;
