@@ -530,7 +530,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   // weights (which need the pair rows).  Unconditional loads from clamped
   // addresses, zero by select, a spare LDS row for chunks past the tile: the
   // code is straight-line and every wait is exact.
-  constexpr int SB = 4;
+  constexpr int SB = BM == 32 ? 5 : 4;  // one batch covers a 32-row tile of h codes at F = 640
   const int hrow0 = tr.hrow0, rlast = tr.rows - 1;
   const int cpr = Fg * EH / 16, nch = BM * cpr, nkb = Fg / 128, gpr = a.hstride / 128;
   const uint8_t* hsrc = (const uint8_t*)a.h;
@@ -661,8 +661,10 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
     }
 }
 
+// (256, 2): at most 256 registers per lane, so the products accumulate in
+// vector registers rather than in accumulation registers read back one by one.
 template <int BM, int WT, int RT, bool A16 = false>
-__global__ __launch_bounds__(256) void down_mfma_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(256, 2) void down_mfma_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   down_block<BM, WT, RT, 4, false, A16>(a, blockIdx.x, smem);
 }
@@ -1054,7 +1056,7 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
 }
 
 template <int RT>
-__global__ __launch_bounds__(256) void down_u4_kernel(ExpertArgs a) {
+__global__ __launch_bounds__(256, 2) void down_u4_kernel(ExpertArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   down_block_u4<RT, 4, false>(a, blockIdx.x, smem);
 }
