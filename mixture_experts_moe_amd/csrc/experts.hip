@@ -141,6 +141,13 @@ __device__ __forceinline__ TileRows block_rows(const ExpertArgs& a, int b, int& 
 // ---------------------------------------------------------------------------
 constexpr int kGateUpWaves = 8;
 
+// Taller FP8 tiles stage their activations in LDS as bf16, one part of K at a
+// time (K blocks [0, n), then [n, d/128)), so the bf16 row is no wider than
+// the row of E4M3 codes it replaces and each activation element is decoded
+// once per block rather than once per wave.  n is even: the product loop takes
+// its single-block stages in pairs, and the switch falls between two pairs.
+__host__ __device__ constexpr int gateup_x_part_blocks(int nkb) { return nkb < 4 ? nkb : (nkb + 3) / 4 * 2; }
+
 // Device-coherent 32-bit store and load (agent-scope relaxed atomics: written
 // through to, and read from, the point where all XCDs see the same data), for
 // results one block hands to blocks on other XCDs within one launch.
@@ -164,6 +171,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   constexpr int EX = XQ ? 1 : 2;        // bytes per activation element in HBM
   constexpr int NT = kGateUpWaves * 64;
   constexpr bool XBF = WT == 1 || XB;  // activations in LDS as bf16 (else E4M3 codes)
+  constexpr bool XH = BM > 16 && XQ && !XB;  // bf16 activations in LDS by parts of K (gateup_x_part_blocks)
   int nb;
   const TileRows tr = block_rows(a, b, nb);
   if (tr.g < 0) return false;
@@ -173,7 +181,8 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   const int RB = a.d * EB;        // bytes per weight row in HBM
   const int RX = a.d * EX;        // bytes per activation row in HBM
   const int nbb = RB / 128;       // 128-byte K blocks of a weight row
-  const int xstride = (XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
+  const int nkh = XH ? gateup_x_part_blocks(a.d / 128) : a.d / 128;  // K blocks of the first part
+  const int xstride = (XH ? nkh * 256 : XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
   uint8_t* xs = smem;
   float* sxs = (float*)(smem + (BM + 1) * xstride);     // [d/128][BM] (FP8 only): one K block's rows adjacent
   float* wsc = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [2][d/128] gate, up block scales (FP8 only)
@@ -256,59 +265,88 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   // All loads are unconditional (clamped addresses, zero by select) and the
   // chunks past the tile land in a spare LDS row, so the code is straight-line
   // and every wait is exact.  The first batch of SB chunks per thread covers a
-  // 16-row tile at d = 2048.
+  // 16-row tile at d = 2048, and one part of a 32-row tile (XH).
+  // XH: part 0 of the rows is staged here, part 1 between two barriers when
+  // the products reach it (next_part).
   constexpr int SB = 4;
-  const int cpr = RX / 16, nch = BM * cpr, nkb = a.d / 128;
+  const int cpr = RX / 16, nkb = a.d / 128;
+  const int cps0 = XH ? nkh * 8 : cpr, cps1 = XH ? max(cpr - cps0, 1) : 1;  // chunks per row of part 0, 1
   const uint8_t* xa = (const uint8_t*)a.xa;
   const int rlast = tr.rows - 1;
   auto row_token = [&](int r) { return a.ri.tok[tr.hrow0 + min(r, rlast)]; };  // token of tile row r (clamped)
-  auto stage = [&](int i0, bool first) {
-    int tk[SB];
+  auto chunk_tokens = [&](int i0, int part, int (&tk)[SB]) {
 #pragma unroll
-    for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / cpr);
+    for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / (part ? cps1 : cps0));
+  };
+  auto chunk_load = [&](int i0, int part, const int (&tk)[SB], v4i (&v)[SB]) {
+    const int cps = part ? cps1 : cps0, c0 = part ? cps0 : 0;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int c = min(c0 + (i0 + u * NT) % cps, cpr - 1);  // clamped: in bounds
+      v[u] = *(const v4i*)(xa + (size_t)tk[u] * RX + c * 16);
+    }
+  };
+  auto chunk_store = [&](int i0, int part, const v4i (&v)[SB]) {
+    const int cps = part ? cps1 : cps0, nchp = BM * cps;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int i = i0 + u * NT, r = i / cps, c = i % cps;
+      const bool live = i < nchp && r <= rlast;
+      const v4i z = {0, 0, 0, 0};
+      const v4i x = live ? v[u] : z;
+      uint8_t* dst = xs + (i < nchp ? r : BM) * xstride;
+      if constexpr (XQ && (XB || XH)) {  // E4M3 codes -> bf16 once per block (exact)
+        v4i lo, hi;
+        e4m3x16_to_bf16(x, lo, hi);
+        *(v4i*)(dst + (i < nchp ? c : 0) * 32) = lo;
+        *(v4i*)(dst + (i < nchp ? c : 0) * 32 + 16) = hi;
+      } else {
+        *(v4i*)(dst + (i < nchp ? c : 0) * 16) = x;
+      }
+    }
+  };
+  {
+    int tk[SB];
+    chunk_tokens(tid, 0, tk);
     float sv = 0.f, wv = 0.f;
-    if (WT == 2 && first) {
+    if (WT == 2) {
       sv = XQ ? a.sxa[(size_t)row_token(tid % BM) * nkb + min(tid / BM, nkb - 1)] : 1.0f;  // clamped: in bounds
       wv = tid < nkb ? sgp[tid] : sup[min(tid - nkb, nkb - 1)];  // the slice's weight block scales
     }
-    if (first) {
-      __builtin_amdgcn_sched_barrier(0);
-      load(Ic<0>{}, 0);
-      load(Ic<1>{}, 1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    load(Ic<0>{}, 0);
+    load(Ic<1>{}, 1);
+    __builtin_amdgcn_sched_barrier(0);
     v4i v[SB];
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, c = i % cpr;
-      v[u] = *(const v4i*)(xa + (size_t)tk[u] * RX + c * 16);
-    }
-#pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
-      const bool live = i < nch && r <= rlast;
-      const v4i z = {0, 0, 0, 0};
-      const v4i x = live ? v[u] : z;
-      uint8_t* dst = xs + (i < nch ? r : BM) * xstride;
-      if constexpr (XQ && XB) {  // E4M3 codes -> bf16 once per block (exact)
-        v4i lo, hi;
-        e4m3x16_to_bf16(x, lo, hi);
-        *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
-        *(v4i*)(dst + (i < nch ? c : 0) * 32 + 16) = hi;
-      } else {
-        *(v4i*)(dst + (i < nch ? c : 0) * 16) = x;
-      }
-    }
-    if (WT == 2 && first && tid < BM * nkb) sxs[tid] = tid % BM <= rlast ? sv : 0.f;
-    if (WT == 2 && first && tid < 2 * nkb) wsc[tid] = wv;
-  };
-  stage(tid, true);
-  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
+    chunk_load(tid, 0, tk, v);
+    chunk_store(tid, 0, v);
+    if (WT == 2 && tid < BM * nkb) sxs[tid] = tid % BM <= rlast ? sv : 0.f;
+    if (WT == 2 && tid < 2 * nkb) wsc[tid] = wv;
+  }
+  for (int i0 = tid + NT * SB; i0 < BM * cps0; i0 += NT * SB) {  // tall tiles or wide rows only
+    int tk[SB];
+    v4i v[SB];
+    chunk_tokens(i0, 0, tk);
+    chunk_load(i0, 0, tk, v);
+    chunk_store(i0, 0, v);
+  }
   if (WT == 2) {
     for (int i = tid + NT; i < BM * nkb; i += NT)  // tall tiles or wide rows only
       sxs[i] = i % BM <= rlast ? (XQ ? a.sxa[(size_t)row_token(i % BM) * nkb + i / BM] : 1.0f) : 0.f;
   }
   __syncthreads();
+  // XH: every wave is past part 0's products; part 1 replaces it in LDS
+  auto next_part = [&]() {
+    __syncthreads();
+    for (int i0 = tid; i0 < BM * cps1; i0 += NT * SB) {
+      int tk[SB];
+      v4i v[SB];
+      chunk_tokens(i0, 1, tk);
+      chunk_load(i0, 1, tk, v);
+      chunk_store(i0, 1, v);
+    }
+    __syncthreads();
+  };
 
   auto compute_run = [&](auto R, auto S, int q) {
     constexpr int r = decltype(R)::value, sl = decltype(S)::value;
@@ -346,7 +384,8 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     }
   };
   // taller tiles: both tiles' blocks of group q; each activation chunk and each
-  // weight block decoded from its E4M3 codes once
+  // weight block decoded from its E4M3 codes once (XH: the activations were
+  // decoded when staged)
   auto compute_pair = [&](auto S, int q) {
     constexpr int sl = decltype(S)::value;
 #pragma unroll
@@ -357,9 +396,18 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       float sx[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
-        e4m3x16_to_bf16(*(const v4i*)bp, b[c][0], b[c][1]);
-        e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[c][2], b[c][3]);
+        if constexpr (XH) {  // bf16, in the weight codes' K order (as for XB)
+          const int bl = bb < nkh ? bb : bb - nkh;  // K block within the staged part
+          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bl * 256 + 2 * lk;
+          b[c][0] = *(const v4i*)bp;
+          b[c][1] = *(const v4i*)(bp + 16);
+          b[c][2] = *(const v4i*)(bp + 128);
+          b[c][3] = *(const v4i*)(bp + 144);
+        } else {
+          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
+          e4m3x16_to_bf16(*(const v4i*)bp, b[c][0], b[c][1]);
+          e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[c][2], b[c][3]);
+        }
         sx[c] = sxs[bb * BM + c * 16 + lr];
       }
 #pragma unroll
@@ -381,13 +429,17 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       compute_run(Ic<1>{}, S, st - nq);
     }
   };
+  static_assert(!XH || KGP == 1, "the part switch falls on a stage boundary");
+  const int st_part = XH && nkh < nkb ? nkh : -1;  // first stage of part 1 (even)
   int st = 0;
   for (; st + 2 < ns; st += 2) {  // both loads of the body are in range
+    if (st == st_part) next_part();
     compute(Ic<0>{}, st);
     load(Ic<0>{}, st + 2);
     compute(Ic<1>{}, st + 1);
     load(Ic<1>{}, st + 3);
   }
+  if (st == st_part) next_part();
   compute(Ic<0>{}, st);
   if (st + 1 < ns) compute(Ic<1>{}, st + 1);  // taller tiles: the number of groups may be odd
 
@@ -1298,8 +1350,8 @@ static hipError_t launch_dyn(K kernel, dim3 grid, size_t lds, hipStream_t st, co
   return hipGetLastError();
 }
 
-// Activations in LDS as bf16 for 16-row tiles; taller tiles keep the E4M3 codes
-// (decoded per use) so that two blocks fit a CU.
+// Activations in LDS as bf16 for 16-row tiles; taller FP8 tiles stage them as
+// bf16 by parts of K (gateup_x_part_blocks), so that two blocks fit a CU.
 static bool gateup_x_bf16(int BM, int wmode) { return wmode != 2 || BM <= 16; }
 
 // wmode: the moe_dtype of the weights (0 f32, 1 bf16, 2 FP8, 3 FP8 as W8A16,
@@ -1307,7 +1359,8 @@ static bool gateup_x_bf16(int BM, int wmode) { return wmode != 2 || BM <= 16; }
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
   if (wmode == 4) return (size_t)(BM + 1) * (d * 2 + 16) + (size_t)(d / 64) * BM * 4;
-  size_t b = (size_t)(BM + 1) * ((gateup_x_bf16(BM, wmode) ? d * 2 : d) + 16);  // plus a spare row
+  const int xrow = gateup_x_bf16(BM, wmode) ? d * 2 : gateup_x_part_blocks(d / 128) * 256;
+  size_t b = (size_t)(BM + 1) * (xrow + 16);  // plus a spare row
   if (wmode >= 2) b += (size_t)BM * (d / 128) * 4 + 2 * (d / 128) * 4;
   return b + kGateUpWaves * BM * 4;
 }
