@@ -492,6 +492,28 @@ def test_forward_repeats_on_one_plan():
         assert torch.equal(ys[0].view(torch.int16), y.view(torch.int16))
 
 
+def test_routing_calls_share_a_plan():
+    """One plan buffer, sized for the largest shape, serves routing and forward
+    calls of any length and routing path in any order (short batches, the
+    per-chunk path, 32-row tiles with XCD schedules): each result equals the one
+    on a fresh plan, bit for bit."""
+    cases = [("decode_t32", None), ("prefill_t2048", 100), ("decode_t32", None), ("prefill_t2048", 2048),
+             ("prefill_t2048", 48), ("decode_t32", None), ("prefill_t2048", 1)]
+    inps = [synth.make_inputs(c) if T is None else synth.make_inputs(c, T=T) for c, T in cases]
+    plan = torch.empty(max(moe.plan_bytes(moe.shape_of(i["shape"])) for i in inps), dtype=torch.uint8, device=DEV)
+    for inp in inps:
+        s = inp["shape"]
+        say(f"T={s.T}: fresh plan vs the shared one")
+        fresh = run_gpu(inp)
+        r = moe.alloc_routing(moe.shape_of(s), DEV)
+        r.plan = plan
+        shared = run_gpu(inp, routing=r)
+        for n in ("topk_idx", "counts", "offsets", "perm", "inv_perm", "status"):
+            assert np.array_equal(fresh[n], shared[n]), n
+        for n in ("topk_w", "logits", "y"):
+            assert np.array_equal(fresh[n].view(np.uint32), shared[n].view(np.uint32)), n
+
+
 def test_forward_wait_timeout_is_reported_and_sticky():
     """The one-launch expert kernel's bounded wait, forced to run out from the
     host (MOE_FORWARD_TEST_WAIT_TIMEOUT: each down block waits for one gate/up
