@@ -9,7 +9,10 @@ C ABI, against the oracle with the parity bars of the main workloads.
     ten 16-row tiles per expert;
   * the most experts and the largest top_k (512 experts, top 8: eight candidates
     per lane in the selection), with the one-block dispatch (800 pairs) and the
-    chunked one (2,400 pairs), free and forced.
+    chunked one (2,400 pairs), free and forced;
+  * the longest batch timed by the bench: the decode layer at T = 32768 with
+    free routing (128-token router blocks, 32-row tiles, about 16 per expert),
+    the dispatch checked whole and the outputs on sampled tokens.
 Layers: weights N(0, 0.02) quantised to E4M3 with 128x128 block scales, router
 weights N(0, 0.05), activations N(0, 1) in bf16 (the recipe of the main
 workloads at other sizes).
@@ -20,8 +23,8 @@ import pytest
 from mixture_experts_moe_amd import moe, synth
 from oracle import moe_oracle as O
 
-from test_gpu_parity import (DEV, W_ABS, check_dispatch, check_logits, check_y, route_agreement, run_gpu, say,
-                             selection_scores)
+from test_gpu_parity import (DEV, W_ABS, check_dispatch, check_dispatch_properties, check_logits, check_y,
+                             route_agreement, run_gpu, say, selection_scores)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,3 +115,32 @@ def test_most_experts_top8(T, kind):
     say(f"E={E} k={k} T={T} ({T * k} pairs) {kind}")
     g = run_gpu(inp, forced=forced, dev=_dev(inp))
     _check(inp, g, forced=forced)
+
+
+def test_long_prefill_t32768_sampled():
+    """T = 32768 on the decode layer, free routing, as the bench times it: the
+    dispatch is the stable sort of the GPU's own ids (whole batch); logits, ids,
+    weights and y against the oracle on every 64th token, the last token, and
+    the last 32 rows (the ragged tail tile) of the three most loaded experts."""
+    inp = synth.make_inputs("prefill_t32768")
+    s = inp["shape"]
+    say(f"prefill_t32768: T={s.T} free routing")
+    g = run_gpu(inp)
+    check_dispatch_properties(g, s.E)
+    counts = g["counts"]
+    say(f"  expert load: max {counts.max()} mean {counts.mean():.1f} min {counts.min()}")
+    L = O.Layer(inp)
+    heavy = np.argsort(-counts, kind="stable")[:3]
+    tail = np.concatenate([g["perm"][max(g["offsets"][e], g["offsets"][e + 1] - 32):g["offsets"][e + 1]] // s.k
+                           for e in heavy])
+    tok = np.unique(np.concatenate([np.arange(0, s.T, 64), tail, [s.T - 1]]))
+    _, lg, idx, w = O.route_threads(L, tok)
+    check_logits(g["logits"][tok], lg)
+    bad, ex = route_agreement(g["topk_idx"][tok], idx, selection_scores(inp, lg), s.k)
+    say(f"  ids on {len(tok)} sampled tokens: {bad} mismatches, {ex} exempt")
+    assert bad == 0
+    same = (g["topk_idx"][tok] == idx).all(axis=1)
+    assert np.max(np.abs(g["topk_w"][tok][same] - w[same])) <= W_ABS
+    ts = tok[same]
+    _, acc_ref = O.forward_threads(L, idx[same], w[same], ts)
+    check_y(g["y"][ts], acc_ref)
