@@ -170,7 +170,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   constexpr int EB = WT == 2 ? 1 : 2;   // bytes per weight element
   constexpr int EX = XQ ? 1 : 2;        // bytes per activation element in HBM
   constexpr int NT = kGateUpWaves * 64;
-  constexpr bool XBF = WT == 1 || XB;  // activations in LDS as bf16 (else E4M3 codes)
+  constexpr bool XBF = WT == 1 || XB;  // whole activation rows in LDS as bf16 (else XH, or E4M3 codes)
   constexpr bool XH = BM > 16 && XQ && !XB;  // bf16 activations in LDS by parts of K (gateup_x_part_blocks)
   int nb;
   const TileRows tr = block_rows(a, b, nb);
@@ -228,7 +228,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   constexpr bool SEQ = BM == 16;
   constexpr int KG = SEQ ? MOE_GU_KG : MOE_GU_KG_TALL;
   constexpr int KGP = KG / 2;  // blocks per tile in a taller-tile stage
-  static_assert(SEQ || (KG % 2 == 0 && WT == 2 && !XB), "taller tiles: FP8 codes, a stage split between the tiles");
+  static_assert(SEQ || (KG % 2 == 0 && WT == 2 && !XB), "taller tiles: FP8 weights, a stage split between the tiles");
   const int nq = SEQ ? (nbb + KG - 1) / KG : (nbb + KGP - 1) / KGP;
   const int ns = SEQ ? 2 * nq : nq;
   v4i wlo[2][KG], whi[2][KG];
