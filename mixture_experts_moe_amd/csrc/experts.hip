@@ -262,9 +262,9 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   // the activation and weight block scales, then the weight stream, then the
   // activation rows (which need the tokens).  The scales go to LDS, so the
   // product loop reads no global memory besides the weight stream.
-  // All loads are unconditional (clamped addresses, zero by select) and the
-  // chunks past the tile land in a spare LDS row, so the code is straight-line
-  // and every wait is exact.  The first batch of SB chunks per thread covers a
+  // All loads are unconditional (clamped addresses) and the chunks past the
+  // tile land in a spare LDS row, so the code is straight-line and every wait
+  // is exact.  The first batch of SB chunks per thread covers a
   // 16-row tile at d = 2048, and one part of a 32-row tile (XH).
   // XH: part 0 of the rows is staged here, part 1 between two barriers when
   // the products reach it (next_part).
@@ -274,40 +274,67 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   const uint8_t* xa = (const uint8_t*)a.xa;
   const int rlast = tr.rows - 1;
   auto row_token = [&](int r) { return a.ri.tok[tr.hrow0 + min(r, rlast)]; };  // token of tile row r (clamped)
-  auto chunk_tokens = [&](int i0, int part, int (&tk)[SB]) {
-#pragma unroll
-    for (int u = 0; u < SB; ++u) tk[u] = row_token((i0 + u * NT) / (part ? cps1 : cps0));
+  // Chunk i of a part (cps chunks per row) is chunk i % cps of row i / cps.  A
+  // thread's batch is chunks i0 + u*NT, whose row and chunk advance by NT / cps
+  // and NT % cps: one division per batch rather than two per chunk.
+  struct Batch {
+    int r[SB], c[SB];
   };
-  auto chunk_load = [&](int i0, int part, const int (&tk)[SB], v4i (&v)[SB]) {
-    const int cps = part ? cps1 : cps0, c0 = part ? cps0 : 0;
+  auto chunk_walk = [&](int i0, int part) {
+    const int cps = part ? cps1 : cps0;
+    const int dr = NT / cps, dc = NT - dr * cps;
+    int r = i0 / cps, c = i0 - r * cps;
+    Batch bt;
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int c = min(c0 + (i0 + u * NT) % cps, cpr - 1);  // clamped: in bounds
+      bt.r[u] = r;
+      bt.c[u] = c;
+      r += dr;
+      c += dc;
+      const bool wrap = c >= cps;
+      r += wrap ? 1 : 0;
+      c -= wrap ? cps : 0;
+    }
+    return bt;
+  };
+  auto chunk_tokens = [&](const Batch& bt, int (&tk)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) tk[u] = row_token(bt.r[u]);
+  };
+  auto chunk_load = [&](const Batch& bt, int part, const int (&tk)[SB], v4i (&v)[SB]) {
+    const int c0 = part ? cps0 : 0;
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const int c = min(c0 + bt.c[u], cpr - 1);  // clamped: in bounds
       v[u] = *(const v4i*)(xa + (size_t)tk[u] * RX + c * 16);
     }
   };
-  auto chunk_store = [&](int i0, int part, const v4i (&v)[SB]) {
-    const int cps = part ? cps1 : cps0, nchp = BM * cps;
+  // Rows past the tile (r > rlast) hold copies of the last row (row_token
+  // clamps): their products are never stored, and no output row reads another
+  // row's activations.  Chunks past the part's last row (r >= BM) go to the
+  // spare row.
+  auto chunk_store = [&](const Batch& bt, const v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = i / cps, c = i % cps;
-      const bool live = i < nchp && r <= rlast;
-      const v4i z = {0, 0, 0, 0};
-      const v4i x = live ? v[u] : z;
-      uint8_t* dst = xs + (i < nchp ? r : BM) * xstride;
+      const int r = bt.r[u];
+      const bool in = r < BM;
+      const v4i x = v[u];
+      uint8_t* dst = xs + (in ? r : BM) * xstride;
+      const int c = in ? bt.c[u] : 0;
       if constexpr (XQ && (XB || XH)) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
         e4m3x16_to_bf16(x, lo, hi);
-        *(v4i*)(dst + (i < nchp ? c : 0) * 32) = lo;
-        *(v4i*)(dst + (i < nchp ? c : 0) * 32 + 16) = hi;
+        *(v4i*)(dst + c * 32) = lo;
+        *(v4i*)(dst + c * 32 + 16) = hi;
       } else {
-        *(v4i*)(dst + (i < nchp ? c : 0) * 16) = x;
+        *(v4i*)(dst + c * 16) = x;
       }
     }
   };
   {
     int tk[SB];
-    chunk_tokens(tid, 0, tk);
+    const Batch bt = chunk_walk(tid, 0);
+    chunk_tokens(bt, tk);
     float sv = 0.f, wv = 0.f;
     if (WT == 2) {
       sv = XQ ? a.sxa[(size_t)row_token(tid % BM) * nkb + min(tid / BM, nkb - 1)] : 1.0f;  // clamped: in bounds
@@ -318,17 +345,18 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     load(Ic<1>{}, 1);
     __builtin_amdgcn_sched_barrier(0);
     v4i v[SB];
-    chunk_load(tid, 0, tk, v);
-    chunk_store(tid, 0, v);
+    chunk_load(bt, 0, tk, v);
+    chunk_store(bt, v);
     if (WT == 2 && tid < BM * nkb) sxs[tid] = tid % BM <= rlast ? sv : 0.f;
     if (WT == 2 && tid < 2 * nkb) wsc[tid] = wv;
   }
   for (int i0 = tid + NT * SB; i0 < BM * cps0; i0 += NT * SB) {  // tall tiles or wide rows only
     int tk[SB];
     v4i v[SB];
-    chunk_tokens(i0, 0, tk);
-    chunk_load(i0, 0, tk, v);
-    chunk_store(i0, 0, v);
+    const Batch bt = chunk_walk(i0, 0);
+    chunk_tokens(bt, tk);
+    chunk_load(bt, 0, tk, v);
+    chunk_store(bt, v);
   }
   if (WT == 2) {
     for (int i = tid + NT; i < BM * nkb; i += NT)  // tall tiles or wide rows only
@@ -341,9 +369,10 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     for (int i0 = tid; i0 < BM * cps1; i0 += NT * SB) {
       int tk[SB];
       v4i v[SB];
-      chunk_tokens(i0, 1, tk);
-      chunk_load(i0, 1, tk, v);
-      chunk_store(i0, 1, v);
+      const Batch bt = chunk_walk(i0, 1);
+      chunk_tokens(bt, tk);
+      chunk_load(bt, 1, tk, v);
+      chunk_store(bt, v);
     }
     __syncthreads();
   };
@@ -450,7 +479,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float gv = acc[0][c][i], uv = acc[1][c][i];
-      h[c][i] = gv / (1.0f + expf(-gv)) * uv;
+      h[c][i] = silu_f32(gv) * uv;
     }
   const int hrow0 = tr.hrow0;
   const int fcol = f0 + 4 * (lane >> 4);
@@ -580,8 +609,8 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   // the wait counter goes): the pair rows, the h scales, the W_down scales and
   // the first batch of h rows, then the weight stream, then the routing
   // weights (which need the pair rows).  Unconditional loads from clamped
-  // addresses, zero by select, a spare LDS row for chunks past the tile: the
-  // code is straight-line and every wait is exact.
+  // addresses and a spare LDS row for chunks past the tile: the code is
+  // straight-line and every wait is exact.
   constexpr int SB = BM == 32 ? 5 : 4;  // one batch covers a 32-row tile of h codes at F = 640
   const int hrow0 = tr.hrow0, rlast = tr.rows - 1;
   const int cpr = Fg * EH / 16, nch = BM * cpr, nkb = Fg / 128, gpr = a.hstride / 128;
@@ -594,14 +623,35 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
     const float* sd = (tr.shared ? a.ssd : a.sd + (size_t)tr.g * (a.d / 128) * nkb) + (size_t)srow0 * nkb;
     dv = sd[min(tid, nsr * nkb - 1)];
   }
-  auto stage_load = [&](int i0, v4i (&v)[SB]) {
+  // Chunk i is chunk i % cpr of row i / cpr.  A thread's batch is chunks
+  // i0 + u*NT, whose row and chunk advance by NT / cpr and NT % cpr: one
+  // division per batch rather than two per chunk.
+  struct Batch {
+    int r[SB], c[SB];
+  };
+  auto stage_walk = [&](int i0) {
+    const int dr = NT / cpr, dc = NT - dr * cpr;
+    int r = i0 / cpr, c = i0 - r * cpr;
+    Batch bt;
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = min(i / cpr, rlast), c = i % cpr;
-      const uint8_t* hp = hsrc + (size_t)(hrow0 + r) * hstride_b + c * 16;
+      bt.r[u] = r;
+      bt.c[u] = c;
+      r += dr;
+      c += dc;
+      const bool wrap = c >= cpr;
+      r += wrap ? 1 : 0;
+      c -= wrap ? cpr : 0;
+    }
+    return bt;
+  };
+  auto stage_load = [&](const Batch& bt, v4i (&v)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const uint8_t* hp = hsrc + (size_t)(hrow0 + min(bt.r[u], rlast)) * hstride_b + bt.c[u] * 16;
       if constexpr (COH) {  // coherent loads skip the L2: fetch only chunks of live rows
         v[u] = v4i{0, 0, 0, 0};
-        if (i < nch && i / cpr <= rlast)
+        if (bt.r[u] <= rlast)
           v[u] = v4i{(int)load_coherent(hp), (int)load_coherent(hp + 4), (int)load_coherent(hp + 8),
                      (int)load_coherent(hp + 12)};
       } else {
@@ -609,35 +659,38 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
       }
     }
   };
-  auto stage_store = [&](int i0, const v4i (&v)[SB]) {
+  // Rows past the tile (r > rlast) hold copies of the last row (clamped loads;
+  // zeros in the coherent path): their products are never stored.  Chunks
+  // past the tile's last row (r >= BM) go to the spare row.
+  auto stage_store = [&](const Batch& bt, const v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
-      const bool live = i < nch && r <= rlast;
-      const v4i z = {0, 0, 0, 0};
-      const v4i x = live ? v[u] : z;
-      uint8_t* dst = hs + (i < nch ? r : BM) * lstride;
+      const bool in = bt.r[u] < BM;
+      uint8_t* dst = hs + (in ? bt.r[u] : BM) * lstride;
+      const int c = in ? bt.c[u] : 0;
       if constexpr (HQ) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
-        e4m3x16_to_bf16(x, lo, hi);
-        *(v4i*)(dst + (i < nch ? c : 0) * 32) = lo;
-        *(v4i*)(dst + (i < nch ? c : 0) * 32 + 16) = hi;
+        e4m3x16_to_bf16(v[u], lo, hi);
+        *(v4i*)(dst + c * 32) = lo;
+        *(v4i*)(dst + c * 32 + 16) = hi;
       } else {
-        *(v4i*)(dst + (i < nch ? c : 0) * 16) = x;
+        *(v4i*)(dst + c * 16) = v[u];
       }
     }
   };
   v4i hv[SB];
-  stage_load(tid, hv);
+  const Batch bt0 = stage_walk(tid);
+  stage_load(bt0, hv);
   __builtin_amdgcn_sched_barrier(0);
   load(0, 0, 0);
   if (RT > 1) load(1, 1, 0);
   __builtin_amdgcn_sched_barrier(0);
   const float wt = a.ri.w[hrow0 + min(tid, rlast)];
-  stage_store(tid, hv);
+  stage_store(bt0, hv);
   for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) {  // tall tiles or wide rows only
-    stage_load(i0, hv);
-    stage_store(i0, hv);
+    const Batch bt = stage_walk(i0);
+    stage_load(bt, hv);
+    stage_store(bt, hv);
   }
   if (WT == 2) {
     if (tid < BM * nkb) shs[tid] = tid % BM <= rlast ? sv : 0.f;
@@ -939,7 +992,7 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const float gv = acc[0][v], uv = acc[1][v];
-    hv[v] = gv / (1.0f + expf(-gv)) * uv;
+    hv[v] = silu_f32(gv) * uv;
   }
   hv = quad_transpose(hv);
   const int rr = 4 * q4 + (lane & 3);
