@@ -76,24 +76,51 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const void* __restri
 // row-major layout lane l reads row (16*rt + l%16) at byte 16*(l/16) of each
 // 128-byte K block (and 64 further for the upper half); in the tiled layout the
 // same bytes sit at 16*l of the tile's 2 KB (upper half: +1024).
+// The stream goes through a buffer resource over the wave's n16 tiles of 16
+// rows (base and size wave-uniform): the lane's byte offset is fixed and the K
+// block's offset is a scalar, so a load costs no vector address arithmetic.
+// Offsets past the resource's size would read zeros, never another buffer.
 struct WeightStream {
-  const uint8_t* p;  // this lane's first byte in K block 0 of the tile
-  int kb_stride;     // bytes from one K block to the next
-  int hi_off;        // bytes from the lower to the upper 64-byte half
+  __amdgpu_buffer_rsrc_t r;  // the wave's rows
+  int voff;                  // this lane's first byte in K block 0 of its first tile
+  int kb_stride;             // bytes from one K block to the next
+  int hi_off;                // bytes from the lower to the upper 64-byte half
+  int tile_step;             // bytes from one 16-row tile to the next
 };
 __device__ __forceinline__ WeightStream weight_stream(const uint8_t* mat, int row_bytes, int row0, bool tiled,
-                                                      int lane) {
+                                                      int lane, int n16 = 1) {
   WeightStream w;
+  const uint8_t* base = mat + (size_t)row0 * row_bytes;  // the tiled layout keeps a 16-row tile's bytes together
+  w.r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, n16 * 16 * row_bytes, 0x00020000);
   if (tiled) {
-    w.p = mat + (size_t)(row0 / 16) * (row_bytes / 128) * 2048 + lane * 16;
+    w.voff = lane * 16;
     w.kb_stride = 2048;
     w.hi_off = 1024;
+    w.tile_step = (row_bytes / 128) * 2048;
   } else {
-    w.p = mat + (size_t)(row0 + (lane & 15)) * row_bytes + (lane >> 4) * 16;
+    w.voff = (lane & 15) * row_bytes + (lane >> 4) * 16;
     w.kb_stride = 128;
     w.hi_off = 64;
+    w.tile_step = 16 * row_bytes;
   }
   return w;
+}
+// 16 bytes of the stream at scalar offset soff; NT: non-temporal.
+template <bool NT>
+__device__ __forceinline__ v4i stream_load(const WeightStream& w, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(w.r, w.voff, soff, NT ? 2 : 0));
+}
+// A buffer resource over `bytes` bytes from a wave-uniform base, and 16- and
+// 8-byte loads at a lane offset plus a scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_over(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+template <bool NT>
+__device__ __forceinline__ v4i buffer_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, NT ? 2 : 0));
+}
+__device__ __forceinline__ uint2 buffer_load8(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
 // Rows of one tile: for each of its BM rows, the activation (token) row, the
@@ -184,9 +211,10 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   const int nkh = XH ? gateup_x_part_blocks(a.d / 128) : a.d / 128;  // K blocks of the first part
   const int xstride = (XH ? nkh * 256 : XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
   uint8_t* xs = smem;
-  float* sxs = (float*)(smem + (BM + 1) * xstride);     // [d/128][BM] (FP8 only): one K block's rows adjacent
-  float* wsc = sxs + (WT == 2 ? BM * (a.d / 128) : 0);  // [2][d/128] gate, up block scales (FP8 only)
-  float* red = wsc + (WT == 2 ? 2 * (a.d / 128) : 0);   // [waves][BM]
+  // [2][d/128][BM] (FP8 only): per matrix (gate, up), K block and row, the
+  // activation scale times the weight block scale; one K block's rows adjacent
+  float* csc = (float*)(smem + (BM + 1) * xstride);
+  float* red = csc + (WT == 2 ? 2 * BM * (a.d / 128) : 0);  // [waves][BM]
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lk = (lane >> 4) * 16;
@@ -237,31 +265,29 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     if constexpr (SEQ) {
       const bool up = st >= nq;
       const int q = up ? st - nq : st;
-      const uint8_t* base = up ? ws[1].p : ws[0].p;
+      const WeightStream& w = ws[up ? 1 : 0];
 #pragma unroll
       for (int j = 0; j < KG; ++j) {
-        const int kb = min(q * KG + j, nbb - 1);
-        const uint8_t* p = base + (size_t)kb * ws[0].kb_stride;
-        wlo[sl][j] = stream_load<WT == 2>(p);
-        whi[sl][j] = stream_load<WT == 2>(p + ws[0].hi_off);
+        const int so = min(q * KG + j, nbb - 1) * ws[0].kb_stride;
+        wlo[sl][j] = stream_load<WT == 2>(w, so);
+        whi[sl][j] = stream_load<WT == 2>(w, so + ws[0].hi_off);
       }
     } else {
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int j = 0; j < KGP; ++j) {
-          const int kb = min(st * KGP + j, nbb - 1);
-          const uint8_t* p = ws[m].p + (size_t)kb * ws[0].kb_stride;
-          wlo[sl][m * KGP + j] = stream_load<false>(p);
-          whi[sl][m * KGP + j] = stream_load<false>(p + ws[0].hi_off);
+          const int so = min(st * KGP + j, nbb - 1) * ws[0].kb_stride;
+          wlo[sl][m * KGP + j] = stream_load<false>(ws[m], so);
+          whi[sl][m * KGP + j] = stream_load<false>(ws[m], so + ws[0].hi_off);
         }
     }
   };
   // Staging.  Loads complete in issue order as far as the wait counter goes,
   // so the order is pinned: the token of each row this thread stages (perm),
   // the activation and weight block scales, then the weight stream, then the
-  // activation rows (which need the tokens).  The scales go to LDS, so the
-  // product loop reads no global memory besides the weight stream.
+  // activation rows (which need the tokens).  The scale products go to LDS, so
+  // the product loop reads no global memory besides the weight stream.
   // All loads are unconditional (clamped addresses) and the chunks past the
   // tile land in a spare LDS row, so the code is straight-line and every wait
   // is exact.  The first batch of SB chunks per thread covers a
@@ -335,10 +361,12 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     int tk[SB];
     const Batch bt = chunk_walk(tid, 0);
     chunk_tokens(bt, tk);
-    float sv = 0.f, wv = 0.f;
-    if (WT == 2) {
-      sv = XQ ? a.sxa[(size_t)row_token(tid % BM) * nkb + min(tid / BM, nkb - 1)] : 1.0f;  // clamped: in bounds
-      wv = tid < nkb ? sgp[tid] : sup[min(tid - nkb, nkb - 1)];  // the slice's weight block scales
+    float sv = 0.f, gv = 0.f, uv = 0.f;
+    if (WT == 2) {  // row tid % BM, K block tid / BM (clamped: in bounds)
+      const int kb = min(tid / BM, nkb - 1);
+      sv = XQ ? a.sxa[(size_t)row_token(tid % BM) * nkb + kb] : 1.0f;
+      gv = sgp[kb];  // the slice's weight block scales
+      uv = sup[kb];
     }
     __builtin_amdgcn_sched_barrier(0);
     load(Ic<0>{}, 0);
@@ -347,8 +375,11 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     v4i v[SB];
     chunk_load(bt, 0, tk, v);
     chunk_store(bt, v);
-    if (WT == 2 && tid < BM * nkb) sxs[tid] = tid % BM <= rlast ? sv : 0.f;
-    if (WT == 2 && tid < 2 * nkb) wsc[tid] = wv;
+    if (WT == 2 && tid < BM * nkb) {
+      const float sx = tid % BM <= rlast ? sv : 0.f;
+      csc[tid] = sx * gv;
+      csc[BM * nkb + tid] = sx * uv;
+    }
   }
   for (int i0 = tid + NT * SB; i0 < BM * cps0; i0 += NT * SB) {  // tall tiles or wide rows only
     int tk[SB];
@@ -359,8 +390,11 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
     chunk_store(bt, v);
   }
   if (WT == 2) {
-    for (int i = tid + NT; i < BM * nkb; i += NT)  // tall tiles or wide rows only
-      sxs[i] = i % BM <= rlast ? (XQ ? a.sxa[(size_t)row_token(i % BM) * nkb + i / BM] : 1.0f) : 0.f;
+    for (int i = tid + NT; i < BM * nkb; i += NT) {  // tall tiles or wide rows only
+      const float sx = i % BM <= rlast ? (XQ ? a.sxa[(size_t)row_token(i % BM) * nkb + i / BM] : 1.0f) : 0.f;
+      csc[i] = sx * sgp[i / BM];
+      csc[BM * nkb + i] = sx * sup[i / BM];
+    }
   }
   __syncthreads();
   // XH: every wave is past part 0's products; part 1 replaces it in LDS
@@ -400,8 +434,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
             e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
             e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[2], b[3]);
           }
-          const float cs = sxs[bb * BM + c * 16 + lr] * wsc[r * nbb + bb];
-          acc[r][c] += kblock_e4m3_exact(wlo[sl][j], whi[sl][j], b) * cs;
+          acc[r][c] += kblock_e4m3_exact(wlo[sl][j], whi[sl][j], b) * csc[(r * nbb + bb) * BM + c * 16 + lr];
         } else {
           const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
           const v4i blo = *(const v4i*)bp;
@@ -422,7 +455,6 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       const int bb = q * KGP + j;
       if (bb >= nbb) break;
       v4i b[NC][4];
-      float sx[NC];
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if constexpr (XH) {  // bf16, in the weight codes' K order (as for XB)
@@ -437,15 +469,13 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
           e4m3x16_to_bf16(*(const v4i*)bp, b[c][0], b[c][1]);
           e4m3x16_to_bf16(*(const v4i*)(bp + 64), b[c][2], b[c][3]);
         }
-        sx[c] = sxs[bb * BM + c * 16 + lr];
       }
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         v4i w[4];
         kblock_decode(wlo[sl][m * KGP + j], whi[sl][m * KGP + j], w);
-        const float sw = wsc[m * nbb + bb];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) acc[m][c] += kblock_bf16(w, b[c]) * (sx[c] * sw);
+        for (int c = 0; c < NC; ++c) acc[m][c] += kblock_bf16(w, b[c]) * csc[(m * nbb + bb) * BM + c * 16 + lr];
       }
     }
   };
@@ -584,9 +614,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   const bool wave_live = n0 < a.d;  // d is a multiple of 16*RT here: whole waves are live or not
   const uint8_t* wd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * a.d * RB;
   const int nl = wave_live ? n0 : 0;
-  const WeightStream ws = weight_stream(wd, RB, nl, a.w_tiled, lane);
-  // 16-row tile r of the wave starts 16*r rows (tiled: r tiles) further on
-  const size_t tile_step = a.w_tiled ? (size_t)nbb * 2048 : (size_t)16 * RB;
+  const WeightStream ws = weight_stream(wd, RB, nl, a.w_tiled, lane, RT);
   // W_down block scales of the block's NW*16*RT rows (one or two 128-row scale
   // blocks), staged in LDS with h; the wave's row of them
   constexpr int nsr = NW * 16 * RT > 128 ? NW * 16 * RT / 128 : 1;
@@ -600,9 +628,9 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   auto load = [&](int slot, int r, int q0) {
 #pragma unroll
     for (int j = 0; j < KG; ++j) {  // unconditional: past the row's end the last K block is read again
-      const uint8_t* p = ws.p + r * tile_step + (size_t)min(q0 + j, nbb - 1) * ws.kb_stride;
-      wlo[slot][j] = stream_load<WT == 2 && BM == 16>(p);
-      whi[slot][j] = stream_load<WT == 2 && BM == 16>(p + ws.hi_off);
+      const int so = r * ws.tile_step + min(q0 + j, nbb - 1) * ws.kb_stride;
+      wlo[slot][j] = stream_load<WT == 2 && BM == 16>(ws, so);
+      whi[slot][j] = stream_load<WT == 2 && BM == 16>(ws, so + ws.hi_off);
     }
   };
   // Staging, in pinned issue order (loads complete in issue order as far as
@@ -901,8 +929,9 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
   const uint8_t* pu = tr.shared ? (const uint8_t*)a.ssu : (const uint8_t*)a.su + (size_t)tr.g * pbytes;
   const int f0 = nb * 128 + wave * 16;
   const size_t t0 = (size_t)(f0 / 16) * nkb;  // the wave's first tile block
-  const uint8_t* const cs[2] = {cg + t0 * 1024 + lane * 16, cu + t0 * 1024 + lane * 16};
-  const uint8_t* const ps[2] = {pg + t0 * 128 + lr * 8, pu + t0 * 128 + lr * 8};
+  // the wave's tile of each matrix: codes (1 KB per block) and parameters (128 B)
+  const __amdgpu_buffer_rsrc_t rc[2] = {buffer_over(cg + t0 * 1024, nkb * 1024), buffer_over(cu + t0 * 1024, nkb * 1024)};
+  const __amdgpu_buffer_rsrc_t rp[2] = {buffer_over(pg + t0 * 128, nkb * 128), buffer_over(pu + t0 * 128, nkb * 128)};
 
   // Stage q: blocks [q*KG, q*KG + KG) of W_gate, then of W_up.  Loads are
   // unconditional (a short last stage re-reads the final block, in bounds).
@@ -916,8 +945,8 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
 #pragma unroll
       for (int j = 0; j < KG; ++j) {
         const int kb = min(q * KG + j, nkb - 1);
-        wc[sl][m][j] = stream_load<true>(cs[m] + (size_t)kb * 1024);
-        wp[sl][m][j] = *(const uint2*)(ps[m] + (size_t)kb * 128);
+        wc[sl][m][j] = buffer_load16<true>(rc[m], lane * 16, kb * 1024);
+        wp[sl][m][j] = buffer_load8(rp[m], lr * 8, kb * 128);
       }
   };
 
@@ -926,10 +955,29 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
   const int cpr = d / 8, nch = BM * cpr;  // 16-byte chunks per row / per tile
   const uint8_t* xa = (const uint8_t*)a.xa;
   const int rlast = tr.rows - 1;
+  // Chunk i is chunk i % cpr of row i / cpr; a thread's chunks i0 + u*NT
+  // advance by NT / cpr rows and NT % cpr chunks (one division per batch).
+  // Rows past the tile hold copies of the last row (their outputs are never
+  // stored); chunks past the tile's last row go to the spare row.
   auto stage = [&](int i0, bool first) {
+    int rs[SB], cs[SB];
+    {
+      const int dr = NT / cpr, dc = NT - dr * cpr;
+      int r = i0 / cpr, c = i0 - r * cpr;
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        rs[u] = r;
+        cs[u] = c;
+        r += dr;
+        c += dc;
+        const bool wrap = c >= cpr;
+        r += wrap ? 1 : 0;
+        c -= wrap ? cpr : 0;
+      }
+    }
     int tk[SB];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) tk[u] = a.ri.tok[tr.hrow0 + min((i0 + u * NT) / cpr, rlast)];
+    for (int u = 0; u < SB; ++u) tk[u] = a.ri.tok[tr.hrow0 + min(rs[u], rlast)];
     if (first) {
       __builtin_amdgcn_sched_barrier(0);
       load(Ic<0>{}, 0);
@@ -938,15 +986,13 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
     }
     v4i v[SB];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) v[u] = *(const v4i*)(xa + (size_t)tk[u] * d * 2 + ((i0 + u * NT) % cpr) * 16);
+    for (int u = 0; u < SB; ++u) v[u] = *(const v4i*)(xa + (size_t)tk[u] * d * 2 + cs[u] * 16);
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
-      const v4i z = {0, 0, 0, 0};
-      const v4i x = i < nch && r <= rlast ? v[u] : z;
-      *(v4i*)(xs + (i < nch ? r : BM) * xstride + (i < nch ? c : 0) * 16) = x;
-      const float s = group_sum_bf16x8(x);  // the group's 8 chunks sit in 8 consecutive lanes
-      if ((tid & 7) == 0 && i < nch) xsum[(c / 8) * BM + r] = s;
+      const bool in = rs[u] < BM;
+      *(v4i*)(xs + (in ? rs[u] : BM) * xstride + (in ? cs[u] : 0) * 16) = v[u];
+      const float s = group_sum_bf16x8(v[u]);  // the group's 8 chunks sit in 8 consecutive lanes
+      if ((tid & 7) == 0 && in) xsum[(cs[u] / 8) * BM + rs[u]] = s;
     }
   };
   stage(tid, true);
@@ -1046,8 +1092,9 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   const uint8_t* cd = tr.shared ? (const uint8_t*)a.shd : (const uint8_t*)a.wd + (size_t)tr.g * cbytes;
   const uint8_t* pd = tr.shared ? (const uint8_t*)a.ssd : (const uint8_t*)a.sd + (size_t)tr.g * pbytes;
   const size_t t0 = (size_t)(nl / 16) * nkb;
-  const uint8_t* cs = cd + t0 * 1024 + lane * 16;  // tile r of the wave: + r * nkb blocks
-  const uint8_t* ps = pd + t0 * 128 + lr * 8;
+  // the wave's RT tiles (tile r: + r * nkb blocks): codes and parameters
+  const __amdgpu_buffer_rsrc_t rc = buffer_over(cd + t0 * 1024, RT * nkb * 1024);
+  const __amdgpu_buffer_rsrc_t rp = buffer_over(pd + t0 * 128, RT * nkb * 128);
 
   v4i wc[2][KG];
   uint2 wp[2][KG];
@@ -1055,9 +1102,9 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
     constexpr int sl = decltype(S)::value;
 #pragma unroll
     for (int j = 0; j < KG; ++j) {
-      const size_t kb = (size_t)r * nkb + min(q * KG + j, nkb - 1);
-      wc[sl][j] = stream_load<true>(cs + kb * 1024);
-      wp[sl][j] = *(const uint2*)(ps + kb * 128);
+      const int kb = r * nkb + min(q * KG + j, nkb - 1);
+      wc[sl][j] = buffer_load16<true>(rc, lane * 16, kb * 1024);
+      wp[sl][j] = buffer_load8(rp, lr * 8, kb * 128);
     }
   };
 
@@ -1067,14 +1114,34 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   const int cpr = Fg / 8, nch = BM * cpr;
   const uint8_t* hsrc = (const uint8_t*)a.h;
   const int o = a.ri.prow[hrow0 + min(tid, rlast)];
-  auto stage_load = [&](int i0, v4i (&v)[SB]) {
+  // Chunk i is chunk i % cpr of row i / cpr; a thread's chunks i0 + u*NT
+  // advance by NT / cpr rows and NT % cpr chunks (one division per batch).
+  struct Batch {
+    int r[SB], c[SB];
+  };
+  auto stage_walk = [&](int i0) {
+    const int dr = NT / cpr, dc = NT - dr * cpr;
+    int r = i0 / cpr, c = i0 - r * cpr;
+    Batch bt;
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = min(i / cpr, rlast), c = i % cpr;
-      const uint8_t* hp = hsrc + ((size_t)(hrow0 + r) * a.hstride + c * 8) * 2;
+      bt.r[u] = r;
+      bt.c[u] = c;
+      r += dr;
+      c += dc;
+      const bool wrap = c >= cpr;
+      r += wrap ? 1 : 0;
+      c -= wrap ? cpr : 0;
+    }
+    return bt;
+  };
+  auto stage_load = [&](const Batch& bt, v4i (&v)[SB]) {
+#pragma unroll
+    for (int u = 0; u < SB; ++u) {
+      const uint8_t* hp = hsrc + ((size_t)(hrow0 + min(bt.r[u], rlast)) * a.hstride + bt.c[u] * 8) * 2;
       if constexpr (COH) {  // coherent loads skip the L2: fetch only chunks of live rows
         v[u] = v4i{0, 0, 0, 0};
-        if (i < nch && i / cpr <= rlast)
+        if (bt.r[u] <= rlast)
           v[u] = v4i{(int)load_coherent(hp), (int)load_coherent(hp + 4), (int)load_coherent(hp + 8),
                      (int)load_coherent(hp + 12)};
       } else {
@@ -1082,29 +1149,32 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
       }
     }
   };
-  auto stage_store = [&](int i0, const v4i (&v)[SB]) {
+  // Rows past the tile hold copies of the last row (zeros in the coherent
+  // path): their outputs are never stored.  Chunks past the tile's last row go
+  // to the spare row.
+  auto stage_store = [&](const Batch& bt, const v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const int i = i0 + u * NT, r = i / cpr, c = i % cpr;
-      const v4i z = {0, 0, 0, 0};
-      const v4i x = i < nch && r <= rlast ? v[u] : z;
-      *(v4i*)(hs + (i < nch ? r : BM) * lstride + (i < nch ? c : 0) * 16) = x;
-      const float s = group_sum_bf16x8(x);
-      if ((tid & 7) == 0 && i < nch) hsum[(c / 8) * BM + r] = s;
+      const bool in = bt.r[u] < BM;
+      *(v4i*)(hs + (in ? bt.r[u] : BM) * lstride + (in ? bt.c[u] : 0) * 16) = v[u];
+      const float s = group_sum_bf16x8(v[u]);
+      if ((tid & 7) == 0 && in) hsum[(bt.c[u] / 8) * BM + bt.r[u]] = s;
     }
   };
   v4i hv[SB];
-  stage_load(tid, hv);
+  const Batch bt0 = stage_walk(tid);
+  stage_load(bt0, hv);
   __builtin_amdgcn_sched_barrier(0);
   load(Ic<0>{}, 0, 0);
   if (RT == 2) load(Ic<1>{}, 1, 0);
   else load(Ic<1>{}, 0, 1);
   __builtin_amdgcn_sched_barrier(0);
   const float wt = a.ri.w[hrow0 + min(tid, rlast)];
-  stage_store(tid, hv);
+  stage_store(bt0, hv);
   for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) {
-    stage_load(i0, hv);
-    stage_store(i0, hv);
+    const Batch bt = stage_walk(i0);
+    stage_load(bt, hv);
+    stage_store(bt, hv);
   }
   if (tid < BM) {
     orow[tid] = tid <= rlast ? o : -1;
@@ -1414,7 +1484,7 @@ size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 4) return (size_t)(BM + 1) * (d * 2 + 16) + (size_t)(d / 64) * BM * 4;
   const int xrow = gateup_x_bf16(BM, wmode) ? d * 2 : gateup_x_part_blocks(d / 128) * 256;
   size_t b = (size_t)(BM + 1) * (xrow + 16);  // plus a spare row
-  if (wmode >= 2) b += (size_t)BM * (d / 128) * 4 + 2 * (d / 128) * 4;
+  if (wmode >= 2) b += 2 * (size_t)BM * (d / 128) * 4;  // scale products
   return b + kGateUpWaves * BM * 4;
 }
 
