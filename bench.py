@@ -161,7 +161,8 @@ def run_workload(name, steps, warmup, rotate, layout):
     # every weight tensor rotates: routed and shared expert matrices, their block
     # scales or group parameters, the router and the selection bias
     wkeys = [k for k in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down", "sh_gate", "sh_up", "sh_down",
-                         "ss_gate", "ss_up", "ss_down", "w_router", "sel_bias") if dev.get(k) is not None]
+                         "ss_gate", "ss_up", "ss_down", "w_router", "w_router_planes", "sel_bias")
+             if dev.get(k) is not None]
     copies = [dev] + [dict(dev, **{k: dev[k].clone() for k in wkeys}) for _ in range(max(0, rotate - 1))]
     r = moe.alloc_routing(shape, "cuda:0")
     ws = moe.alloc_workspace(shape, "cuda:0")

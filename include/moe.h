@@ -133,6 +133,11 @@ typedef struct {
   const void *ss_gate;    /* [Fs/128, d/128] */
   const void *ss_up;      /* [Fs/128, d/128] */
   const void *ss_down;    /* [d/128, Fs/128] */
+  const void *w_router_planes; /* w_router packed by moe_pack_router, or NULL.  Optional: when
+                            given, routing calls with bf16 activations and more than 1024
+                            (token, slot) pairs read the router weights from it instead of
+                            splitting w_router in every call; the logits are the same bit
+                            for bit.  It must hold the current w_router (16-byte aligned). */
 } moe_weights;
 
 /* Routing results (written by moe_route / moe_route_forced, read by moe_forward).
@@ -307,6 +312,22 @@ int moe_pack_weights(int64_t n_mats, int32_t rows, int32_t row_bytes, const void
 int moe_pack_weights_u4(int64_t n_mats, int32_t rows, int32_t cols, const void *codes, const uint16_t *scales,
                         const uint16_t *biases, void *codes_out, void *params_out, void *stream);
 
+/* Bytes of the packed router weights for E experts and d_model d (0 for an
+ * invalid pair: 1 <= E <= 512, d a multiple of 128). */
+size_t moe_router_planes_bytes(int32_t n_experts, int32_t d_model);
+/* Packs the fp32 router weights w_router [E, d] (device) into `planes`
+ * (moe_router_planes_bytes(E, d) bytes, device, 16-byte aligned, not
+ * overlapping w_router), once per layer ([port] part 3 of "Taking it apart":
+ * the router runs in float32).  Each weight w is split exactly into three bf16
+ * terms, hi = bf16(w), mid = bf16(w - hi), lo = bf16(w - hi - mid) (round to
+ * nearest even; w = hi + mid + lo), the same split the router kernels make
+ * from w_router; stored in matrix-core operand order: fragment (expert tile
+ * et of 16 experts, 32-deep K step ks, plane p = hi, mid, lo) is 1 KB at
+ * 1024 * ((et * (d/32) + ks) * 3 + p), where the 16 bytes at 16 * l hold
+ * expert 16 et + l%16 at K = 32 ks + 8 (l/16) + [0, 8) (zero past E).  A
+ * layout choice of this library.  Errors: MOE_ERR_INVALID_ARG for an invalid
+ * shape, a null or misaligned pointer. */
+int moe_pack_router(int32_t n_experts, int32_t d_model, const float *w_router, void *planes, void *stream);
 /* Routing compared as a distribution: the third part of the check [port]
  * "Taking it apart" proposes (force the routing, compare the rest closely,
  * check the routing itself as a distribution), with sigma, a layer's RMS

@@ -209,7 +209,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!w || !w->w_router || !x || check_routing_out(out) != MOE_OK) return MOE_ERR_INVALID_ARG;
-  if (misaligned(x)) return MOE_ERR_INVALID_ARG;
+  if (misaligned(x) || misaligned(w->w_router_planes)) return MOE_ERR_INVALID_ARG;
   if (shape->T == 0) return MOE_OK;
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);
@@ -219,6 +219,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   R.x = x;
   R.x_bf16 = shape->act_dtype == MOE_BF16;
   R.w_router = w->w_router;
+  R.planes = (const uint8_t*)w->w_router_planes;
   R.bias = w->sel_bias;
   R.forced = forced;
   R.T = shape->T;
@@ -286,6 +287,20 @@ int moe_route_forced(const moe_shape* shape, const moe_weights* w, const void* x
                      const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
   if (!forced_idx) return MOE_ERR_INVALID_ARG;
   return route_common(shape, w, x, forced_idx, out, ws, ws_bytes, stream);
+}
+
+size_t moe_router_planes_bytes(int32_t n_experts, int32_t d_model) {
+  if (n_experts < 1 || n_experts > 512 || d_model < 128 || d_model % 128 != 0) return 0;
+  return moe::router_planes_bytes(d_model, n_experts);
+}
+
+int moe_pack_router(int32_t n_experts, int32_t d_model, const float* w_router, void* planes, void* stream) {
+  if (moe_router_planes_bytes(n_experts, d_model) == 0 || !w_router || !planes) return MOE_ERR_INVALID_ARG;
+  if (misaligned(w_router) || misaligned(planes)) return MOE_ERR_INVALID_ARG;
+  const uintptr_t a = (uintptr_t)w_router, b = (uintptr_t)planes;
+  const size_t na = (size_t)n_experts * d_model * 4, nb = moe_router_planes_bytes(n_experts, d_model);
+  if (a < b + nb && b < a + na) return MOE_ERR_INVALID_ARG;  // overlapping buffers
+  return hip_status(moe::launch_pack_router(w_router, planes, d_model, n_experts, (hipStream_t)stream));
 }
 
 int moe_forward(const moe_shape* shape, const moe_weights* w, const void* x, const moe_routing* r, void* y, void* ws,

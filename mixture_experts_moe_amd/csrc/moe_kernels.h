@@ -75,6 +75,7 @@ struct RouteLaunch {
   const void* x;
   bool x_bf16;
   const float* w_router;
+  const uint8_t* planes;   // the router weights packed by launch_pack_router, or null
   const float* bias;       // selection bias or null
   const int32_t* forced;   // forced ids or null
   int T, d, E, k;
@@ -86,6 +87,10 @@ struct RouteLaunch {
   PlanCtx plan;            // the dispatch plan the last launch writes
 };
 hipError_t launch_route(const RouteLaunch& L, hipStream_t st);
+// The router weights [E][d] fp32 as three exact bf16 planes in matrix-core
+// operand order (the layout is described at pack_router_planes_kernel).
+size_t router_planes_bytes(int d, int E);
+hipError_t launch_pack_router(const float* W, void* planes, int d, int E, hipStream_t st);
 
 hipError_t launch_quantize_rows(const void* in, bool bf16, int64_t n_rows, int n_cols, uint8_t* codes, float* scales,
                                 hipStream_t st);

@@ -427,6 +427,180 @@ __global__ __launch_bounds__(256) void router_tile2_kernel(const uint16_t* __res
 }
 
 // ---------------------------------------------------------------------------
+// The router weights as three bf16 planes in matrix-core operand order, written
+// once per layer by moe_pack_router: the exact split above (w = hi + mid + lo),
+// so products of the planes are the products the other kernels form from the
+// fp32 weights.  Fragment (expert tile et of 16, 32-deep K step ks, plane p) is
+// 1 KB at 1024 * ((et * (d/32) + ks) * 3 + p); lane l's 16 bytes hold expert
+// 16 et + l%16, K = 32 ks + 8 (l/16) + [0, 8).  Experts past E are zero.
+// One thread per (expert tile, K step, lane).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void pack_router_planes_kernel(const float* __restrict__ W,
+                                                                 uint8_t* __restrict__ planes, int d, int E,
+                                                                 int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int l = (int)(i & 63), nks = d / 32;
+  const int64_t f = i >> 6;  // et * nks + ks
+  const int ks = (int)(f % nks), et = (int)(f / nks);
+  const int e = 16 * et + (l & 15), k = 32 * ks + 8 * (l >> 4);
+  float w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (e < E) {
+    const float4 a = *(const float4*)(W + (size_t)e * d + k), b = *(const float4*)(W + (size_t)e * d + k + 4);
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+  }
+  v8bf hi, mid, lo;
+  split3_bf16(w, hi, mid, lo);
+  uint8_t* o = planes + (size_t)f * 3 * 1024 + 16 * l;
+  *(v8bf*)o = hi;
+  *(v8bf*)(o + 1024) = mid;
+  *(v8bf*)(o + 2048) = lo;
+}
+
+#ifndef MOE_RP_MINB
+#define MOE_RP_MINB 2  // planes kernel: blocks per CU the registers must allow
+#endif
+// ---------------------------------------------------------------------------
+// Router partial logits for long inputs from the packed planes: blocks of
+// 32*NJ tokens x 64 experts over one half of K, 4 waves of 16*NJ tokens x 32
+// experts.  A stage is KS 32-deep K steps; its operands are 2*NJ*KS + 12*KS
+// fragments of 1 KB (x gathered per token in operand order, then per expert
+// tile its K steps of the three planes, one contiguous run), which the waves
+// move straight into LDS (16 bytes per lane, no registers, no conversion), NB
+// stage buffers in a ring, a stage's loads issued NB - 1 stages before it is
+// multiplied.  Sum order per logit as in the other router kernels (a chain of
+// six products per 64-deep chunk from zero, hi, mid, lo per K step; four
+// chunks into a slice in order; the half's slices in order), so the logits are
+// the same bit for bit.
+// ---------------------------------------------------------------------------
+template <int NJ, int KS, int NB>
+__global__ __launch_bounds__(256, MOE_RP_MINB) void router_planes_kernel(const uint16_t* __restrict__ x,
+                                                                         const uint8_t* __restrict__ planes,
+                                                                         float* __restrict__ part, int T, int d,
+                                                                         int E, int gsl,
+                                                                         int32_t* __restrict__ status) {
+  constexpr int NXF = 2 * NJ * KS, NF = NXF + 12 * KS, FPW = NF / 4;  // fragments per stage, per wave
+  constexpr int BUF = NF * 1024;
+  static_assert(FPW * 4 == NF && (KS == 1 || KS == 2), "fragments per wave");
+  __shared__ __align__(16) uint8_t lds[NB * BUF];
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int lr = lane & 15, kg = lane >> 4, wt = wave & 1, we = wave >> 1;
+  const int t0 = blockIdx.x * (32 * NJ), e0 = blockIdx.y * 64, half = blockIdx.z;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && half == 0 && tid == 0) *status = 0;
+  const int c0 = half ? gsl * 4 : 0, c1 = half ? d / 64 : gsl * 4;  // a multiple of 4 chunks, >= 4
+  const int s0 = c0 * 2 / KS, s1 = c1 * 2 / KS;                    // stages of the half
+  const int nks = d / 32, n_et = (E + 15) / 16;
+  // Wave w moves fragments w*FPW .. w*FPW + FPW - 1 of every stage; per
+  // fragment the lane's source at stage 0 (a stage adds 64*KS bytes of x row,
+  // or 3*KS KB of planes) and its LDS slot.
+  const uint8_t* src[FPW];
+  bool isx[FPW];
+#pragma unroll
+  for (int u = 0; u < FPW; ++u) {
+    const int f = wave * FPW + u;
+    isx[u] = f < NXF;
+    if (f < NXF) {  // token tile f/KS, K step f%KS
+      const int t = min(t0 + 16 * (f / KS) + lr, T - 1);
+      src[u] = (const uint8_t*)(x + (size_t)t * d) + 64 * (f % KS) + 16 * kg;
+    } else {  // expert tile g/(3 KS), then [K step][plane]
+      const int g = f - NXF, et = min(e0 / 16 + g / (3 * KS), n_et - 1);
+      src[u] = planes + ((size_t)et * nks * 3 + g % (3 * KS)) * 1024 + 16 * lane;
+    }
+  }
+  auto issue = [&](int st) {
+    uint8_t* L = lds + (st % NB) * BUF;
+#pragma unroll
+    for (int u = 0; u < FPW; ++u) {
+      const size_t off = isx[u] ? (size_t)st * 64 * KS : (size_t)st * 3072 * KS;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src[u] + off),
+                                       (__attribute__((address_space(3))) void*)(L + (wave * FPW + u) * 1024), 16, 0,
+                                       0);
+    }
+  };
+  v4f tot[2][NJ], sl[2][NJ], cc[2][NJ];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) tot[i][j] = sl[i][j] = cc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](int st) {
+    const uint8_t* L = lds + (st % NB) * BUF;
+    // All of the stage's fragments are requested before the first product
+    // (lane holds K = 32*ks + 8*kg + [0, 8)); within a step the products run
+    // plane by plane over all 2 x NJ accumulators, so consecutive products are
+    // independent while each accumulator still sees hi, mid, lo per step.
+    v8bf b[KS][NJ], a[KS][3][2];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) b[ks][j] = *(const v8bf*)(L + (KS * (wt * NJ + j) + ks) * 1024 + 16 * lane);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a[ks][p][i] = *(const v8bf*)(L + (NXF + 3 * KS * (2 * we + i) + 3 * ks + p) * 1024 + 16 * lane);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every read in flight before the first product waits
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int kk = st * KS + ks;  // K step within the row; even steps open a 64-deep chunk
+      if (kk % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) cc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            cc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks][p][i], b[ks][j], cc[i][j], 0, 0, 0);
+      if (kk % 2 == 1) {
+        const int q = (kk / 2 - c0) % 4, slice = (kk / 2 - c0) / 4;  // chunk -> slice -> half total
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            sl[i][j] = q == 0 ? cc[i][j] : sl[i][j] + cc[i][j];
+            if (q == 3) tot[i][j] = slice == 0 ? sl[i][j] : tot[i][j] + sl[i][j];
+          }
+      }
+    }
+  };
+  // vmcnt waits (expcnt and lgkmcnt left open): stage st has landed once at
+  // most the loads of the stages issued after it are outstanding.
+  constexpr int kWaitSteady = ((FPW * (NB - 2)) & 15) | (((FPW * (NB - 2)) >> 4) << 14) | (7 << 4) | (15 << 8);
+  constexpr int kWaitAll = (7 << 4) | (15 << 8);
+  static_assert(FPW * (NB - 2) < 64, "vmcnt range");
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (s0 + u < s1) issue(s0 + u);
+  for (int st = s0; st < s1; ++st) {
+    // Wait for this wave's loads of stage st, then for every wave's (the
+    // barrier), which also frees the buffer stage st - 1 was read from.
+    if (st + NB - 2 < s1) __builtin_amdgcn_s_waitcnt(kWaitSteady);
+    else __builtin_amdgcn_s_waitcnt(kWaitAll);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + NB - 1 < s1) issue(st + NB - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(st);
+  }
+  float* out = part + (size_t)half * T * E;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int e = e0 + 32 * we + 16 * i + 4 * kg + r, t = t0 + 16 * NJ * wt + 16 * j + lr;
+        if (e < E && t < T) out[(size_t)t * E + e] = tot[i][j][r];
+      }
+}
+
+// ---------------------------------------------------------------------------
 // Router logits for fp32 activations: plain fp32 multiply-add, LDS-tiled; tiles
 // of TT tokens x TE experts, each of the 256 threads owning a (TT/16) x (TE/16)
 // register tile.
@@ -985,6 +1159,34 @@ static TopkArgs topk_args(const RouteLaunch& L, int tpc) {
     default: return hipErrorInvalidValue;                                                \
   }
 
+#ifndef MOE_RP_NJ_LONG
+#define MOE_RP_NJ_LONG 4   // planes kernel: 16-token tiles per wave, batches of kPlanesLongT tokens and more
+#endif
+#ifndef MOE_RP_NB_LONG
+#define MOE_RP_NB_LONG 2   // planes kernel: LDS buffers in the ring
+#endif
+#ifndef MOE_RP_KS_LONG
+#define MOE_RP_KS_LONG 2   // planes kernel: 32-deep K steps per LDS stage
+#endif
+#ifndef MOE_RP_KS_SHORT
+#define MOE_RP_KS_SHORT 2
+#endif
+#ifndef MOE_RP_NJ_SHORT
+#define MOE_RP_NJ_SHORT 2
+#endif
+#ifndef MOE_RP_NB_SHORT
+#define MOE_RP_NB_SHORT 2
+#endif
+constexpr int kPlanesLongT = 4096;
+
+size_t router_planes_bytes(int d, int E) { return (size_t)((E + 15) / 16) * (d / 32) * 3 * 1024; }
+
+hipError_t launch_pack_router(const float* W, void* planes, int d, int E, hipStream_t st) {
+  const int64_t n = (int64_t)((E + 15) / 16) * (d / 32) * 64;
+  pack_router_planes_kernel<<<(unsigned)((n + 255) / 256), 256, 0, st>>>(W, (uint8_t*)planes, d, E, n);
+  return hipGetLastError();
+}
+
 // Router launch: bf16 activations go through the K-split kernel (short inputs)
 // or the tiled kernel (long inputs), which leave partial sums that top-k adds in
 // one order, so a token's logits never depend on T; fp32 activations (small
@@ -996,7 +1198,18 @@ static hipError_t launch_router(const RouteLaunch& L, hipStream_t st, const floa
     const int ksl = router_kslice(L.d), ns = L.d / ksl, halves = ns > 1 ? 2 : 1;
     const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64, halves);
     const uint16_t* x = (const uint16_t*)L.x;
-    if (ksl == 256 && halves == 2 && L.T >= 4096) {  // 128-token blocks once they fill the chip
+    if (L.planes && ksl == 256 && halves == 2) {  // packed planes
+      const int gsl = (ns + 1) / 2;
+      if (L.T >= kPlanesLongT) {
+        const dim3 g((L.T + 32 * MOE_RP_NJ_LONG - 1) / (32 * MOE_RP_NJ_LONG), (L.E + 63) / 64, 2);
+        router_planes_kernel<MOE_RP_NJ_LONG, MOE_RP_KS_LONG, MOE_RP_NB_LONG><<<g, 256, 0, st>>>(
+            x, L.planes, L.rpart, L.T, L.d, L.E, gsl, L.status);
+      } else {
+        const dim3 g((L.T + 32 * MOE_RP_NJ_SHORT - 1) / (32 * MOE_RP_NJ_SHORT), (L.E + 63) / 64, 2);
+        router_planes_kernel<MOE_RP_NJ_SHORT, MOE_RP_KS_SHORT, MOE_RP_NB_SHORT><<<g, 256, 0, st>>>(
+            x, L.planes, L.rpart, L.T, L.d, L.E, gsl, L.status);
+      }
+    } else if (ksl == 256 && halves == 2 && L.T >= 4096) {  // 128-token blocks once they fill the chip
       const dim3 g2((L.T + 127) / 128, (L.E + 63) / 64, 2);
       router_tile2_kernel<4><<<g2, 256, 0, st>>>(x, L.w_router, L.rpart, L.T, L.d, L.E, (ns + 1) / 2, L.status);
     } else if (ksl == 256)

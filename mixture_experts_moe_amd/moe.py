@@ -23,7 +23,8 @@ DTYPES = {"f32": 0, "bf16": 1, "fp8": 2, "fp8a16": 3, "u4": 4}
 # Every function the header declares (checked against include/moe.h by the tests).
 ABI_FUNCTIONS = ("moe_workspace_bytes", "moe_plan_bytes", "moe_route", "moe_route_forced", "moe_forward",
                  "moe_forward_noalloc", "moe_forward_stages", "moe_quantize_rows", "moe_pack_weights",
-                 "moe_pack_weights_u4", "moe_route_compare_workspace_bytes", "moe_route_compare", "moe_status_string")
+                 "moe_pack_weights_u4", "moe_route_compare_workspace_bytes", "moe_route_compare", "moe_status_string",
+                 "moe_router_planes_bytes", "moe_pack_router")
 MOE_ERR_SCRATCH_LIMIT = -7
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES
 LAYOUTS = {"rowmajor": 0, "tiled": 1}
@@ -44,7 +45,7 @@ class Shape(C.Structure):
 
 
 _WEIGHT_FIELDS = ("w_router", "sel_bias", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
-                  "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down")
+                  "sh_gate", "sh_up", "sh_down", "ss_gate", "ss_up", "ss_down", "w_router_planes")
 
 
 class Weights(C.Structure):
@@ -86,6 +87,9 @@ def lib() -> C.CDLL:
         L.moe_route_compare_workspace_bytes.restype = C.c_size_t
         L.moe_route_compare_workspace_bytes.argtypes = [i32]
         L.moe_route_compare.argtypes = [i32, i32, i32, p, p, p, p, p, p, p, p, p, p, C.c_size_t, p]
+        L.moe_router_planes_bytes.restype = C.c_size_t
+        L.moe_router_planes_bytes.argtypes = [i32, i32]
+        L.moe_pack_router.argtypes = [i32, i32, p, p, p]
         L.moe_status_string.restype = C.c_char_p
         L.moe_status_string.argtypes = [C.c_int]
         _lib = L
@@ -257,11 +261,25 @@ def pack_weights_u4(codes: torch.Tensor, scales: torch.Tensor, biases: torch.Ten
     return out, params
 
 
+def pack_router(w_router: torch.Tensor, stream=None) -> torch.Tensor:
+    """The [E, d] fp32 router weights as moe_pack_router's three bf16 planes."""
+    E, d = w_router.shape
+    n = int(lib().moe_router_planes_bytes(E, d))
+    if n == 0 or w_router.dtype != torch.float32:
+        raise MoeError(MOE_ERR_INVALID_ARG, "moe_router_planes_bytes")
+    out = torch.empty(n, dtype=torch.uint8, device=w_router.device)
+    _check(lib().moe_pack_router(E, d, _ptr(w_router), _ptr(out), _stream(stream)), "moe_pack_router")
+    return out
+
+
 def pack_layer_weights(w: dict, stream=None) -> dict:
-    """The weight dict with every expert matrix packed (scales, router, x
-    untouched).  4-bit weights (recognised by their biases b_*): codes and group
-    parameters packed together, the parameters taking the scales' place."""
+    """The weight dict with every expert matrix packed (scales, x untouched) and
+    the router's packed planes added as w_router_planes.  4-bit weights
+    (recognised by their biases b_*): codes and group parameters packed
+    together, the parameters taking the scales' place."""
     out = dict(w)
+    if w.get("w_router") is not None:
+        out["w_router_planes"] = pack_router(w["w_router"], stream)
     if w.get("b_gate") is not None:
         for c, sc, b in (("w_gate", "s_gate", "b_gate"), ("w_up", "s_up", "b_up"), ("w_down", "s_down", "b_down"),
                          ("sh_gate", "ss_gate", "sb_gate"), ("sh_up", "ss_up", "sb_up"),

@@ -240,6 +240,25 @@ def test_pack_weights_host_validation():
     assert L.moe_pack_weights(2, 16, 128, a, C.c_void_p(C.addressof(buf) + 2048), None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_pack_router_host_validation():
+    L = _lib()
+    assert L.moe_router_planes_bytes(384, 2048) == 24 * 64 * 3 * 1024
+    assert L.moe_router_planes_bytes(17, 256) == 2 * 8 * 3 * 1024      # experts rounded up to 16
+    for E, d in ((0, 2048), (513, 2048), (384, 2000), (384, 0)):
+        assert L.moe_router_planes_bytes(E, d) == 0
+        assert L.moe_pack_router(E, d, FAKE, C.c_void_p(0x100000), None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(384, 2048, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(384, 2048, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_pack_router(384, 2048, C.c_void_p(0x1008), C.c_void_p(0x10000000), None) == moe.MOE_ERR_INVALID_ARG
+    # w_router [16, 128] fp32 = 8 KB at a; the 12 KB of planes at a + 4 KB overlap it
+    assert L.moe_pack_router(16, 128, C.c_void_p(0x100000), C.c_void_p(0x101000), None) == moe.MOE_ERR_INVALID_ARG
+    # a routing call rejects misaligned packed planes before any launch
+    good = moe.make_shape(2048, 2048, 384, 6, 640, 640)
+    w = _weights_struct()
+    w.w_router_planes = 0x3008
+    assert _route(good, w=w) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_layout_field_validation():
     _lib()
     assert moe.workspace_bytes(moe.make_shape(32, 2048, 384, 6, 640, 640, layout="tiled")) > 0
