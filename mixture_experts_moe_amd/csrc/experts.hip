@@ -951,15 +951,19 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
   };
 
   // Staging, in pinned issue order: row tokens, the weight stream, then the
-  // activation rows (bf16, zero past the tile) and their per-group sums.
-  const int cpr = d / 8, nch = BM * cpr;  // 16-byte chunks per row / per tile
+  // activation rows (bf16) and their per-group sums.  Only the tile's live
+  // rows are staged: rows past them keep whatever the LDS held, and feed only
+  // output rows that are never stored (each output row of a product reads its
+  // own activation row and group sums alone).
+  const int cpr = d / 8, nch = tr.rows * cpr;  // 16-byte chunks per row / of the live rows
   const uint8_t* xa = (const uint8_t*)a.xa;
   const int rlast = tr.rows - 1;
   // Chunk i is chunk i % cpr of row i / cpr; a thread's chunks i0 + u*NT
   // advance by NT / cpr rows and NT % cpr chunks (one division per batch).
-  // Rows past the tile hold copies of the last row (their outputs are never
-  // stored); chunks past the tile's last row go to the spare row.
+  // A batch runs only the chunk slots some thread needs (a uniform count);
+  // chunks past the live rows re-read the last row and go to the spare row.
   auto stage = [&](int i0, bool first) {
+    const int slots = min(SB, (nch - (i0 - tid) + NT - 1) / NT);  // >= 1
     int rs[SB], cs[SB];
     {
       const int dr = NT / cpr, dc = NT - dr * cpr;
@@ -977,7 +981,8 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
     }
     int tk[SB];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) tk[u] = a.ri.tok[tr.hrow0 + min(rs[u], rlast)];
+    for (int u = 0; u < SB; ++u)
+      if (u < slots) tk[u] = a.ri.tok[tr.hrow0 + min(rs[u], rlast)];
     if (first) {
       __builtin_amdgcn_sched_barrier(0);
       load(Ic<0>{}, 0);
@@ -986,17 +991,19 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
     }
     v4i v[SB];
 #pragma unroll
-    for (int u = 0; u < SB; ++u) v[u] = *(const v4i*)(xa + (size_t)tk[u] * d * 2 + cs[u] * 16);
+    for (int u = 0; u < SB; ++u)
+      if (u < slots) v[u] = *(const v4i*)(xa + (size_t)tk[u] * d * 2 + cs[u] * 16);
 #pragma unroll
-    for (int u = 0; u < SB; ++u) {
-      const bool in = rs[u] < BM;
-      *(v4i*)(xs + (in ? rs[u] : BM) * xstride + (in ? cs[u] : 0) * 16) = v[u];
-      const float s = group_sum_bf16x8(v[u]);  // the group's 8 chunks sit in 8 consecutive lanes
-      if ((tid & 7) == 0 && in) xsum[(cs[u] / 8) * BM + rs[u]] = s;
-    }
+    for (int u = 0; u < SB; ++u)
+      if (u < slots) {
+        const bool in = rs[u] <= rlast;
+        *(v4i*)(xs + (in ? rs[u] : BM) * xstride + (in ? cs[u] : 0) * 16) = v[u];
+        const float s = group_sum_bf16x8(v[u]);  // the group's 8 chunks sit in 8 consecutive lanes
+        if ((tid & 7) == 0 && in) xsum[(cs[u] / 8) * BM + rs[u]] = s;
+      }
   };
   stage(tid, true);
-  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) stage(i0, false);
+  for (int i0 = tid + NT * SB; i0 - tid < nch; i0 += NT * SB) stage(i0, false);
   __syncthreads();
 
   v4f acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
@@ -1111,18 +1118,20 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   // Staging, in pinned issue order: h rows, the weight stream, the rows'
   // routing weights and output rows; then h to LDS with its group sums.
   const int hrow0 = tr.hrow0, rlast = tr.rows - 1;
-  const int cpr = Fg / 8, nch = BM * cpr;
+  const int cpr = Fg / 8, nch = tr.rows * cpr;  // chunks of the live rows
   const uint8_t* hsrc = (const uint8_t*)a.h;
   const int o = a.ri.prow[hrow0 + min(tid, rlast)];
   // Chunk i is chunk i % cpr of row i / cpr; a thread's chunks i0 + u*NT
   // advance by NT / cpr rows and NT % cpr chunks (one division per batch).
   struct Batch {
-    int r[SB], c[SB];
+    int r[SB], c[SB], slots;
   };
+  // A batch runs only the chunk slots some thread needs (a uniform count).
   auto stage_walk = [&](int i0) {
     const int dr = NT / cpr, dc = NT - dr * cpr;
     int r = i0 / cpr, c = i0 - r * cpr;
     Batch bt;
+    bt.slots = min(SB, (nch - (i0 - tid) + NT - 1) / NT);  // >= 1
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
       bt.r[u] = r;
@@ -1138,6 +1147,7 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   auto stage_load = [&](const Batch& bt, v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
+      if (u >= bt.slots) continue;
       const uint8_t* hp = hsrc + ((size_t)(hrow0 + min(bt.r[u], rlast)) * a.hstride + bt.c[u] * 8) * 2;
       if constexpr (COH) {  // coherent loads skip the L2: fetch only chunks of live rows
         v[u] = v4i{0, 0, 0, 0};
@@ -1149,13 +1159,15 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
       }
     }
   };
-  // Rows past the tile hold copies of the last row (zeros in the coherent
-  // path): their outputs are never stored.  Chunks past the tile's last row go
-  // to the spare row.
+  // Only the live rows are staged: rows past them keep whatever the LDS held
+  // and feed only output rows that are never stored.  Chunks past the live
+  // rows (a re-read of the last row, or zeros in the coherent path) go to the
+  // spare row.
   auto stage_store = [&](const Batch& bt, const v4i (&v)[SB]) {
 #pragma unroll
     for (int u = 0; u < SB; ++u) {
-      const bool in = bt.r[u] < BM;
+      if (u >= bt.slots) continue;
+      const bool in = bt.r[u] <= rlast;
       *(v4i*)(hs + (in ? bt.r[u] : BM) * lstride + (in ? bt.c[u] : 0) * 16) = v[u];
       const float s = group_sum_bf16x8(v[u]);
       if ((tid & 7) == 0 && in) hsum[(bt.c[u] / 8) * BM + bt.r[u]] = s;
@@ -1171,7 +1183,7 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   __builtin_amdgcn_sched_barrier(0);
   const float wt = a.ri.w[hrow0 + min(tid, rlast)];
   stage_store(bt0, hv);
-  for (int i0 = tid + NT * SB; i0 < nch; i0 += NT * SB) {
+  for (int i0 = tid + NT * SB; i0 - tid < nch; i0 += NT * SB) {
     const Batch bt = stage_walk(i0);
     stage_load(bt, hv);
     stage_store(bt, hv);
