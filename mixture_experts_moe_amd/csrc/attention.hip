@@ -36,7 +36,7 @@ namespace moe {
 constexpr int kAttD = 128;    // head dimension
 constexpr int kAttKT = 64;    // keys per tile
 constexpr int kAttRows = 64;  // (query, head) rows per block of 4 waves (8 waves: 128)
-constexpr int kKStride = kAttD + 8;   // bf16 elements per LDS key row
+constexpr int kKStride = kAttD + 16;  // bf16 elements per LDS key row (288 bytes: 32 modulo 64)
 constexpr int kVStride = kAttKT + 4;  // bf16 elements per LDS value-transposed row
 constexpr int kAttSplitMax = 512;     // key splits per row (decode)
 

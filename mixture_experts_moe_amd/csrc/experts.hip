@@ -189,6 +189,18 @@ __device__ __forceinline__ uint32_t load_coherent(const void* p) {
 // for a block without work.  COH: h codes and scales are stored coherently
 // (the fused expert launch).  A16 (with WT = 2): W8A16 -- the activation rows
 // are bf16 (not quantised, unit scales) and h is stored as bf16.
+// LDS rows of bf16 activations (or h) in the FP8 weight codes' K order,
+// arranged so that the four 16-byte fragments a lane reads per 128-element K
+// block sit at 16 * (lane / 16) + 64 * i: the 16-element unit u of a row (K
+// elements 16u .. 16u + 15) keeps its first 8 elements at xunit_pos(u) and
+// the other 8 at xunit_pos(u) + 64.  Each fragment read is then 16 rows x 4
+// lanes at 16-byte steps, which with row strides of 32 bytes past a multiple
+// of 64 (rows of 2 * 64n + 32 bytes) touches every LDS bank once per group of
+// lanes the hardware serves together (measured: 32-byte steps conflict at any
+// 16-byte-aligned row stride).
+__device__ __forceinline__ int xunit_pos(int u) { return (u >> 3) * 256 + ((u >> 2) & 1) * 128 + (u & 3) * 16; }
+constexpr int kLdsRowPad = 32;  // bytes past a row's data: a row stride of 32 modulo 64 bytes
+
 template <int BM, int WT, bool XB, bool COH = false, bool A16 = false>
 __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t* smem) {
   static_assert(!A16 || (WT == 2 && XB), "W8A16 stages bf16 activations for FP8 weights");
@@ -209,7 +221,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
   const int RX = a.d * EX;        // bytes per activation row in HBM
   const int nbb = RB / 128;       // 128-byte K blocks of a weight row
   const int nkh = XH ? gateup_x_part_blocks(a.d / 128) : a.d / 128;  // K blocks of the first part
-  const int xstride = (XH ? nkh * 256 : XBF ? a.d * 2 : a.d) + 16;  // padded LDS row of activations
+  const int xstride = (XH ? nkh * 256 : XBF ? a.d * 2 : a.d) + kLdsRowPad;  // padded LDS row of activations
   uint8_t* xs = smem;
   // [2][d/128][BM] (FP8 only): per matrix (gate, up), K block and row, the
   // activation scale times the weight block scale; one K block's rows adjacent
@@ -350,8 +362,10 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       if constexpr (XQ && (XB || XH)) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
         e4m3x16_to_bf16(x, lo, hi);
-        *(v4i*)(dst + c * 32) = lo;
-        *(v4i*)(dst + c * 32 + 16) = hi;
+        *(v4i*)(dst + xunit_pos(c)) = lo;
+        *(v4i*)(dst + xunit_pos(c) + 64) = hi;
+      } else if constexpr (WT == 2 && XBF) {  // bf16 activations (W8A16): 8 elements of a unit
+        *(v4i*)(dst + xunit_pos(c >> 1) + 64 * (c & 1)) = x;
       } else {
         *(v4i*)(dst + c * 16) = x;
       }
@@ -423,12 +437,12 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
           v4i b[4];
           if constexpr (XB) {
             // bf16 activations of K block bb in the weight codes' K order: codes
-            // 16*(lane/16) + [0,16) of each 64-element half
-            const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 256 + 2 * lk;
+            // 16*(lane/16) + [0,16) of each 64-element half (xunit_pos layout)
+            const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 256 + lk;
             b[0] = *(const v4i*)bp;
-            b[1] = *(const v4i*)(bp + 16);
+            b[1] = *(const v4i*)(bp + 64);
             b[2] = *(const v4i*)(bp + 128);
-            b[3] = *(const v4i*)(bp + 144);
+            b[3] = *(const v4i*)(bp + 192);
           } else {  // codes, decoded here
             const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
             e4m3x16_to_bf16(*(const v4i*)bp, b[0], b[1]);
@@ -459,11 +473,11 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       for (int c = 0; c < NC; ++c) {
         if constexpr (XH) {  // bf16, in the weight codes' K order (as for XB)
           const int bl = bb < nkh ? bb : bb - nkh;  // K block within the staged part
-          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bl * 256 + 2 * lk;
+          const uint8_t* bp = xs + (c * 16 + lr) * xstride + bl * 256 + lk;
           b[c][0] = *(const v4i*)bp;
-          b[c][1] = *(const v4i*)(bp + 16);
+          b[c][1] = *(const v4i*)(bp + 64);
           b[c][2] = *(const v4i*)(bp + 128);
-          b[c][3] = *(const v4i*)(bp + 144);
+          b[c][3] = *(const v4i*)(bp + 192);
         } else {
           const uint8_t* bp = xs + (c * 16 + lr) * xstride + bb * 128 + lk;
           e4m3x16_to_bf16(*(const v4i*)bp, b[c][0], b[c][1]);
@@ -601,7 +615,7 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
   const int RB = Fg * EB;          // bytes per W_down row
   const int nbb = RB / 128;
   const int hstride_b = a.hstride * EH;
-  const int lstride = Fg * 2 + 16;  // padded LDS row: h as bf16
+  const int lstride = Fg * 2 + kLdsRowPad;  // padded LDS row: h as bf16
   uint8_t* hs = smem;
   float* shs = (float*)(smem + (BM + 1) * lstride);          // [Fg/128][BM] (FP8): one K block's rows adjacent
   float* wrow = shs + (WT == 2 ? BM * (Fg / 128) : 0);       // [BM] routing weight
@@ -699,8 +713,10 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
       if constexpr (HQ) {  // E4M3 codes -> bf16 once per block (exact)
         v4i lo, hi;
         e4m3x16_to_bf16(v[u], lo, hi);
-        *(v4i*)(dst + c * 32) = lo;
-        *(v4i*)(dst + c * 32 + 16) = hi;
+        *(v4i*)(dst + xunit_pos(c)) = lo;
+        *(v4i*)(dst + xunit_pos(c) + 64) = hi;
+      } else if constexpr (WT == 2) {  // bf16 h (W8A16): 8 elements of a unit
+        *(v4i*)(dst + xunit_pos(c >> 1) + 64 * (c & 1)) = v[u];
       } else {
         *(v4i*)(dst + c * 16) = v[u];
       }
@@ -750,9 +766,9 @@ __device__ __forceinline__ void down_block(const ExpertArgs& a, int b, uint8_t* 
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         if constexpr (WT == 2) {
-          const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 256 + 2 * lk;
-          const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 16), *(const v4i*)(bp + 128),
-                            *(const v4i*)(bp + 144)};
+          const uint8_t* bp = hs + (c * 16 + lr) * lstride + bb * 256 + lk;  // xunit_pos layout
+          const v4i b[4] = {*(const v4i*)bp, *(const v4i*)(bp + 64), *(const v4i*)(bp + 128),
+                            *(const v4i*)(bp + 192)};
           // the wave's 16*RT <= 64 rows start at a multiple of 64: one 128-row scale block
           acc[r][c] += kblock_bf16(wd, b) * (shs[bb * BM + c * 16 + lr] * sdp[bb]);
         } else {
@@ -916,7 +932,7 @@ __device__ __forceinline__ bool gateup_block_u4(const ExpertArgs& a, int b, uint
   const int Fg = tr.shared ? a.Fs : a.F;
   if (nb * 128 >= Fg) return false;
   const int d = a.d, nkb = d / 128, ng = d / 64;
-  const int xstride = d * 2 + 16;                     // padded LDS row of bf16 activations
+  const int xstride = d * 2 + kLdsRowPad;             // padded LDS row of bf16 activations
   uint8_t* xs = smem;                                 // [BM + 1][xstride] (a spare row)
   float* xsum = (float*)(smem + (BM + 1) * xstride);  // [d/64][BM] group sums of each row
 
@@ -1084,7 +1100,7 @@ __device__ __forceinline__ void down_block_u4(const ExpertArgs& a, int b, uint8_
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
   const int nkb = Fg / 128, ng = Fg / 64;
-  const int lstride = Fg * 2 + 16;
+  const int lstride = Fg * 2 + kLdsRowPad;
   uint8_t* hs = smem;                                 // [BM + 1][lstride] bf16 h rows
   float* hsum = (float*)(smem + (BM + 1) * lstride);  // [Fg/64][BM] group sums of each row
   float* wrow = hsum + ng * BM;                       // [BM] routing weight
@@ -1493,17 +1509,17 @@ static bool gateup_x_bf16(int BM, int wmode) { return wmode != 2 || BM <= 16; }
 // 4 4-bit groups).
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
   if (wmode == 0) return (size_t)BM * d * 4;
-  if (wmode == 4) return (size_t)(BM + 1) * (d * 2 + 16) + (size_t)(d / 64) * BM * 4;
+  if (wmode == 4) return (size_t)(BM + 1) * (d * 2 + kLdsRowPad) + (size_t)(d / 64) * BM * 4;
   const int xrow = gateup_x_bf16(BM, wmode) ? d * 2 : gateup_x_part_blocks(d / 128) * 256;
-  size_t b = (size_t)(BM + 1) * (xrow + 16);  // plus a spare row
+  size_t b = (size_t)(BM + 1) * (xrow + kLdsRowPad);  // plus a spare row
   if (wmode >= 2) b += 2 * (size_t)BM * (d / 128) * 4;  // scale products
   return b + kGateUpWaves * BM * 4;
 }
 
 size_t down_lds_bytes(int BM, int wmode, int Fg) {
   if (wmode == 0) return (size_t)BM * Fg * 4;
-  if (wmode == 4) return (size_t)(BM + 1) * (Fg * 2 + 16) + (size_t)(Fg / 64) * BM * 4 + BM * 4 + BM * 4;
-  size_t b = (size_t)(BM + 1) * (Fg * 2 + 16);  // h as bf16, plus a spare row
+  if (wmode == 4) return (size_t)(BM + 1) * (Fg * 2 + kLdsRowPad) + (size_t)(Fg / 64) * BM * 4 + BM * 4 + BM * 4;
+  size_t b = (size_t)(BM + 1) * (Fg * 2 + kLdsRowPad);  // h as bf16, plus a spare row
   if (wmode >= 2) b += (size_t)BM * (Fg / 128) * 4 + 2 * (Fg / 128) * 4;
   return b + BM * 4 + BM * 4;
 }
