@@ -1126,9 +1126,21 @@ size_t dispatch_chunk_hist_ints(int T, int k, int E) {
 
 int router_kslice(int d) { return d % 256 == 0 ? 256 : 128; }
 
+#ifndef MOE_SPLIT_ROUTER_MAX_T
+#define MOE_SPLIT_ROUTER_MAX_T 384
+#endif
+// Batches of up to this many tokens use the K-split router whatever their
+// dispatch path: the tiled routers' blocks (64 or more tokens x 64 experts x
+// half of K) would leave most of the chip idle (measured with packed planes:
+// routing 35 -> 30 us at 256 tokens; 36 -> 37 at 512 and 38 -> 48 at 1024,
+// where the split's repeated weight reads cost more).
+constexpr int kSplitRouterMaxT = MOE_SPLIT_ROUTER_MAX_T;
+
+static bool split_router(int T, int k) { return (int64_t)T * k <= kMaxChunkPairs || T <= kSplitRouterMaxT; }
+
 size_t router_part_floats(int T, int k, int d, int E, bool x_bf16) {
   if (!x_bf16) return 0;
-  if ((int64_t)T * k > kMaxChunkPairs) return (size_t)2 * T * E;  // two halves of K
+  if (!split_router(T, k)) return (size_t)2 * T * E;  // two halves of K
   return (size_t)(d / router_kslice(d)) * T * E;
 }
 
@@ -1194,7 +1206,7 @@ hipError_t launch_pack_router(const float* W, void* planes, int d, int E, hipStr
 static hipError_t launch_router(const RouteLaunch& L, hipStream_t st, const float*& part, int& n_parts, int& gs,
                                 float*& logits_out) {
   const bool shortin = (int64_t)L.T * L.k <= kMaxChunkPairs;
-  if (L.x_bf16 && !shortin) {  // tiles over two halves of K
+  if (L.x_bf16 && !split_router(L.T, L.k)) {  // tiles over two halves of K
     const int ksl = router_kslice(L.d), ns = L.d / ksl, halves = ns > 1 ? 2 : 1;
     const dim3 grid((L.T + 63) / 64, (L.E + 63) / 64, halves);
     const uint16_t* x = (const uint16_t*)L.x;
