@@ -174,19 +174,50 @@ __global__ __launch_bounds__(NW * KS * 64) void attention_kernel(AttnArgs a) {
   // row.  V: the thread takes chunk ch = c/64 of two neighbouring keys,
   // 2 (c%32) and 2 (c%32) + 1 with c over the 512 pair slots, so that each
   // 4-byte LDS store of the transposed tile holds one d of both keys.
+  // Each thread's chunks sit at fixed offsets from the tile's first key: the
+  // key within the tile and the 16-byte column are set once, a tile adds a
+  // block-uniform offset, and keys past the range are simply not loaded.
+  // With two key groups (four waves per SIMD, 128 registers) the clamped,
+  // unconditional loads of the first form measured faster (whole-context
+  // chunk 122-126 us against 132); with one group the precomputed,
+  // conditional loads (window chunk 25 against 28-31 us, decode 20.5 against
+  // 22.1).
   v4i kreg[CPT], vreg[CPT];
+  int kkey[CPT], vkey[CPT];
+  const uint16_t *kp[CPT], *vp[CPT];
+  const size_t key_stride = (size_t)a.Hkv * kAttD;  // elements from one key to the next
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int c = tid + u * NT;
+    kkey[u] = c >> 4;
+    kp[u] = a.k + ((size_t)kkey[u] * a.Hkv + kvh) * kAttD + (c & 15) * 8;
+    const int pc = tid + (u >> 1) * NT;  // pair slot
+    vkey[u] = 2 * (pc & 31) + (u & 1);
+    vp[u] = a.v + ((size_t)vkey[u] * a.Hkv + kvh) * kAttD + (pc >> 5) * 8;
+  }
   auto fetch = [&](int tile) {
     const int k0 = k_lo + tile * kAttKT;
+    if constexpr (KS > 1) {
 #pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-      const int c = tid + u * NT;
-      const int kk = k0 + (c >> 4);
-      const size_t ko = ((size_t)min(kk, a.Tk - 1) * a.Hkv + kvh) * kAttD + (c & 15) * 8;
-      kreg[u] = kk < k_hi ? *(const v4i*)(a.k + ko) : v4i{0, 0, 0, 0};
-      const int pc = tid + (u >> 1) * NT;  // pair slot
-      const int kv = k0 + 2 * (pc & 31) + (u & 1);
-      const size_t vo = ((size_t)min(kv, a.Tk - 1) * a.Hkv + kvh) * kAttD + (pc >> 5) * 8;
-      vreg[u] = kv < k_hi ? *(const v4i*)(a.v + vo) : v4i{0, 0, 0, 0};
+      for (int u = 0; u < CPT; ++u) {
+        const int c = tid + u * NT;
+        const int kk = k0 + (c >> 4);
+        const size_t ko = ((size_t)min(kk, a.Tk - 1) * a.Hkv + kvh) * kAttD + (c & 15) * 8;
+        kreg[u] = kk < k_hi ? *(const v4i*)(a.k + ko) : v4i{0, 0, 0, 0};
+        const int pc = tid + (u >> 1) * NT;  // pair slot
+        const int kv = k0 + 2 * (pc & 31) + (u & 1);
+        const size_t vo = ((size_t)min(kv, a.Tk - 1) * a.Hkv + kvh) * kAttD + (pc >> 5) * 8;
+        vreg[u] = kv < k_hi ? *(const v4i*)(a.v + vo) : v4i{0, 0, 0, 0};
+      }
+    } else {
+      const size_t off = (size_t)k0 * key_stride;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        kreg[u] = v4i{0, 0, 0, 0};
+        if (k0 + kkey[u] < k_hi) kreg[u] = *(const v4i*)(kp[u] + off);
+        vreg[u] = v4i{0, 0, 0, 0};
+        if (k0 + vkey[u] < k_hi) vreg[u] = *(const v4i*)(vp[u] + off);
+      }
     }
   };
   auto stage = [&]() {
