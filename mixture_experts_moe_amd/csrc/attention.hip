@@ -292,8 +292,7 @@ __global__ __launch_bounds__(NW * KS * 64) void attention_kernel(AttnArgs a) {
           mx = fmaxf(mx, st[t][v]);
         }
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = max_xor32(max_xor16(mx));
     const float mnew = fmaxf(mrow, mx);
     const float alpha = mnew == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(mrow - mnew);
     const float msub = mnew == -INFINITY ? 0.f : mnew;  // all masked so far: every exp2 is of -inf
@@ -305,8 +304,7 @@ __global__ __launch_bounds__(NW * KS * 64) void attention_kernel(AttnArgs a) {
         st[t][v] = __builtin_amdgcn_exp2f(st[t][v] - msub);
         sum += st[t][v];
       }
-    sum += __shfl_xor(sum, 16, kWave);
-    sum += __shfl_xor(sum, 32, kWave);
+    sum = sum_xor32(sum_xor16(sum));
     lrow = lrow * alpha + sum;
     mrow = mnew;
 #pragma unroll

@@ -533,8 +533,7 @@ __device__ __forceinline__ bool gateup_block(const ExpertArgs& a, int b, uint8_t
       float m = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(h[c][i]));
-      m = fmaxf(m, __shfl_xor(m, 16, kWave));
-      m = fmaxf(m, __shfl_xor(m, 32, kWave));
+      m = max_xor32(max_xor16(m));
       if (lane < 16) red[wave * BM + c * 16 + lane] = m;
     }
     __syncthreads();

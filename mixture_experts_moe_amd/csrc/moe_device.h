@@ -28,6 +28,29 @@ __device__ __forceinline__ float sat448(float v) { return v > 448.0f ? 448.0f : 
 
 // Four fp32 values -> four OCP E4M3 codes (round to nearest even) packed
 // little-endian into one word: byte i holds the code of value i.
+// x combined with the x of lane ^ 16 (or lane ^ 32) through gfx950's lane-swap
+// instructions (v_permlane16_swap / v_permlane32_swap: a register swaps its odd
+// 16-lane rows, or its upper 32 lanes, with another's), instead of an LDS
+// permute.  Called with the value in both operands, the two results hold, in
+// every lane, x of the lane and of its partner (in either order); max and sum
+// are commutative, so the result is bitwise that of op(x, shfl_xor(x, 16/32)).
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), w, true);
