@@ -1337,76 +1337,117 @@ __global__ __launch_bounds__(kGateUpWaves * 64) void experts_fused_kernel(Expert
 
 // ---------------------------------------------------------------------------
 // fp32 expert projections (fp32 activations and weights): plain fp32
-// multiply-add, one output feature per thread.  blockIdx.x = 64-feature slice.
+// multiply-add, one output feature per thread, each sum a single chain over
+// the input columns in order.  blockIdx.x = 64-feature slice.  The inputs go
+// through LDS in chunks of kF32Chunk columns: the tile's rows (zeros past the
+// live rows) and the slice's 64 weight rows, read with 16-byte loads where 16
+// threads cover a row's chunk; weight rows padded to kF32Chunk + 1 floats so
+// that 64 lanes reading one column of 64 rows hit distinct banks.  Thread
+// (feature f, row group g) takes rows g, g + 4, g + 8, g + 12.
 // ---------------------------------------------------------------------------
+constexpr int kF32Chunk = 64;
+
 template <int BM>
 __global__ __launch_bounds__(256) void gateup_f32_kernel(ExpertArgs a) {
+  static_assert(BM == 16, "four rows per thread");
   int sl;
   const TileRows tr = block_rows(a, blockIdx.x, sl);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int f = sl * 64 + (threadIdx.x & 63);
   if (sl * 64 >= Fg) return;
-  extern __shared__ __align__(16) uint8_t smem[];
-  float* xs = (float*)smem;  // [BM][d]
-  const int tid = threadIdx.x;
+  __shared__ __align__(16) float xs[BM][kF32Chunk];
+  __shared__ float gs[64][kF32Chunk + 1], us[64][kF32Chunk + 1];
+  const int tid = threadIdx.x, fl = tid & 63, rg = tid >> 6, f = sl * 64 + fl;
   const float* x = (const float*)a.xa;
-  for (int i = tid; i < BM * a.d; i += 256) {
-    const int r = i / a.d, c = i - r * a.d;
-    float v = 0.f;
-    if (r < tr.rows) {
-      const int t = tr.shared ? tr.m0 + r : a.perm[tr.hrow0 + r] / a.k;
-      v = x[(size_t)t * a.d + c];
-    }
-    xs[i] = v;
-  }
-  __syncthreads();
-  if (f >= Fg) return;
   const size_t wsz = (size_t)a.F * a.d;
-  const float* wg = (tr.shared ? (const float*)a.shg : (const float*)a.wg + tr.g * wsz) + (size_t)f * a.d;
-  const float* wu = (tr.shared ? (const float*)a.shu : (const float*)a.wu + tr.g * wsz) + (size_t)f * a.d;
-  const int hrow0 = tr.hrow0;
-  for (int r = tid >> 6; r < tr.rows; r += 4) {
-    float g = 0.f, u = 0.f;
-    for (int c = 0; c < a.d; ++c) {
-      g = fmaf(wg[c], xs[r * a.d + c], g);
-      u = fmaf(wu[c], xs[r * a.d + c], u);
+  const float* wg = tr.shared ? (const float*)a.shg : (const float*)a.wg + tr.g * wsz;
+  const float* wu = tr.shared ? (const float*)a.shu : (const float*)a.wu + tr.g * wsz;
+  // this thread's staging slots: x row tid / 16 (one per thread), weight rows
+  // tid / 16 + 16 j, each 4 floats at column 4 * (tid % 16)
+  const int sr = tid >> 4, sc = 4 * (tid & 15);
+  int tok = -1;
+  if (sr < tr.rows) tok = tr.shared ? tr.m0 + sr : a.perm[tr.hrow0 + sr] / a.k;
+  float g[4] = {0.f, 0.f, 0.f, 0.f}, u[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < a.d; k0 += kF32Chunk) {
+    __syncthreads();  // the previous chunk's reads are done
+    *(float4*)&xs[sr][sc] = tok >= 0 ? *(const float4*)(x + (size_t)tok * a.d + k0 + sc) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int fr = min(sl * 64 + sr + 16 * j, Fg - 1);  // rows past the matrix: a clamped copy, never stored
+      const float4 vg = *(const float4*)(wg + (size_t)fr * a.d + k0 + sc);
+      const float4 vu = *(const float4*)(wu + (size_t)fr * a.d + k0 + sc);
+      float* dg = &gs[sr + 16 * j][sc];
+      float* du = &us[sr + 16 * j][sc];
+      dg[0] = vg.x; dg[1] = vg.y; dg[2] = vg.z; dg[3] = vg.w;
+      du[0] = vu.x; du[1] = vu.y; du[2] = vu.z; du[3] = vu.w;
     }
-    ((float*)a.h)[(size_t)(hrow0 + r) * a.hstride + f] = g / (1.0f + expf(-g)) * u;
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < kF32Chunk; ++c) {
+      const float wgv = gs[fl][c], wuv = us[fl][c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        g[i] = fmaf(wgv, xs[rg + 4 * i][c], g[i]);
+        u[i] = fmaf(wuv, xs[rg + 4 * i][c], u[i]);
+      }
+    }
+  }
+  if (f >= Fg) return;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = rg + 4 * i;
+    if (r < tr.rows) ((float*)a.h)[(size_t)(tr.hrow0 + r) * a.hstride + f] = g[i] / (1.0f + expf(-g[i])) * u[i];
   }
 }
 
 template <int BM>
 __global__ __launch_bounds__(256) void down_f32_kernel(ExpertArgs a) {
+  static_assert(BM == 16, "four rows per thread");
   int sl;
   const TileRows tr = block_rows(a, blockIdx.x, sl);
   if (tr.g < 0) return;
   const int Fg = tr.shared ? a.Fs : a.F;
-  const int n = sl * 64 + (threadIdx.x & 63);
-  extern __shared__ __align__(16) uint8_t smem[];
-  float* hs = (float*)smem;  // [BM][Fg]
-  const int tid = threadIdx.x;
-  const int hrow0 = tr.hrow0;
-  for (int i = tid; i < BM * Fg; i += 256) {
-    const int r = i / Fg, c = i - r * Fg;
-    hs[i] = r < tr.rows ? ((const float*)a.h)[(size_t)(hrow0 + r) * a.hstride + c] : 0.f;
+  if (sl * 64 >= a.d) return;
+  __shared__ __align__(16) float hs[BM][kF32Chunk];
+  __shared__ float ws[64][kF32Chunk + 1];
+  const int tid = threadIdx.x, nl = tid & 63, rg = tid >> 6, n = sl * 64 + nl;
+  const float* wd = tr.shared ? (const float*)a.shd : (const float*)a.wd + tr.g * (size_t)a.d * Fg;
+  const int sr = tid >> 4, sc = 4 * (tid & 15);
+  const float* hrow = sr < tr.rows ? (const float*)a.h + (size_t)(tr.hrow0 + sr) * a.hstride : nullptr;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k0 = 0; k0 < Fg; k0 += kF32Chunk) {
+    __syncthreads();
+    *(float4*)&hs[sr][sc] = hrow ? *(const float4*)(hrow + k0 + sc) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nr = min(sl * 64 + sr + 16 * j, a.d - 1);
+      const float4 v = *(const float4*)(wd + (size_t)nr * Fg + k0 + sc);
+      float* dst = &ws[sr + 16 * j][sc];
+      dst[0] = v.x; dst[1] = v.y; dst[2] = v.z; dst[3] = v.w;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int c = 0; c < kF32Chunk; ++c) {
+      const float w = ws[nl][c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, hs[rg + 4 * i][c], acc[i]);
+    }
   }
-  __syncthreads();
   if (n >= a.d) return;
-  const float* wd = (tr.shared ? (const float*)a.shd : (const float*)a.wd + tr.g * (size_t)a.d * Fg) + (size_t)n * Fg;
-  for (int r = tid >> 6; r < tr.rows; r += 4) {
-    float acc = 0.f;
-    for (int c = 0; c < Fg; ++c) acc = fmaf(wd[c], hs[r * Fg + c], acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = rg + 4 * i;
+    if (r >= tr.rows) continue;
     int o;
     float w;
     if (tr.shared) {
       o = a.P + tr.m0 + r;
       w = 1.f;
     } else {
-      o = a.perm[hrow0 + r];
+      o = a.perm[tr.hrow0 + r];
       w = a.topk_w[o];
     }
-    a.part[(size_t)o * a.d + n] = acc * w;
+    a.part[(size_t)o * a.d + n] = acc[i] * w;
   }
 }
 
@@ -1507,7 +1548,7 @@ static bool gateup_x_bf16(int BM, int wmode) { return wmode != 2 || BM <= 16; }
 // wmode: the moe_dtype of the weights (0 f32, 1 bf16, 2 FP8, 3 FP8 as W8A16,
 // 4 4-bit groups).
 size_t gateup_lds_bytes(int BM, int wmode, int d) {
-  if (wmode == 0) return (size_t)BM * d * 4;
+  if (wmode == 0) return 1;  // static LDS only
   if (wmode == 4) return (size_t)(BM + 1) * (d * 2 + kLdsRowPad) + (size_t)(d / 64) * BM * 4;
   const int xrow = gateup_x_bf16(BM, wmode) ? d * 2 : gateup_x_part_blocks(d / 128) * 256;
   size_t b = (size_t)(BM + 1) * (xrow + kLdsRowPad);  // plus a spare row
@@ -1516,7 +1557,7 @@ size_t gateup_lds_bytes(int BM, int wmode, int d) {
 }
 
 size_t down_lds_bytes(int BM, int wmode, int Fg) {
-  if (wmode == 0) return (size_t)BM * Fg * 4;
+  if (wmode == 0) return 1;  // static LDS only
   if (wmode == 4) return (size_t)(BM + 1) * (Fg * 2 + kLdsRowPad) + (size_t)(Fg / 64) * BM * 4 + BM * 4 + BM * 4;
   size_t b = (size_t)(BM + 1) * (Fg * 2 + kLdsRowPad);  // h as bf16, plus a spare row
   if (wmode >= 2) b += (size_t)BM * (Fg / 128) * 4 + 2 * (Fg / 128) * 4;

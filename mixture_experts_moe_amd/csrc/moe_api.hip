@@ -115,6 +115,7 @@ int validate_shape(const moe_shape* s) {
   if (s->d_model % 128 || s->d_ffn % 128 || s->d_ffn_shared % 128) return MOE_ERR_UNSUPPORTED;
   if (s->d_model > 8192 || s->d_ffn > 4096 || s->d_ffn_shared > 4096) return MOE_ERR_UNSUPPORTED;
   const int Fmax = s->d_ffn > s->d_ffn_shared ? s->d_ffn : s->d_ffn_shared;
+  if (s->w_dtype == MOE_F32 && (s->d_model > 2560 || Fmax > 2560)) return MOE_ERR_UNSUPPORTED;  // documented limit
   if (moe::gateup_lds_bytes(16, s->w_dtype, s->d_model) > kMaxLds) return MOE_ERR_UNSUPPORTED;
   if (moe::down_lds_bytes(16, s->w_dtype, Fmax) > kMaxLds) return MOE_ERR_UNSUPPORTED;
   if (max_tiles_for(*s, 16) * (s->d_model / 64 + Fmax / 64 + 16) > INT_MAX / 2) return MOE_ERR_UNSUPPORTED;
@@ -331,6 +332,9 @@ int forward_common(const moe_shape* shape, const moe_weights* w, const void* x, 
   if (scaled && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
   if (has_shared && (!w->sh_gate || !w->sh_up || !w->sh_down)) return MOE_ERR_INVALID_ARG;
   if (has_shared && scaled && (!w->ss_gate || !w->ss_up || !w->ss_down)) return MOE_ERR_INVALID_ARG;
+  if (misaligned(w->w_gate) || misaligned(w->w_up) || misaligned(w->w_down)) return MOE_ERR_INVALID_ARG;
+  if (has_shared && (misaligned(w->sh_gate) || misaligned(w->sh_up) || misaligned(w->sh_down)))
+    return MOE_ERR_INVALID_ARG;
   if (shape->T == 0) return MOE_OK;
   const Layout L = layout(*shape, noalloc);
   if (noalloc) {
