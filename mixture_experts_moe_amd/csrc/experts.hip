@@ -48,12 +48,6 @@ namespace moe {
 // -4.5 us per launch.  Taller tiles (XCD schedules) read an expert's weights
 // once per row tile and rely on L2 keeping them between the tiles, so they use
 // ordinary loads.
-// A compile-time integer as a value (register-slot and run selectors).
-template <int N>
-struct Ic {
-  static constexpr int value = N;
-};
-
 template <bool NT>
 __device__ __forceinline__ v4i stream_load(const uint8_t* p) {
   if constexpr (NT) return __builtin_nontemporal_load((const v4i*)p);

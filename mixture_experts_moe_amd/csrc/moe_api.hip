@@ -210,7 +210,7 @@ int route_common(const moe_shape* shape, const moe_weights* w, const void* x, co
   int rc = validate_shape(shape);
   if (rc != MOE_OK) return rc;
   if (!w || !w->w_router || !x || check_routing_out(out) != MOE_OK) return MOE_ERR_INVALID_ARG;
-  if (misaligned(x) || misaligned(w->w_router_planes)) return MOE_ERR_INVALID_ARG;
+  if (misaligned(x) || misaligned(w->w_router) || misaligned(w->w_router_planes)) return MOE_ERR_INVALID_ARG;
   if (shape->T == 0) return MOE_OK;
   if (!ws) return MOE_ERR_INVALID_ARG;
   const Layout L = layout(*shape);

@@ -87,6 +87,12 @@ __device__ __forceinline__ float silu_f32(float g) {
   return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.44269504088896341f));
 }
 
+// A compile-time integer as a value (register-slot and run selectors).
+template <int N>
+struct Ic {
+  static constexpr int value = N;
+};
+
 // Maximum of an unsigned value over the 64 lanes of a wave, returned to every
 // lane.  DPP row shifts build each 16-lane row's maximum in its lane 15, two
 // row broadcasts carry it to lane 63, and readlane returns it; lanes whose DPP

@@ -601,49 +601,89 @@ __global__ __launch_bounds__(256, MOE_RP_MINB) void router_planes_kernel(const u
 }
 
 // ---------------------------------------------------------------------------
-// Router logits for fp32 activations: plain fp32 multiply-add, LDS-tiled; tiles
-// of TT tokens x TE experts, each of the 256 threads owning a (TT/16) x (TE/16)
-// register tile.
+// Router logits for fp32 activations: plain fp32 multiply-add, each logit one
+// chain over the columns in order; tiles of TT tokens x TE experts, each of
+// the 256 threads owning a (TT/16) x (TE/16) register tile.  The inputs go
+// through LDS (transposed, padded) in chunks of 64 columns, read from memory
+// with 16-byte loads two chunks ahead, so that a launch of few blocks (short
+// batches) waits for about one memory round trip instead of one per chunk.
 // ---------------------------------------------------------------------------
 template <int TT, int TE>
 __global__ __launch_bounds__(256) void router_f32_kernel(const float* __restrict__ x, const float* __restrict__ W,
                                                           float* __restrict__ logits, int T, int d, int E,
                                                           int32_t* __restrict__ status) {
-  constexpr int KC = 32, MT = TT / 16, ME = TE / 16;
+  constexpr int KC = 64, MT = TT / 16, ME = TE / 16;
+  constexpr int XV = TT * KC / 4 / 256, WV = TE * KC / 4 / 256;  // 16-byte loads per thread and chunk
+  static_assert(XV >= 1 && WV >= 1, "every thread loads a piece of both tiles");
   __shared__ float xs[KC][TT + 1];
   __shared__ float ws[KC][TE + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int t0 = blockIdx.x * TT, e0 = blockIdx.y * TE;
   if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *status = 0;
+  // piece u of a chunk: row i / 16, columns 4 (i % 16) + [0, 4), i = tid + 256 u
+  float4 xr[2][XV], wr[2][WV];
+  auto load = [&](auto B, int k0) {
+    constexpr int b = decltype(B)::value;
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+      const int i = tid + 256 * u, t = t0 + (i >> 4);
+      xr[b][u] = t < T ? *(const float4*)(x + (size_t)t * d + k0 + 4 * (i & 15)) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < WV; ++u) {
+      const int i = tid + 256 * u, e = e0 + (i >> 4);
+      wr[b][u] = e < E ? *(const float4*)(W + (size_t)e * d + k0 + 4 * (i & 15)) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
   float acc[MT][ME];
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll
     for (int j = 0; j < ME; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < d; k0 += KC) {
-    for (int i = tid; i < TT * KC; i += 256) {
-      const int r = i / KC, c = i % KC, t = t0 + r;
-      xs[c][r] = t < T ? x[(size_t)t * d + k0 + c] : 0.f;
+  const int nk = d / KC;
+  // chunk kc: its registers to LDS, the loads of chunk kc + 2 issued, products
+  auto step = [&](auto B, int kc) {
+    constexpr int b = decltype(B)::value;
+    __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+    for (int u = 0; u < XV; ++u) {
+      const int i = tid + 256 * u, r = i >> 4, c = 4 * (i & 15);
+      xs[c][r] = xr[b][u].x;
+      xs[c + 1][r] = xr[b][u].y;
+      xs[c + 2][r] = xr[b][u].z;
+      xs[c + 3][r] = xr[b][u].w;
     }
-    for (int i = tid; i < TE * KC; i += 256) {
-      const int r = i / KC, c = i % KC, e = e0 + r;
-      ws[c][r] = e < E ? W[(size_t)e * d + k0 + c] : 0.f;
+#pragma unroll
+    for (int u = 0; u < WV; ++u) {
+      const int i = tid + 256 * u, r = i >> 4, c = 4 * (i & 15);
+      ws[c][r] = wr[b][u].x;
+      ws[c + 1][r] = wr[b][u].y;
+      ws[c + 2][r] = wr[b][u].z;
+      ws[c + 3][r] = wr[b][u].w;
     }
     __syncthreads();
+    if (kc + 2 < nk) load(B, (kc + 2) * KC);
 #pragma unroll 8
     for (int k = 0; k < KC; ++k) {
-      float a[MT], b[ME];
+      float a[MT], bb[ME];
 #pragma unroll
       for (int i = 0; i < MT; ++i) a[i] = xs[k][ty + 16 * i];
 #pragma unroll
-      for (int j = 0; j < ME; ++j) b[j] = ws[k][tx + 16 * j];
+      for (int j = 0; j < ME; ++j) bb[j] = ws[k][tx + 16 * j];
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < ME; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < ME; ++j) acc[i][j] = fmaf(a[i], bb[j], acc[i][j]);
     }
-    __syncthreads();
+  };
+  load(Ic<0>{}, 0);
+  if (nk > 1) load(Ic<1>{}, KC);
+  int kc = 0;
+  for (; kc + 1 < nk; kc += 2) {
+    step(Ic<0>{}, kc);
+    step(Ic<1>{}, kc + 1);
   }
+  if (kc < nk) step(Ic<0>{}, kc);
 #pragma unroll
   for (int i = 0; i < MT; ++i)
 #pragma unroll

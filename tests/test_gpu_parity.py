@@ -192,6 +192,38 @@ def test_tiny_free_and_forced():
     assert r < 1e-4  # all-fp32 path: only summation order differs
 
 
+def test_tiny_f32_long_batch():
+    """The fp32 layer at T=700: 1,400 pairs take the long-batch router tiles and
+    the chunked top-k and dispatch, and the expert tiles end in ragged tails.
+    Free and forced routing against the oracle; the first 64 tokens' logits,
+    ids and outputs equal the 64-token batch's bit for bit (every fp32 logit
+    and output is one chain in a fixed order, whatever the batch)."""
+    big = synth.make_inputs("tiny_f32", T=700)
+    s = big["shape"]
+    say(f"tiny_f32 T={s.T} d={s.d} E={s.E} k={s.k} free")
+    L = O.Layer(big)
+    _, lg, idx, w = O.route(L)
+    g = run_gpu(big)
+    check_logits(g["logits"], lg)
+    bad, ex = route_agreement(g["topk_idx"], idx, selection_scores(big, lg), s.k)
+    assert bad == 0 and ex <= 8
+    same = (g["topk_idx"] == idx).all(axis=1)
+    _, acc_ref = O.forward(L, idx, w)
+    check_y(g["y"][same], acc_ref[same])
+    say("tiny_f32 T=700 forced from the oracle's recorded ids")
+    gf = run_gpu(big, forced=idx)
+    assert np.array_equal(gf["topk_idx"], idx)
+    check_dispatch(gf, idx, s.E)
+    assert check_y(gf["y"], acc_ref) < 1e-4
+    say("tiny_f32: the first 64 tokens alone")
+    small = synth.make_inputs("tiny_f32")
+    assert small["shape"].T == 64 and np.array_equal(small["x"], big["x"][:64])
+    gs = run_gpu(small)
+    assert np.array_equal(gs["logits"].view(np.uint32), g["logits"][:64].view(np.uint32))
+    assert np.array_equal(gs["topk_idx"], g["topk_idx"][:64])
+    assert np.array_equal(gs["y"].view(np.uint32), g["y"][:64].view(np.uint32))
+
+
 # ------------------------------------------------------------------ decode shape, FP8 experts
 
 def test_decode_free():
