@@ -381,20 +381,28 @@ __global__ __launch_bounds__(NW * KS * 64) void attention_kernel(AttnArgs a) {
   }
 }
 
-// Merge the splits of one (query, head) row: one block per row.  The
-// splits' maxima and weights first (threads over splits, fixed-order
-// reductions), then thread t sums output elements 2 (t % 64) .. +1 over the
-// splits s = t / 64 (mod 4), loads unrolled so many are in flight; the four
-// partial sums are added in a fixed order.
+// Merge the splits of one (query, head) row: one block per row, one memory
+// round trip per phase.  Thread t holds the (max, sum) pairs of splits t and
+// t + 256 (fixed-order reductions give the row's maximum M and weighted sum
+// L, each split weighted by 2^(m_s - M)); then thread t sums output elements
+// 4 (t % 32) .. +3 over the splits s = t / 32 (mod 8), sixteen loads issued
+// before the first is used, and the eight partial sums are added in a fixed
+// order.
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
+  static_assert(kAttSplitMax <= 512 && kAttD == 128, "two splits per thread, 32 x 4 output elements");
   __shared__ float wsh[kAttSplitMax];
   __shared__ float red[4];
-  __shared__ float2 osum[4][64];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float4 osum[8][32];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = a.n_split;
   const int64_t rows = (int64_t)a.Tq * a.Hq;
   const int64_t r = blockIdx.x;
-  float M = -INFINITY;
-  for (int s = tid; s < a.n_split; s += 256) M = fmaxf(M, a.part_ml[((size_t)s * rows + r) * 2]);
+  float2 ml[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sp = tid + 256 * u;
+    ml[u] = sp < n ? *(const float2*)(a.part_ml + ((size_t)sp * rows + r) * 2) : make_float2(-INFINITY, 0.f);
+  }
+  float M = fmaxf(ml[0].x, ml[1].x);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, kWave));
   if (lane == 0) red[wave] = M;
@@ -402,32 +410,49 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   float L = 0.f;
-  for (int s = tid; s < a.n_split; s += 256) {
-    const float2 ml = *(const float2*)(a.part_ml + ((size_t)s * rows + r) * 2);
-    const float w = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-    wsh[s] = w;
-    L += ml.y * w;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int sp = tid + 256 * u;
+    const float w = ml[u].x == -INFINITY ? 0.f : exp2f(ml[u].x - M);
+    if (sp < n) wsh[sp] = w;
+    L += ml[u].y * w;
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, kWave);
   if (lane == 0) red[wave] = L;
   __syncthreads();
   L = (red[0] + red[1]) + (red[2] + red[3]);
-  float2 acc = make_float2(0.f, 0.f);
-#pragma unroll 8
-  for (int s = wave; s < a.n_split; s += 4) {
-    const float w = wsh[s];
-    const float2 o = *(const float2*)(a.part_o + ((size_t)s * rows + r) * kAttD + 2 * lane);
-    acc.x += o.x * w;
-    acc.y += o.y * w;
+  const int g = tid >> 5, c = tid & 31;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  constexpr int NB = 16;  // loads in flight per thread: splits g + 8 i, i < NB, per batch
+  for (int s0 = g; s0 < n; s0 += 8 * NB) {
+    float4 o[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)  // clamped to the last split: unconditional, all issued first
+      o[i] = *(const float4*)(a.part_o + ((size_t)min(s0 + 8 * i, n - 1) * rows + r) * kAttD + 4 * c);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const float w = s0 + 8 * i < n ? wsh[s0 + 8 * i] : 0.f;
+      acc.x += o[i].x * w;
+      acc.y += o[i].y * w;
+      acc.z += o[i].z * w;
+      acc.w += o[i].w * w;
+    }
   }
-  osum[wave][lane] = acc;
+  osum[g][c] = acc;
   __syncthreads();
-  if (wave == 0) {
+  if (tid < 32) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    const float x = ((osum[0][lane].x + osum[1][lane].x) + (osum[2][lane].x + osum[3][lane].x)) * inv;
-    const float y = ((osum[0][lane].y + osum[1][lane].y) + (osum[2][lane].y + osum[3][lane].y)) * inv;
-    *(uint32_t*)(a.o + r * kAttD + 2 * lane) = bf16x2(x, y);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      auto e = [&](int gg) { return ((const float*)&osum[gg][c])[i]; };
+      v[i] = (((e(0) + e(1)) + (e(2) + e(3))) + ((e(4) + e(5)) + (e(6) + e(7)))) * inv;
+    }
+    uint2 pk;
+    pk.x = bf16x2(v[0], v[1]);
+    pk.y = bf16x2(v[2], v[3]);
+    *(uint2*)(a.o + r * kAttD + 4 * c) = pk;
   }
 }
 

@@ -100,6 +100,8 @@ def _check_attention(Hq, Hkv, window, Tq, Tk, q_pos0, rows=None, seed=0):
     (16, 4, W, 37, 37, 0),          # start of a sequence: ragged block, windows clipped at 0
     (16, 4, 0, 128, 640, 512),      # whole context, prefill chunk
     (16, 4, 0, 1, 4096, 4095),      # whole-context decode: keys split over blocks
+    (16, 4, 0, 1, 4196, 4195),      # 66 splits, not a multiple of the merge's eight split groups
+    (16, 1, 0, 1, 32768, 32767),    # one key/value head: 512 splits, two per merge thread
     (16, 4, W, 3, 2000, 1997),      # sliding-window decode of three tokens
     (8, 8, W, 100, 700, 600),       # one query head per key/value head (64 queries a block)
     (32, 2, 0, 20, 300, 280),       # groups of 16 heads (4 queries a block)
