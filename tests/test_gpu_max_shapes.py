@@ -10,6 +10,7 @@ C ABI, against the oracle with the parity bars of the main workloads.
   * the most experts and the largest top_k (512 experts, top 8: eight candidates
     per lane in the selection), with the one-block dispatch (800 pairs) and the
     chunked one (2,400 pairs), free and forced;
+  * the widest fp32 layer (d_model and d_ffn 2560), short and long batches;
   * the longest batch timed by the bench: the decode layer at T = 32768 with
     free routing (128-token router blocks, 32-row tiles, about 16 per expert),
     the dispatch checked whole and the outputs on sampled tokens.
@@ -79,7 +80,34 @@ def _check(inp, g, forced=None, n_sample=None):
     assert np.array_equal(idf, ids)
     assert np.max(np.abs(g["topk_w"][tok] - wf)) <= W_ABS
     _, acc_ref = O.forward(L, idf, wf, tok)
-    check_y(g["y"][tok], acc_ref)
+    return check_y(g["y"][tok], acc_ref)
+
+
+def _f32_layer(T, d, E, k, F, Fs, seed):
+    """An all-fp32 layer: activations N(0, 1), router N(0, 0.05), expert and
+    shared weights N(0, 0.02)."""
+    rng = np.random.default_rng(seed)
+    inp = dict(shape=synth.LayerShape(T=T, d=d, E=E, k=k, F=F, Fs=Fs, act="f32", w="f32"),
+               x=rng.standard_normal((T, d), dtype=np.float32),
+               w_router=rng.standard_normal((E, d), dtype=np.float32) * np.float32(0.05), sel_bias=None)
+    for key, shp in (("w_gate", (E, F, d)), ("w_up", (E, F, d)), ("w_down", (E, d, F)),
+                     ("sh_gate", (Fs, d)), ("sh_up", (Fs, d)), ("sh_down", (d, Fs))):
+        inp[key] = rng.standard_normal(shp, dtype=np.float32) * np.float32(0.02)
+    return inp
+
+
+@pytest.mark.parametrize("T", [40, 600])
+def test_widest_f32_layer(T):
+    """The widest fp32 layer (d_model and d_ffn 2560, the fp32 limit): 40 tokens
+    (the short-batch router, ragged 16-row tiles) and 600 tokens (the long-batch
+    router tiles and chunked top-k; sampled outputs).  All-fp32 arithmetic, so
+    the outputs sit within 1e-4 of the oracle's RMS (only summation order
+    differs)."""
+    d, E, k, F = 2560, 4, 2, 2560
+    inp = _f32_layer(T, d, E, k, F, F, seed=17)
+    say(f"widest f32 layer T={T} d={d} E={E} k={k} F=Fs={F}")
+    g = run_gpu(inp, dev=_dev(inp))
+    assert _check(inp, g, n_sample=None if T <= 40 else 8) < 1e-4
 
 
 @pytest.mark.parametrize("w", ["fp8", "fp8a16", "u4"])
