@@ -226,6 +226,28 @@ def test_misaligned_activations_rejected():
             moe.MOE_ERR_INVALID_ARG
 
 
+def test_misaligned_weights_rejected():
+    """Expert, shared-expert and router weights are read 16 bytes per lane: a
+    pointer that is 8- but not 16-byte aligned is rejected before any launch
+    (the shared pointers only when the layer has a shared expert)."""
+    good = moe.make_shape(32, 2048, 384, 6, 640, 640)
+    for field in ("w_gate", "w_up", "w_down", "sh_gate", "sh_up", "sh_down"):
+        w = _weights_struct()
+        setattr(w, field, 0x3008)
+        assert _forward(good, w=w) == moe.MOE_ERR_INVALID_ARG, field
+    w = _weights_struct()
+    w.w_router = 0x3008
+    assert _route(good, w=w) == moe.MOE_ERR_INVALID_ARG
+    f32 = moe.make_shape(64, 256, 16, 2, 128, 128, act="f32", w="f32")
+    w = _weights_struct()
+    w.w_down = 0x3004
+    assert _forward(f32, w=w) == moe.MOE_ERR_INVALID_ARG
+    noshared = moe.make_shape(0, 2048, 384, 6, 640, 0)
+    w = _weights_struct()
+    w.sh_gate = 0x3008
+    assert _forward(noshared, w=w) == moe.MOE_OK  # T = 0, and no shared expert to check
+
+
 def test_pack_weights_host_validation():
     L = _lib()
     buf = (C.c_uint8 * 8192)()
